@@ -1,0 +1,138 @@
+/*
+ * i2s.h - C ABI of the gfx950 (MI355X) library for the I2_S ternary-weight x
+ * int8-activation matmul (W2A8).
+ *
+ * The op, as the pages define it:
+ *   "ggml-cpu: ternary I2_S matmul kernel (VibeASR, 3/4)", section Interface:
+ *     a plain matmul of an I2_S weight (src0) with F32 activations (src1),
+ *     giving F32 out;
+ *   same page, section Arithmetic: the codes {0,1,2} stand for {-1,0,+1}; the
+ *     kernel accumulates sum(code*q) in int32 and the epilogue computes
+ *     dst = (float)(dot - row_sum) * (weight_scale * act_scale), with both
+ *     scales multipliers (amax/127 for activations, the weight absmax for
+ *     I2_S);
+ *   "ggml: additive INT8/ternary types, fused CPU ops, and kernels for VibeASR
+ *     (1/2)", section Two new types: I2_S holds 128 values per 32-byte group,
+ *     then one padded F32 absmax in band, after the payload;
+ *   same page, section Kernels: byte gp of a group holds the group-relative
+ *     positions gp, 32+gp, 64+gp, 96+gp in the bit pairs at shifts 6/4/2/0;
+ *   "VibeASR in audio.cpp", Architecture / Decoder: packed over the whole flat
+ *     tensor; the kernel asserts K % 128 == 0;
+ *   "VibeASR in audio.cpp", Architecture / Encoder: amax floored at 1e-5.
+ * Activation rounding is half away from zero with a clamp to +-127.
+ *
+ * Conventions shared by every call:
+ *   - Every data pointer is a DEVICE pointer (hipMalloc'd or a device tensor's
+ *     storage) owned by the caller; the library never keeps, frees or
+ *     allocates them.  Arrays are dense and row-major as stated per argument.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns without synchronizing.
+ *   - Arguments are checked on the host before anything is launched; a bad
+ *     argument returns a nonzero status and launches nothing.  Faults inside
+ *     a kernel surface at the caller's next synchronization on that stream.
+ *   - N == 0 or rows == 0 is a successful no-op.
+ *   - Calls are stateless and may be made from several host threads.
+ *   - Results are bit-identical to the defining formulas above: integer steps
+ *     are exact and the three F32 operations (x / s, ws * s, and the final
+ *     multiply) are single IEEE round-to-nearest operations in a fixed order.
+ */
+#ifndef I2S_H
+#define I2S_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define I2S_OK 0
+#define I2S_EINVAL 1     /* null pointer where one is needed, or a negative size */
+#define I2S_EALIGN 2     /* K is not a positive multiple of 128 */
+#define I2S_EWORKSPACE 3 /* workspace NULL or smaller than i2s_act_workspace_bytes */
+#define I2S_EHIP 4       /* the HIP runtime reported an error at launch */
+#define I2S_ERANGE 5     /* a size beyond what this library addresses */
+#define I2S_EKERNEL 6    /* i2s_mul_mat_ex: unknown kernel or variant, or one
+                            that does not accept this N */
+
+/* Bytes of an I2_S tensor of `rows` x `K` weights: rows*K/4 bytes of 2-bit
+ * codes, then a 32-byte slot whose first 4 bytes are the F32 weight scale
+ * (little-endian) and whose other 28 bytes are zero.  0 if K is not a positive
+ * multiple of 128 or rows < 0.
+ * ("ggml: additive INT8/ternary types, ... (1/2)", Two new types.) */
+size_t i2s_packed_bytes(int64_t rows, int64_t K);
+
+/* Bytes of the activation workspace i2s_mul_mat needs for N rows of length K:
+ * the int8 activations, then N F32 activation scales, then N int32 row sums
+ * (the sidecar of "ggml-cpu: ternary I2_S matmul kernel (VibeASR, 3/4)",
+ * Interface).  The layout inside is private to the library.  0 if K is not a
+ * positive multiple of 128 or N < 0. */
+size_t i2s_act_workspace_bytes(int64_t N, int64_t K);
+
+/* Pack ternary weights into I2_S.
+ *   w            [rows][K] int8, values in {-1,0,+1}; any other value packs
+ *                by its sign (code = sign(w) + 1).
+ *   weight_scale F32 multiplier stored in band (the weight absmax; 0 allowed).
+ *   packed       [i2s_packed_bytes(rows, K)] bytes, fully overwritten
+ *                (payload, scale, and the 28 zero padding bytes).
+ * Errors: I2S_EINVAL (null pointer, rows < 0), I2S_EALIGN, I2S_ERANGE,
+ * I2S_EHIP.  ("ggml: additive INT8/ternary types, ... (1/2)", Two new types
+ * and Kernels; "VibeASR in audio.cpp", Architecture / Decoder.) */
+int i2s_pack(const int8_t *w, float weight_scale, int64_t rows, int64_t K,
+             uint8_t *packed, void *stream);
+
+/* Quantize F32 activation rows to int8, one scale and one int8 sum per row:
+ *   amax = max_k |x[n][k]|, floored at 1e-5f;  act_scale[n] = amax / 127;
+ *   q[n][k] = clamp(round_half_away(x[n][k] / act_scale[n]), -127, 127);
+ *   row_sum[n] = sum_k q[n][k].
+ *   x         [N][K] F32, finite values (NaN/Inf are not supported).
+ *   q         [N][K] int8 (plain row-major order).
+ *   act_scale [N] F32;  row_sum [N] int32.
+ * Errors: I2S_EINVAL, I2S_EALIGN, I2S_ERANGE, I2S_EHIP.
+ * ("ggml-cpu: ternary I2_S matmul kernel (VibeASR, 3/4)", Arithmetic and
+ * Kernels/threading: a row is never split because its absmax is row-wide.) */
+int i2s_quantize_act(const float *x, int64_t N, int64_t K,
+                     int8_t *q, float *act_scale, int32_t *row_sum, void *stream);
+
+/* The matmul: y[n][o] = (float)(dot[n][o] - row_sum[n]) * (ws * act_scale[n])
+ * with dot[n][o] = sum_k code[o][k] * q[n][k] in int32 and ws read on the
+ * device from the packed tensor's scale slot.  Quantizes x into `workspace`,
+ * then runs the contraction with the epilogue fused: a weight-streaming GEMV
+ * for N <= 8, an int8-MFMA GEMM above.
+ *   packed     I2_S tensor of rows x K (as written by i2s_pack).
+ *   x          [N][K] F32 activations, finite.
+ *   workspace  >= i2s_act_workspace_bytes(N, K) bytes, 256-byte aligned;
+ *              overwritten.  Must not be shared by overlapping calls.
+ *   y          [N][rows] F32 (rows contiguous), fully overwritten.
+ *   dot_out    NULL, or [N][rows] int32 receiving sum(code*q).
+ * Errors: I2S_EINVAL, I2S_EALIGN, I2S_EWORKSPACE, I2S_ERANGE, I2S_EHIP.
+ * ("ggml-cpu: ternary I2_S matmul kernel (VibeASR, 3/4)", Interface,
+ * Arithmetic, Kernels.) */
+int i2s_mul_mat(const uint8_t *packed, int64_t rows, int64_t K,
+                const float *x, int64_t N,
+                void *workspace, size_t workspace_bytes,
+                float *y, int32_t *dot_out, void *stream);
+
+/* i2s_mul_mat with the contraction kernel chosen by the caller, for checking
+ * that every launch geometry gives identical bits and for timing each kernel
+ * on its own.  kernel: 0 = automatic (as i2s_mul_mat), 1 = GEMV (N <= 8),
+ * 2 = MFMA GEMM (any N >= 1).  variant: 0 = automatic, else a 1-based index
+ * into the kernel's tile configurations (i2s_kernel_variants).  Returns
+ * I2S_EKERNEL for an unknown pair or a GEMV with N > 8. */
+int i2s_mul_mat_ex(const uint8_t *packed, int64_t rows, int64_t K,
+                   const float *x, int64_t N,
+                   void *workspace, size_t workspace_bytes,
+                   float *y, int32_t *dot_out, int kernel, int variant, void *stream);
+
+/* Number of tile configurations kernel `kernel` (1 or 2) offers; 0 otherwise. */
+int i2s_kernel_variants(int kernel);
+
+/* A short static English description of a status code. */
+const char *i2s_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I2S_H */

@@ -1,0 +1,128 @@
+"""Python access to the CPU oracle (oracle.c) for the I2_S W2A8 matmul.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg load this; the product path never does.  It shares no code
+with the GPU library and imports nothing from it.
+
+``build()`` compiles oracle.c with gcc (no fast-math, no FP contraction, so
+every float operation in it is one IEEE binary32 operation).  The wrappers
+take and return numpy arrays.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "oracle.c")
+_LIB = os.path.join(_DIR, "liboracle.so")
+_CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+           "-fno-strict-aliasing", "-Wall", "-Wextra"]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so next to it; returns the path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_packed_bytes.restype = ctypes.c_size_t
+        lib.oracle_packed_bytes.argtypes = [i64, i64]
+        lib.oracle_pack.restype = ctypes.c_int
+        lib.oracle_pack.argtypes = [p, ctypes.c_float, i64, i64, p]
+        lib.oracle_weight_scale.restype = ctypes.c_float
+        lib.oracle_weight_scale.argtypes = [p, i64, i64]
+        lib.oracle_quantize_act.restype = None
+        lib.oracle_quantize_act.argtypes = [p, i64, i64, p, p, p]
+        lib.oracle_dot.restype = None
+        lib.oracle_dot.argtypes = [p, i64, i64, p, i64, p]
+        lib.oracle_epilogue.restype = None
+        lib.oracle_epilogue.argtypes = [p, p, p, ctypes.c_float, i64, i64, p]
+        lib.oracle_mul_mat.restype = ctypes.c_int
+        lib.oracle_mul_mat.argtypes = [p, i64, i64, p, i64, p, p]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def packed_bytes(rows: int, K: int) -> int:
+    return int(_load().oracle_packed_bytes(rows, K))
+
+
+def pack(w: np.ndarray, ws: float) -> np.ndarray:
+    """I2_S bytes (payload then the 32-byte scale slot) of ternary w[rows][K]."""
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    rows, K = w.shape
+    out = np.empty(packed_bytes(rows, K), dtype=np.uint8)
+    rc = _load().oracle_pack(_ptr(w), float(np.float32(ws)), rows, K, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_pack: bad shape {w.shape}")
+    return out
+
+
+def weight_scale(packed: np.ndarray, rows: int, K: int) -> np.float32:
+    return np.float32(_load().oracle_weight_scale(_ptr(np.ascontiguousarray(packed)), rows, K))
+
+
+def quantize_act(x: np.ndarray):
+    """(q int8[N][K], act_scale f32[N], row_sum i32[N]) of F32 x[N][K]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    N, K = x.shape
+    q = np.empty((N, K), dtype=np.int8)
+    s = np.empty(N, dtype=np.float32)
+    rs = np.empty(N, dtype=np.int32)
+    _load().oracle_quantize_act(_ptr(x), N, K, _ptr(q), _ptr(s), _ptr(rs))
+    return q, s, rs
+
+
+def dot(packed: np.ndarray, rows: int, K: int, q: np.ndarray) -> np.ndarray:
+    """int32 dot[N][rows] = sum_k code*q, codes decoded from packed bytes."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    N = q.shape[0]
+    assert q.shape[1] == K and packed.size >= rows * K // 4
+    out = np.empty((N, rows), dtype=np.int32)
+    _load().oracle_dot(_ptr(packed), rows, K, _ptr(q), N, _ptr(out))
+    return out
+
+
+def epilogue(dot_: np.ndarray, row_sum: np.ndarray, act_scale: np.ndarray, ws: float) -> np.ndarray:
+    dot_ = np.ascontiguousarray(dot_, dtype=np.int32)
+    row_sum = np.ascontiguousarray(row_sum, dtype=np.int32)
+    act_scale = np.ascontiguousarray(act_scale, dtype=np.float32)
+    N, rows = dot_.shape
+    y = np.empty((N, rows), dtype=np.float32)
+    _load().oracle_epilogue(_ptr(dot_), _ptr(row_sum), _ptr(act_scale), float(np.float32(ws)), N, rows, _ptr(y))
+    return y
+
+
+def mul_mat(packed: np.ndarray, rows: int, K: int, x: np.ndarray, with_dot: bool = False):
+    """F32 y[N][rows] (and optionally int32 dot[N][rows]) of the whole op."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    N = x.shape[0]
+    assert x.shape[1] == K
+    y = np.empty((N, rows), dtype=np.float32)
+    d = np.empty((N, rows), dtype=np.int32) if with_dot else None
+    rc = _load().oracle_mul_mat(_ptr(packed), rows, K, _ptr(x), N, _ptr(y), _ptr(d) if with_dot else None)
+    if rc != 0:
+        raise ValueError(f"oracle_mul_mat failed ({rc}) for rows={rows} K={K} N={N}")
+    return (y, d) if with_dot else y

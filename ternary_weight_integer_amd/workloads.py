@@ -1,0 +1,154 @@
+"""Seeded synthetic inputs for the I2_S ternary-weight x int8-activation matmul.
+
+This module only draws random numbers.  It holds none of the method's
+arithmetic (no packing, no quantization, no dot products), so that both the
+GPU path and the CPU oracle can be fed the very same bytes from it without
+sharing any of the computation.
+
+Shapes follow the Qwen2-1.5B decoder geometry given in "VibeASR in audio.cpp"
+(Architecture / Decoder): hidden 1536, intermediate 8960, 12 query heads and
+2 KV heads of width 128, so the seven ternary projections are
+q/o 1536x1536, k/v 256x1536, gate/up 8960x1536 and down 1536x8960
+(stored [out][K], K contiguous).
+
+Recipe (every workload): ``numpy.random.default_rng(seed)`` with seed 0,
+weights drawn before activations.  Ternary weights are i.i.d. over
+{-1, 0, +1} with probabilities 0.3 / 0.4 / 0.3.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+TERNARY_P = (0.3, 0.4, 0.3)
+
+# Qwen2-1.5B projection shapes, (out, K).
+QWEN2_1P5B_PROJ = {
+    "q": (1536, 1536),
+    "k": (256, 1536),
+    "v": (256, 1536),
+    "o": (1536, 1536),
+    "gate": (8960, 1536),
+    "up": (8960, 1536),
+    "down": (1536, 8960),
+}
+
+
+@dataclass
+class Case:
+    """One matmul case: ternary weight w[out][K] (int8 in {-1,0,1}), weight
+    scale ws, and F32 activations x[N][K]."""
+
+    name: str
+    w: np.ndarray
+    ws: float
+    x: np.ndarray
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return int(self.w.shape[0])
+
+    @property
+    def K(self) -> int:
+        return int(self.w.shape[1])
+
+    @property
+    def N(self) -> int:
+        return int(self.x.shape[0])
+
+
+def ternary(rng: np.random.Generator, rows: int, K: int, p=TERNARY_P) -> np.ndarray:
+    """i.i.d. ternary matrix [rows][K] over {-1, 0, +1} with probabilities p."""
+    return rng.choice(np.array([-1, 0, 1], dtype=np.int8), size=(rows, K), p=list(p)).astype(np.int8)
+
+
+def normal(rng: np.random.Generator, N: int, K: int, std: float = 1.0) -> np.ndarray:
+    return (rng.standard_normal((N, K)) * std).astype(np.float32)
+
+
+def with_outliers(rng: np.random.Generator, x: np.ndarray, frac: float = 0.01, factor: float = 20.0) -> np.ndarray:
+    """Scale round(frac*K) positions per row (drawn without replacement) by factor."""
+    x = x.copy()
+    N, K = x.shape
+    cnt = int(round(frac * K))
+    for n in range(N):
+        idx = rng.choice(K, size=cnt, replace=False)
+        x[n, idx] = (x[n, idx] * np.float32(factor)).astype(np.float32)
+    return x
+
+
+def relu(x: np.ndarray) -> np.ndarray:
+    return np.maximum(x, np.float32(0)).astype(np.float32)
+
+
+def random_case(seed: int, rows: int, K: int, N: int, ws: float = 0.015, std: float = 1.0, name: str | None = None) -> Case:
+    rng = np.random.default_rng(seed)
+    w = ternary(rng, rows, K)
+    x = normal(rng, N, K, std)
+    return Case(name or f"rand_s{seed}_{rows}x{K}_N{N}", w, ws, x)
+
+
+# --- the five workloads ----------------------------------------------------
+
+def small_case(seed: int = 0) -> Case:
+    """Single matmul: w[64][256], ws 0.02, x[4][256] ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    w = ternary(rng, 64, 256)
+    x = normal(rng, 4, 256)
+    return Case("small_64x256_N4", w, 0.02, x)
+
+
+def decode_up_case(seed: int = 0) -> Case:
+    """Decode GEMV: FFN up w[8960][1536], ws 0.015, one row x[1][1536] ~ N(0,1)
+    with 1% of its entries (15 positions) scaled by 20."""
+    rng = np.random.default_rng(seed)
+    w = ternary(rng, 8960, 1536)
+    x = with_outliers(rng, normal(rng, 1, 1536))
+    return Case("decode_up_8960x1536_N1", w, 0.015, x)
+
+
+def down_small_batch_case(seed: int = 0) -> Case:
+    """Down projection: w[1536][8960], ws 0.015, x[8][8960] = ReLU(N(0, 0.5))."""
+    rng = np.random.default_rng(seed)
+    w = ternary(rng, 1536, 8960)
+    x = relu(normal(rng, 8, 8960, 0.5))
+    return Case("down_1536x8960_N8", w, 0.015, x)
+
+
+def prefill_gate_case(seed: int = 0, N: int = 512) -> Case:
+    """Prefill GEMM: gate w[8960][1536], ws 0.015, x[512][1536] ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    w = ternary(rng, 8960, 1536)
+    x = normal(rng, N, 1536)
+    return Case(f"prefill_gate_8960x1536_N{N}", w, 0.015, x)
+
+
+def layer_sweep_cases(seed: int = 0, Ns=(1, 64)) -> list[Case]:
+    """All seven Qwen2-1.5B projections at each N, ws 0.015, x ~ N(0,1)."""
+    out = []
+    for proj, (rows, K) in QWEN2_1P5B_PROJ.items():
+        rng = np.random.default_rng(seed)
+        w = ternary(rng, rows, K)
+        for N in Ns:
+            x = normal(rng, N, K)
+            out.append(Case(f"layer_{proj}_{rows}x{K}_N{N}", w, 0.015, x, {"proj": proj}))
+    return out
+
+
+def headroom_case(N: int = 1) -> Case:
+    """int32 headroom: w[1536][8960] all +1 (every code 2), x == 127.0."""
+    w = np.ones((1536, 8960), dtype=np.int8)
+    x = np.full((N, 8960), 127.0, dtype=np.float32)
+    return Case(f"headroom_1536x8960_N{N}", w, 0.015, x)
+
+
+def zero_row_case(N: int = 1, zero_row: int = 0, seed: int = 0) -> Case:
+    """Gate shape w[8960][1536] with activation row `zero_row` all zero."""
+    rng = np.random.default_rng(seed)
+    w = ternary(rng, 8960, 1536)
+    x = normal(rng, N, 1536)
+    x[zero_row, :] = 0.0
+    return Case(f"zero_row_8960x1536_N{N}_r{zero_row}", w, 0.015, x)

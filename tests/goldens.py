@@ -1,0 +1,97 @@
+"""Readers for the hand-worked fixtures in tests/golden/ (see each file's header
+for the page passages they are worked from)."""
+
+from __future__ import annotations
+
+import os
+import struct
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line
+
+
+def hex_f32(h: str) -> np.float32:
+    return np.float32(struct.unpack("<f", struct.pack("<I", int(h, 16)))[0])
+
+
+def _expand_bytes(tokens):
+    out = []
+    for t in tokens:
+        if "*" in t:
+            b, n = t.split("*")
+            out += [int(b, 16)] * int(n)
+        else:
+            out.append(int(t, 16))
+    return bytes(out)
+
+
+def pack_cases():
+    cases, cur = [], None
+    for line in _lines("pack_layout.txt"):
+        head, _, rest = line.partition(" ")
+        if head == "case":
+            name, *kv = rest.split(" ")
+            d = dict(x.split("=", 1) for x in kv)
+            rows, K = int(d["rows"]), int(d["K"])
+            w = np.full((rows, K), int(d["fill"]), dtype=np.int8)
+            if d["set"]:
+                for item in d["set"].split(","):
+                    r, k, v = (int(t) for t in item.split(":"))
+                    w[r, k] = v
+            cur = {"name": name, "w": w, "ws": hex_f32(d["ws_hex"])}
+            cases.append(cur)
+        elif head == "bytes":
+            cur["bytes"] = _expand_bytes(rest.split())
+        elif head == "scale":
+            cur["scale"] = bytes.fromhex(rest)
+    return cases
+
+
+def quantize_cases():
+    cases, cur = [], None
+    for line in _lines("quantize_vectors.txt"):
+        head, _, rest = line.partition(" ")
+        if head == "case":
+            name, kv = rest.split(" ")
+            K = int(kv.split("=")[1])
+            cur = {"name": name, "K": K}
+            cases.append(cur)
+        elif head == "x_hex":
+            lead = [hex_f32(t) for t in rest.split()]
+            x = np.zeros(cur["K"], dtype=np.float32)
+            x[: len(lead)] = lead
+            cur["x"] = x
+        elif head == "q":
+            lead = [int(t) for t in rest.split()]
+            q = np.zeros(cur["K"], dtype=np.int8)
+            q[: len(lead)] = lead
+            cur["q"] = q
+        elif head == "scale_hex":
+            cur["scale"] = hex_f32(rest)
+        elif head == "row_sum":
+            cur["row_sum"] = int(rest)
+    return cases
+
+
+def headroom():
+    d = {}
+    for line in _lines("headroom.txt"):
+        k, v = line.split()
+        d[k] = v
+    return {
+        "K": int(d["K"]),
+        "ws": hex_f32(d["ws_hex"]),
+        "scale": hex_f32(d["scale_hex"]),
+        "row_sum": int(d["row_sum"]),
+        "dot": int(d["dot"]),
+        "y_bits": int(d["y_hex"], 16),
+    }
