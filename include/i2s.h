@@ -125,6 +125,25 @@ int i2s_mul_mat_ex(const uint8_t *packed, int64_t rows, int64_t K,
                    void *workspace, size_t workspace_bytes,
                    float *y, int32_t *dot_out, int kernel, int variant, void *stream);
 
+/* The two phases of i2s_mul_mat as separate calls, so that one quantized
+ * activation can feed several weights (the sidecar of "ggml-cpu: ternary I2_S
+ * matmul kernel (VibeASR, 3/4)", Interface; its Kernels/threading section
+ * quantizes all rows first, then splits the output features).
+ *
+ * i2s_quantize_act_ws: quantize x[N][K] into `workspace` (private layout,
+ * >= i2s_act_workspace_bytes(N, K) bytes, 256-byte aligned).
+ * Errors: as i2s_mul_mat. */
+int i2s_quantize_act_ws(const float *x, int64_t N, int64_t K,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* i2s_mul_mat_ws: contraction + epilogue of the packed weight against the
+ * activations already quantized into `workspace` by i2s_quantize_act_ws with
+ * the same N and K (stream-ordered after it).  kernel/variant as in
+ * i2s_mul_mat_ex.  The workspace is only read. */
+int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
+                   const void *workspace, size_t workspace_bytes,
+                   float *y, int32_t *dot_out, int kernel, int variant, void *stream);
+
 /* Number of tile configurations kernel `kernel` (1 or 2) offers; 0 otherwise. */
 int i2s_kernel_variants(int kernel);
 

@@ -1,0 +1,691 @@
+// gfx950 (MI355X) kernels and C ABI for the I2_S ternary-weight x int8-activation
+// matmul.  The ABI is declared, with its contract, in include/i2s.h.
+//
+// The op ("ggml-cpu: ternary I2_S matmul kernel (VibeASR, 3/4)", Interface and
+// Arithmetic): weights are 2-bit codes {0,1,2} for {-1,0,+1}; activations are
+// quantized per row to int8 with the multiplier scale amax/127; the
+// contraction accumulates sum(code*q) in int32 and the epilogue computes
+// (float)(dot - row_sum) * (weight_scale * act_scale).
+//
+// Packed layout ("ggml: additive INT8/ternary types, fused CPU ops, and kernels
+// for VibeASR (1/2)", Two new types and Kernels): 128 values per 32-byte group;
+// byte gp of a group holds group-relative positions gp, 32+gp, 64+gp, 96+gp in
+// the bit pairs at shifts 6/4/2/0; one F32 scale in band after the payload.
+// A packed dword (bytes gp..gp+3 of a group) therefore yields, for slice s,
+// (dword >> (6-2s)) & 0x03030303 = the codes of the four consecutive positions
+// 32s+gp .. 32s+gp+3, one per byte, ready for a 4-way int8 dot.
+//
+// Private activation layout in the i2s_mul_mat workspace ("group-interleaved"):
+// within each 128-value group, the 16 bytes that pair with packed dword c
+// (bytes 4c..4c+3 of the group, c = 0..7) are stored together, slice by slice:
+//     qp[g*128 + 16c + 4s + t] = q[g*128 + 32s + 4c + t]      (s, t in 0..3)
+// so packed byte b of a row pairs with qp bytes 4b..4b+3, and a 16-byte
+// chunk j of packed weights (row bytes 16j..16j+15) pairs with the 64
+// contiguous qp bytes 64j..64j+63.  Integer sums do not depend on the order
+// of their terms, so this permutation changes no result bit.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "i2s.h"
+
+namespace {
+
+constexpr int kGroupValues = 128;
+constexpr int kScaleSlot = 32;
+constexpr unsigned kCodeMask = 0x03030303u;
+constexpr int64_t kMaxK = 8454528;  // 2*127*K stays below 2^31 (int32 accumulators)
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct ActWorkspace {
+  int8_t *q;
+  float *scale;
+  int32_t *row_sum;
+};
+
+inline ActWorkspace carve_workspace(void *base, int64_t N, int64_t K) {
+  char *p = static_cast<char *>(base);
+  size_t q_bytes = align_up(static_cast<size_t>(N) * static_cast<size_t>(K), 256);
+  size_t s_bytes = align_up(static_cast<size_t>(N) * 4, 256);
+  ActWorkspace ws;
+  ws.q = reinterpret_cast<int8_t *>(p);
+  ws.scale = reinterpret_cast<float *>(p + q_bytes);
+  ws.row_sum = reinterpret_cast<int32_t *>(p + q_bytes + s_bytes);
+  return ws;
+}
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// Block-wide reductions (256 threads = 4 wave64s).
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Activation quantization + row sum: one workgroup per activation row (the
+// row-wide absmax cannot be split).  Pass 1 reduces max|x| over the row;
+// pass 2 quantizes 16 values per thread-step and accumulates the int8 sum.
+//   amax = max(max|x|, 1e-5f); s = amax / 127 (IEEE division);
+//   q = clamp(roundf(x / s), -127, 127)   (roundf: halfway away from zero).
+// kInterleaved selects the workspace order above; otherwise q is row-major.
+
+constexpr int kQuantThreads = 256;
+
+template <bool kInterleaved>
+__global__ void __launch_bounds__(kQuantThreads)
+quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int8_t *__restrict__ q,
+                       float *__restrict__ act_scale, int32_t *__restrict__ row_sum) {
+  __shared__ float red_f[kQuantThreads / 64];
+  __shared__ int red_i[kQuantThreads / 64];
+  const int64_t n = blockIdx.x;
+  const float *xr = x + n * K;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+
+  float amax = 0.0f;
+  const float4 *x4 = reinterpret_cast<const float4 *>(xr);
+  for (int64_t i = tid; i < K / 4; i += kQuantThreads) {
+    float4 v = x4[i];
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  amax = wave_max(amax);
+  if (lane == 0) red_f[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  amax = fmaxf(amax, 1e-5f);
+  const float s = amax / 127.0f;
+
+  int sum = 0;
+  int8_t *qr = q + n * K;
+  for (int64_t u = tid; u < K / 16; u += kQuantThreads) {
+    uint32_t out[4];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      int64_t p = kInterleaved ? (u / 8) * 128 + 32 * sl + 4 * (u % 8) : 16 * u + 4 * sl;
+      float4 v = *reinterpret_cast<const float4 *>(xr + p);
+      float e[4] = {v.x, v.y, v.z, v.w};
+      uint32_t packed = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float r = roundf(e[t] / s);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        int qi = static_cast<int>(r);
+        sum += qi;
+        packed |= (static_cast<uint32_t>(qi) & 0xffu) << (8 * t);
+      }
+      out[sl] = packed;
+    }
+    *reinterpret_cast<uint4 *>(qr + 16 * u) = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) red_i[wave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    act_scale[n] = s;
+    row_sum[n] = red_i[0] + red_i[1] + red_i[2] + red_i[3];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pack: each thread writes 16 packed bytes (half a group) from the 4x16
+// ternary values they hold; thread 0 also writes the scale slot.
+
+constexpr int kPackThreads = 256;
+
+__device__ inline uint32_t code_of(int8_t w) { return w > 0 ? 2u : (w < 0 ? 0u : 1u); }
+
+__global__ void __launch_bounds__(kPackThreads)
+pack_kernel(const int8_t *__restrict__ w, float weight_scale, int64_t units, int64_t payload,
+            uint8_t *__restrict__ packed) {
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * kPackThreads + threadIdx.x;
+  if (u == 0) {
+    uint32_t slot[8] = {__float_as_uint(weight_scale), 0, 0, 0, 0, 0, 0, 0};
+    uint4 *dst = reinterpret_cast<uint4 *>(packed + payload);
+    dst[0] = make_uint4(slot[0], slot[1], slot[2], slot[3]);
+    dst[1] = make_uint4(slot[4], slot[5], slot[6], slot[7]);
+  }
+  if (u >= units) return;
+  const int64_t base = (u / 2) * kGroupValues + 16 * (u % 2);
+  int8_t v[4][16];
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) *reinterpret_cast<uint4 *>(v[sl]) = *reinterpret_cast<const uint4 *>(w + base + 32 * sl);
+  uint32_t out[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int b = 0; b < 16; ++b) {
+    uint32_t byte = (code_of(v[0][b]) << 6) | (code_of(v[1][b]) << 4) | (code_of(v[2][b]) << 2) | code_of(v[3][b]);
+    out[b / 4] |= byte << (8 * (b % 4));
+  }
+  *reinterpret_cast<uint4 *>(packed + 16 * u) = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue shared by both contraction kernels: two IEEE multiplies in the
+// stated order, t = ws * s first, then (float)(dot - row_sum) * t.
+
+__device__ inline float epilogue(int32_t dot, int32_t rsum, float t) {
+  return static_cast<float>(dot - rsum) * t;
+}
+
+// ---------------------------------------------------------------------------
+// GEMV for N <= 8 columns: streams packed weights with 128-bit loads and
+// accumulates with v_dot4 (4-way int8 dot into int32).
+//
+// A workgroup is 4 wave64s; in a wave, L consecutive lanes share a weight row
+// and split its 16-byte chunks (chunk j goes to lane j mod L), 64/L rows per
+// pass, RPL passes per wave, so a wave covers RPL*64/L rows.  Each lane loads
+// its weight chunks for all RPL rows before touching activations; the 64
+// group-interleaved activation bytes of a chunk are loaded once and reused for
+// the RPL rows.  Partial sums are reduced across the L lanes of a row and the
+// epilogue is applied in registers.
+
+constexpr int kGemvThreads = 256;
+
+template <int L>
+__device__ inline int lanes_sum(int v) {
+#pragma unroll
+  for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <int NC, int L, int RPL, int CPL>
+__global__ void __launch_bounds__(kGemvThreads)
+gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
+            const int8_t *__restrict__ qp, const float *__restrict__ act_scale,
+            const int32_t *__restrict__ row_sum, float *__restrict__ y,
+            int32_t *__restrict__ dot_out) {
+  constexpr int kSlots = 64 / L;
+  constexpr int kRowsPerWave = kSlots * RPL;
+  constexpr int kRowsPerBlock = kRowsPerWave * (kGemvThreads / 64);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lam = lane % L, slot = lane / L;
+  const int64_t C = K / 64;               // 16-byte chunks per packed row
+  const int64_t row_bytes = K / 4;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave * kRowsPerWave + slot;
+
+  int acc[RPL][NC];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m)
+#pragma unroll
+    for (int n = 0; n < NC; ++n) acc[m][n] = 0;
+
+  for (int64_t jb = 0; jb < C; jb += static_cast<int64_t>(L) * CPL) {
+    uint4 wv[RPL][CPL];
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+      const int64_t r = row0 + static_cast<int64_t>(m) * kSlots;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int64_t j = jb + lam + static_cast<int64_t>(L) * c;
+        if (r < rows && j < C)
+          wv[m][c] = *reinterpret_cast<const uint4 *>(packed + r * row_bytes + 16 * j);
+        else
+          wv[m][c] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int64_t j = jb + lam + static_cast<int64_t>(L) * c;
+      if (j >= C) continue;
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+        const uint4 *qv = reinterpret_cast<const uint4 *>(qp + static_cast<int64_t>(n) * K + 64 * j);
+        uint4 qd[4] = {qv[0], qv[1], qv[2], qv[3]};
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+          const uint32_t wd[4] = {wv[m][c].x, wv[m][c].y, wv[m][c].z, wv[m][c].w};
+          int a = acc[m][n];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t w = wd[d];
+            a = __builtin_amdgcn_sdot4(static_cast<int>((w >> 6) & kCodeMask), static_cast<int>(qd[d].x), a, false);
+            a = __builtin_amdgcn_sdot4(static_cast<int>((w >> 4) & kCodeMask), static_cast<int>(qd[d].y), a, false);
+            a = __builtin_amdgcn_sdot4(static_cast<int>((w >> 2) & kCodeMask), static_cast<int>(qd[d].z), a, false);
+            a = __builtin_amdgcn_sdot4(static_cast<int>(w & kCodeMask), static_cast<int>(qd[d].w), a, false);
+          }
+          acc[m][n] = a;
+        }
+      }
+    }
+  }
+
+  const float ws = *reinterpret_cast<const float *>(packed + rows * row_bytes);
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) {
+    const int64_t r = row0 + static_cast<int64_t>(m) * kSlots;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      const int total = lanes_sum<L>(acc[m][n]);
+      if (r < rows && lam == n % L) {
+        const float t = ws * act_scale[n];
+        y[static_cast<int64_t>(n) * rows + r] = epilogue(total, row_sum[n], t);
+        if (dot_out) dot_out[static_cast<int64_t>(n) * rows + r] = total;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM for larger N: int8 MFMA (v_mfma_i32_16x16x64_i8).
+//
+// One MFMA multiplies a 16(out) x 64 tile of codes by a 64 x 16(N) tile of
+// activations.  Lane l supplies row/column l%16 and k-block l/16 of both
+// operands, and only the pairing of A and B bytes matters: for K-step kk (256
+// positions = 64 packed bytes of a row), lane (i, kb) loads the 16 packed
+// bytes 64kk+16kb..+15 of weight row i; their dword d unpacks, slice by
+// slice, into that lane's 16 A bytes of MFMA d, whose group-interleaved
+// activation partners are qp bytes 256kk+64kb+16d..+15 of each column.
+//
+// A workgroup has WAVES_M x WAVES_N waves; each wave owns WM x WN 16x16 output
+// tiles.  Activation tiles for one K-step are staged in LDS (double buffered)
+// and shared by the waves; weight tiles go from global memory straight to
+// registers.  Accumulators are int32; the epilogue runs in registers.
+
+template <int WM, int WN, int WAVES_M, int WAVES_N>
+struct GemmCfg {
+  static constexpr int kWM = WM, kWN = WN, kWavesM = WAVES_M, kWavesN = WAVES_N;
+  static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+  static constexpr int kBM = 16 * WM * WAVES_M;   // output features per block
+  static constexpr int kBN = 16 * WN * WAVES_N;   // activation rows per block
+  static constexpr int kLdsStride = 256 + 16;     // bytes per activation row in LDS (padded)
+  static constexpr int kLdsStage = kBN * kLdsStride;
+};
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+template <class Cfg>
+__global__ void __launch_bounds__(Cfg::kThreads)
+gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
+            const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
+            const int32_t *__restrict__ row_sum, float *__restrict__ y,
+            int32_t *__restrict__ dot_out, int64_t tiles_m) {
+  constexpr int WM = Cfg::kWM, WN = Cfg::kWN;
+  __shared__ __attribute__((aligned(16))) int8_t lds[2 * Cfg::kLdsStage];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave % Cfg::kWavesM, wn = wave / Cfg::kWavesM;
+  const int li = lane & 15, kb = lane >> 4;
+  const int64_t tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
+  const int64_t o_base = tile_m * Cfg::kBM + wm * 16 * WM;
+  const int64_t n_blk = tile_n * Cfg::kBN;
+  const int64_t row_bytes = K / 4;
+  const int64_t steps = K / 256 + ((K % 256) ? 1 : 0);  // K is a multiple of 128
+
+  v4i acc[WM][WN];
+#pragma unroll
+  for (int m = 0; m < WM; ++m)
+#pragma unroll
+    for (int n = 0; n < WN; ++n) acc[m][n] = v4i{0, 0, 0, 0};
+
+  // Cooperative copy of one K-step of activations (kBN rows x 256 bytes) into LDS.
+  auto stage_act = [&](int64_t kk, int buf) {
+    constexpr int kPieces = Cfg::kBN * 16;  // 16-byte pieces
+    const int64_t kbytes = (K - 256 * kk) >= 256 ? 256 : (K - 256 * kk);
+    for (int p = tid; p < kPieces; p += Cfg::kThreads) {
+      const int r = p / 16, c = p % 16;
+      const int64_t n = n_blk + r;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < N && 16 * c < kbytes) v = *reinterpret_cast<const uint4 *>(qp + n * K + 256 * kk + 16 * c);
+      *reinterpret_cast<uint4 *>(lds + buf * Cfg::kLdsStage + r * Cfg::kLdsStride + 16 * c) = v;
+    }
+  };
+
+  auto load_w = [&](int64_t kk, uint4 (&wv)[WM]) {
+    const int64_t kbytes = (K - 256 * kk) >= 256 ? 256 : (K - 256 * kk);
+#pragma unroll
+    for (int m = 0; m < WM; ++m) {
+      const int64_t o = o_base + 16 * m + li;
+      if (o < rows && 16 * kb < kbytes / 4)  // tail step: only 32 of the 64 packed bytes exist
+        wv[m] = *reinterpret_cast<const uint4 *>(packed + o * row_bytes + 64 * kk + 16 * kb);
+      else
+        wv[m] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);  // code 1 = weight 0
+    }
+  };
+
+  uint4 wcur[WM], wnext[WM];
+  load_w(0, wcur);
+  stage_act(0, 0);
+  __syncthreads();
+
+  for (int64_t kk = 0; kk < steps; ++kk) {
+    const int buf = static_cast<int>(kk & 1);
+    if (kk + 1 < steps) {
+      load_w(kk + 1, wnext);
+      stage_act(kk + 1, buf ^ 1);
+    }
+    const int8_t *lb = lds + buf * Cfg::kLdsStage;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      v4i b[WN];
+#pragma unroll
+      for (int n = 0; n < WN; ++n) {
+        const int r = wn * 16 * WN + 16 * n + li;
+        b[n] = *reinterpret_cast<const v4i *>(lb + r * Cfg::kLdsStride + 64 * kb + 16 * d);
+      }
+#pragma unroll
+      for (int m = 0; m < WM; ++m) {
+        const uint32_t wd = d == 0 ? wcur[m].x : d == 1 ? wcur[m].y : d == 2 ? wcur[m].z : wcur[m].w;
+        v4i a;
+        a[0] = static_cast<int>((wd >> 6) & kCodeMask);
+        a[1] = static_cast<int>((wd >> 4) & kCodeMask);
+        a[2] = static_cast<int>((wd >> 2) & kCodeMask);
+        a[3] = static_cast<int>(wd & kCodeMask);
+#pragma unroll
+        for (int n = 0; n < WN; ++n) acc[m][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[m][n], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < WM; ++m) wcur[m] = wnext[m];
+  }
+
+  // Epilogue: lane l holds C[4*(l/16) + r][l % 16], r = 0..3, of each tile,
+  // i.e. four consecutive output features of one activation row.
+  const float ws = *reinterpret_cast<const float *>(packed + rows * row_bytes);
+#pragma unroll
+  for (int n = 0; n < WN; ++n) {
+    const int64_t nn = n_blk + wn * 16 * WN + 16 * n + li;
+    if (nn >= N) continue;
+    const float t = ws * act_scale[nn];
+    const int32_t rs = row_sum[nn];
+#pragma unroll
+    for (int m = 0; m < WM; ++m) {
+      const int64_t o = o_base + 16 * m + 4 * kb;
+      float *yr = y + nn * rows;
+      if (o + 3 < rows && (rows % 4) == 0) {
+        *reinterpret_cast<float4 *>(yr + o) = make_float4(epilogue(acc[m][n][0], rs, t), epilogue(acc[m][n][1], rs, t),
+                                                         epilogue(acc[m][n][2], rs, t), epilogue(acc[m][n][3], rs, t));
+        if (dot_out)
+          *reinterpret_cast<int4 *>(dot_out + nn * rows + o) = make_int4(acc[m][n][0], acc[m][n][1], acc[m][n][2], acc[m][n][3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (o + r < rows) {
+            yr[o + r] = epilogue(acc[m][n][r], rs, t);
+            if (dot_out) dot_out[nn * rows + o + r] = acc[m][n][r];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch helpers.
+
+inline int hip_status() { return hipGetLastError() == hipSuccess ? I2S_OK : I2S_EHIP; }
+
+template <int NC, int L, int RPL, int CPL>
+int launch_gemv_cfg(const uint8_t *packed, int64_t rows, int64_t K, const ActWorkspace &ws,
+                    float *y, int32_t *dot_out, hipStream_t stream) {
+  constexpr int kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
+  const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > kMaxDim) return I2S_ERANGE;
+  hipLaunchKernelGGL((gemv_kernel<NC, L, RPL, CPL>), dim3(static_cast<unsigned>(blocks)), dim3(kGemvThreads), 0,
+                     stream, packed, rows, K, ws.q, ws.scale, ws.row_sum, y, dot_out);
+  return hip_status();
+}
+
+// GEMV tile configurations: (lanes per row, rows per lane pass, chunk batch).
+// Variant v selects the v-th entry (1-based); 0 picks by K.
+template <int NC>
+int launch_gemv_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K, const ActWorkspace &ws,
+                   float *y, int32_t *dot_out, hipStream_t stream) {
+  if (variant == 0) {
+    const int64_t C = K / 64;
+    variant = C <= 8 ? 1 : (C <= 32 ? 2 : 3);
+  }
+  switch (variant) {
+    case 1: return launch_gemv_cfg<NC, 4, 1, 2>(packed, rows, K, ws, y, dot_out, stream);
+    case 2: return launch_gemv_cfg<NC, 8, 1, 4>(packed, rows, K, ws, y, dot_out, stream);
+    case 3: return launch_gemv_cfg<NC, 64, 1, 3>(packed, rows, K, ws, y, dot_out, stream);
+    case 4: return launch_gemv_cfg<NC, 8, 2, 3>(packed, rows, K, ws, y, dot_out, stream);
+    case 5: return launch_gemv_cfg<NC, 16, 1, 2>(packed, rows, K, ws, y, dot_out, stream);
+    default: return I2S_EKERNEL;
+  }
+}
+constexpr int kGemvVariants = 5;
+
+int launch_gemv(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
+                float *y, int32_t *dot_out, hipStream_t stream) {
+  switch (N) {
+    case 1: return launch_gemv_nc<1>(variant, packed, rows, K, ws, y, dot_out, stream);
+    case 2: return launch_gemv_nc<2>(variant, packed, rows, K, ws, y, dot_out, stream);
+    case 3: return launch_gemv_nc<3>(variant, packed, rows, K, ws, y, dot_out, stream);
+    case 4: return launch_gemv_nc<4>(variant, packed, rows, K, ws, y, dot_out, stream);
+    case 5: return launch_gemv_nc<5>(variant, packed, rows, K, ws, y, dot_out, stream);
+    case 6: return launch_gemv_nc<6>(variant, packed, rows, K, ws, y, dot_out, stream);
+    case 7: return launch_gemv_nc<7>(variant, packed, rows, K, ws, y, dot_out, stream);
+    case 8: return launch_gemv_nc<8>(variant, packed, rows, K, ws, y, dot_out, stream);
+    default: return I2S_EKERNEL;
+  }
+}
+
+template <class Cfg>
+int launch_gemm_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
+                    float *y, int32_t *dot_out, hipStream_t stream) {
+  const int64_t tiles_m = (rows + Cfg::kBM - 1) / Cfg::kBM;
+  const int64_t tiles_n = (N + Cfg::kBN - 1) / Cfg::kBN;
+  const int64_t blocks = tiles_m * tiles_n;
+  if (blocks > kMaxDim) return I2S_ERANGE;
+  hipLaunchKernelGGL((gemm_kernel<Cfg>), dim3(static_cast<unsigned>(blocks)), dim3(Cfg::kThreads), 0, stream,
+                     packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out, tiles_m);
+  return hip_status();
+}
+
+using GemmA = GemmCfg<4, 4, 4, 1>;  // 256 x 64 block, 4 waves
+using GemmB = GemmCfg<4, 2, 2, 2>;  // 128 x 64 block, 4 waves
+using GemmC = GemmCfg<5, 4, 4, 1>;  // 320 x 64 block, 4 waves
+using GemmD = GemmCfg<2, 2, 4, 1>;  // 128 x 32 block, 4 waves
+constexpr int kGemmVariants = 4;
+
+template <class Cfg>
+int64_t gemm_blocks(int64_t rows, int64_t N) {
+  return ((rows + Cfg::kBM - 1) / Cfg::kBM) * ((N + Cfg::kBN - 1) / Cfg::kBN);
+}
+
+// Pick the configuration whose most loaded compute unit (256 CUs, one block
+// each at a time) does the least padded MFMA work.
+int pick_gemm_variant(int64_t rows, int64_t N) {
+  const int64_t cus = 256;
+  int64_t best_cost = -1;
+  int best = 1;
+  const int64_t blocks[kGemmVariants] = {gemm_blocks<GemmA>(rows, N), gemm_blocks<GemmB>(rows, N),
+                                         gemm_blocks<GemmC>(rows, N), gemm_blocks<GemmD>(rows, N)};
+  const int64_t area[kGemmVariants] = {GemmA::kBM * GemmA::kBN, GemmB::kBM * GemmB::kBN,
+                                       GemmC::kBM * GemmC::kBN, GemmD::kBM * GemmD::kBN};
+  for (int v = 0; v < kGemmVariants; ++v) {
+    const int64_t rounds = (blocks[v] + cus - 1) / cus;
+    const int64_t cost = rounds * area[v];
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = v + 1;
+    }
+  }
+  return best;
+}
+
+int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
+                float *y, int32_t *dot_out, hipStream_t stream) {
+  if (variant == 0) variant = pick_gemm_variant(rows, N);
+  switch (variant) {
+    case 1: return launch_gemm_cfg<GemmA>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 2: return launch_gemm_cfg<GemmB>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 3: return launch_gemm_cfg<GemmC>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 4: return launch_gemm_cfg<GemmD>(packed, rows, K, N, ws, y, dot_out, stream);
+    default: return I2S_EKERNEL;
+  }
+}
+
+inline bool k_ok(int64_t K) { return K > 0 && K % kGroupValues == 0; }
+
+int check_common(int64_t rows, int64_t K) {
+  if (rows < 0) return I2S_EINVAL;
+  if (!k_ok(K)) return I2S_EALIGN;
+  if (K > kMaxK || rows > kMaxDim) return I2S_ERANGE;
+  return I2S_OK;
+}
+
+int quantize_launch(const float *x, int64_t N, int64_t K, int8_t *q, float *s, int32_t *rs, bool interleaved,
+                    hipStream_t stream) {
+  if (N > kMaxDim) return I2S_ERANGE;
+  if (interleaved)
+    hipLaunchKernelGGL((quantize_rowsum_kernel<true>), dim3(static_cast<unsigned>(N)), dim3(kQuantThreads), 0, stream,
+                       x, K, q, s, rs);
+  else
+    hipLaunchKernelGGL((quantize_rowsum_kernel<false>), dim3(static_cast<unsigned>(N)), dim3(kQuantThreads), 0, stream,
+                       x, K, q, s, rs);
+  return hip_status();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI.
+
+extern "C" size_t i2s_packed_bytes(int64_t rows, int64_t K) {
+  if (rows < 0 || !k_ok(K)) return 0;
+  return static_cast<size_t>(rows) * static_cast<size_t>(K / 4) + kScaleSlot;
+}
+
+extern "C" size_t i2s_act_workspace_bytes(int64_t N, int64_t K) {
+  if (N < 0 || !k_ok(K)) return 0;
+  return align_up(static_cast<size_t>(N) * static_cast<size_t>(K), 256) + 2 * align_up(static_cast<size_t>(N) * 4, 256);
+}
+
+extern "C" int i2s_pack(const int8_t *w, float weight_scale, int64_t rows, int64_t K, uint8_t *packed, void *stream) {
+  int st = check_common(rows, K);
+  if (st != I2S_OK) return st;
+  if (!packed || (rows > 0 && !w)) return I2S_EINVAL;
+  if (!aligned16(packed) || (rows > 0 && !aligned16(w))) return I2S_EINVAL;
+  const int64_t units = rows * K / 64;
+  const int64_t blocks = units > 0 ? (units + kPackThreads - 1) / kPackThreads : 1;
+  if (blocks > kMaxDim) return I2S_ERANGE;
+  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kPackThreads), 0,
+                     static_cast<hipStream_t>(stream), w, weight_scale, units, rows * K / 4, packed);
+  return hip_status();
+}
+
+extern "C" int i2s_quantize_act(const float *x, int64_t N, int64_t K, int8_t *q, float *act_scale, int32_t *row_sum,
+                                void *stream) {
+  if (N < 0) return I2S_EINVAL;
+  int st = check_common(0, K);
+  if (st != I2S_OK) return st;
+  if (N == 0) return I2S_OK;
+  if (!x || !q || !act_scale || !row_sum) return I2S_EINVAL;
+  if (!aligned16(x) || !aligned16(q)) return I2S_EINVAL;
+  return quantize_launch(x, N, K, q, act_scale, row_sum, false, static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+// Host-side checks shared by the matmul entry points; I2S_OK means launchable
+// (or a no-op when N == 0 or rows == 0, reported through *noop).
+int check_mul_mat(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const void *workspace,
+                  size_t workspace_bytes, const float *y, const int32_t *dot_out, int kernel, int variant,
+                  bool *noop) {
+  *noop = false;
+  if (N < 0) return I2S_EINVAL;
+  int st = check_common(rows, K);
+  if (st != I2S_OK) return st;
+  if (kernel < 0 || kernel > 2 || variant < 0) return I2S_EKERNEL;
+  if (kernel == 1 && (N > 8 || variant > kGemvVariants)) return I2S_EKERNEL;
+  if (kernel == 2 && variant > kGemmVariants) return I2S_EKERNEL;
+  if (kernel == 0 && variant != 0) return I2S_EKERNEL;
+  if (N == 0 || rows == 0) {
+    *noop = true;
+    return I2S_OK;
+  }
+  if (N > kMaxDim) return I2S_ERANGE;
+  if (!packed || !y) return I2S_EINVAL;
+  if (!aligned16(packed) || !aligned16(y) || (dot_out && !aligned16(dot_out))) return I2S_EINVAL;
+  if (!workspace || workspace_bytes < i2s_act_workspace_bytes(N, K)) return I2S_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I2S_EWORKSPACE;
+  return I2S_OK;
+}
+
+int contract(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
+             int32_t *dot_out, int kernel, int variant, hipStream_t s) {
+  const bool use_gemv = kernel == 1 || (kernel == 0 && N <= 8);
+  if (use_gemv) return launch_gemv(variant, packed, rows, K, N, ws, y, dot_out, s);
+  return launch_gemm(variant, packed, rows, K, N, ws, y, dot_out, s);
+}
+
+}  // namespace
+
+extern "C" int i2s_quantize_act_ws(const float *x, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  if (N < 0) return I2S_EINVAL;
+  int st = check_common(0, K);
+  if (st != I2S_OK) return st;
+  if (N == 0) return I2S_OK;
+  if (N > kMaxDim) return I2S_ERANGE;
+  if (!x || !aligned16(x)) return I2S_EINVAL;
+  if (!workspace || workspace_bytes < i2s_act_workspace_bytes(N, K)) return I2S_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I2S_EWORKSPACE;
+  ActWorkspace ws = carve_workspace(workspace, N, K);
+  return quantize_launch(x, N, K, ws.q, ws.scale, ws.row_sum, true, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const void *workspace,
+                              size_t workspace_bytes, float *y, int32_t *dot_out, int kernel, int variant,
+                              void *stream) {
+  bool noop;
+  int st = check_mul_mat(packed, rows, K, N, workspace, workspace_bytes, y, dot_out, kernel, variant, &noop);
+  if (st != I2S_OK || noop) return st;
+  ActWorkspace ws = carve_workspace(const_cast<void *>(workspace), N, K);
+  return contract(packed, rows, K, N, ws, y, dot_out, kernel, variant, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int i2s_mul_mat_ex(const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t N,
+                              void *workspace, size_t workspace_bytes, float *y, int32_t *dot_out, int kernel,
+                              int variant, void *stream) {
+  bool noop;
+  int st = check_mul_mat(packed, rows, K, N, workspace, workspace_bytes, y, dot_out, kernel, variant, &noop);
+  if (st != I2S_OK || noop) return st;
+  if (!x || !aligned16(x)) return I2S_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ActWorkspace ws = carve_workspace(workspace, N, K);
+  st = quantize_launch(x, N, K, ws.q, ws.scale, ws.row_sum, true, s);
+  if (st != I2S_OK) return st;
+  return contract(packed, rows, K, N, ws, y, dot_out, kernel, variant, s);
+}
+
+extern "C" int i2s_mul_mat(const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t N,
+                           void *workspace, size_t workspace_bytes, float *y, int32_t *dot_out, void *stream) {
+  return i2s_mul_mat_ex(packed, rows, K, x, N, workspace, workspace_bytes, y, dot_out, 0, 0, stream);
+}
+
+extern "C" int i2s_kernel_variants(int kernel) {
+  if (kernel == 1) return kGemvVariants;
+  if (kernel == 2) return kGemmVariants;
+  return 0;
+}
+
+extern "C" const char *i2s_strerror(int status) {
+  switch (status) {
+    case I2S_OK: return "success";
+    case I2S_EINVAL: return "invalid argument: null pointer, negative size, or pointer not 16-byte aligned";
+    case I2S_EALIGN: return "K must be a positive multiple of 128";
+    case I2S_EWORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than i2s_act_workspace_bytes";
+    case I2S_EHIP: return "HIP runtime error at launch";
+    case I2S_ERANGE: return "size beyond what the library addresses";
+    case I2S_EKERNEL: return "unknown kernel or variant, or a GEMV with more than 8 columns";
+    default: return "unknown status";
+  }
+}

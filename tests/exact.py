@@ -92,3 +92,23 @@ def epilogue(sum_wq: int, ws: float, s: np.float32) -> np.float32:
 
 def f32_bits(v) -> int:
     return int(np.asarray(v, dtype=np.float32).view(np.uint32))
+
+
+def near_tie_rows(amaxes=(100.0, 3.3, 0.77, 12345.678)) -> list[np.ndarray]:
+    """F32 rows (length a multiple of 128) whose values sit on, or one or two
+    floats either side of, each .5 boundary of x/s, for scales s that are not
+    powers of two, so that the last bit of the division decides q."""
+    rows = []
+    for amax in (np.float32(a) for a in amaxes):
+        s = f32_round(frac(amax) / 127)
+        vals = [amax]
+        for m in range(-126, 127):
+            centre = np.float32(float((frac(m) + Fraction(1, 2)) * frac(s)))
+            up, down = np.float32(np.inf), np.float32(-np.inf)
+            u1 = np.nextafter(centre, up)
+            d1 = np.nextafter(centre, down)
+            vals += [np.nextafter(d1, down), d1, centre, u1, np.nextafter(u1, up)]
+        row = np.array([v for v in vals if abs(v) <= amax], dtype=np.float32)
+        pad = (-row.size) % 128
+        rows.append(np.concatenate([row, np.zeros(pad, np.float32)]))
+    return rows

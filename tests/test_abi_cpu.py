@@ -1,0 +1,96 @@
+"""CPU-side checks of the C ABI: the built library loads, exports every symbol
+include/i2s.h declares, answers the size queries, and rejects bad arguments on
+the host before any launch (these calls return before touching the GPU)."""
+
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+from ternary_weight_integer_amd import i2s
+
+
+def test_every_declared_symbol_is_exported():
+    names = i2s.declared_symbols()
+    assert set(names) >= {"i2s_pack", "i2s_quantize_act", "i2s_mul_mat", "i2s_packed_bytes",
+                          "i2s_act_workspace_bytes", "i2s_strerror"}
+    raw = ctypes.CDLL(i2s.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_size_queries():
+    # rows*K/4 payload + 32-byte scale slot
+    assert i2s.i2s_packed_bytes(8960, 1536) == 8960 * 1536 // 4 + 32
+    assert i2s.i2s_packed_bytes(0, 128) == 32
+    assert i2s.i2s_packed_bytes(4, 100) == 0
+    assert i2s.i2s_packed_bytes(-1, 128) == 0
+    # q (N*K, 256-aligned) + scales + row sums (each 256-aligned)
+    assert i2s.i2s_act_workspace_bytes(1, 1536) == 1536 + 256 + 256
+    assert i2s.i2s_act_workspace_bytes(512, 1536) == 512 * 1536 + 2048 + 2048
+    assert i2s.i2s_act_workspace_bytes(3, 200) == 0
+
+
+def test_kernel_variant_counts():
+    assert i2s.i2s_kernel_variants(1) >= 2
+    assert i2s.i2s_kernel_variants(2) >= 2
+    assert i2s.i2s_kernel_variants(0) == 0
+    assert i2s.i2s_kernel_variants(3) == 0
+
+
+def test_strerror_covers_every_status():
+    seen = set()
+    for st in range(0, 7):
+        msg = i2s.i2s_strerror(st)
+        assert msg and msg != "unknown status"
+        seen.add(msg)
+    assert len(seen) == 7
+    assert i2s.i2s_strerror(99) == "unknown status"
+
+
+FAKE = 1 << 20  # a 16- and 256-byte aligned non-null address; never dereferenced here
+
+
+@pytest.mark.parametrize("args,expect", [
+    # (packed, rows, K, x, N, ws, ws_bytes, y, dot, kernel, variant) -> status
+    ((FAKE, 4, 100, FAKE, 1, FAKE, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EALIGN),
+    ((FAKE, 4, 0, FAKE, 1, FAKE, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EALIGN),
+    ((FAKE, -1, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EINVAL),
+    ((FAKE, 4, 128, FAKE, -1, FAKE, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EINVAL),
+    ((None, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EINVAL),
+    ((FAKE, 4, 128, None, 1, FAKE, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EINVAL),
+    ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, None, None, 0, 0), i2s.I2S_EINVAL),
+    ((FAKE + 4, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EINVAL),
+    ((FAKE, 4, 128, FAKE, 1, None, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EWORKSPACE),
+    ((FAKE, 4, 128, FAKE, 2, FAKE, 128, FAKE, None, 0, 0), i2s.I2S_EWORKSPACE),
+    ((FAKE, 4, 128, FAKE, 1, FAKE + 16, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EWORKSPACE),
+    ((FAKE, 4, 128, FAKE, 9, FAKE, 1 << 20, FAKE, None, 1, 0), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 3, 0), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 2, 99), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 0, 1), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 8454656, FAKE, 1, FAKE, 1 << 40, FAKE, None, 0, 0), i2s.I2S_ERANGE),
+    # N == 0 or rows == 0: success, nothing launched
+    ((None, 4, 128, None, 0, None, 0, None, None, 0, 0), i2s.I2S_OK),
+    ((None, 0, 128, None, 3, None, 0, None, None, 0, 0), i2s.I2S_OK),
+])
+def test_mul_mat_ex_host_validation(args, expect):
+    assert i2s.lib().i2s_mul_mat_ex(*args, None) == expect
+
+
+def test_mul_mat_host_validation():
+    L = i2s.lib()
+    assert L.i2s_mul_mat(FAKE, 4, 96, FAKE, 1, FAKE, 1 << 20, FAKE, None, None) == i2s.I2S_EALIGN
+    assert L.i2s_mul_mat(FAKE, 4, 128, FAKE, 1, FAKE, 16, FAKE, None, None) == i2s.I2S_EWORKSPACE
+
+
+def test_pack_and_quantize_host_validation():
+    L = i2s.lib()
+    assert L.i2s_pack(FAKE, 1.0, 4, 192, FAKE, None) == i2s.I2S_EALIGN
+    assert L.i2s_pack(None, 1.0, 4, 128, FAKE, None) == i2s.I2S_EINVAL
+    assert L.i2s_pack(FAKE, 1.0, 4, 128, None, None) == i2s.I2S_EINVAL
+    assert L.i2s_pack(FAKE + 8, 1.0, 4, 128, FAKE, None) == i2s.I2S_EINVAL
+    assert L.i2s_quantize_act(FAKE, 2, 130, FAKE, FAKE, FAKE, None) == i2s.I2S_EALIGN
+    assert L.i2s_quantize_act(FAKE, -2, 128, FAKE, FAKE, FAKE, None) == i2s.I2S_EINVAL
+    assert L.i2s_quantize_act(FAKE, 2, 128, None, FAKE, FAKE, None) == i2s.I2S_EINVAL
+    assert L.i2s_quantize_act(None, 0, 128, None, None, None, None) == i2s.I2S_OK

@@ -1,0 +1,308 @@
+"""GPU parity: the HIP library against the CPU oracle, bit for bit.
+
+Packed bytes, int8 activations, activation-scale bits, row sums, int32 dots and
+F32 outputs must all be identical to the oracle's (the integer steps are exact
+and the three F32 operations are single IEEE round-to-nearest operations in a
+fixed order, so there is exactly one correct bit pattern).  Every case goes
+through the C ABI (via the ctypes binding) on the same seeded inputs the
+oracle gets.  Full-size workloads are compared on sampled output rows that the
+oracle computes one by one.
+"""
+
+from __future__ import annotations
+
+import itertools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact import near_tie_rows
+from ternary_weight_integer_amd import i2s, workloads
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # only reachable when gpu tests are selected on a host without a GPU
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def gpu_pack(w: np.ndarray, ws: float) -> torch.Tensor:
+    return i2s.i2s_pack(dev(w), ws)
+
+
+def oracle_rows(packed: np.ndarray, rows: int, K: int, x: np.ndarray, sample: np.ndarray):
+    """Oracle y and dot for the sampled output rows only (all N)."""
+    q, s, rs = oracle.quantize_act(x)
+    ws = oracle.weight_scale(packed, rows, K)
+    ys, ds = [], []
+    for o in sample:
+        d = oracle.dot(packed[o * K // 4:(o + 1) * K // 4], 1, K, q)
+        ds.append(d[:, 0])
+        ys.append(oracle.epilogue(d, rs, s, ws)[:, 0])
+    return np.stack(ys, 1), np.stack(ds, 1)
+
+
+def check_mul_mat(case: workloads.Case, kernel=0, variant=0, sample=None, packed_gpu=None, packed_np=None):
+    rows, K, N = case.rows, case.K, case.N
+    say(f"[parity] {case.name} rows={rows} K={K} N={N} kernel={kernel} variant={variant}")
+    if packed_np is None:
+        packed_np = oracle.pack(case.w, case.ws)
+    if packed_gpu is None:
+        packed_gpu = gpu_pack(case.w, case.ws)
+    x = dev(case.x)
+    y, d = i2s.i2s_mul_mat_ex(packed_gpu, rows, K, x, dot_out=True, kernel=kernel, variant=variant)
+    y, d = host(y), host(d)
+    if sample is None:
+        ye, de = oracle.mul_mat(packed_np, rows, K, case.x, with_dot=True)
+    else:
+        ye, de = oracle_rows(packed_np, rows, K, case.x, sample)
+        y, d = y[:, sample], d[:, sample]
+    assert np.array_equal(d, de), f"dot mismatch at {np.argwhere(d != de)[:5]}"
+    assert np.array_equal(bits(y), bits(ye)), f"y mismatch at {np.argwhere(bits(y) != bits(ye))[:5]}"
+    return y
+
+
+# --- pack ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,K", [(1, 128), (3, 256), (64, 256), (70, 1152), (8960, 1536), (1536, 8960), (256, 1536)])
+def test_pack_bytes_match_oracle(rows, K):
+    say(f"[pack] rows={rows} K={K}")
+    rng = np.random.default_rng(rows + K)
+    w = workloads.ternary(rng, rows, K)
+    p = host(gpu_pack(w, 0.015))
+    pe = oracle.pack(w, 0.015)
+    assert p.shape == pe.shape
+    assert np.array_equal(p, pe)
+
+
+def test_pack_maps_other_values_by_sign():
+    rng = np.random.default_rng(1)
+    w = rng.integers(-128, 128, size=(5, 384), dtype=np.int8)
+    assert np.array_equal(host(gpu_pack(w, 2.0)), oracle.pack(w, 2.0))
+
+
+# --- quantize -------------------------------------------------------------------
+
+def _quant_inputs():
+    out = [("small", workloads.small_case().x), ("decode_up", workloads.decode_up_case().x),
+           ("down_relu", workloads.down_small_batch_case().x[:, :]),
+           ("prefill", workloads.prefill_gate_case().x)]
+    ties = near_tie_rows()
+    L = max(r.size for r in ties)
+    out.append(("near_ties", np.stack([np.pad(r, (0, L - r.size)) for r in ties])))
+    z = np.zeros((3, 256), np.float32)
+    z[1] = np.float32(1e-7)
+    z[2, 5] = np.float32(-3e-6)
+    out.append(("zero_and_tiny", z))
+    out.append(("headroom", np.full((2, 8960), 127.0, np.float32)))
+    return out
+
+
+@pytest.mark.parametrize("name,x", _quant_inputs(), ids=lambda v: v if isinstance(v, str) else "")
+def test_quantize_matches_oracle(name, x):
+    say(f"[quantize] {name} shape={x.shape}")
+    q, s, rs = i2s.i2s_quantize_act(dev(x))
+    qe, se, rse = oracle.quantize_act(x)
+    assert np.array_equal(host(q), qe)
+    assert np.array_equal(bits(host(s)), bits(se))
+    assert np.array_equal(host(rs), rse)
+
+
+# --- the five workloads, through the automatic dispatch that the benchmark uses -------
+
+def test_small_case():
+    check_mul_mat(workloads.small_case())
+
+
+def test_decode_up_gemv_full():
+    check_mul_mat(workloads.decode_up_case())
+
+
+def test_down_small_batch_full():
+    check_mul_mat(workloads.down_small_batch_case())
+
+
+def test_prefill_gate_gemm_sampled():
+    case = workloads.prefill_gate_case()
+    sample = np.unique(np.concatenate([np.arange(0, 48), np.arange(8960 - 40, 8960),
+                                       np.random.default_rng(0).choice(8960, 64, replace=False)]))
+    check_mul_mat(case, sample=sample)
+
+
+@pytest.mark.parametrize("case", workloads.layer_sweep_cases(), ids=lambda c: c.name)
+def test_layer_sweep(case):
+    rows = case.rows
+    sample = None
+    if case.N * rows * case.K > 60_000_000:
+        sample = np.unique(np.concatenate([np.arange(0, 20), np.arange(rows - 20, rows),
+                                           np.random.default_rng(1).choice(rows, 40, replace=False)]))
+    check_mul_mat(case, sample=sample)
+
+
+# --- every launch geometry gives the same bits (the M2 grid) -------------------------
+
+GRID_K = (128, 1024, 1152)
+GRID_DIM = (1, 2, 64, 70, 100)
+
+
+@pytest.mark.parametrize("K", GRID_K)
+def test_grid_all_kernels_and_variants(K):
+    rng = np.random.default_rng(K + 5)
+    wmax = workloads.ternary(rng, max(GRID_DIM), K)
+    xmax = workloads.normal(rng, max(GRID_DIM), K)
+    nv1, nv2 = i2s.i2s_kernel_variants(1), i2s.i2s_kernel_variants(2)
+    for rows in GRID_DIM:
+        w = wmax[:rows]
+        pnp = oracle.pack(w, 0.015)
+        pg = gpu_pack(w, 0.015)
+        assert np.array_equal(host(pg), pnp)
+        for N in GRID_DIM:
+            x = xmax[:N]
+            ye, de = oracle.mul_mat(pnp, rows, K, x, with_dot=True)
+            combos = [(0, 0)] + [(2, v) for v in range(1, nv2 + 1)]
+            if N <= 8:
+                combos += [(1, v) for v in range(1, nv1 + 1)]
+            say(f"[grid] K={K} rows={rows} N={N} combos={len(combos)}")
+            xg = dev(x)
+            for kern, var in combos:
+                y, d = i2s.i2s_mul_mat_ex(pg, rows, K, xg, dot_out=True, kernel=kern, variant=var)
+                y, d = host(y), host(d)
+                assert np.array_equal(d, de), (K, rows, N, kern, var)
+                assert np.array_equal(bits(y), bits(ye)), (K, rows, N, kern, var)
+
+
+@pytest.mark.parametrize("N", [1, 3, 8])
+def test_all_gemv_variants_full_decode_shapes(N):
+    """GEMV variants on the decoder shapes (K = 1536 and 8960) against the oracle."""
+    for rows, K in [(8960, 1536), (1536, 8960), (256, 1536)]:
+        case = workloads.random_case(21, rows, K, N)
+        pnp = oracle.pack(case.w, case.ws)
+        pg = gpu_pack(case.w, case.ws)
+        sample = np.unique(np.concatenate([np.arange(0, 24), np.arange(rows - 24, rows),
+                                           np.random.default_rng(2).choice(rows, 48, replace=False)]))
+        for v in range(1, i2s.i2s_kernel_variants(1) + 1):
+            check_mul_mat(case, kernel=1, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
+
+
+def test_all_gemm_variants_prefill_shape():
+    case = workloads.prefill_gate_case(N=200)
+    pnp = oracle.pack(case.w, case.ws)
+    pg = gpu_pack(case.w, case.ws)
+    sample = np.unique(np.concatenate([np.arange(0, 40), np.arange(8960 - 40, 8960),
+                                       np.random.default_rng(3).choice(8960, 40, replace=False)]))
+    for v in range(1, i2s.i2s_kernel_variants(2) + 1):
+        check_mul_mat(case, kernel=2, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
+
+
+# --- edge cases -----------------------------------------------------------------------
+
+@pytest.mark.parametrize("N", [1, 8, 64])
+def test_headroom(N):
+    case = workloads.headroom_case(N)
+    y = check_mul_mat(case, sample=np.array([0, 1, 777, 1535]))
+    assert (bits(y) == 0x46855999).all()
+
+
+@pytest.mark.parametrize("N,row", [(1, 0), (64, 17)])
+def test_zero_activation_row(N, row):
+    case = workloads.zero_row_case(N, row)
+    y = check_mul_mat(case, sample=np.array([0, 5, 4000, 8959]))
+    assert (bits(y[row]) == 0).all()
+    assert not np.isnan(y).any()
+
+
+def test_zero_weights_zero_scale():
+    rng = np.random.default_rng(4)
+    for N in (1, 5, 33):
+        case = workloads.Case("zero_w", np.zeros((96, 1024), np.int8), 0.0, workloads.normal(rng, N, 1024))
+        y = check_mul_mat(case)
+        assert not np.isnan(y).any() and (y == 0).all()
+
+
+@pytest.mark.parametrize("rows,K,N", [(1, 128, 1), (17, 384, 9), (33, 640, 3), (130, 1152, 17), (8961 - 16, 1536, 2),
+                                      (5, 8960, 100), (1000, 256, 300)])
+def test_ragged_shapes(rows, K, N):
+    case = workloads.random_case(rows + N, rows, K, N, ws=0.031)
+    sample = None if rows * K * N < 40_000_000 else np.arange(0, rows, 97)
+    check_mul_mat(case, sample=sample)
+    if N <= 8:
+        check_mul_mat(case, kernel=2, variant=1, sample=sample)
+
+
+def test_empty_inputs_are_noops():
+    pg = gpu_pack(np.zeros((4, 128), np.int8), 1.0)
+    y = torch.full((1, 4), 7.0, device=DEV)
+    i2s.i2s_mul_mat(pg, 4, 128, torch.empty((0, 128), device=DEV), y=y)  # N == 0
+    assert (host(y) == 7.0).all()
+    yy = torch.full((3, 1), 5.0, device=DEV)
+    i2s.i2s_mul_mat(gpu_pack(np.zeros((0, 128), np.int8), 1.0), 0, 128, torch.zeros((3, 128), device=DEV), y=yy)
+    assert (host(yy) == 5.0).all()  # rows == 0
+
+
+def test_error_codes_through_binding():
+    pg = gpu_pack(np.zeros((4, 128), np.int8), 1.0)
+    x = torch.zeros((2, 128), device=DEV)
+    with pytest.raises(i2s.I2SError) as e:
+        i2s.i2s_mul_mat(pg, 4, 128, x, workspace=torch.empty(64, dtype=torch.uint8, device=DEV))
+    assert e.value.status == i2s.I2S_EWORKSPACE
+    with pytest.raises(i2s.I2SError) as e:
+        i2s.i2s_mul_mat_ex(pg, 4, 128, torch.zeros((9, 128), device=DEV), kernel=1)
+    assert e.value.status == i2s.I2S_EKERNEL
+
+
+def test_non_default_stream_and_reuse():
+    """Calls on a side stream, reusing one workspace, in order."""
+    case = workloads.random_case(8, 512, 1024, 12)
+    pnp = oracle.pack(case.w, case.ws)
+    pg = gpu_pack(case.w, case.ws)
+    ye = oracle.mul_mat(pnp, 512, 1024, case.x)
+    s = torch.cuda.Stream()
+    ws = i2s.new_workspace(12, 1024, DEV)
+    x = dev(case.x)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        outs = [i2s.i2s_mul_mat(pg, 512, 1024, x[: n], workspace=ws, stream=s) for n in (12, 3, 12)]
+    s.synchronize()
+    assert np.array_equal(bits(host(outs[0])), bits(ye))
+    assert np.array_equal(bits(host(outs[1])), bits(ye[:3]))
+    assert np.array_equal(bits(host(outs[2])), bits(ye))
+
+
+def test_shared_workspace_feeds_several_weights():
+    """One i2s_quantize_act_ws, then i2s_mul_mat_ws against q, k and v shaped
+    weights: each result equals the oracle's."""
+    rng = np.random.default_rng(30)
+    K = 1536
+    for N in (1, 16):
+        x = workloads.normal(rng, N, K)
+        ws = i2s.new_workspace(N, K, DEV)
+        i2s.i2s_quantize_act_ws(dev(x), ws)
+        for rows in (1536, 256, 256):
+            w = workloads.ternary(rng, rows, K)
+            pnp = oracle.pack(w, 0.015)
+            y, d = i2s.i2s_mul_mat_ws(gpu_pack(w, 0.015), rows, K, N, ws, dot_out=True)
+            ye, de = oracle.mul_mat(pnp, rows, K, x, with_dot=True)
+            assert np.array_equal(host(d), de)
+            assert np.array_equal(bits(host(y)), bits(ye))

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from exact import AMAX_FLOOR, epilogue, f32_bits, f32_round, frac, quantize_row, round_half_away
+from exact import AMAX_FLOOR, epilogue, f32_bits, f32_round, frac, near_tie_rows, quantize_row, round_half_away
 from goldens import headroom, pack_cases, quantize_cases
 from ternary_weight_integer_amd import workloads
 
@@ -73,30 +73,10 @@ def test_quantize_matches_hand_worked_vector(case):
     assert int(rs[0]) == case["row_sum"]
 
 
-def _near_tie_rows():
-    """Rows whose values sit on or next to a .5 boundary of x/s for a scale s
-    that is not a power of two, so the division's last bit decides q."""
-    rows = []
-    for amax in [np.float32(100.0), np.float32(3.3), np.float32(0.77), np.float32(12345.678)]:
-        s = f32_round(frac(amax) / 127)
-        vals = [amax]
-        for m in range(-126, 127):
-            centre = np.float32(float((frac(m) + frac(0.5)) * frac(s)))
-            for d in (-2, -1, 0, 1, 2):
-                vals.append(np.nextafter(centre, np.float32(np.inf) if d > 0 else np.float32(-np.inf))
-                            if d else centre)
-                if abs(d) == 2:
-                    vals[-1] = np.nextafter(vals[-1], np.float32(np.inf) if d > 0 else np.float32(-np.inf))
-        row = np.array([v for v in vals if abs(v) <= amax], dtype=np.float32)
-        pad = (-row.size) % 128
-        rows.append(np.concatenate([row, np.zeros(pad, np.float32)]))
-    return rows
-
-
 def test_quantize_matches_exact_rational_on_near_ties():
     found_recip_flip = 0
     found_tie = 0
-    for x in _near_tie_rows():
+    for x in near_tie_rows():
         q, s, rs = oracle.quantize_act(x[None, :])
         eq, es, ers = quantize_row(x)
         assert f32_bits(s[0]) == f32_bits(es)
