@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Throughput of the I2_S W2A8 matmul hot path on one MI355X.
+
+One step = the whole hot path on one batch: quantize the F32 activation rows
+(amax/127 scale, int8 values, int8 row sums) and run the ternary contraction
+with its fused epilogue (i2s_mul_mat).  Packing the weights happens once,
+before timing, as it does offline for a checkpoint.
+
+Default workload: the Qwen2-1.5B FFN up projection at decode time, ternary
+weight [8960][1536] (P(-1,0,+1) = 0.3/0.4/0.3, scale 0.015) against one F32
+activation row ~ N(0,1) with 1% of its entries scaled by 20, seed 0.
+
+Measurement:
+  * every input is resident in device memory before the timed region; the
+    packed weight is replicated into enough distinct copies (>= 512 MiB in
+    total, twice the 256 MiB Infinity Cache) and step i uses copy i mod R,
+    so each step reads its weights from HBM, as a 28-layer decode does;
+  * the K timed steps are captured once in a HIP graph (launches from Python
+    would otherwise be slower than the kernels) and replayed between two HIP
+    events on the launch stream, bracketed by device synchronizations;
+  * the dominant kernel's average launch duration comes from a second graph of
+    back-to-back launches of that kernel alone, timed the same way inside the
+    same bracket; roofline.achieved = algorithmic bytes per launch / that time;
+  * cpu_baseline: the CPU oracle (plain scalar C, one thread) on the same
+    workload, repeated for about --cpu-seconds.
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "I2_S W2A8 matmul: weight GB/s & int8 TOPS at 1 GPU; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8.0 TB/s
+INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
+ROTATE_BYTES = 512 << 20
+KERNEL_SRC = os.path.join(ROOT, "ternary_weight_integer_amd", "csrc", "i2s.hip")
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--workload", default="decode_up",
+                   choices=["decode_up", "prefill_gate", "down_small_batch", "small"])
+    p.add_argument("--copies", type=int, default=0, help="weight copies to rotate over (0 = enough for 512 MiB)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--eager", action="store_true",
+                   help="launch from Python without graphs (for counter collection runs)")
+    p.add_argument("--copy-kernel-mib", type=int, default=0,
+                   help="only run a plain copy of this many MiB (counter calibration) and exit")
+    return p.parse_args(argv)
+
+
+def make_case(name):
+    from ternary_weight_integer_amd import workloads
+    return {
+        "decode_up": workloads.decode_up_case,
+        "prefill_gate": workloads.prefill_gate_case,
+        "down_small_batch": workloads.down_small_batch_case,
+        "small": workloads.small_case,
+    }[name]()
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9.]+)", text, re.M)
+    m_h = re.search(r"^kernel_source_sha256_16:\s*([0-9a-f]+)", text, re.M)
+    if not m_b or not m_h or m_h.group(1) != kernel_source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(case, seconds: float):
+    import numpy as np
+
+    import oracle
+    packed = oracle.pack(case.w, case.ws)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.mul_mat(packed, case.rows, case.K, case.x)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    wbytes = case.rows * case.K // 4
+    return {"value": round(wbytes * calls / el / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full calls of the same workload ({case.name}, quantize+contract+epilogue, "
+                      f"scalar C, 1 thread) in {el:.1f} s",
+            "cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0)),
+            "ms_per_call": round(el / calls * 1e3, 3)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def graph_of(fn, torch):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the allocator and the launch path outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def copy_kernel_only(mib: int):
+    import torch
+    dev = torch.device("cuda:0")
+    n = (mib << 20) // 4
+    a = torch.ones(n, device=dev)
+    b = torch.empty(n, device=dev)
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}), flush=True)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the kernel runs on one GPU's share; see the sharding note in the design document)",
+              file=sys.stderr, flush=True)
+        return 2
+    if args.copy_kernel_mib:
+        copy_kernel_only(args.copy_kernel_mib)
+        return 0
+
+    import numpy as np
+    import torch
+
+    from ternary_weight_integer_amd import i2s
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    case = make_case(args.workload)
+    rows, K, N = case.rows, case.K, case.N
+    wbytes = rows * K // 4
+    packed0 = i2s.i2s_pack(torch.from_numpy(case.w).to(dev), case.ws)
+    R = args.copies or max(1, -(-ROTATE_BYTES // packed0.numel()))
+    copies = [packed0] + [packed0.clone() for _ in range(R - 1)]
+    x = torch.from_numpy(case.x).to(dev)
+    ws = i2s.new_workspace(N, K, dev)
+    y = torch.empty((N, rows), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        i2s.i2s_mul_mat(copies[i % R], rows, K, x, workspace=ws, y=y)
+
+    gemv = N <= 8
+    kernel_kind = 1 if gemv else 2
+
+    def contraction(i):
+        i2s.i2s_mul_mat_ws(copies[i % R], rows, K, N, ws, y=y, kernel=kernel_kind)
+
+    # Warm-up steps (eager), then a correctness check of the graph path.
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+
+    K_steps = args.steps
+    if args.eager:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(K_steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = e0.elapsed_time(e1) / K_steps
+        kern_us = None
+    else:
+        g_step = graph_of(lambda: [step(i) for i in range(K_steps)], torch)
+        n_kern = max(R, 256)
+        g_kern = graph_of(lambda: [contraction(i) for i in range(n_kern)], torch)
+        g_step.replay()
+        g_kern.replay()
+        torch.cuda.synchronize()
+        # y now holds the last contraction of copy (n_kern-1) % R; every copy is identical.
+        if not torch.equal(y.view(torch.int32), y_eager.view(torch.int32)):
+            raise RuntimeError("graph replay result differs from the eager result")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record()
+        g_step.replay()
+        ev[1].record()
+        g_kern.replay()
+        ev[2].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = ev[0].elapsed_time(ev[1]) / K_steps
+        kern_us = ev[1].elapsed_time(ev[2]) * 1e3 / n_kern
+        if not torch.equal(y.view(torch.int32), y_eager.view(torch.int32)):
+            raise RuntimeError("graph replay result differs from the eager result")
+
+    ops = 2 * rows * K * N
+    value = wbytes / (step_ms * 1e-3) / 1e9
+    # Algorithmic bytes of one contraction launch: packed weights + int8
+    # activations + F32 outputs + per-row scale and row sum + the weight scale.
+    alg_bytes = wbytes + N * K + 4 * N * rows + 8 * N + 4
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": case.name, "rows": rows, "K": K, "N": N, "weight_scale": case.ws,
+                   "weight_copies_rotated": R, "rotated_bytes": R * packed0.numel(),
+                   "timing": "eager" if args.eager else "hip_graph"},
+        "int8_tops": round(ops / (step_ms * 1e-3) / 1e12, 4),
+        "wall_s": round(wall, 4),
+    }
+    if kern_us is not None:
+        if gemv:
+            achieved = alg_bytes / (kern_us * 1e-6) / 1e9
+            out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                               "kernel": "gemv_kernel", "kernel_us": round(kern_us, 4),
+                               "alg_bytes_per_launch": alg_bytes}
+        else:
+            achieved = ops / (kern_us * 1e-6) / 1e12
+            out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_MFMA_PEAK_TOPS,
+                               "unit": "TOP/s", "frac": round(achieved / INT8_MFMA_PEAK_TOPS, 4),
+                               "traffic": measured_traffic(args.workload), "kernel": "gemm_kernel",
+                               "kernel_us": round(kern_us, 4), "alg_ops_per_launch": ops,
+                               "alg_bytes_per_launch": alg_bytes}
+    props = torch.cuda.get_device_properties(0)
+    out["gpu"] = {"name": props.name, "cus": props.multi_processor_count,
+                  "arch": getattr(props, "gcnArchName", "")}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
