@@ -29,6 +29,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "i2s.h"
 
 namespace {
@@ -307,6 +309,17 @@ struct GemmCfg {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+// The 16 codes of one packed dword as an MFMA operand: dword s holds slice s
+// ((w >> (6-2s)) & 0x03030303), i.e. positions 32s+gp .. 32s+gp+3.
+__device__ inline v4i unpack_codes(uint32_t w) {
+  v4i a;
+  a[0] = static_cast<int>((w >> 6) & kCodeMask);
+  a[1] = static_cast<int>((w >> 4) & kCodeMask);
+  a[2] = static_cast<int>((w >> 2) & kCodeMask);
+  a[3] = static_cast<int>(w & kCodeMask);
+  return a;
+}
+
 template <class Cfg>
 __global__ void __launch_bounds__(Cfg::kThreads)
 gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
@@ -332,16 +345,28 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 #pragma unroll
     for (int n = 0; n < WN; ++n) acc[m][n] = v4i{0, 0, 0, 0};
 
-  // Cooperative copy of one K-step of activations (kBN rows x 256 bytes) into LDS.
-  auto stage_act = [&](int64_t kk, int buf) {
-    constexpr int kPieces = Cfg::kBN * 16;  // 16-byte pieces
+  // Cooperative copy of one K-step of activations (kBN rows x 256 bytes):
+  // global loads into registers first, LDS stores later, so the loads of step
+  // kk+1 are in flight while step kk's MFMAs run.
+  constexpr int kPieces = Cfg::kBN * 16;  // 16-byte pieces per step
+  constexpr int kPer = (kPieces + Cfg::kThreads - 1) / Cfg::kThreads;
+  auto load_act = [&](int64_t kk, uint4 (&v)[kPer]) {
     const int64_t kbytes = (K - 256 * kk) >= 256 ? 256 : (K - 256 * kk);
-    for (int p = tid; p < kPieces; p += Cfg::kThreads) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = tid + i * Cfg::kThreads;
       const int r = p / 16, c = p % 16;
       const int64_t n = n_blk + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < N && 16 * c < kbytes) v = *reinterpret_cast<const uint4 *>(qp + n * K + 256 * kk + 16 * c);
-      *reinterpret_cast<uint4 *>(lds + buf * Cfg::kLdsStage + r * Cfg::kLdsStride + 16 * c) = v;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (p < kPieces && n < N && 16 * c < kbytes) v[i] = *reinterpret_cast<const uint4 *>(qp + n * K + 256 * kk + 16 * c);
+    }
+  };
+  auto store_act = [&](int buf, const uint4 (&v)[kPer]) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = tid + i * Cfg::kThreads;
+      const int r = p / 16, c = p % 16;
+      if (p < kPieces) *reinterpret_cast<uint4 *>(lds + buf * Cfg::kLdsStage + r * Cfg::kLdsStride + 16 * c) = v[i];
     }
   };
 
@@ -358,15 +383,18 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   };
 
   uint4 wcur[WM], wnext[WM];
+  uint4 anext[kPer];
   load_w(0, wcur);
-  stage_act(0, 0);
+  load_act(0, anext);
+  store_act(0, anext);
   __syncthreads();
 
   for (int64_t kk = 0; kk < steps; ++kk) {
     const int buf = static_cast<int>(kk & 1);
-    if (kk + 1 < steps) {
+    const bool more = kk + 1 < steps;
+    if (more) {
       load_w(kk + 1, wnext);
-      stage_act(kk + 1, buf ^ 1);
+      load_act(kk + 1, anext);
     }
     const int8_t *lb = lds + buf * Cfg::kLdsStage;
 #pragma unroll
@@ -380,15 +408,13 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 #pragma unroll
       for (int m = 0; m < WM; ++m) {
         const uint32_t wd = d == 0 ? wcur[m].x : d == 1 ? wcur[m].y : d == 2 ? wcur[m].z : wcur[m].w;
-        v4i a;
-        a[0] = static_cast<int>((wd >> 6) & kCodeMask);
-        a[1] = static_cast<int>((wd >> 4) & kCodeMask);
-        a[2] = static_cast<int>((wd >> 2) & kCodeMask);
-        a[3] = static_cast<int>(wd & kCodeMask);
+        const v4i a = unpack_codes(wd);
 #pragma unroll
         for (int n = 0; n < WN; ++n) acc[m][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[m][n], 0, 0, 0);
       }
     }
+    // The other buffer was last read in step kk-1, before the barrier that ended it.
+    if (more) store_act(buf ^ 1, anext);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < WM; ++m) wcur[m] = wnext[m];
@@ -418,6 +444,152 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
           if (o + r < rows) {
             yr[o + r] = epilogue(acc[m][n][r], rs, t);
             if (dot_out) dot_out[nn * rows + o + r] = acc[m][n][r];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Activation-resident GEMM (same MFMA operand mapping as above).  The
+// workgroup's activation tile, BN = 16*WN rows by the whole K (zero-padded to
+// a multiple of 256 and to BN rows), is copied into LDS once; the row pitch
+// is 16 bytes past a multiple of 256 so the 16 lanes that read one 16-byte
+// column of 16 rows hit distinct banks.  The tile's ms 16-row weight subtiles
+// are dealt to the 4 waves round-robin; a wave streams its weight rows
+// straight from HBM into registers one K-step ahead, accumulates G subtiles
+// x WN column blocks at a time, and stores each finished group before it
+// starts the next, so output stores overlap the following MFMAs.  No barrier
+// after the copy: waves run independently.
+
+constexpr int kResThreads = 256;
+constexpr int kResMaxLds = 160 * 1024;
+
+__host__ __device__ inline int64_t res_pitch(int64_t K) { return (K + 255) / 256 * 256 + 16; }
+
+template <int G, int WN>
+__global__ void __launch_bounds__(kResThreads)
+gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
+                const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
+                const int32_t *__restrict__ row_sum, float *__restrict__ y,
+                int32_t *__restrict__ dot_out, int64_t tiles_m, int ms) {
+  extern __shared__ __attribute__((aligned(16))) int8_t lds_res[];
+  constexpr int BN = 16 * WN;
+  constexpr int kStageBatch = 8;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, kb = lane >> 4;
+  const int64_t tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
+  const int64_t o_tile = tile_m * ms * 16;
+  const int64_t n0 = tile_n * BN;
+  const int64_t row_bytes = K / 4;
+  const int steps = static_cast<int>((K + 255) / 256);
+  const int64_t pitch = res_pitch(K);
+  const int64_t present = (rows - o_tile + 15) / 16;
+  const int msub = static_cast<int>(present < ms ? present : ms);
+  const int mine = msub > wave ? (msub - wave + 3) / 4 : 0;  // subtiles wave, wave+4, ...
+  const int groups = (mine + G - 1) / G;
+
+  auto load_w = [&](int grp, int kk, uint4 (&wv)[G]) {
+    const int64_t pbytes = (row_bytes - 64 * static_cast<int64_t>(kk)) >= 64 ? 64 : 32;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const int idx = grp * G + gi;
+      const int64_t o = o_tile + 16 * (wave + 4 * idx) + li;
+      if (idx < mine && o < rows && 16 * kb < pbytes)
+        wv[gi] = *reinterpret_cast<const uint4 *>(packed + o * row_bytes + 64 * static_cast<int64_t>(kk) + 16 * kb);
+      else
+        wv[gi] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);  // code 1 = weight 0
+    }
+  };
+
+  uint4 wcur[G], wnext[G];
+  if (groups > 0) load_w(0, 0, wcur);
+
+  // Copy the activation tile into LDS, kStageBatch 16-byte pieces per thread
+  // in flight at a time.
+  {
+    const int64_t per_row = static_cast<int64_t>(steps) * 16;  // 16-byte pieces per padded row
+    const int64_t total = per_row * BN;
+    for (int64_t base = 0; base < total; base += static_cast<int64_t>(kResThreads) * kStageBatch) {
+      uint4 v[kStageBatch];
+#pragma unroll
+      for (int i = 0; i < kStageBatch; ++i) {
+        const int64_t p = base + tid + static_cast<int64_t>(i) * kResThreads;
+        const int64_t r = p / per_row, c = p % per_row;
+        const int64_t n = n0 + r;
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (p < total && n < N && 16 * c < K) v[i] = *reinterpret_cast<const uint4 *>(qp + n * K + 16 * c);
+      }
+#pragma unroll
+      for (int i = 0; i < kStageBatch; ++i) {
+        const int64_t p = base + tid + static_cast<int64_t>(i) * kResThreads;
+        const int64_t r = p / per_row, c = p % per_row;
+        if (p < total) *reinterpret_cast<uint4 *>(lds_res + r * pitch + 16 * c) = v[i];
+      }
+    }
+  }
+  __syncthreads();
+
+  const float ws = *reinterpret_cast<const float *>(packed + rows * row_bytes);
+  v4i acc[G][WN];
+  for (int grp = 0; grp < groups; ++grp) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int n = 0; n < WN; ++n) acc[gi][n] = v4i{0, 0, 0, 0};
+    for (int kk = 0; kk < steps; ++kk) {
+      if (kk + 1 < steps)
+        load_w(grp, kk + 1, wnext);
+      else if (grp + 1 < groups)
+        load_w(grp + 1, 0, wnext);
+      const int8_t *lb = lds_res + 256 * static_cast<int64_t>(kk) + 64 * kb;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        v4i b[WN];
+#pragma unroll
+        for (int n = 0; n < WN; ++n) b[n] = *reinterpret_cast<const v4i *>(lb + (16 * n + li) * pitch + 16 * d);
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+          if (grp * G + gi < mine) {  // wave-uniform
+            const uint32_t wd = d == 0 ? wcur[gi].x : d == 1 ? wcur[gi].y : d == 2 ? wcur[gi].z : wcur[gi].w;
+            const v4i a = unpack_codes(wd);
+#pragma unroll
+            for (int n = 0; n < WN; ++n) acc[gi][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[gi][n], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) wcur[gi] = wnext[gi];
+    }
+    // Epilogue for this group: lane l holds C[4*(l/16) + r][l % 16].
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+      const int64_t nn = n0 + 16 * n + li;
+      if (nn >= N) continue;
+      const float t = ws * act_scale[nn];
+      const int32_t rs = row_sum[nn];
+      float *yr = y + nn * rows;
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const int idx = grp * G + gi;
+        if (idx >= mine) continue;
+        const int64_t o = o_tile + 16 * (wave + 4 * idx) + 4 * kb;
+        if (o + 3 < rows && (rows % 4) == 0) {
+          *reinterpret_cast<float4 *>(yr + o) =
+              make_float4(epilogue(acc[gi][n][0], rs, t), epilogue(acc[gi][n][1], rs, t),
+                          epilogue(acc[gi][n][2], rs, t), epilogue(acc[gi][n][3], rs, t));
+          if (dot_out)
+            *reinterpret_cast<int4 *>(dot_out + nn * rows + o) =
+                make_int4(acc[gi][n][0], acc[gi][n][1], acc[gi][n][2], acc[gi][n][3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (o + r < rows) {
+              yr[o + r] = epilogue(acc[gi][n][r], rs, t);
+              if (dot_out) dot_out[nn * rows + o + r] = acc[gi][n][r];
+            }
           }
         }
       }
@@ -492,24 +664,23 @@ using GemmA = GemmCfg<4, 4, 4, 1>;  // 256 x 64 block, 4 waves
 using GemmB = GemmCfg<4, 2, 2, 2>;  // 128 x 64 block, 4 waves
 using GemmC = GemmCfg<5, 4, 4, 1>;  // 320 x 64 block, 4 waves
 using GemmD = GemmCfg<2, 2, 4, 1>;  // 128 x 32 block, 4 waves
-constexpr int kGemmVariants = 4;
 
 template <class Cfg>
 int64_t gemm_blocks(int64_t rows, int64_t N) {
   return ((rows + Cfg::kBM - 1) / Cfg::kBM) * ((N + Cfg::kBN - 1) / Cfg::kBN);
 }
 
-// Pick the configuration whose most loaded compute unit (256 CUs, one block
-// each at a time) does the least padded MFMA work.
-int pick_gemm_variant(int64_t rows, int64_t N) {
+// Pick the streaming configuration whose most loaded compute unit (256 CUs,
+// one block each at a time) does the least padded MFMA work.
+int pick_stream_variant(int64_t rows, int64_t N) {
   const int64_t cus = 256;
   int64_t best_cost = -1;
   int best = 1;
-  const int64_t blocks[kGemmVariants] = {gemm_blocks<GemmA>(rows, N), gemm_blocks<GemmB>(rows, N),
-                                         gemm_blocks<GemmC>(rows, N), gemm_blocks<GemmD>(rows, N)};
-  const int64_t area[kGemmVariants] = {GemmA::kBM * GemmA::kBN, GemmB::kBM * GemmB::kBN,
-                                       GemmC::kBM * GemmC::kBN, GemmD::kBM * GemmD::kBN};
-  for (int v = 0; v < kGemmVariants; ++v) {
+  const int64_t blocks[4] = {gemm_blocks<GemmA>(rows, N), gemm_blocks<GemmB>(rows, N),
+                             gemm_blocks<GemmC>(rows, N), gemm_blocks<GemmD>(rows, N)};
+  const int64_t area[4] = {GemmA::kBM * GemmA::kBN, GemmB::kBM * GemmB::kBN, GemmC::kBM * GemmC::kBN,
+                           GemmD::kBM * GemmD::kBN};
+  for (int v = 0; v < 4; ++v) {
     const int64_t rounds = (blocks[v] + cus - 1) / cus;
     const int64_t cost = rounds * area[v];
     if (best_cost < 0 || cost < best_cost) {
@@ -520,14 +691,70 @@ int pick_gemm_variant(int64_t rows, int64_t N) {
   return best;
 }
 
+// Activation-resident launch: BN = 16*WN activation rows per block; the
+// output features are split into tiles of ms 16-row subtiles so that the grid
+// is about one block per compute unit.
+template <int G, int WN>
+int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
+                   int32_t *dot_out, hipStream_t stream) {
+  constexpr int64_t BN = 16 * WN;
+  const int64_t lds = BN * res_pitch(K);
+  if (lds > kResMaxLds) return I2S_EKERNEL;
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t mt = (rows + 15) / 16;
+  int64_t tiles_m = 256 / tiles_n;
+  if (tiles_m < 1) tiles_m = 1;
+  int64_t ms = (mt + tiles_m - 1) / tiles_m;
+  if (ms < 1) ms = 1;
+  tiles_m = (mt + ms - 1) / ms;
+  const int64_t blocks = tiles_m * tiles_n;
+  if (blocks > kMaxDim || ms > kMaxDim) return I2S_ERANGE;
+  // Allow up to 160 KiB of dynamic LDS, once per device for this instantiation
+  // (repeating it from racing threads is harmless).
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return I2S_EHIP;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_res_kernel<G, WN>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kResMaxLds) != hipSuccess)
+      return I2S_EHIP;
+    attr_done.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL((gemm_res_kernel<G, WN>), dim3(static_cast<unsigned>(blocks)), dim3(kResThreads),
+                     static_cast<size_t>(lds), stream, packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out,
+                     tiles_m, static_cast<int>(ms));
+  return hip_status();
+}
+
+// GEMM variants (1-based): 1-4 streaming (GemmA..D), 5-9 activation-resident
+// (G, WN) = (3,4), (5,4), (2,4), (3,2), (4,1).  Automatic: the widest
+// activation-resident tile whose LDS copy fits, else the streaming pick.
+constexpr int kGemmVariants = 9;
+
 int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
                 float *y, int32_t *dot_out, hipStream_t stream) {
-  if (variant == 0) variant = pick_gemm_variant(rows, N);
+  if (variant == 0) {
+    const int64_t pitch = res_pitch(K);
+    if (64 * pitch <= kResMaxLds && N > 32)
+      variant = 5;
+    else if (32 * pitch <= kResMaxLds && N > 16)
+      variant = 8;
+    else if (16 * pitch <= kResMaxLds)
+      variant = 9;
+    else
+      variant = pick_stream_variant(rows, N);
+  }
   switch (variant) {
     case 1: return launch_gemm_cfg<GemmA>(packed, rows, K, N, ws, y, dot_out, stream);
     case 2: return launch_gemm_cfg<GemmB>(packed, rows, K, N, ws, y, dot_out, stream);
     case 3: return launch_gemm_cfg<GemmC>(packed, rows, K, N, ws, y, dot_out, stream);
     case 4: return launch_gemm_cfg<GemmD>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 5: return launch_res_cfg<3, 4>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 6: return launch_res_cfg<5, 4>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 7: return launch_res_cfg<2, 4>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 8: return launch_res_cfg<3, 2>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 9: return launch_res_cfg<4, 1>(packed, rows, K, N, ws, y, dot_out, stream);
     default: return I2S_EKERNEL;
   }
 }
