@@ -452,147 +452,334 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 }
 
 // ---------------------------------------------------------------------------
-// Activation-resident GEMM (same MFMA operand mapping as above).  The
-// workgroup's activation tile, BN = 16*WN rows by the whole K (zero-padded to
-// a multiple of 256 and to BN rows), is copied into LDS once; the row pitch
-// is 16 bytes past a multiple of 256 so the 16 lanes that read one 16-byte
-// column of 16 rows hit distinct banks.  The tile's ms 16-row weight subtiles
-// are dealt to the 4 waves round-robin; a wave streams its weight rows
-// straight from HBM into registers one K-step ahead, accumulates G subtiles
-// x WN column blocks at a time, and stores each finished group before it
-// starts the next, so output stores overlap the following MFMAs.  No barrier
-// after the copy: waves run independently.
+// Activation-resident GEMM (same MFMA operand mapping as above).
+//
+// The workgroup's activation tile -- BN = 16*WN rows by the whole K, padded
+// with zeros to chunks*S*256 columns -- is copied into LDS once; each wave
+// copies BN/WAVES whole rows with all of its loads in flight before the first
+// LDS store.  The row pitch is 16 bytes past a multiple of 256, so the 16
+// lanes that read one 16-byte column of 16 rows hit distinct banks.
+//
+// The tile's ms 16-row weight subtiles are dealt to the WAVES waves
+// round-robin.  A wave works through its subtiles G at a time and through K
+// in chunks of S steps (256 positions each).  Before computing a (group,
+// chunk) it issues the loads of the next one -- G x S x 16 bytes per lane,
+// straight from HBM into the other of two register sets -- so a chunk of MFMAs
+// covers the memory latency.  Each finished group is stored at once, so output
+// stores overlap later MFMAs.
+//
+// Every global access is a buffer access whose descriptor bounds the tensor
+// (out-of-range loads read 0, out-of-range stores are dropped by the
+// hardware), and no load or store sits under a branch.  The number of memory
+// operations in flight is therefore known at compile time, so each wait is
+// for the operations it needs (the weights of the current chunk) and never
+// for the prefetch or the stores issued after them.  Weight reads past the
+// last row, past K, or for a group shorter than G only ever meet zero
+// activations or feed outputs that are not stored.
 
-constexpr int kResThreads = 256;
 constexpr int kResMaxLds = 160 * 1024;
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // buffer offset beyond every descriptor's range
+constexpr int kBufferFlags = 0x00020000;       // raw buffer, 32-bit data format
 
-__host__ __device__ inline int64_t res_pitch(int64_t K) { return (K + 255) / 256 * 256 + 16; }
+__host__ __device__ inline int64_t res_pitch(int64_t K, int S) { return (K + 256 * S - 1) / (256 * S) * (256 * S) + 16; }
 
-template <int G, int WN>
-__global__ void __launch_bounds__(kResThreads)
+__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           kBufferFlags);
+}
+
+// Accumulate GS subtiles x WN column blocks over the S steps of one chunk.
+template <int GS, int G, int WN, int S>
+__device__ __forceinline__ void res_mfma_chunk(v4i (&acc)[G][WN], const v4i (&wv)[G][S], const int8_t *lb,
+                                               uint32_t pitch) {
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      v4i b[WN];
+#pragma unroll
+      for (int n = 0; n < WN; ++n) b[n] = *reinterpret_cast<const v4i *>(lb + 256 * st + 16 * n * pitch + 16 * d);
+#pragma unroll
+      for (int gi = 0; gi < GS; ++gi) {
+        const v4i a = unpack_codes(static_cast<uint32_t>(wv[gi][st][d]));
+#pragma unroll
+        for (int n = 0; n < WN; ++n) acc[gi][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[gi][n], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// One K-step (256 positions) of res_mfma_chunk.
+template <int GS, int G, int WN, int S>
+__device__ __forceinline__ void res_mfma_step(v4i (&acc)[G][WN], const v4i (&wv)[G][S], int st, const int8_t *lb,
+                                              uint32_t pitch) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    v4i b[WN];
+#pragma unroll
+    for (int n = 0; n < WN; ++n) b[n] = *reinterpret_cast<const v4i *>(lb + 256 * st + 16 * n * pitch + 16 * d);
+#pragma unroll
+    for (int gi = 0; gi < GS; ++gi) {
+      const v4i a = unpack_codes(static_cast<uint32_t>(wv[gi][st][d]));
+#pragma unroll
+      for (int n = 0; n < WN; ++n) acc[gi][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[gi][n], 0, 0, 0);
+    }
+  }
+}
+
+template <int G, int WN, int S, int WAVES, bool VEC4, bool DOT, bool SINGLE>
+__global__ void __launch_bounds__(64 * WAVES)
 gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
                 const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
                 const int32_t *__restrict__ row_sum, float *__restrict__ y,
                 int32_t *__restrict__ dot_out, int64_t tiles_m, int ms) {
   extern __shared__ __attribute__((aligned(16))) int8_t lds_res[];
   constexpr int BN = 16 * WN;
-  constexpr int kStageBatch = 8;
+  static_assert(BN % WAVES == 0, "whole activation rows per wave");
+  constexpr int kRowsPerWave = BN / WAVES;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kb = lane >> 4;
   const int64_t tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
   const int64_t o_tile = tile_m * ms * 16;
   const int64_t n0 = tile_n * BN;
-  const int64_t row_bytes = K / 4;
+  const int64_t n_here = N - n0 < BN ? N - n0 : BN;  // activation rows present in this tile
+  const uint32_t row_bytes = static_cast<uint32_t>(K / 4);
   const int steps = static_cast<int>((K + 255) / 256);
-  const int64_t pitch = res_pitch(K);
+  const int chunks = (steps + S - 1) / S;
+  const uint32_t pitch = static_cast<uint32_t>(res_pitch(K, S));
   const int64_t present = (rows - o_tile + 15) / 16;
   const int msub = static_cast<int>(present < ms ? present : ms);
-  const int mine = msub > wave ? (msub - wave + 3) / 4 : 0;  // subtiles wave, wave+4, ...
+  const int mine = msub > wave ? (msub - wave + WAVES - 1) / WAVES : 0;  // subtiles wave, wave+WAVES, ...
   const int groups = (mine + G - 1) / G;
+  const int iters = groups * chunks;
 
-  auto load_w = [&](int grp, int kk, uint4 (&wv)[G]) {
-    const int64_t pbytes = (row_bytes - 64 * static_cast<int64_t>(kk)) >= 64 ? 64 : 32;
+  // Weights: one descriptor over the payload; lane (li, kb) of subtile
+  // (o_tile + 16*(wave + WAVES*idx)) reads row li's bytes 64*kk + 16*kb..
+  const __amdgpu_buffer_rsrc_t wbuf = buffer_of(packed + o_tile * row_bytes, static_cast<uint32_t>((rows - o_tile) * row_bytes));
+  const uint32_t lane_off = li * row_bytes + 16 * kb;
+  auto load_w = [&](int grp, int ch, v4i (&wv)[G][S]) {
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
-      const int idx = grp * G + gi;
-      const int64_t o = o_tile + 16 * (wave + 4 * idx) + li;
-      if (idx < mine && o < rows && 16 * kb < pbytes)
-        wv[gi] = *reinterpret_cast<const uint4 *>(packed + o * row_bytes + 64 * static_cast<int64_t>(kk) + 16 * kb);
-      else
-        wv[gi] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);  // code 1 = weight 0
+      const uint32_t sub_off = static_cast<uint32_t>(16 * (wave + WAVES * (grp * G + gi))) * row_bytes + 64 * S * ch;
+#pragma unroll
+      for (int st = 0; st < S; ++st)
+        wv[gi][st] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lane_off + sub_off + 64 * st, 0, 0);
     }
   };
 
-  uint4 wcur[G], wnext[G];
-  if (groups > 0) load_w(0, 0, wcur);
-
-  // Copy the activation tile into LDS, kStageBatch 16-byte pieces per thread
-  // in flight at a time.
+  // Epilogue constants of this lane's activation rows (clamped inside the
+  // tensor; lanes past N never store), loaded before any prefetch so that
+  // waiting for them never waits for the prefetches.
+  const float ws = *reinterpret_cast<const float *>(packed + rows * static_cast<int64_t>(row_bytes));
+  float sn[WN];
+  int32_t rsn[WN];
   {
-    const int64_t per_row = static_cast<int64_t>(steps) * 16;  // 16-byte pieces per padded row
-    const int64_t total = per_row * BN;
-    for (int64_t base = 0; base < total; base += static_cast<int64_t>(kResThreads) * kStageBatch) {
-      uint4 v[kStageBatch];
+    // Buffer loads keep their place ahead of the prefetches (a plain
+    // read-only load may be sunk to its first use, behind them).
+    const __amdgpu_buffer_rsrc_t sbuf = buffer_of(act_scale + n0, static_cast<uint32_t>(4 * n_here));
+    const __amdgpu_buffer_rsrc_t rbuf = buffer_of(row_sum + n0, static_cast<uint32_t>(4 * n_here));
 #pragma unroll
-      for (int i = 0; i < kStageBatch; ++i) {
-        const int64_t p = base + tid + static_cast<int64_t>(i) * kResThreads;
-        const int64_t r = p / per_row, c = p % per_row;
-        const int64_t n = n0 + r;
-        v[i] = make_uint4(0, 0, 0, 0);
-        if (p < total && n < N && 16 * c < K) v[i] = *reinterpret_cast<const uint4 *>(qp + n * K + 16 * c);
-      }
-#pragma unroll
-      for (int i = 0; i < kStageBatch; ++i) {
-        const int64_t p = base + tid + static_cast<int64_t>(i) * kResThreads;
-        const int64_t r = p / per_row, c = p % per_row;
-        if (p < total) *reinterpret_cast<uint4 *>(lds_res + r * pitch + 16 * c) = v[i];
-      }
+    for (int n = 0; n < WN; ++n) {
+      const uint32_t off = static_cast<uint32_t>(4 * (16 * n + li));  // past N: reads 0, never stored
+      sn[n] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, off, 0, 0));
+      rsn[n] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, off, 0, 0);
     }
   }
-  __syncthreads();
 
-  const float ws = *reinterpret_cast<const float *>(packed + rows * row_bytes);
+  v4i wa[G][S], wb[G][S];
+  const int k_pieces = static_cast<int>(K / 16);
+  const __amdgpu_buffer_rsrc_t qbuf = buffer_of(qp + n0 * K, static_cast<uint32_t>(n_here * K));
+
+  // Activation-tile pieces of one K-step for this wave: kRowsPerWave rows x
+  // 16 pieces of 16 bytes, kPieceLanes per lane.
+  constexpr int kStepPieces = kRowsPerWave * 16;
+  constexpr int kPieceLanes = (kStepPieces + 63) / 64;
+  auto step_goff = [&](int st, int p) -> uint32_t {
+    const int pc = 64 * p + lane;
+    const int r = wave * kRowsPerWave + pc / 16;
+    const int c = 16 * st + pc % 16;  // 16-byte piece index within the padded row
+    return pc < kStepPieces && c < k_pieces ? static_cast<uint32_t>(r * K + 16 * c) : kOutOfRange;
+  };
+  auto step_loff = [&](int st, int p) -> uint32_t {
+    const int pc = 64 * p + lane;
+    const int r = wave * kRowsPerWave + pc / 16;
+    return static_cast<uint32_t>(r) * pitch + 16 * (16 * st + pc % 16);
+  };
+
+  v4i bst[SINGLE ? S : 1][kPieceLanes];
+  if constexpr (SINGLE) {
+    // Pipelined prologue: the loads of activation step st and of the first
+    // group's weights for step st go out together, step by step, followed by
+    // the next group's weights.  Below, the steps are written to LDS and
+    // multiplied one at a time, so the first MFMAs wait for 256 columns of
+    // the tile, not for all of it.
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+#pragma unroll
+      for (int p = 0; p < kPieceLanes; ++p) bst[st][p] = __builtin_amdgcn_raw_buffer_load_b128(qbuf, step_goff(st, p), 0, 0);
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const uint32_t sub_off = static_cast<uint32_t>(16 * (wave + WAVES * gi)) * row_bytes;
+        wa[gi][st] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lane_off + sub_off + 64 * st, 0, 0);
+      }
+    }
+    load_w(groups > 1 ? 1 : 0, 0, wb);
+  } else {
+    load_w(0, 0, wa);
+    // Copy the whole activation tile: wave w copies rows w*kRowsPerWave..,
+    // 16-byte pieces lane, lane+64, ... of each padded row; pieces past K
+    // read as zero.
+    const int per_row = chunks * S * 16;
+    for (int c0 = 0; c0 < per_row; c0 += 128) {
+      v4i v[kRowsPerWave][2];
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        const int r = wave * kRowsPerWave + i;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = c0 + 64 * h + lane;
+          const uint32_t off = c < k_pieces ? static_cast<uint32_t>(r * K + 16 * c) : kOutOfRange;
+          v[i][h] = __builtin_amdgcn_raw_buffer_load_b128(qbuf, off, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        const int r = wave * kRowsPerWave + i;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = c0 + 64 * h + lane;
+          if (c < per_row) *reinterpret_cast<v4i *>(lds_res + r * pitch + 16 * c) = v[i][h];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  const uint32_t out_bytes = static_cast<uint32_t>(n_here * rows * 4);
+  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + n0 * rows, out_bytes);
+  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + n0 * rows : nullptr, DOT ? out_bytes : 0);
+  const int8_t *lb0 = lds_res + li * pitch + 64 * kb;
+
+  float tn[WN];
+#pragma unroll
+  for (int n = 0; n < WN; ++n) tn[n] = ws * sn[n];
+
   v4i acc[G][WN];
-  for (int grp = 0; grp < groups; ++grp) {
+  // Stores of a finished group, non-temporal (the outputs are not read
+  // again by this kernel); subtiles past the group (gi >= gs) and outputs
+  // past the tensor get an out-of-range offset instead of a branch.
+  constexpr int kStreamStore = 2;
+  auto epilogue_group = [&](int grp, int gs) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const bool sub_ok = gi < gs;
+      const int64_t o = o_tile + 16 * static_cast<int64_t>(wave + WAVES * (grp * G + gi)) + 4 * kb;
+#pragma unroll
+      for (int n = 0; n < WN; ++n) {
+        const uint32_t base = static_cast<uint32_t>((16 * n + li) * rows);  // element offset of this lane's row
+        if constexpr (VEC4) {
+          const uint32_t off = sub_ok && o < rows ? 4 * (base + static_cast<uint32_t>(o)) : kOutOfRange;
+          const v4i yv = {__float_as_int(epilogue(acc[gi][n][0], rsn[n], tn[n])),
+                          __float_as_int(epilogue(acc[gi][n][1], rsn[n], tn[n])),
+                          __float_as_int(epilogue(acc[gi][n][2], rsn[n], tn[n])),
+                          __float_as_int(epilogue(acc[gi][n][3], rsn[n], tn[n]))};
+          __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, kStreamStore);
+          if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b128(acc[gi][n], dbuf, off, 0, kStreamStore);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t off = sub_ok && o + r < rows ? 4 * (base + static_cast<uint32_t>(o + r)) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(epilogue(acc[gi][n][r], rsn[n], tn[n])), ybuf, off,
+                                                  0, kStreamStore);
+            if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(acc[gi][n][r], dbuf, off, 0, kStreamStore);
+          }
+        }
+      }
+    }
+  };
+
+  auto zero_acc = [&]() {
 #pragma unroll
     for (int gi = 0; gi < G; ++gi)
 #pragma unroll
       for (int n = 0; n < WN; ++n) acc[gi][n] = v4i{0, 0, 0, 0};
-    for (int kk = 0; kk < steps; ++kk) {
-      if (kk + 1 < steps)
-        load_w(grp, kk + 1, wnext);
-      else if (grp + 1 < groups)
-        load_w(grp + 1, 0, wnext);
-      const int8_t *lb = lds_res + 256 * static_cast<int64_t>(kk) + 64 * kb;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        v4i b[WN];
-#pragma unroll
-        for (int n = 0; n < WN; ++n) b[n] = *reinterpret_cast<const v4i *>(lb + (16 * n + li) * pitch + 16 * d);
-#pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-          if (grp * G + gi < mine) {  // wave-uniform
-            const uint32_t wd = d == 0 ? wcur[gi].x : d == 1 ? wcur[gi].y : d == 2 ? wcur[gi].z : wcur[gi].w;
-            const v4i a = unpack_codes(wd);
-#pragma unroll
-            for (int n = 0; n < WN; ++n) acc[gi][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[gi][n], 0, 0, 0);
-          }
-        }
+  };
+
+  auto mfma_group = [&](const v4i (&cur)[G][S], int gs, const int8_t *lb) {
+    if (gs == G) {
+      res_mfma_chunk<G, G, WN, S>(acc, cur, lb, pitch);
+    } else {
+      switch (gs) {
+        case 1: res_mfma_chunk<1, G, WN, S>(acc, cur, lb, pitch); break;
+        case 2: if constexpr (G > 2) res_mfma_chunk<2, G, WN, S>(acc, cur, lb, pitch); break;
+        case 3: if constexpr (G > 3) res_mfma_chunk<3, G, WN, S>(acc, cur, lb, pitch); break;
+        case 4: if constexpr (G > 4) res_mfma_chunk<4, G, WN, S>(acc, cur, lb, pitch); break;
+        default: break;
       }
-#pragma unroll
-      for (int gi = 0; gi < G; ++gi) wcur[gi] = wnext[gi];
     }
-    // Epilogue for this group: lane l holds C[4*(l/16) + r][l % 16].
+  };
+
+  // One (group, chunk) item: prefetch the next item into `nxt` (past the last
+  // item this re-reads the first one, harmlessly), then compute `cur`.  With
+  // a single chunk (K <= 256*S) an item is a whole group and the body has no
+  // branch around any memory operation.
+  int grp = 0, ch = 0;
+  auto item = [&](const v4i (&cur)[G][S], v4i (&nxt)[G][S]) {
+    const int gs = grp + 1 < groups ? G : mine - grp * G;
+    if constexpr (SINGLE) {
+      load_w(grp + 1 < groups ? grp + 1 : 0, 0, nxt);
+      zero_acc();
+      mfma_group(cur, gs, lb0);
+      epilogue_group(grp, gs);
+      ++grp;
+    } else {
+      const int ngrp = ch + 1 < chunks ? grp : grp + 1;
+      const int nch = ch + 1 < chunks ? ch + 1 : 0;
+      load_w(ngrp < groups ? ngrp : 0, nch, nxt);
+      if (ch == 0) zero_acc();
+      mfma_group(cur, gs, lb0 + 256 * S * ch);
+      if (ch == chunks - 1) epilogue_group(grp, gs);
+      grp = ngrp;
+      ch = nch;
+    }
+  };
+
+  if constexpr (SINGLE) {
+    // First group, step by step, interleaved with the activation copy; waves
+    // without subtiles (gs0 == 0) still copy and meet every barrier.
+    const int gs0 = groups > 1 ? G : mine;
+    zero_acc();
 #pragma unroll
-    for (int n = 0; n < WN; ++n) {
-      const int64_t nn = n0 + 16 * n + li;
-      if (nn >= N) continue;
-      const float t = ws * act_scale[nn];
-      const int32_t rs = row_sum[nn];
-      float *yr = y + nn * rows;
+    for (int st = 0; st < S; ++st) {
 #pragma unroll
-      for (int gi = 0; gi < G; ++gi) {
-        const int idx = grp * G + gi;
-        if (idx >= mine) continue;
-        const int64_t o = o_tile + 16 * (wave + 4 * idx) + 4 * kb;
-        if (o + 3 < rows && (rows % 4) == 0) {
-          *reinterpret_cast<float4 *>(yr + o) =
-              make_float4(epilogue(acc[gi][n][0], rs, t), epilogue(acc[gi][n][1], rs, t),
-                          epilogue(acc[gi][n][2], rs, t), epilogue(acc[gi][n][3], rs, t));
-          if (dot_out)
-            *reinterpret_cast<int4 *>(dot_out + nn * rows + o) =
-                make_int4(acc[gi][n][0], acc[gi][n][1], acc[gi][n][2], acc[gi][n][3]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (o + r < rows) {
-              yr[o + r] = epilogue(acc[gi][n][r], rs, t);
-              if (dot_out) dot_out[nn * rows + o + r] = acc[gi][n][r];
-            }
-          }
+      for (int p = 0; p < kPieceLanes; ++p)
+        if (64 * p + lane < kStepPieces) *reinterpret_cast<v4i *>(lds_res + step_loff(st, p)) = bst[st][p];
+      __syncthreads();
+      if (gs0 == G) {
+        res_mfma_step<G, G, WN, S>(acc, wa, st, lb0, pitch);
+      } else {
+        switch (gs0) {
+          case 1: res_mfma_step<1, G, WN, S>(acc, wa, st, lb0, pitch); break;
+          case 2: if constexpr (G > 2) res_mfma_step<2, G, WN, S>(acc, wa, st, lb0, pitch); break;
+          case 3: if constexpr (G > 3) res_mfma_step<3, G, WN, S>(acc, wa, st, lb0, pitch); break;
+          case 4: if constexpr (G > 4) res_mfma_step<4, G, WN, S>(acc, wa, st, lb0, pitch); break;
+          default: break;
         }
       }
+    }
+    epilogue_group(0, gs0);
+    grp = 1;
+    for (int g = 1; g < groups; g += 2) {
+      item(wb, wa);
+      if (g + 1 >= groups) break;
+      item(wa, wb);
+    }
+  } else {
+    for (int it = 0; it < iters; it += 2) {
+      item(wa, wb);
+      if (it + 1 >= iters) break;
+      item(wb, wa);
     }
   }
 }
@@ -693,13 +880,43 @@ int pick_stream_variant(int64_t rows, int64_t N) {
 
 // Activation-resident launch: BN = 16*WN activation rows per block; the
 // output features are split into tiles of ms 16-row subtiles so that the grid
-// is about one block per compute unit.
-template <int G, int WN>
+// is about one block per compute unit.  Buffer offsets are 32-bit, so the
+// packed payload, the activation tile and the block's outputs must stay below
+// 2^31 bytes (else I2S_EKERNEL, and the automatic choice streams instead).
+template <int G, int WN, int S, int WAVES, bool VEC4, bool DOT, bool SINGLE>
+int launch_res_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
+                    const ActWorkspace &ws, float *y, int32_t *dot_out, int64_t tiles_m, int64_t ms,
+                    hipStream_t stream) {
+  // Allow up to 160 KiB of dynamic LDS, once per device for this instantiation
+  // (repeating it from racing threads is harmless).
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return I2S_EHIP;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_res_kernel<G, WN, S, WAVES, VEC4, DOT, SINGLE>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kResMaxLds) != hipSuccess)
+      return I2S_EHIP;
+    attr_done.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL((gemm_res_kernel<G, WN, S, WAVES, VEC4, DOT, SINGLE>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * WAVES), static_cast<size_t>(lds), stream, packed, rows, K, ws.q, N, ws.scale,
+                     ws.row_sum, y, dot_out, tiles_m, static_cast<int>(ms));
+  return hip_status();
+}
+
+template <int G, int WN, int S, int WAVES>
 int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
                    int32_t *dot_out, hipStream_t stream) {
   constexpr int64_t BN = 16 * WN;
-  const int64_t lds = BN * res_pitch(K);
+  const int64_t lds = BN * res_pitch(K, S);
   if (lds > kResMaxLds) return I2S_EKERNEL;
+  const int64_t lim = int64_t{1} << 31;
+  // Largest weight offset: rows past the tile by up to 16*WAVES*G (re-reads of
+  // a short or finished group), plus a chunk padded up to S steps.
+  if ((rows + 16 * WAVES * G + 16) * (K / 4) + 64 * S * ((K + 255) / 256 + S) >= lim || BN * K >= lim ||
+      BN * rows * 4 >= lim)
+    return I2S_EKERNEL;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t mt = (rows + 15) / 16;
   int64_t tiles_m = 256 / tiles_n;
@@ -709,38 +926,42 @@ int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, co
   tiles_m = (mt + ms - 1) / ms;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > kMaxDim || ms > kMaxDim) return I2S_ERANGE;
-  // Allow up to 160 KiB of dynamic LDS, once per device for this instantiation
-  // (repeating it from racing threads is harmless).
-  static std::atomic<uint64_t> attr_done{0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return I2S_EHIP;
-  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
-  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_res_kernel<G, WN>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kResMaxLds) != hipSuccess)
-      return I2S_EHIP;
-    attr_done.fetch_or(bit, std::memory_order_acq_rel);
+  const bool vec4 = (rows % 4) == 0;
+  const bool single = (K + 255) / 256 <= S;
+#define I2S_RES(V, D, SG)                                                                                         \
+  return launch_res_inst<G, WN, S, WAVES, V, D, SG>(blocks, lds, packed, rows, K, N, ws, y, dot_out, tiles_m, ms, \
+                                                    stream)
+  if (single) {
+    if (vec4) {
+      if (dot_out) I2S_RES(true, true, true);
+      I2S_RES(true, false, true);
+    }
+    if (dot_out) I2S_RES(false, true, true);
+    I2S_RES(false, false, true);
   }
-  hipLaunchKernelGGL((gemm_res_kernel<G, WN>), dim3(static_cast<unsigned>(blocks)), dim3(kResThreads),
-                     static_cast<size_t>(lds), stream, packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out,
-                     tiles_m, static_cast<int>(ms));
-  return hip_status();
+  if (vec4) {
+    if (dot_out) I2S_RES(true, true, false);
+    I2S_RES(true, false, false);
+  }
+  if (dot_out) I2S_RES(false, true, false);
+  I2S_RES(false, false, false);
+#undef I2S_RES
 }
 
 // GEMM variants (1-based): 1-4 streaming (GemmA..D), 5-9 activation-resident
-// (G, WN) = (3,4), (5,4), (2,4), (3,2), (4,1).  Automatic: the widest
+// (G, WN, S, waves) = (3,4,6,4), (2,4,6,8), (3,4,3,8), (3,2,6,8), (3,1,6,8).  Automatic: the widest
 // activation-resident tile whose LDS copy fits, else the streaming pick.
 constexpr int kGemmVariants = 9;
 
 int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
                 float *y, int32_t *dot_out, hipStream_t stream) {
   if (variant == 0) {
-    const int64_t pitch = res_pitch(K);
-    if (64 * pitch <= kResMaxLds && N > 32)
-      variant = 5;
-    else if (32 * pitch <= kResMaxLds && N > 16)
-      variant = 8;
-    else if (16 * pitch <= kResMaxLds)
+    // Measured on MI355X (8960 x 1536, N = 64 .. 4096): the 8-wave,
+    // 3-subtile, 3-step resident kernel is fastest wherever its 64-row
+    // activation tile fits in LDS; narrower tiles for longer K.
+    if (64 * res_pitch(K, 3) <= kResMaxLds && N > 16)
+      variant = 7;
+    else if (16 * res_pitch(K, 6) <= kResMaxLds)
       variant = 9;
     else
       variant = pick_stream_variant(rows, N);
@@ -750,11 +971,11 @@ int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int
     case 2: return launch_gemm_cfg<GemmB>(packed, rows, K, N, ws, y, dot_out, stream);
     case 3: return launch_gemm_cfg<GemmC>(packed, rows, K, N, ws, y, dot_out, stream);
     case 4: return launch_gemm_cfg<GemmD>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 5: return launch_res_cfg<3, 4>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 6: return launch_res_cfg<5, 4>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 7: return launch_res_cfg<2, 4>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 8: return launch_res_cfg<3, 2>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 9: return launch_res_cfg<4, 1>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 5: return launch_res_cfg<3, 4, 6, 4>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 6: return launch_res_cfg<2, 4, 6, 8>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 7: return launch_res_cfg<3, 4, 3, 8>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 8: return launch_res_cfg<3, 2, 6, 8>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 9: return launch_res_cfg<3, 1, 6, 8>(packed, rows, K, N, ws, y, dot_out, stream);
     default: return I2S_EKERNEL;
   }
 }

@@ -73,7 +73,10 @@ def check_mul_mat(case: workloads.Case, kernel=0, variant=0, sample=None, packed
         packed_gpu = gpu_pack(case.w, case.ws)
     x = dev(case.x)
     y, d = i2s.i2s_mul_mat_ex(packed_gpu, rows, K, x, dot_out=True, kernel=kernel, variant=variant)
-    y, d = host(y), host(d)
+    # The same call without dot_out may take other store paths: it must give the same y.
+    y_only = i2s.i2s_mul_mat_ex(packed_gpu, rows, K, x, kernel=kernel, variant=variant)
+    y, d, y_only = host(y), host(d), host(y_only)
+    assert np.array_equal(bits(y), bits(y_only)), "y differs with and without dot_out"
     if sample is None:
         ye, de = oracle.mul_mat(packed_np, rows, K, case.x, with_dot=True)
     else:
@@ -188,9 +191,11 @@ def test_grid_all_kernels_and_variants(K):
             xg = dev(x)
             for kern, var in combos:
                 y, d = i2s.i2s_mul_mat_ex(pg, rows, K, xg, dot_out=True, kernel=kern, variant=var)
-                y, d = host(y), host(d)
+                y2 = i2s.i2s_mul_mat_ex(pg, rows, K, xg, kernel=kern, variant=var)
+                y, d, y2 = host(y), host(d), host(y2)
                 assert np.array_equal(d, de), (K, rows, N, kern, var)
                 assert np.array_equal(bits(y), bits(ye)), (K, rows, N, kern, var)
+                assert np.array_equal(bits(y2), bits(ye)), (K, rows, N, kern, var, "no dot_out")
 
 
 @pytest.mark.parametrize("N", [1, 3, 8])
