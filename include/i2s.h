@@ -53,8 +53,8 @@ extern "C" {
 #define I2S_EWORKSPACE 3 /* workspace NULL or smaller than i2s_act_workspace_bytes */
 #define I2S_EHIP 4       /* the HIP runtime reported an error at launch */
 #define I2S_ERANGE 5     /* a size beyond what this library addresses */
-#define I2S_EKERNEL 6    /* i2s_mul_mat_ex: unknown kernel or variant, or one
-                            that does not accept this N */
+#define I2S_EKERNEL 6    /* i2s_mul_mat_ex/_ws: unknown kernel or variant, or
+                            one that does not accept this N or K */
 
 /* Bytes of an I2_S tensor of `rows` x `K` weights: rows*K/4 bytes of 2-bit
  * codes, then a 32-byte slot whose first 4 bytes are the F32 weight scale
@@ -117,9 +117,12 @@ int i2s_mul_mat(const uint8_t *packed, int64_t rows, int64_t K,
 /* i2s_mul_mat with the contraction kernel chosen by the caller, for checking
  * that every launch geometry gives identical bits and for timing each kernel
  * on its own.  kernel: 0 = automatic (as i2s_mul_mat), 1 = GEMV (N <= 8),
- * 2 = MFMA GEMM (any N >= 1).  variant: 0 = automatic, else a 1-based index
- * into the kernel's tile configurations (i2s_kernel_variants).  Returns
- * I2S_EKERNEL for an unknown pair or a GEMV with N > 8. */
+ * 2 = MFMA GEMM (any N >= 1), 3 = fused quantize + GEMV in one launch
+ * (N <= 4, K <= 9216; it does not use the workspace).  variant: 0 =
+ * automatic, else a 1-based index into the kernel's tile configurations
+ * (i2s_kernel_variants).  Returns I2S_EKERNEL for an unknown pair or a kernel
+ * that does not accept this N or K.  After any matmul call the workspace
+ * contents are unspecified. */
 int i2s_mul_mat_ex(const uint8_t *packed, int64_t rows, int64_t K,
                    const float *x, int64_t N,
                    void *workspace, size_t workspace_bytes,
@@ -144,7 +147,12 @@ int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
                    const void *workspace, size_t workspace_bytes,
                    float *y, int32_t *dot_out, int kernel, int variant, void *stream);
 
-/* Number of tile configurations kernel `kernel` (1 or 2) offers; 0 otherwise. */
+/* The contraction kernel i2s_mul_mat launches for this shape (1 = GEMV after
+ * a separate quantize launch, 2 = MFMA GEMM after a separate quantize launch,
+ * 3 = fused quantize + GEMV, one launch), or minus a status code. */
+int i2s_mul_mat_kernel(int64_t rows, int64_t K, int64_t N);
+
+/* Number of tile configurations kernel `kernel` (1, 2 or 3) offers; 0 otherwise. */
 int i2s_kernel_variants(int kernel);
 
 /* A short static English description of a status code. */

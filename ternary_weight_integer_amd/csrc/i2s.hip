@@ -281,6 +281,169 @@ gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   }
 }
 
+// Raw buffer accesses: the descriptor bounds the tensor, out-of-range loads
+// read 0 and out-of-range stores are dropped by the hardware.
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // buffer offset beyond every descriptor's range
+constexpr int kBufferFlags = 0x00020000;       // raw buffer, 32-bit data format
+
+__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           kBufferFlags);
+}
+
+// ---------------------------------------------------------------------------
+// Fused quantize + GEMV for small N*K (the decode shapes): one launch per
+// step.  Each workgroup issues all of its weight loads first, then quantizes
+// the N activation rows itself while they are in flight -- block-wide absmax,
+// s = amax/127, q = clamp(roundf(x/s), +-127), block-wide int8 row sum, the
+// same single IEEE operations as quantize_rowsum_kernel -- into LDS in the
+// group-interleaved order, and runs the v_dot4 contraction of gemv_kernel on
+// it.  Requires K <= 64*L*CPL (one weight batch) and K <= 4*kGemvThreads*XPT
+// (XPT float4 activation loads per thread per row).
+
+template <int NC, int L, int RPL, int CPL, int XPT>
+__global__ void __launch_bounds__(kGemvThreads)
+gemv_fused_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
+                  const float *__restrict__ x, float *__restrict__ y, int32_t *__restrict__ dot_out) {
+  extern __shared__ __attribute__((aligned(16))) int8_t qs[];  // NC x K group-interleaved int8
+  __shared__ float red_f[NC][kGemvThreads / 64];
+  __shared__ int red_i[NC][kGemvThreads / 64];
+  constexpr int kSlots = 64 / L;
+  constexpr int kRowsPerWave = kSlots * RPL;
+  constexpr int kRowsPerBlock = kRowsPerWave * (kGemvThreads / 64);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lam = lane % L, slot = lane / L;
+  const int C = static_cast<int>(K / 64);  // 16-byte chunks per packed row
+  const int64_t row_bytes = K / 4;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave * kRowsPerWave + slot;
+
+  // 1. Activation rows first: their absmax is the critical path, and loads
+  // retire in order, so they must not queue behind the weights.
+  const int k4 = static_cast<int>(K / 4);
+  float4 xv[NC][XPT];
+#pragma unroll
+  for (int n = 0; n < NC; ++n)
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int idx = tid + kGemvThreads * i;
+      xv[n][i] = idx < k4 ? reinterpret_cast<const float4 *>(x + static_cast<int64_t>(n) * K)[idx]
+                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+
+  // 2. Weight loads for every row and chunk of this lane, unconditional:
+  // rows past the end read as 0x00 bytes (all codes 0, which add nothing to
+  // sum(code*q)) and are never stored.
+  const __amdgpu_buffer_rsrc_t wbuf = buffer_of(packed, static_cast<uint32_t>(rows * row_bytes));
+  v4i wv[RPL][CPL];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) {
+    const int64_t r = row0 + static_cast<int64_t>(m) * kSlots;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int j = lam + L * c;
+      const uint32_t off = r < rows && j < C ? static_cast<uint32_t>(r * row_bytes + 16 * j) : kOutOfRange;
+      wv[m][c] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, off, 0, 0);
+    }
+  }
+
+  float amax[NC];
+#pragma unroll
+  for (int n = 0; n < NC; ++n) {
+    amax[n] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i)
+      amax[n] = fmaxf(amax[n], fmaxf(fmaxf(fabsf(xv[n][i].x), fabsf(xv[n][i].y)),
+                                     fmaxf(fabsf(xv[n][i].z), fabsf(xv[n][i].w))));
+    amax[n] = wave_max(amax[n]);
+    if (lane == 0) red_f[n][wave] = amax[n];
+  }
+  __syncthreads();
+
+  // 3. Quantize into LDS: the 4 consecutive positions of a float4 land on 4
+  // consecutive bytes of the interleaved order (position 128g + 32s + 4c + t
+  // goes to 128g + 16c + 4s + t).
+  float sc[NC];
+#pragma unroll
+  for (int n = 0; n < NC; ++n) {
+    float a = fmaxf(fmaxf(red_f[n][0], red_f[n][1]), fmaxf(red_f[n][2], red_f[n][3]));
+    a = fmaxf(a, 1e-5f);
+    sc[n] = a / 127.0f;
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int idx = tid + kGemvThreads * i;
+      if (idx < k4) {
+        const float e[4] = {xv[n][i].x, xv[n][i].y, xv[n][i].z, xv[n][i].w};
+        uint32_t packed4 = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float r = roundf(e[t] / sc[n]);
+          r = fminf(fmaxf(r, -127.0f), 127.0f);
+          const int qi = static_cast<int>(r);
+          sum += qi;
+          packed4 |= (static_cast<uint32_t>(qi) & 0xffu) << (8 * t);
+        }
+        const int p = 4 * idx;
+        const int jj = p & 127;
+        const int off = (p & ~127) + 16 * ((jj & 31) >> 2) + 4 * (jj >> 5);
+        *reinterpret_cast<uint32_t *>(qs + n * K + off) = packed4;
+      }
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) red_i[n][wave] = sum;
+  }
+  __syncthreads();
+
+  // 4. Contraction from LDS.
+  int acc[RPL][NC];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m)
+#pragma unroll
+    for (int n = 0; n < NC; ++n) acc[m][n] = 0;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int j = lam + L * c;
+    if (j >= C) continue;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      const uint4 *qv = reinterpret_cast<const uint4 *>(qs + n * K + 64 * j);
+      const uint4 qd[4] = {qv[0], qv[1], qv[2], qv[3]};
+#pragma unroll
+      for (int m = 0; m < RPL; ++m) {
+        int a = acc[m][n];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t w = static_cast<uint32_t>(wv[m][c][d]);
+          a = __builtin_amdgcn_sdot4(static_cast<int>((w >> 6) & kCodeMask), static_cast<int>(qd[d].x), a, false);
+          a = __builtin_amdgcn_sdot4(static_cast<int>((w >> 4) & kCodeMask), static_cast<int>(qd[d].y), a, false);
+          a = __builtin_amdgcn_sdot4(static_cast<int>((w >> 2) & kCodeMask), static_cast<int>(qd[d].z), a, false);
+          a = __builtin_amdgcn_sdot4(static_cast<int>(w & kCodeMask), static_cast<int>(qd[d].w), a, false);
+        }
+        acc[m][n] = a;
+      }
+    }
+  }
+
+  // 5. Epilogue.
+  const float ws = *reinterpret_cast<const float *>(packed + rows * row_bytes);
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) {
+    const int64_t r = row0 + static_cast<int64_t>(m) * kSlots;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      const int total = lanes_sum<L>(acc[m][n]);
+      if (r < rows && lam == n % L) {
+        const int32_t rs = red_i[n][0] + red_i[n][1] + red_i[n][2] + red_i[n][3];
+        const float t = ws * sc[n];
+        y[static_cast<int64_t>(n) * rows + r] = epilogue(total, rs, t);
+        if (dot_out) dot_out[static_cast<int64_t>(n) * rows + r] = total;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // GEMM for larger N: int8 MFMA (v_mfma_i32_16x16x64_i8).
 //
@@ -307,7 +470,6 @@ struct GemmCfg {
   static constexpr int kLdsStage = kBN * kLdsStride;
 };
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 // The 16 codes of one packed dword as an MFMA operand: dword s holds slice s
 // ((w >> (6-2s)) & 0x03030303), i.e. positions 32s+gp .. 32s+gp+3.
@@ -478,15 +640,8 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 // activations or feed outputs that are not stored.
 
 constexpr int kResMaxLds = 160 * 1024;
-constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // buffer offset beyond every descriptor's range
-constexpr int kBufferFlags = 0x00020000;       // raw buffer, 32-bit data format
-
 __host__ __device__ inline int64_t res_pitch(int64_t K, int S) { return (K + 256 * S - 1) / (256 * S) * (256 * S) + 16; }
 
-__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
-                                           kBufferFlags);
-}
 
 // Accumulate GS subtiles x WN column blocks over the S steps of one chunk.
 template <int GS, int G, int WN, int S>
@@ -835,6 +990,58 @@ int launch_gemv(int variant, const uint8_t *packed, int64_t rows, int64_t K, int
   }
 }
 
+template <int NC, int L, int RPL, int CPL, int XPT>
+int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float *x, float *y, int32_t *dot_out,
+                     hipStream_t stream) {
+  if (K > 64 * L * CPL || K > 4 * kGemvThreads * XPT) return I2S_EKERNEL;
+  if (rows * (K / 4) >= (int64_t{1} << 31)) return I2S_EKERNEL;  // 32-bit buffer offsets
+  constexpr int kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
+  const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > kMaxDim) return I2S_ERANGE;
+  hipLaunchKernelGGL((gemv_fused_kernel<NC, L, RPL, CPL, XPT>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kGemvThreads), static_cast<size_t>(NC * K), stream, packed, rows, K, x, y, dot_out);
+  return hip_status();
+}
+
+// Fused quantize + GEMV configurations (1-based): (L, RPL, CPL, XPT) =
+// (8, 2, 3, 2), (8, 1, 4, 2), (16, 1, 2, 2) for K <= 1536/2048/2048, and
+// (64, 1, 3, 9), (32, 1, 5, 9) for K <= 9216 (the down projection).
+// Automatic: measured fastest on MI355X for the decoder shapes.
+constexpr int kFusedVariants = 5;
+constexpr int64_t kFusedMaxK = 9216;
+
+template <int NC>
+int launch_fused_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K, const float *x, float *y,
+                    int32_t *dot_out, hipStream_t stream) {
+  if (variant == 0) variant = K <= 2048 ? (rows <= 2048 ? 3 : 2) : 5;
+  switch (variant) {
+    case 1: return launch_fused_cfg<NC, 8, 2, 3, 2>(packed, rows, K, x, y, dot_out, stream);
+    case 2: return launch_fused_cfg<NC, 8, 1, 4, 2>(packed, rows, K, x, y, dot_out, stream);
+    case 3: return launch_fused_cfg<NC, 16, 1, 2, 2>(packed, rows, K, x, y, dot_out, stream);
+    case 4: return launch_fused_cfg<NC, 64, 1, 3, 9>(packed, rows, K, x, y, dot_out, stream);
+    case 5: return launch_fused_cfg<NC, 32, 1, 5, 9>(packed, rows, K, x, y, dot_out, stream);
+    default: return I2S_EKERNEL;
+  }
+}
+
+int launch_fused(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const float *x, float *y,
+                 int32_t *dot_out, hipStream_t stream) {
+  switch (N) {
+    case 1: return launch_fused_nc<1>(variant, packed, rows, K, x, y, dot_out, stream);
+    case 2: return launch_fused_nc<2>(variant, packed, rows, K, x, y, dot_out, stream);
+    case 3: return launch_fused_nc<3>(variant, packed, rows, K, x, y, dot_out, stream);
+    case 4: return launch_fused_nc<4>(variant, packed, rows, K, x, y, dot_out, stream);
+    default: return I2S_EKERNEL;
+  }
+}
+
+// The fused path is chosen automatically for N <= 4 activation rows (each
+// workgroup quantizes them itself; measured faster than a separate quantize
+// launch up to N = 4 on the decoder shapes).
+inline bool fused_auto(int64_t rows, int64_t N, int64_t K) {
+  return N <= 4 && K <= kFusedMaxK && rows * (K / 4) < (int64_t{1} << 31);
+}
+
 template <class Cfg>
 int launch_gemm_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
                     float *y, int32_t *dot_out, hipStream_t stream) {
@@ -1051,9 +1258,10 @@ int check_mul_mat(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, con
   if (N < 0) return I2S_EINVAL;
   int st = check_common(rows, K);
   if (st != I2S_OK) return st;
-  if (kernel < 0 || kernel > 2 || variant < 0) return I2S_EKERNEL;
+  if (kernel < 0 || kernel > 3 || variant < 0) return I2S_EKERNEL;
   if (kernel == 1 && (N > 8 || variant > kGemvVariants)) return I2S_EKERNEL;
   if (kernel == 2 && variant > kGemmVariants) return I2S_EKERNEL;
+  if (kernel == 3 && (N > 4 || variant > kFusedVariants || K > kFusedMaxK)) return I2S_EKERNEL;
   if (kernel == 0 && variant != 0) return I2S_EKERNEL;
   if (N == 0 || rows == 0) {
     *noop = true;
@@ -1094,6 +1302,7 @@ extern "C" int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, in
                               size_t workspace_bytes, float *y, int32_t *dot_out, int kernel, int variant,
                               void *stream) {
   bool noop;
+  if (kernel == 3) return I2S_EKERNEL;  // the fused kernel quantizes x itself; x is not an argument here
   int st = check_mul_mat(packed, rows, K, N, workspace, workspace_bytes, y, dot_out, kernel, variant, &noop);
   if (st != I2S_OK || noop) return st;
   ActWorkspace ws = carve_workspace(const_cast<void *>(workspace), N, K);
@@ -1108,6 +1317,7 @@ extern "C" int i2s_mul_mat_ex(const uint8_t *packed, int64_t rows, int64_t K, co
   if (st != I2S_OK || noop) return st;
   if (!x || !aligned16(x)) return I2S_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kernel == 3 || (kernel == 0 && fused_auto(rows, N, K))) return launch_fused(variant, packed, rows, K, N, x, y, dot_out, s);
   ActWorkspace ws = carve_workspace(workspace, N, K);
   st = quantize_launch(x, N, K, ws.q, ws.scale, ws.row_sum, true, s);
   if (st != I2S_OK) return st;
@@ -1119,9 +1329,17 @@ extern "C" int i2s_mul_mat(const uint8_t *packed, int64_t rows, int64_t K, const
   return i2s_mul_mat_ex(packed, rows, K, x, N, workspace, workspace_bytes, y, dot_out, 0, 0, stream);
 }
 
+extern "C" int i2s_mul_mat_kernel(int64_t rows, int64_t K, int64_t N) {
+  if (rows < 0 || N < 0) return -I2S_EINVAL;
+  if (!k_ok(K)) return -I2S_EALIGN;
+  if (fused_auto(rows, N, K)) return 3;
+  return N <= 8 ? 1 : 2;
+}
+
 extern "C" int i2s_kernel_variants(int kernel) {
   if (kernel == 1) return kGemvVariants;
   if (kernel == 2) return kGemmVariants;
+  if (kernel == 3) return kFusedVariants;
   return 0;
 }
 
@@ -1133,7 +1351,7 @@ extern "C" const char *i2s_strerror(int status) {
     case I2S_EWORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than i2s_act_workspace_bytes";
     case I2S_EHIP: return "HIP runtime error at launch";
     case I2S_ERANGE: return "size beyond what the library addresses";
-    case I2S_EKERNEL: return "unknown kernel or variant, or a GEMV with more than 8 columns";
+    case I2S_EKERNEL: return "unknown kernel or variant, or one that does not accept this N or K";
     default: return "unknown status";
   }
 }

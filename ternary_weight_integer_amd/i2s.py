@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.i2s_quantize_act_ws.argtypes = [p, i64, i64, p, sz, p]
         L.i2s_mul_mat_ws.restype = ci
         L.i2s_mul_mat_ws.argtypes = [p, i64, i64, i64, p, sz, p, p, ci, ci, p]
+        L.i2s_mul_mat_kernel.restype = ci
+        L.i2s_mul_mat_kernel.argtypes = [i64, i64, i64]
         L.i2s_kernel_variants.restype = ci
         L.i2s_kernel_variants.argtypes = [ci]
         L.i2s_strerror.restype = ctypes.c_char_p
@@ -87,6 +89,17 @@ def i2s_packed_bytes(rows: int, K: int) -> int:
 
 def i2s_act_workspace_bytes(N: int, K: int) -> int:
     return int(lib().i2s_act_workspace_bytes(N, K))
+
+
+KERNEL_FUSED = 3
+
+
+def i2s_mul_mat_kernel(rows: int, K: int, N: int) -> int:
+    """Kernel id i2s_mul_mat launches for this shape (1 GEMV, 2 GEMM, 3 fused)."""
+    k = int(lib().i2s_mul_mat_kernel(rows, K, N))
+    if k < 0:
+        raise I2SError("i2s_mul_mat_kernel", -k)
+    return k
 
 
 def i2s_kernel_variants(kernel: int) -> int:

@@ -35,8 +35,9 @@ def test_size_queries():
 def test_kernel_variant_counts():
     assert i2s.i2s_kernel_variants(1) >= 2
     assert i2s.i2s_kernel_variants(2) >= 2
+    assert i2s.i2s_kernel_variants(3) >= 1
     assert i2s.i2s_kernel_variants(0) == 0
-    assert i2s.i2s_kernel_variants(3) == 0
+    assert i2s.i2s_kernel_variants(4) == 0
 
 
 def test_strerror_covers_every_status():
@@ -66,7 +67,9 @@ FAKE = 1 << 20  # a 16- and 256-byte aligned non-null address; never dereference
     ((FAKE, 4, 128, FAKE, 2, FAKE, 128, FAKE, None, 0, 0), i2s.I2S_EWORKSPACE),
     ((FAKE, 4, 128, FAKE, 1, FAKE + 16, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EWORKSPACE),
     ((FAKE, 4, 128, FAKE, 9, FAKE, 1 << 20, FAKE, None, 1, 0), i2s.I2S_EKERNEL),
-    ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 3, 0), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 4, 0), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 128, FAKE, 5, FAKE, 1 << 20, FAKE, None, 3, 0), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 9344, FAKE, 1, FAKE, 1 << 20, FAKE, None, 3, 0), i2s.I2S_EKERNEL),
     ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 2, 99), i2s.I2S_EKERNEL),
     ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 0, 1), i2s.I2S_EKERNEL),
     ((FAKE, 4, 8454656, FAKE, 1, FAKE, 1 << 40, FAKE, None, 0, 0), i2s.I2S_ERANGE),
@@ -94,3 +97,14 @@ def test_pack_and_quantize_host_validation():
     assert L.i2s_quantize_act(FAKE, -2, 128, FAKE, FAKE, FAKE, None) == i2s.I2S_EINVAL
     assert L.i2s_quantize_act(FAKE, 2, 128, None, FAKE, FAKE, None) == i2s.I2S_EINVAL
     assert L.i2s_quantize_act(None, 0, 128, None, None, None, None) == i2s.I2S_OK
+
+
+def test_mul_mat_kernel_choice():
+    assert i2s.i2s_mul_mat_kernel(8960, 1536, 1) == i2s.KERNEL_FUSED   # decode: one launch
+    assert i2s.i2s_mul_mat_kernel(1536, 8960, 1) == i2s.KERNEL_FUSED   # long K too
+    assert i2s.i2s_mul_mat_kernel(1536, 9344, 1) == i2s.KERNEL_GEMV    # beyond the fused K limit
+    assert i2s.i2s_mul_mat_kernel(1536, 8960, 8) == i2s.KERNEL_GEMV
+    assert i2s.i2s_mul_mat_kernel(8960, 1536, 512) == i2s.KERNEL_GEMM
+    assert i2s.i2s_mul_mat_kernel(8960, 1536, 9) == i2s.KERNEL_GEMM
+    with pytest.raises(i2s.I2SError):
+        i2s.i2s_mul_mat_kernel(4, 100, 1)

@@ -187,6 +187,8 @@ def test_grid_all_kernels_and_variants(K):
             combos = [(0, 0)] + [(2, v) for v in range(1, nv2 + 1)]
             if N <= 8:
                 combos += [(1, v) for v in range(1, nv1 + 1)]
+            if N <= 4:
+                combos += [(3, v) for v in range(1, i2s.i2s_kernel_variants(3) + 1)]
             say(f"[grid] K={K} rows={rows} N={N} combos={len(combos)}")
             xg = dev(x)
             for kern, var in combos:
@@ -196,6 +198,24 @@ def test_grid_all_kernels_and_variants(K):
                 assert np.array_equal(d, de), (K, rows, N, kern, var)
                 assert np.array_equal(bits(y), bits(ye)), (K, rows, N, kern, var)
                 assert np.array_equal(bits(y2), bits(ye)), (K, rows, N, kern, var, "no dot_out")
+
+
+@pytest.mark.parametrize("N", [1, 2, 4])
+def test_all_fused_variants_decode_shapes(N):
+    """Fused quantize + GEMV variants on the decoder shapes (K = 1536 and the
+    K = 8960 down projection); variants whose K limit is exceeded are refused."""
+    for rows, K in ((8960, 1536), (1536, 1536), (256, 1536), (1536, 8960)):
+        case = workloads.random_case(23, rows, K, N)
+        pnp = oracle.pack(case.w, case.ws)
+        pg = gpu_pack(case.w, case.ws)
+        sample = np.unique(np.concatenate([np.arange(0, 24), np.arange(rows - 24, rows),
+                                           np.random.default_rng(4).choice(rows, 48, replace=False)]))
+        for v in range(1, i2s.i2s_kernel_variants(3) + 1):
+            if K > 2048 and v <= 3:
+                with pytest.raises(i2s.I2SError):
+                    i2s.i2s_mul_mat_ex(pg, rows, K, dev(case.x), kernel=3, variant=v)
+                continue
+            check_mul_mat(case, kernel=3, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
 
 
 @pytest.mark.parametrize("N", [1, 3, 8])
