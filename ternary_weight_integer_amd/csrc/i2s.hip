@@ -142,6 +142,67 @@ quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int8_t *__restric
   }
 }
 
+// Block per row, single pass, for K <= 4*256*XPT: each of the 256 threads
+// loads up to XPT float4 of the row into registers, the row's absmax and int8
+// sum are block reductions, and each float4 becomes 4 bytes of q (4
+// consecutive positions stay consecutive in the interleaved order).  Same
+// arithmetic as quantize_rowsum_kernel, with a few divisions per thread.
+template <bool kInterleaved, int XPT>
+__global__ void __launch_bounds__(kQuantThreads)
+quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int8_t *__restrict__ q,
+                           float *__restrict__ act_scale, int32_t *__restrict__ row_sum) {
+  __shared__ float red_f[kQuantThreads / 64];
+  __shared__ int red_i[kQuantThreads / 64];
+  const int64_t n = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const float4 *xr = reinterpret_cast<const float4 *>(x + n * K);
+  const int k4 = static_cast<int>(K / 4);
+  float4 v[XPT];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int idx = tid + kQuantThreads * i;
+    v[i] = idx < k4 ? xr[idx] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+  }
+  amax = wave_max(amax);
+  if (lane == 0) red_f[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  amax = fmaxf(amax, 1e-5f);
+  const float s = amax / 127.0f;
+  int sum = 0;
+  int8_t *qr = q + n * K;
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int idx = tid + kQuantThreads * i;
+    if (idx < k4) {
+      const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      uint32_t packed = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float r = roundf(e[t] / s);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        const int qi = static_cast<int>(r);
+        sum += qi;
+        packed |= (static_cast<uint32_t>(qi) & 0xffu) << (8 * t);
+      }
+      const int p = 4 * idx;
+      const int jj = p & 127;
+      const int off = kInterleaved ? (p & ~127) + 16 * ((jj & 31) >> 2) + 4 * (jj >> 5) : p;
+      *reinterpret_cast<uint32_t *>(qr + off) = packed;
+    }
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) red_i[wave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    act_scale[n] = s;
+    row_sum[n] = red_i[0] + red_i[1] + red_i[2] + red_i[3];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Pack: each thread writes 16 packed bytes (half a group) from the 4x16
 // ternary values they hold; thread 0 also writes the scale slot.
@@ -1199,6 +1260,20 @@ int check_common(int64_t rows, int64_t K) {
 int quantize_launch(const float *x, int64_t N, int64_t K, int8_t *q, float *s, int32_t *rs, bool interleaved,
                     hipStream_t stream) {
   if (N > kMaxDim) return I2S_ERANGE;
+#define I2S_QREG(XPT)                                                                                      \
+  do {                                                                                                     \
+    if (interleaved)                                                                                       \
+      hipLaunchKernelGGL((quantize_rowsum_reg_kernel<true, XPT>), dim3(static_cast<unsigned>(N)),          \
+                         dim3(kQuantThreads), 0, stream, x, K, q, s, rs);                                  \
+    else                                                                                                   \
+      hipLaunchKernelGGL((quantize_rowsum_reg_kernel<false, XPT>), dim3(static_cast<unsigned>(N)),         \
+                         dim3(kQuantThreads), 0, stream, x, K, q, s, rs);                                  \
+    return hip_status();                                                                                   \
+  } while (0)
+  if (K <= 4 * kQuantThreads * 2) I2S_QREG(2);
+  if (K <= 4 * kQuantThreads * 4) I2S_QREG(4);
+  if (K <= 4 * kQuantThreads * 9) I2S_QREG(9);
+#undef I2S_QREG
   if (interleaved)
     hipLaunchKernelGGL((quantize_rowsum_kernel<true>), dim3(static_cast<unsigned>(N)), dim3(kQuantThreads), 0, stream,
                        x, K, q, s, rs);

@@ -120,6 +120,8 @@ def _quant_inputs():
     z[2, 5] = np.float32(-3e-6)
     out.append(("zero_and_tiny", z))
     out.append(("headroom", np.full((2, 8960), 127.0, np.float32)))
+    out.append(("long_k", workloads.normal(np.random.default_rng(6), 3, 10240)))  # the two-pass kernel (K > 9216)
+    out.append(("mid_k", workloads.normal(np.random.default_rng(7), 5, 3072)))
     return out
 
 
@@ -267,7 +269,7 @@ def test_zero_weights_zero_scale():
 
 
 @pytest.mark.parametrize("rows,K,N", [(1, 128, 1), (17, 384, 9), (33, 640, 3), (130, 1152, 17), (8961 - 16, 1536, 2),
-                                      (5, 8960, 100), (1000, 256, 300)])
+                                      (5, 8960, 100), (1000, 256, 300), (50, 10240, 3), (70, 3072, 6)])
 def test_ragged_shapes(rows, K, N):
     case = workloads.random_case(rows + N, rows, K, N, ws=0.031)
     sample = None if rows * K * N < 40_000_000 else np.arange(0, rows, 97)
@@ -331,3 +333,35 @@ def test_shared_workspace_feeds_several_weights():
             ye, de = oracle.mul_mat(pnp, rows, K, x, with_dot=True)
             assert np.array_equal(host(d), de)
             assert np.array_equal(bits(host(y)), bits(ye))
+
+
+@pytest.mark.parametrize("rows,K,N", [(8960, 1536, 1), (1536, 8960, 1), (1536, 8960, 8), (2048, 1536, 100)])
+def test_graph_replay_matches_eager(rows, K, N):
+    """i2s_mul_mat captured in a HIP graph: every replay, with eager work and
+    synchronizations in between, gives the eager bits (and the oracle's)."""
+    case = workloads.random_case(40 + N, rows, K, N)
+    pg = gpu_pack(case.w, case.ws)
+    x = dev(case.x)
+    ws = i2s.new_workspace(N, K, DEV)
+    y = torch.empty((N, rows), device=DEV)
+    y_eager = host(i2s.i2s_mul_mat(pg, rows, K, x, workspace=ws)).copy()
+    sample = np.arange(0, rows, max(1, rows // 50))
+    ye, _ = oracle_rows(oracle.pack(case.w, case.ws), rows, K, case.x, sample)
+    assert np.array_equal(bits(y_eager[:, sample]), bits(ye))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        i2s.i2s_mul_mat(pg, rows, K, x, workspace=ws, y=y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        i2s.i2s_mul_mat(pg, rows, K, x, workspace=ws, y=y)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(host(y)), bits(y_eager)), rep
+        i2s.i2s_mul_mat(pg, rows, K, x, workspace=ws)  # eager work between replays
+        torch.cuda.synchronize()
