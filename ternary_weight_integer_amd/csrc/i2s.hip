@@ -704,28 +704,10 @@ constexpr int kResMaxLds = 160 * 1024;
 __host__ __device__ inline int64_t res_pitch(int64_t K, int S) { return (K + 256 * S - 1) / (256 * S) * (256 * S) + 16; }
 
 
-// Accumulate GS subtiles x WN column blocks over the S steps of one chunk.
-template <int GS, int G, int WN, int S>
-__device__ __forceinline__ void res_mfma_chunk(v4i (&acc)[G][WN], const v4i (&wv)[G][S], const int8_t *lb,
-                                               uint32_t pitch) {
-#pragma unroll
-  for (int st = 0; st < S; ++st) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      v4i b[WN];
-#pragma unroll
-      for (int n = 0; n < WN; ++n) b[n] = *reinterpret_cast<const v4i *>(lb + 256 * st + 16 * n * pitch + 16 * d);
-#pragma unroll
-      for (int gi = 0; gi < GS; ++gi) {
-        const v4i a = unpack_codes(static_cast<uint32_t>(wv[gi][st][d]));
-#pragma unroll
-        for (int n = 0; n < WN; ++n) acc[gi][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[gi][n], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// One K-step (256 positions) of res_mfma_chunk.
+// Accumulate GS subtiles x WN column blocks over one K-step (256 positions,
+// res_mfma_step) or over the S steps of one chunk (res_mfma_chunk).  lb is the
+// lane's LDS base for the first step of the activation tile (row pitch
+// `pitch`).
 template <int GS, int G, int WN, int S>
 __device__ __forceinline__ void res_mfma_step(v4i (&acc)[G][WN], const v4i (&wv)[G][S], int st, const int8_t *lb,
                                               uint32_t pitch) {
@@ -741,6 +723,13 @@ __device__ __forceinline__ void res_mfma_step(v4i (&acc)[G][WN], const v4i (&wv)
       for (int n = 0; n < WN; ++n) acc[gi][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[gi][n], 0, 0, 0);
     }
   }
+}
+
+template <int GS, int G, int WN, int S>
+__device__ __forceinline__ void res_mfma_chunk(v4i (&acc)[G][WN], const v4i (&wv)[G][S], const int8_t *lb,
+                                               uint32_t pitch) {
+#pragma unroll
+  for (int st = 0; st < S; ++st) res_mfma_step<GS, G, WN, S>(acc, wv, st, lb, pitch);
 }
 
 template <int G, int WN, int S, int WAVES, bool VEC4, bool DOT, bool SINGLE>
@@ -1001,6 +990,277 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 }
 
 // ---------------------------------------------------------------------------
+// Pipelined GEMM for K <= 256*SM (the prefill shapes), same MFMA operand
+// mapping as above.
+//
+// A workgroup owns BN = 16*WN activation rows and ms 16-row weight subtiles,
+// dealt to its WAVES waves round-robin.  A wave works through its subtiles G
+// at a time, each group over the whole K, and stores every finished group at
+// once.  The activation tile (BN rows x K, zero past K and past N) stays in
+// LDS for the whole kernel; it is written step by step (256 positions)
+// during the first group, whose MFMAs start on the first step's data rather
+// than on the whole tile.  Every load of the first group -- activation pieces
+// and weights, step by step -- is issued at the start.
+//
+// Memory access shapes follow the rule that a group of 4 consecutive lanes
+// should touch 64 contiguous bytes (measured on MI355X: global loads that
+// break it run about 2.5x slower out of L2, LDS reads about 1.7x slower):
+//  * weights are loaded row-contiguous -- lane l reads 16 bytes of row l/4 of
+//    the subtile at byte 16*(l%4) of the step -- and moved into MFMA lane
+//    order (lane i + 16*kb holds row i, bytes 16*kb..) by ds_bpermute;
+//  * the LDS activation tile interleaves 4 rows at 16-byte granularity:
+//    piece q (16 bytes, along K) of row r sits at
+//    (r/4)*4*pitch + 64*q + 16*(r%4), so the 16 lanes that read one column
+//    piece of 16 rows read 4 runs of 64 contiguous bytes.
+// Blocks dispatched to one XCD walk K from different steps (rotation by
+// blockIdx/8), so blocks sharing weight rows or an activation tile do not all
+// miss the XCD's L2 on the same lines at once; integer sums do not depend on
+// the order of their terms.  As in gemm_res_kernel, every global access is an
+// unconditional buffer access, so each wait is for exactly the loads it needs.
+// DUAL keeps a second weight register set so that the next group's weights
+// load during the current group; without it they load after its MFMAs.
+
+template <int G, int WN>
+__device__ __forceinline__ void pipe_mfma_step(v4i (&acc)[G][WN], const v4i (&w)[G], const int8_t *lb,
+                                               uint32_t group_stride, int perm) {
+  v4i a4[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a4[j][e] = __builtin_amdgcn_ds_bpermute(perm, w[j][e]);
+  // All permutes in flight before the first use (else they go out one by one).
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    v4i b[WN];
+#pragma unroll
+    for (int n = 0; n < WN; ++n) b[n] = *reinterpret_cast<const v4i *>(lb + 4 * n * group_stride + 64 * d);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const v4i a = unpack_codes(static_cast<uint32_t>(a4[j][d]));
+#pragma unroll
+      for (int n = 0; n < WN; ++n) acc[j][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[j][n], 0, 0, 0);
+    }
+  }
+}
+
+template <int G, int WN, int WAVES, int SM, bool DUAL, bool VEC4, bool DOT>
+__global__ void __launch_bounds__(64 * WAVES)
+gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
+                 const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
+                 const int32_t *__restrict__ row_sum, float *__restrict__ y,
+                 int32_t *__restrict__ dot_out, int64_t tiles_m, int ms) {
+  extern __shared__ __attribute__((aligned(16))) int8_t lds_pipe[];
+  constexpr int BN = 16 * WN;
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kStepPieces = BN * 16;  // 16-byte activation pieces per step
+  constexpr int kPieceLanes = (kStepPieces + kThreads - 1) / kThreads;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, kb = lane >> 4;
+  const int64_t tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
+  const int64_t o_tile = tile_m * ms * 16;
+  const int64_t n0 = tile_n * BN;
+  const int64_t n_here = N - n0 < BN ? N - n0 : BN;
+  const uint32_t row_bytes = static_cast<uint32_t>(K / 4);
+  const int steps = static_cast<int>((K + 255) / 256);
+  const int k_pieces = static_cast<int>(K / 16);
+  const uint32_t pitch = static_cast<uint32_t>(256 * steps + 16);
+  const uint32_t group_stride = 4 * pitch;           // 4 interleaved rows
+  const int64_t present = (rows - o_tile + 15) / 16;
+  const int msub = static_cast<int>(present < ms ? present : ms);
+  const int mine = msub > wave ? (msub - wave + WAVES - 1) / WAVES : 0;  // subtiles wave, wave+WAVES, ...
+  const int groups = (mine + G - 1) / G;
+  const int rot = static_cast<int>((blockIdx.x / 8) % steps);
+  auto phys = [&](int st) -> int { return st + rot < steps ? st + rot : st + rot - steps; };
+
+  // Weights, row-contiguous: lane l reads row 16*s + l/4 of subtile s, bytes
+  // 64*step + 16*(l%4); subtiles past the wave's share read nothing (0).
+  // (24-bit multiplies: operands below 2^24, products below 2^31, checked
+  // on the host.)
+  const __amdgpu_buffer_rsrc_t wbuf =
+      buffer_of(packed + o_tile * row_bytes, static_cast<uint32_t>((rows - o_tile) * row_bytes));
+  const uint32_t lane_off = __umul24(lane >> 2, row_bytes) + 16 * (lane & 3);
+  const int perm = 4 * (4 * li + kb);  // ds_bpermute source lane (bytes) of MFMA lane (li, kb)
+  auto w_off = [&](int grp, int j, int st) -> uint32_t {
+    const int t = G * grp + j;
+    return t < mine && st < steps ? __umul24(16 * (wave + WAVES * t), row_bytes) + lane_off + 64 * phys(st)
+                                  : kOutOfRange;
+  };
+  auto load_w = [&](int grp, v4i (&wv)[G][SM]) {
+#pragma unroll
+    for (int st = 0; st < SM; ++st)
+#pragma unroll
+      for (int j = 0; j < G; ++j) wv[j][st] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, w_off(grp, j, st), 0, 0);
+  };
+
+  // Activation pieces of step st: piece pc = tid + kThreads*p is row pc/16,
+  // piece 16*step + pc%16 along K; pieces past K or past N read as zero.
+  const __amdgpu_buffer_rsrc_t qbuf = buffer_of(qp + n0 * K, static_cast<uint32_t>(n_here * K));
+  auto act_goff = [&](int st, int p) -> uint32_t {
+    const int pc = tid + kThreads * p;
+    const int c = 16 * phys(st) + (pc & 15);
+    return pc < kStepPieces && c < k_pieces ? __umul24(pc >> 4, static_cast<uint32_t>(K)) + 16 * c : kOutOfRange;
+  };
+  auto act_loff = [&](int st, int p) -> uint32_t {
+    const int pc = tid + kThreads * p;
+    const int r = pc >> 4;
+    return static_cast<uint32_t>(r >> 2) * group_stride + 64 * (16 * phys(st) + (pc & 15)) + 16 * (r & 3);
+  };
+
+  v4i wa[G][SM];
+  v4i wb[DUAL ? G : 1][DUAL ? SM : 1];
+  v4i bst[SM][kPieceLanes];
+#pragma unroll
+  for (int st = 0; st < SM; ++st) {
+#pragma unroll
+    for (int p = 0; p < kPieceLanes; ++p) bst[st][p] = __builtin_amdgcn_raw_buffer_load_b128(qbuf, act_goff(st, p), 0, 0);
+#pragma unroll
+    for (int j = 0; j < G; ++j) wa[j][st] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, w_off(0, j, st), 0, 0);
+  }
+  if constexpr (DUAL) load_w(1, wb);
+  // Epilogue constants last: the first group's epilogue needs them only after
+  // all of its steps.
+  const __amdgpu_buffer_rsrc_t cbuf = buffer_of(packed + rows * static_cast<int64_t>(row_bytes), 4);
+  const __amdgpu_buffer_rsrc_t sbuf = buffer_of(act_scale + n0, static_cast<uint32_t>(4 * n_here));
+  const __amdgpu_buffer_rsrc_t rbuf = buffer_of(row_sum + n0, static_cast<uint32_t>(4 * n_here));
+  const float ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(cbuf, 0, 0, 0));
+  float sn[WN];
+  int32_t rsn[WN];
+#pragma unroll
+  for (int n = 0; n < WN; ++n) {
+    const uint32_t off = static_cast<uint32_t>(4 * (16 * n + li));  // past N: reads 0, never stored
+    sn[n] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, off, 0, 0));
+    rsn[n] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, off, 0, 0);
+  }
+  // Keep every load above ahead of the first wait below.
+  __builtin_amdgcn_sched_barrier(0);
+
+  const uint32_t out_bytes = static_cast<uint32_t>(n_here * rows * 4);
+  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + n0 * rows, out_bytes);
+  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + n0 * rows : nullptr, DOT ? out_bytes : 0);
+  // This lane's B base: row li of column block 0, piece 4*kb of step 0.
+  const int8_t *lb0 = lds_pipe + (li >> 2) * group_stride + 256 * kb + 16 * (li & 3);
+
+  float tn[WN];
+#pragma unroll
+  for (int n = 0; n < WN; ++n) tn[n] = ws * sn[n];
+
+  v4i acc[G][WN];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int n = 0; n < WN; ++n) acc[j][n] = v4i{0, 0, 0, 0};
+  };
+
+  // Non-temporal stores of a finished group; subtiles past the wave's share
+  // and outputs past the tensor get an out-of-range offset instead of a
+  // branch.  The stored values sit in registers of their own, kept allocated
+  // to the end, so that the MFMAs of the next group never wait for this
+  // group's stores to release a register.
+  constexpr int kStreamStore = 2;
+  v4i yst[G][WN] = {};
+  v4i dst[G][DOT ? WN : 1] = {};
+  auto epilogue_group = [&](int grp) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int t = G * grp + j;
+      const int64_t o = o_tile + 16 * static_cast<int64_t>(wave + WAVES * t) + 4 * kb;
+      const bool ok = t < mine;
+#pragma unroll
+      for (int n = 0; n < WN; ++n) {
+        const uint32_t base = static_cast<uint32_t>((16 * n + li) * rows);  // element offset of this lane's row
+        v4i &yv = yst[j][n];
+        v4i &dv = dst[j][DOT ? n : 0];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yv[r] = __float_as_int(epilogue(acc[j][n][r], rsn[n], tn[n]));
+        if constexpr (DOT) dv = acc[j][n];
+        if constexpr (VEC4) {
+          const uint32_t off = ok && o < rows ? 4 * (base + static_cast<uint32_t>(o)) : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, kStreamStore);
+          if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b128(dv, dbuf, off, 0, kStreamStore);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t off = ok && o + r < rows ? 4 * (base + static_cast<uint32_t>(o + r)) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(yv[r], ybuf, off, 0, kStreamStore);
+            if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(dv[r], dbuf, off, 0, kStreamStore);
+          }
+        }
+      }
+    }
+  };
+
+  auto step_ptr = [&](int st) { return lb0 + 1024 * phys(st); };
+  auto mfma_group = [&](const v4i (&cur)[G][SM]) {
+#pragma unroll
+    for (int st = 0; st < SM; ++st)
+      if (st < steps) {
+        v4i w[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) w[j] = cur[j][st];
+        pipe_mfma_step<G, WN>(acc, w, step_ptr(st), group_stride, perm);
+      }
+  };
+
+  // First group, step by step, interleaved with the activation tile's LDS
+  // writes; every wave meets every barrier, with or without subtiles.
+  zero_acc();
+#pragma unroll
+  for (int st = 0; st < SM; ++st) {
+    if (st < steps) {
+#pragma unroll
+      for (int p = 0; p < kPieceLanes; ++p)
+        if (tid + kThreads * p < kStepPieces) *reinterpret_cast<v4i *>(lds_pipe + act_loff(st, p)) = bst[st][p];
+      __syncthreads();
+      v4i w[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) w[j] = wa[j][st];
+      pipe_mfma_step<G, WN>(acc, w, step_ptr(st), group_stride, perm);
+    }
+  }
+
+  if constexpr (DUAL) {
+    // Each group's MFMAs are followed by the loads of the group two ahead,
+    // into the register set they have just finished with, then its stores.
+    load_w(2, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    epilogue_group(0);
+    for (int g = 1; g < groups; g += 2) {
+      zero_acc();
+      mfma_group(wb);
+      load_w(g + 2, wb);
+      __builtin_amdgcn_sched_barrier(0);
+      epilogue_group(g);
+      if (g + 1 >= groups) break;
+      zero_acc();
+      mfma_group(wa);
+      load_w(g + 3, wa);
+      __builtin_amdgcn_sched_barrier(0);
+      epilogue_group(g + 1);
+    }
+  } else {
+    for (int g = 0;; ++g) {
+      load_w(g + 1, wa);
+      __builtin_amdgcn_sched_barrier(0);
+      epilogue_group(g);
+      if (g + 1 >= groups) break;
+      zero_acc();
+      mfma_group(wa);
+    }
+  }
+  // Keep the store registers allocated up to here (see above).
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+      asm volatile("" ::"v"(yst[j][n]));
+      if constexpr (DOT) asm volatile("" ::"v"(dst[j][n]));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launch helpers.
 
 inline int hip_status() { return hipGetLastError() == hipSuccess ? I2S_OK : I2S_EHIP; }
@@ -1216,18 +1476,81 @@ int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, co
 #undef I2S_RES
 }
 
+// Pipelined launch: BN = 16*WN activation rows per block, about one block per
+// compute unit; K must fit in SM steps and the activation tile in LDS, and
+// buffer offsets must stay below 2^31 bytes (else I2S_EKERNEL).
+template <int G, int WN, int WAVES, int SM, bool DUAL, bool VEC4, bool DOT>
+int launch_pipe_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
+                    const ActWorkspace &ws, float *y, int32_t *dot_out, int64_t tiles_m, int64_t ms,
+                    hipStream_t stream) {
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return I2S_EHIP;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_pipe_kernel<G, WN, WAVES, SM, DUAL, VEC4, DOT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kResMaxLds) != hipSuccess)
+      return I2S_EHIP;
+    attr_done.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL((gemm_pipe_kernel<G, WN, WAVES, SM, DUAL, VEC4, DOT>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * WAVES), static_cast<size_t>(lds), stream, packed, rows, K, ws.q, N, ws.scale,
+                     ws.row_sum, y, dot_out, tiles_m, static_cast<int>(ms));
+  return hip_status();
+}
+
+template <int G, int WN, int WAVES, int SM, bool DUAL>
+int launch_pipe_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
+                   int32_t *dot_out, hipStream_t stream) {
+  constexpr int64_t BN = 16 * WN;
+  const int64_t steps = (K + 255) / 256;
+  const int64_t lds = BN * (256 * steps + 16);
+  if (steps > SM || lds > kResMaxLds) return I2S_EKERNEL;
+  const int64_t lim = int64_t{1} << 31;
+  if ((rows + 16) * (K / 4) >= lim || BN * K >= lim || BN * rows * 4 >= lim || rows >= (int64_t{1} << 24))
+    return I2S_EKERNEL;
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t mt = (rows + 15) / 16;
+  int64_t tiles_m = 256 / tiles_n;
+  if (tiles_m < 1) tiles_m = 1;
+  int64_t ms = (mt + tiles_m - 1) / tiles_m;
+  if (ms < 1) ms = 1;
+  tiles_m = (mt + ms - 1) / ms;
+  const int64_t blocks = tiles_m * tiles_n;
+  if (blocks > kMaxDim || ms > kMaxDim) return I2S_ERANGE;
+  const bool vec4 = (rows % 4) == 0;
+#define I2S_SEQ(V, D) \
+  return launch_pipe_inst<G, WN, WAVES, SM, DUAL, V, D>(blocks, lds, packed, rows, K, N, ws, y, dot_out, tiles_m, ms, \
+                                                         stream)
+  if (vec4) {
+    if (dot_out) I2S_SEQ(true, true);
+    I2S_SEQ(true, false);
+  }
+  if (dot_out) I2S_SEQ(false, true);
+  I2S_SEQ(false, false);
+#undef I2S_SEQ
+}
+
 // GEMM variants (1-based): 1-4 streaming (GemmA..D), 5-9 activation-resident
-// (G, WN, S, waves) = (3,4,6,4), (2,4,6,8), (3,4,3,8), (3,2,6,8), (3,1,6,8).  Automatic: the widest
-// activation-resident tile whose LDS copy fits, else the streaming pick.
-constexpr int kGemmVariants = 9;
+// (G, WN, S, waves) = (3,4,6,4), (2,4,6,8), (3,4,3,8), (3,2,6,8), (3,1,6,8), 10 pipelined
+// (G, WN, waves, steps) = (2,2,4,6).
+constexpr int kGemmVariants = 10;
 
 int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
                 float *y, int32_t *dot_out, hipStream_t stream) {
   if (variant == 0) {
-    // Measured on MI355X (8960 x 1536, N = 64 .. 4096): the 8-wave,
-    // 3-subtile, 3-step resident kernel is fastest wherever its 64-row
-    // activation tile fits in LDS; narrower tiles for longer K.
-    if (64 * res_pitch(K, 3) <= kResMaxLds && N > 16)
+    // Measured on MI355X (rows 256 .. 8960, K 1024 .. 8960, N 64 .. 2048):
+    // the 8-wave, 3-subtile, 3-step resident kernel is fastest while each of
+    // its blocks holds at least one 16-row subtile per wave; with fewer (few
+    // rows or small N) the 4-wave pipelined kernel is, where K fits it.
+    // Narrower resident tiles for longer K.
+    const int64_t tiles_n = (N + 63) / 64;
+    const int64_t tiles_m = tiles_n < 256 ? 256 / tiles_n : 1;
+    const int64_t ms7 = ((rows + 15) / 16 + tiles_m - 1) / tiles_m;  // subtiles per block of variant 7
+    const bool fits7 = 64 * res_pitch(K, 3) <= kResMaxLds && N > 16;
+    if ((K + 255) / 256 <= 6 && (!fits7 || ms7 < 8))
+      variant = 10;
+    else if (fits7)
       variant = 7;
     else if (16 * res_pitch(K, 6) <= kResMaxLds)
       variant = 9;
@@ -1244,6 +1567,7 @@ int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int
     case 7: return launch_res_cfg<3, 4, 3, 8>(packed, rows, K, N, ws, y, dot_out, stream);
     case 8: return launch_res_cfg<3, 2, 6, 8>(packed, rows, K, N, ws, y, dot_out, stream);
     case 9: return launch_res_cfg<3, 1, 6, 8>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 10: return launch_pipe_cfg<2, 2, 4, 6, true>(packed, rows, K, N, ws, y, dot_out, stream);
     default: return I2S_EKERNEL;
   }
 }
