@@ -248,7 +248,11 @@ def main(argv=None):
         alg_bytes = wbytes + 4 * N * K + 4 * N * rows + 4
     else:
         alg_bytes = wbytes + N * K + 4 * N * rows + 8 * N + 4
-    kernel_name = {1: "gemv_kernel", 2: "gemm_res_kernel", 3: "gemv_fused_kernel"}[kernel_kind]
+    variant = i2s.i2s_mul_mat_variant(rows, K, N)
+    if kernel_kind == 2:
+        kernel_name = "gemm_pipe_kernel" if variant == 10 else ("gemm_res_kernel" if variant >= 5 else "gemm_kernel")
+    else:
+        kernel_name = {1: "gemv_kernel", 3: "gemv_fused_kernel", 4: "gemv_mfma_kernel"}[kernel_kind]
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -273,13 +277,13 @@ def main(argv=None):
             achieved = alg_bytes / (kern_us * 1e-6) / 1e9
             out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
-                               "kernel": kernel_name, "kernel_us": round(kern_us, 4),
+                               "kernel": kernel_name, "kernel_variant": variant, "kernel_us": round(kern_us, 4),
                                "alg_bytes_per_launch": alg_bytes}
         else:
             achieved = ops / (kern_us * 1e-6) / 1e12
             out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_MFMA_PEAK_TOPS,
                                "unit": "TOP/s", "frac": round(achieved / INT8_MFMA_PEAK_TOPS, 4),
-                               "traffic": measured_traffic(args.workload), "kernel": kernel_name,
+                               "traffic": measured_traffic(args.workload), "kernel": kernel_name, "kernel_variant": variant,
                                "kernel_us": round(kern_us, 4), "alg_ops_per_launch": ops,
                                "alg_bytes_per_launch": alg_bytes}
     props = torch.cuda.get_device_properties(0)

@@ -98,8 +98,10 @@ int i2s_quantize_act(const float *x, int64_t N, int64_t K,
 /* The matmul: y[n][o] = (float)(dot[n][o] - row_sum[n]) * (ws * act_scale[n])
  * with dot[n][o] = sum_k code[o][k] * q[n][k] in int32 and ws read on the
  * device from the packed tensor's scale slot.  Quantizes x into `workspace`,
- * then runs the contraction with the epilogue fused: a weight-streaming GEMV
- * for N <= 8, an int8-MFMA GEMM above.
+ * then runs the contraction with the epilogue fused: for N <= 3 (K <= 9216)
+ * one fused quantize + v_dot4 GEMV launch; otherwise a weight-streaming v_dot4
+ * GEMV for N = 1, a skinny int8-MFMA kernel up to N = 16, an int8-MFMA GEMM
+ * above (i2s_mul_mat_kernel tells which).
  *   packed     I2_S tensor of rows x K (as written by i2s_pack).
  *   x          [N][K] F32 activations, finite.
  *   workspace  >= i2s_act_workspace_bytes(N, K) bytes, 256-byte aligned;
@@ -118,7 +120,8 @@ int i2s_mul_mat(const uint8_t *packed, int64_t rows, int64_t K,
  * that every launch geometry gives identical bits and for timing each kernel
  * on its own.  kernel: 0 = automatic (as i2s_mul_mat), 1 = GEMV (N <= 8),
  * 2 = MFMA GEMM (any N >= 1), 3 = fused quantize + GEMV in one launch
- * (N <= 4, K <= 9216; it does not use the workspace).  variant: 0 =
+ * (N <= 4, K <= 9216; it does not use the workspace), 4 = skinny MFMA
+ * (N <= 16).  variant: 0 =
  * automatic, else a 1-based index into the kernel's tile configurations
  * (i2s_kernel_variants).  Returns I2S_EKERNEL for an unknown pair or a kernel
  * that does not accept this N or K.  After any matmul call the workspace
@@ -149,10 +152,18 @@ int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
 
 /* The contraction kernel i2s_mul_mat launches for this shape (1 = GEMV after
  * a separate quantize launch, 2 = MFMA GEMM after a separate quantize launch,
- * 3 = fused quantize + GEMV, one launch), or minus a status code. */
+ * 3 = fused quantize + GEMV, one launch, 4 = skinny MFMA after a separate
+ * quantize launch), or minus a status code.  i2s_mul_mat_ws with kernel 0
+ * makes the same choice, except that it never fuses (x is not an argument):
+ * where this returns 3 it runs kernel 1 for N = 1 and for N = 2 with
+ * K <= 2048, kernel 4 otherwise. */
 int i2s_mul_mat_kernel(int64_t rows, int64_t K, int64_t N);
 
-/* Number of tile configurations kernel `kernel` (1, 2 or 3) offers; 0 otherwise. */
+/* The tile configuration (1-based variant) of that kernel which the automatic
+ * choice uses for this shape, or minus a status code. */
+int i2s_mul_mat_variant(int64_t rows, int64_t K, int64_t N);
+
+/* Number of tile configurations kernel `kernel` (1 to 4) offers; 0 otherwise. */
 int i2s_kernel_variants(int kernel);
 
 /* A short static English description of a status code. */

@@ -1261,6 +1261,120 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 }
 
 // ---------------------------------------------------------------------------
+// Skinny int8-MFMA contraction for 1 <= N <= 16 activation rows (the small
+// batches).  At N = 8 the v_dot4 GEMV spends most of its time on VALU work
+// (one v_dot4 per 4 codes per activation row); one v_mfma_i32_16x16x64_i8
+// does the same for 16 weight rows x 64 positions x 16 activation rows.
+//
+// One workgroup per 16-row weight subtile; its W waves take the K-steps (256
+// positions) round-robin, so every wave streams an equal share of the
+// subtile's weights, and their int32 partial dots are summed through LDS.
+// The weights go in as operand A (lane i + 16*kb: row i; loaded
+// row-contiguous -- lane l reads row l/4, bytes 16*(l%4) of the step -- and
+// moved into that order by ds_bpermute), the group-interleaved activation
+// rows as operand B (lane j + 16*kb: activation row j, zero for j >= N).  A
+// wave issues the loads of SPW steps at a time, into one of two register
+// sets, before computing the previous SPW steps.
+
+template <int W, int SPW, bool VEC4, bool DOT>
+__global__ void __launch_bounds__(64 * W)
+gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
+                 const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
+                 const int32_t *__restrict__ row_sum, float *__restrict__ y, int32_t *__restrict__ dot_out) {
+  __shared__ __attribute__((aligned(16))) v4i part[W][64];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, kb = lane >> 4;
+  const int64_t o0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const uint32_t row_bytes = static_cast<uint32_t>(K / 4);
+  const int steps = static_cast<int>((K + 255) / 256);
+  const int64_t rows_here = rows - o0 < 16 ? rows - o0 : 16;
+  const __amdgpu_buffer_rsrc_t wbuf = buffer_of(packed + o0 * row_bytes, static_cast<uint32_t>(rows_here * row_bytes));
+  const __amdgpu_buffer_rsrc_t qbuf = buffer_of(qp, static_cast<uint32_t>(N * K));
+  const uint32_t w_lane = (lane >> 2) * row_bytes + 16 * (lane & 3);
+  const uint32_t q_lane = static_cast<uint32_t>(li * K) + 64 * kb;
+  const bool q_row_ok = li < N;
+  const int perm = 4 * (4 * li + kb);  // ds_bpermute source lane (bytes) of MFMA lane (li, kb)
+
+  // Step slot i of batch g of this wave: K-step wave + W*(SPW*g + i).
+  auto load = [&](int g, v4i (&wv)[SPW], v4i (&qv)[SPW][4]) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int st = wave + W * (SPW * g + i);
+      const bool ok = st < steps;
+      wv[i] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, ok ? w_lane + 64 * st : kOutOfRange, 0, 0);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t qo = q_lane + 256 * st + 16 * d;  // past K (the half step of an odd group count) reads 0
+        qv[i][d] = __builtin_amdgcn_raw_buffer_load_b128(qbuf, ok && q_row_ok && 256 * st + 64 * kb + 16 * d < K ? qo : kOutOfRange,
+                                                         0, 0);
+      }
+    }
+  };
+  v4i acc[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+  auto compute = [&](const v4i (&wv)[SPW], const v4i (&qv)[SPW][4]) {
+    v4i a4[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a4[i][e] = __builtin_amdgcn_ds_bpermute(perm, wv[i][e]);
+    __builtin_amdgcn_sched_barrier(0);  // all permutes in flight before the first use
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        acc[d & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_codes(static_cast<uint32_t>(a4[i][d])), qv[i][d],
+                                                           acc[d & 1], 0, 0, 0);
+  };
+
+  const int mine = steps > wave ? (steps - wave + W - 1) / W : 0;  // this wave's steps
+  const int batches = (mine + SPW - 1) / SPW;
+  v4i wa[SPW], wb[SPW], qa[SPW][4], qb[SPW][4];
+  load(0, wa, qa);
+  for (int g = 0; g < batches; g += 2) {
+    load(g + 1, wb, qb);
+    compute(wa, qa);
+    if (g + 1 >= batches) break;
+    load(g + 2, wa, qa);
+    compute(wb, qb);
+  }
+
+  part[wave][lane] = acc[0] + acc[1];
+  __syncthreads();
+  if (wave != 0) return;
+  v4i tot = part[0][lane];
+#pragma unroll
+  for (int w = 1; w < W; ++w) tot += part[w][lane];
+
+  // Lane (li, kb) holds the dots of weight rows o0 + 4*kb + r (r = 0..3) with
+  // activation row li.
+  const float ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_of(packed + rows * static_cast<int64_t>(row_bytes), 4), 0, 0, 0));
+  const int n = li < N ? li : 0;
+  const float t = ws * act_scale[n];
+  const int32_t rs = row_sum[n];
+  const int64_t o = o0 + 4 * kb;
+  const uint32_t out_bytes = static_cast<uint32_t>(N * rows * 4 - o0 * 4);
+  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + o0, out_bytes);
+  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + o0 : nullptr, DOT ? out_bytes : 0);
+  const uint32_t base = static_cast<uint32_t>(li * rows + 4 * kb);  // element offset from y + o0
+  if constexpr (VEC4) {
+    const uint32_t off = li < N && o < rows ? 4 * base : kOutOfRange;
+    const v4i yv = {__float_as_int(epilogue(tot[0], rs, t)), __float_as_int(epilogue(tot[1], rs, t)),
+                    __float_as_int(epilogue(tot[2], rs, t)), __float_as_int(epilogue(tot[3], rs, t))};
+    __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, 0);
+    if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b128(tot, dbuf, off, 0, 0);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t off = li < N && o + r < rows ? 4 * (base + r) : kOutOfRange;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(epilogue(tot[r], rs, t)), ybuf, off, 0, 0);
+      if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(tot[r], dbuf, off, 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launch helpers.
 
 inline int hip_status() { return hipGetLastError() == hipSuccess ? I2S_OK : I2S_EHIP; }
@@ -1278,13 +1392,15 @@ int launch_gemv_cfg(const uint8_t *packed, int64_t rows, int64_t K, const ActWor
 
 // GEMV tile configurations: (lanes per row, rows per lane pass, chunk batch).
 // Variant v selects the v-th entry (1-based); 0 picks by K.
+int gemv_auto_variant(int64_t K) {
+  const int64_t C = K / 64;
+  return C <= 8 ? 1 : (C <= 32 ? 2 : 3);
+}
+
 template <int NC>
 int launch_gemv_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K, const ActWorkspace &ws,
                    float *y, int32_t *dot_out, hipStream_t stream) {
-  if (variant == 0) {
-    const int64_t C = K / 64;
-    variant = C <= 8 ? 1 : (C <= 32 ? 2 : 3);
-  }
+  if (variant == 0) variant = gemv_auto_variant(K);
   switch (variant) {
     case 1: return launch_gemv_cfg<NC, 4, 1, 2>(packed, rows, K, ws, y, dot_out, stream);
     case 2: return launch_gemv_cfg<NC, 8, 1, 4>(packed, rows, K, ws, y, dot_out, stream);
@@ -1331,10 +1447,12 @@ int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float
 constexpr int kFusedVariants = 5;
 constexpr int64_t kFusedMaxK = 9216;
 
+int fused_auto_variant(int64_t rows, int64_t K) { return K <= 2048 ? (rows <= 2048 ? 3 : 2) : 5; }
+
 template <int NC>
 int launch_fused_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K, const float *x, float *y,
                     int32_t *dot_out, hipStream_t stream) {
-  if (variant == 0) variant = K <= 2048 ? (rows <= 2048 ? 3 : 2) : 5;
+  if (variant == 0) variant = fused_auto_variant(rows, K);
   switch (variant) {
     case 1: return launch_fused_cfg<NC, 8, 2, 3, 2>(packed, rows, K, x, y, dot_out, stream);
     case 2: return launch_fused_cfg<NC, 8, 1, 4, 2>(packed, rows, K, x, y, dot_out, stream);
@@ -1359,8 +1477,11 @@ int launch_fused(int variant, const uint8_t *packed, int64_t rows, int64_t K, in
 // The fused path is chosen automatically for N <= 4 activation rows (each
 // workgroup quantizes them itself; measured faster than a separate quantize
 // launch up to N = 4 on the decoder shapes).
+// Automatic choices, measured on MI355X (decoder projection shapes): the
+// fused quantize + GEMV for N <= 3; otherwise the v_dot4 GEMV for N = 1 (and
+// N = 2 at short K), the skinny MFMA kernel up to N = 16, the MFMA GEMM above.
 inline bool fused_auto(int64_t rows, int64_t N, int64_t K) {
-  return N <= 4 && K <= kFusedMaxK && rows * (K / 4) < (int64_t{1} << 31);
+  return N <= 3 && K <= kFusedMaxK && rows * (K / 4) < (int64_t{1} << 31);
 }
 
 template <class Cfg>
@@ -1536,27 +1657,31 @@ int launch_pipe_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, c
 // (G, WN, waves, steps) = (2,2,4,6).
 constexpr int kGemmVariants = 10;
 
+int gemm_auto_variant(int64_t rows, int64_t K, int64_t N) {
+  int variant;
+  // Measured on MI355X (rows 256 .. 8960, K 1024 .. 8960, N 64 .. 2048):
+  // the 8-wave, 3-subtile, 3-step resident kernel is fastest while each of
+  // its blocks holds at least one 16-row subtile per wave; with fewer (few
+  // rows or small N) the 4-wave pipelined kernel is, where K fits it.
+  // Narrower resident tiles for longer K.
+  const int64_t tiles_n = (N + 63) / 64;
+  const int64_t tiles_m = tiles_n < 256 ? 256 / tiles_n : 1;
+  const int64_t ms7 = ((rows + 15) / 16 + tiles_m - 1) / tiles_m;  // subtiles per block of variant 7
+  const bool fits7 = 64 * res_pitch(K, 3) <= kResMaxLds && N > 16;
+  if ((K + 255) / 256 <= 6 && (!fits7 || ms7 < 8))
+    variant = 10;
+  else if (fits7)
+    variant = 7;
+  else if (16 * res_pitch(K, 6) <= kResMaxLds)
+    variant = 9;
+  else
+    variant = pick_stream_variant(rows, N);
+  return variant;
+}
+
 int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
                 float *y, int32_t *dot_out, hipStream_t stream) {
-  if (variant == 0) {
-    // Measured on MI355X (rows 256 .. 8960, K 1024 .. 8960, N 64 .. 2048):
-    // the 8-wave, 3-subtile, 3-step resident kernel is fastest while each of
-    // its blocks holds at least one 16-row subtile per wave; with fewer (few
-    // rows or small N) the 4-wave pipelined kernel is, where K fits it.
-    // Narrower resident tiles for longer K.
-    const int64_t tiles_n = (N + 63) / 64;
-    const int64_t tiles_m = tiles_n < 256 ? 256 / tiles_n : 1;
-    const int64_t ms7 = ((rows + 15) / 16 + tiles_m - 1) / tiles_m;  // subtiles per block of variant 7
-    const bool fits7 = 64 * res_pitch(K, 3) <= kResMaxLds && N > 16;
-    if ((K + 255) / 256 <= 6 && (!fits7 || ms7 < 8))
-      variant = 10;
-    else if (fits7)
-      variant = 7;
-    else if (16 * res_pitch(K, 6) <= kResMaxLds)
-      variant = 9;
-    else
-      variant = pick_stream_variant(rows, N);
-  }
+  if (variant == 0) variant = gemm_auto_variant(rows, K, N);
   switch (variant) {
     case 1: return launch_gemm_cfg<GemmA>(packed, rows, K, N, ws, y, dot_out, stream);
     case 2: return launch_gemm_cfg<GemmB>(packed, rows, K, N, ws, y, dot_out, stream);
@@ -1568,6 +1693,50 @@ int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int
     case 8: return launch_res_cfg<3, 2, 6, 8>(packed, rows, K, N, ws, y, dot_out, stream);
     case 9: return launch_res_cfg<3, 1, 6, 8>(packed, rows, K, N, ws, y, dot_out, stream);
     case 10: return launch_pipe_cfg<2, 2, 4, 6, true>(packed, rows, K, N, ws, y, dot_out, stream);
+    default: return I2S_EKERNEL;
+  }
+}
+
+// Skinny MFMA launch (kernel 4): one block per 16-row subtile, 8 waves.
+// Variant 1 issues 2 steps per batch, variant 2 issues 4 (measured slower on
+// the decoder shapes; kept for parity coverage of deeper batches).
+constexpr int kSkinnyVariants = 2;
+constexpr int kSkinnyMaxN = 16;
+
+int skinny_auto_variant(int64_t) { return 1; }
+
+bool skinny_fits(int64_t rows, int64_t K, int64_t N) {
+  const int64_t lim = int64_t{1} << 31;
+  return N <= kSkinnyMaxN && N * rows * 4 < lim && N * K < lim && 16 * (K / 4) + 64 < lim && (rows + 15) / 16 <= kMaxDim;
+}
+
+template <int SPW, bool VEC4, bool DOT>
+int launch_skinny_inst(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
+                       int32_t *dot_out, hipStream_t stream) {
+  hipLaunchKernelGGL((gemv_mfma_kernel<8, SPW, VEC4, DOT>), dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(512), 0,
+                     stream, packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out);
+  return hip_status();
+}
+
+template <int SPW>
+int launch_skinny_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
+                      int32_t *dot_out, hipStream_t stream) {
+  // 32-bit buffer offsets: activation rows (N*K), one subtile's weights and
+  // the outputs past the block's first row (N*rows*4) stay below 2^31.
+  if (!skinny_fits(rows, K, N)) return I2S_EKERNEL;
+  const bool vec4 = (rows % 4) == 0;
+  if (vec4) return dot_out ? launch_skinny_inst<SPW, true, true>(packed, rows, K, N, ws, y, dot_out, stream)
+                           : launch_skinny_inst<SPW, true, false>(packed, rows, K, N, ws, y, dot_out, stream);
+  return dot_out ? launch_skinny_inst<SPW, false, true>(packed, rows, K, N, ws, y, dot_out, stream)
+                 : launch_skinny_inst<SPW, false, false>(packed, rows, K, N, ws, y, dot_out, stream);
+}
+
+int launch_skinny(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
+                  float *y, int32_t *dot_out, hipStream_t stream) {
+  if (variant == 0) variant = skinny_auto_variant(K);
+  switch (variant) {
+    case 1: return launch_skinny_cfg<2>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 2: return launch_skinny_cfg<4>(packed, rows, K, N, ws, y, dot_out, stream);
     default: return I2S_EKERNEL;
   }
 }
@@ -1657,10 +1826,11 @@ int check_mul_mat(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, con
   if (N < 0) return I2S_EINVAL;
   int st = check_common(rows, K);
   if (st != I2S_OK) return st;
-  if (kernel < 0 || kernel > 3 || variant < 0) return I2S_EKERNEL;
+  if (kernel < 0 || kernel > 4 || variant < 0) return I2S_EKERNEL;
   if (kernel == 1 && (N > 8 || variant > kGemvVariants)) return I2S_EKERNEL;
   if (kernel == 2 && variant > kGemmVariants) return I2S_EKERNEL;
   if (kernel == 3 && (N > 4 || variant > kFusedVariants || K > kFusedMaxK)) return I2S_EKERNEL;
+  if (kernel == 4 && (N > kSkinnyMaxN || variant > kSkinnyVariants)) return I2S_EKERNEL;
   if (kernel == 0 && variant != 0) return I2S_EKERNEL;
   if (N == 0 || rows == 0) {
     *noop = true;
@@ -1674,10 +1844,17 @@ int check_mul_mat(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, con
   return I2S_OK;
 }
 
+int contract_auto_kernel(int64_t rows, int64_t K, int64_t N) {
+  if (N == 1 || (N == 2 && K <= 2048)) return 1;
+  if (N <= kSkinnyMaxN && skinny_fits(rows, K, N)) return 4;
+  return N <= 8 ? 1 : 2;
+}
+
 int contract(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
              int32_t *dot_out, int kernel, int variant, hipStream_t s) {
-  const bool use_gemv = kernel == 1 || (kernel == 0 && N <= 8);
-  if (use_gemv) return launch_gemv(variant, packed, rows, K, N, ws, y, dot_out, s);
+  if (kernel == 0) kernel = contract_auto_kernel(rows, K, N);
+  if (kernel == 4) return launch_skinny(variant, packed, rows, K, N, ws, y, dot_out, s);
+  if (kernel == 1) return launch_gemv(variant, packed, rows, K, N, ws, y, dot_out, s);
   return launch_gemm(variant, packed, rows, K, N, ws, y, dot_out, s);
 }
 
@@ -1732,13 +1909,25 @@ extern "C" int i2s_mul_mat_kernel(int64_t rows, int64_t K, int64_t N) {
   if (rows < 0 || N < 0) return -I2S_EINVAL;
   if (!k_ok(K)) return -I2S_EALIGN;
   if (fused_auto(rows, N, K)) return 3;
-  return N <= 8 ? 1 : 2;
+  return contract_auto_kernel(rows, K, N);
+}
+
+extern "C" int i2s_mul_mat_variant(int64_t rows, int64_t K, int64_t N) {
+  const int kernel = i2s_mul_mat_kernel(rows, K, N);
+  switch (kernel) {
+    case 1: return gemv_auto_variant(K);
+    case 2: return gemm_auto_variant(rows, K, N);
+    case 3: return fused_auto_variant(rows, K);
+    case 4: return skinny_auto_variant(K);
+    default: return kernel;  // a negative status
+  }
 }
 
 extern "C" int i2s_kernel_variants(int kernel) {
   if (kernel == 1) return kGemvVariants;
   if (kernel == 2) return kGemmVariants;
   if (kernel == 3) return kFusedVariants;
+  if (kernel == 4) return kSkinnyVariants;
   return 0;
 }
 

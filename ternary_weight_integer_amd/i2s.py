@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.i2s_mul_mat_ws.argtypes = [p, i64, i64, i64, p, sz, p, p, ci, ci, p]
         L.i2s_mul_mat_kernel.restype = ci
         L.i2s_mul_mat_kernel.argtypes = [i64, i64, i64]
+        L.i2s_mul_mat_variant.restype = ci
+        L.i2s_mul_mat_variant.argtypes = [i64, i64, i64]
         L.i2s_kernel_variants.restype = ci
         L.i2s_kernel_variants.argtypes = [ci]
         L.i2s_strerror.restype = ctypes.c_char_p
@@ -92,14 +94,23 @@ def i2s_act_workspace_bytes(N: int, K: int) -> int:
 
 
 KERNEL_FUSED = 3
+KERNEL_SKINNY = 4
 
 
 def i2s_mul_mat_kernel(rows: int, K: int, N: int) -> int:
-    """Kernel id i2s_mul_mat launches for this shape (1 GEMV, 2 GEMM, 3 fused)."""
+    """Kernel id i2s_mul_mat launches for this shape (1 GEMV, 2 GEMM, 3 fused, 4 skinny MFMA)."""
     k = int(lib().i2s_mul_mat_kernel(rows, K, N))
     if k < 0:
         raise I2SError("i2s_mul_mat_kernel", -k)
     return k
+
+
+def i2s_mul_mat_variant(rows: int, K: int, N: int) -> int:
+    """Tile configuration (1-based) of that kernel the automatic choice uses."""
+    v = int(lib().i2s_mul_mat_variant(rows, K, N))
+    if v < 0:
+        raise I2SError("i2s_mul_mat_variant", -v)
+    return v
 
 
 def i2s_kernel_variants(kernel: int) -> int:

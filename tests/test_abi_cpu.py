@@ -36,8 +36,9 @@ def test_kernel_variant_counts():
     assert i2s.i2s_kernel_variants(1) >= 2
     assert i2s.i2s_kernel_variants(2) >= 2
     assert i2s.i2s_kernel_variants(3) >= 1
+    assert i2s.i2s_kernel_variants(4) >= 1
     assert i2s.i2s_kernel_variants(0) == 0
-    assert i2s.i2s_kernel_variants(4) == 0
+    assert i2s.i2s_kernel_variants(5) == 0
 
 
 def test_strerror_covers_every_status():
@@ -67,7 +68,9 @@ FAKE = 1 << 20  # a 16- and 256-byte aligned non-null address; never dereference
     ((FAKE, 4, 128, FAKE, 2, FAKE, 128, FAKE, None, 0, 0), i2s.I2S_EWORKSPACE),
     ((FAKE, 4, 128, FAKE, 1, FAKE + 16, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EWORKSPACE),
     ((FAKE, 4, 128, FAKE, 9, FAKE, 1 << 20, FAKE, None, 1, 0), i2s.I2S_EKERNEL),
-    ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 4, 0), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 5, 0), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 128, FAKE, 17, FAKE, 1 << 20, FAKE, None, 4, 0), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 4, 9), i2s.I2S_EKERNEL),
     ((FAKE, 4, 128, FAKE, 5, FAKE, 1 << 20, FAKE, None, 3, 0), i2s.I2S_EKERNEL),
     ((FAKE, 4, 9344, FAKE, 1, FAKE, 1 << 20, FAKE, None, 3, 0), i2s.I2S_EKERNEL),
     ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 2, 99), i2s.I2S_EKERNEL),
@@ -102,9 +105,26 @@ def test_pack_and_quantize_host_validation():
 def test_mul_mat_kernel_choice():
     assert i2s.i2s_mul_mat_kernel(8960, 1536, 1) == i2s.KERNEL_FUSED   # decode: one launch
     assert i2s.i2s_mul_mat_kernel(1536, 8960, 1) == i2s.KERNEL_FUSED   # long K too
+    assert i2s.i2s_mul_mat_kernel(1536, 8960, 3) == i2s.KERNEL_FUSED
     assert i2s.i2s_mul_mat_kernel(1536, 9344, 1) == i2s.KERNEL_GEMV    # beyond the fused K limit
-    assert i2s.i2s_mul_mat_kernel(1536, 8960, 8) == i2s.KERNEL_GEMV
+    assert i2s.i2s_mul_mat_kernel(1536, 9344, 2) == i2s.KERNEL_SKINNY
+    assert i2s.i2s_mul_mat_kernel(1536, 8960, 4) == i2s.KERNEL_SKINNY
+    assert i2s.i2s_mul_mat_kernel(1536, 8960, 8) == i2s.KERNEL_SKINNY
+    assert i2s.i2s_mul_mat_kernel(8960, 1536, 16) == i2s.KERNEL_SKINNY
+    assert i2s.i2s_mul_mat_kernel(8960, 1536, 17) == i2s.KERNEL_GEMM
     assert i2s.i2s_mul_mat_kernel(8960, 1536, 512) == i2s.KERNEL_GEMM
-    assert i2s.i2s_mul_mat_kernel(8960, 1536, 9) == i2s.KERNEL_GEMM
     with pytest.raises(i2s.I2SError):
         i2s.i2s_mul_mat_kernel(4, 100, 1)
+
+
+def test_mul_mat_variant_choice():
+    # every automatic variant is a valid index of its kernel
+    for rows, K, N in [(8960, 1536, 1), (1536, 8960, 8), (8960, 1536, 512), (1536, 1536, 64), (256, 1536, 2048),
+                       (1536, 9344, 1), (64, 128, 40)]:
+        k = i2s.i2s_mul_mat_kernel(rows, K, N)
+        v = i2s.i2s_mul_mat_variant(rows, K, N)
+        assert 1 <= v <= i2s.i2s_kernel_variants(k), (rows, K, N, k, v)
+    assert i2s.i2s_mul_mat_variant(8960, 1536, 512) == 7    # the resident GEMM
+    assert i2s.i2s_mul_mat_variant(1536, 1536, 64) == 10    # the pipelined GEMM
+    with pytest.raises(i2s.I2SError):
+        i2s.i2s_mul_mat_variant(4, 100, 1)

@@ -191,6 +191,8 @@ def test_grid_all_kernels_and_variants(K):
                 combos += [(1, v) for v in range(1, nv1 + 1)]
             if N <= 4:
                 combos += [(3, v) for v in range(1, i2s.i2s_kernel_variants(3) + 1)]
+            if N <= 16:
+                combos += [(4, v) for v in range(0, i2s.i2s_kernel_variants(4) + 1)]
             say(f"[grid] K={K} rows={rows} N={N} combos={len(combos)}")
             xg = dev(x)
             for kern, var in combos:
