@@ -150,6 +150,44 @@ int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
                    const void *workspace, size_t workspace_bytes,
                    float *y, int32_t *dot_out, int kernel, int variant, void *stream);
 
+/* Grouped projections sharing one activation ("VibeASR in audio.cpp",
+ * Architecture/Decoder: every decoder layer applies the ternary q, k and v
+ * projections to one normed hidden state, and gate and up to another; the
+ * q/k/v projections carry F32 biases).  Each projection is the whole op of
+ * i2s_mul_mat on the same x -- quantized once, since quantization depends on
+ * x alone -- followed, if it has a bias, by one F32 add per output
+ * y[n][o] += bias[o] after the epilogue (the separate F32 bias tensor add).
+ * All pointers in an i2s_proj are device pointers owned by the caller. */
+#define I2S_GROUP_MAX 8
+typedef struct i2s_proj {
+    const uint8_t *packed;  /* I2_S tensor of rows x K (i2s_pack), 16-byte aligned     */
+    int64_t rows;           /* output features (>= 0; 0 = skipped)                     */
+    const float *bias;      /* NULL, or [rows] F32, 16-byte aligned                    */
+    float *y;               /* [N][rows] F32, 16-byte aligned, fully overwritten       */
+    int32_t *dot_out;       /* NULL, or [N][rows] int32 receiving sum(code*q)          */
+} i2s_proj;
+
+/* i2s_mul_mat_group: `count` (1..I2S_GROUP_MAX) projections of x[N][K] (F32,
+ * finite, 16-byte aligned).  projs is a HOST array, read before the call
+ * returns.  For N <= 3 and K <= 9216 the group runs as one fused
+ * quantize + GEMV launch; otherwise x is quantized once into `workspace`
+ * (>= i2s_act_workspace_bytes(N, K) bytes, 256-byte aligned, overwritten) and
+ * each projection gets its own contraction launch.  Outputs of different
+ * projections must not overlap.
+ * Errors: I2S_EINVAL (count out of range, a null or misaligned pointer, a
+ * negative size), I2S_EALIGN, I2S_EWORKSPACE, I2S_ERANGE, I2S_EHIP; nothing is
+ * launched unless every projection passes. */
+int i2s_mul_mat_group(const i2s_proj *projs, int count, int64_t K,
+                      const float *x, int64_t N,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* i2s_mul_mat_group with the kernel and variant chosen by the caller, as in
+ * i2s_mul_mat_ex (kernel 3 = the fused group launch). */
+int i2s_mul_mat_group_ex(const i2s_proj *projs, int count, int64_t K,
+                         const float *x, int64_t N,
+                         void *workspace, size_t workspace_bytes,
+                         int kernel, int variant, void *stream);
+
 /* The contraction kernel i2s_mul_mat launches for this shape (1 = GEMV after
  * a separate quantize launch, 2 = MFMA GEMM after a separate quantize launch,
  * 3 = fused quantize + GEMV, one launch, 4 = skinny MFMA after a separate

@@ -55,6 +55,8 @@ def _load():
         lib.oracle_epilogue.argtypes = [p, p, p, ctypes.c_float, i64, i64, p]
         lib.oracle_mul_mat.restype = ctypes.c_int
         lib.oracle_mul_mat.argtypes = [p, i64, i64, p, i64, p, p]
+        lib.oracle_add_bias.restype = None
+        lib.oracle_add_bias.argtypes = [p, p, i64, i64]
         _lib = lib
     return _lib
 
@@ -126,3 +128,27 @@ def mul_mat(packed: np.ndarray, rows: int, K: int, x: np.ndarray, with_dot: bool
     if rc != 0:
         raise ValueError(f"oracle_mul_mat failed ({rc}) for rows={rows} K={K} N={N}")
     return (y, d) if with_dot else y
+
+
+def add_bias(y: np.ndarray, bias: np.ndarray) -> np.ndarray:
+    """y[N][rows] + bias[rows], one F32 add per element (oracle_add_bias)."""
+    out = np.array(y, dtype=np.float32, order="C", copy=True)
+    bias = np.ascontiguousarray(bias, dtype=np.float32)
+    N, rows = out.shape
+    assert bias.shape[0] >= rows
+    _load().oracle_add_bias(_ptr(out), _ptr(bias), N, rows)
+    return out
+
+
+def mul_mat_group(projs, K: int, x: np.ndarray, with_dot: bool = False):
+    """Several projections of one activation: projs is a list of
+    (packed, rows, bias or None); each is the whole op on the same x followed
+    by its bias add.  Returns the list of y (and of dots)."""
+    ys, ds = [], []
+    for packed, rows, bias in projs:
+        y, d = mul_mat(packed, rows, K, x, with_dot=True)
+        if bias is not None:
+            y = add_bias(y, bias)
+        ys.append(y)
+        ds.append(d)
+    return (ys, ds) if with_dot else ys

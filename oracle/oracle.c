@@ -20,7 +20,8 @@
  * Parity pins (tests/test_oracle_pins.py): hand-decoded pack bytes, the
  * rounding vector, the headroom closed form, degenerate scales, sign
  * invariants, exact-rational quantization and Python-integer brute force with
- * signed weights.  The 28 padding bytes of the in-band scale slot are
+ * signed weights; for the bias add, hand-derived binary32 values that tell
+ * one add after the rounded epilogue from a fused multiply-add.  The 28 padding bytes of the in-band scale slot are
  * "parity unpinned": nothing on the pages reads them.
  */
 #include <math.h>
@@ -184,4 +185,16 @@ int oracle_mul_mat(const uint8_t *packed, int64_t rows, int64_t K,
     if (dot_out) memcpy(dot_out, dot, (size_t)(N * rows) * sizeof(int32_t));
     free(q); free(s); free(rs); free(dot);
     return 0;
+}
+
+/* Bias of a projection: y[n][o] = y[n][o] + bias[o], one F32 add per output
+ * after the epilogue.  The decoder's q/k/v projections carry F32 biases
+ * [P3 Architecture/Decoder: norms and the q/k/v biases are F32 tensors]; the
+ * plain reading is the usual separate F32 tensor add on the matmul's F32
+ * output, so the epilogue value is rounded before the bias joins it. */
+void oracle_add_bias(float *y, const float *bias, int64_t N, int64_t rows)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t o = 0; o < rows; ++o)
+            y[n * rows + o] = y[n * rows + o] + bias[o];
 }

@@ -1,8 +1,10 @@
 """Build the gfx950 HIP library (libi2s.so) in-tree with hipcc.
 
-Flags: no fast-math and no denormal flushing, so ``x / s`` stays a correctly
-rounded IEEE division and every float operation in the kernels is a single
-round-to-nearest operation; packed-FP32 instruction selection is disabled.
+Flags: no fast-math, no denormal flushing and no FP contraction, so ``x / s``
+stays a correctly rounded IEEE division and every float operation in the
+kernels is a single round-to-nearest operation (the epilogue multiply and a
+bias add are never fused into an FMA); packed-FP32 instruction selection is
+disabled.
 """
 
 from __future__ import annotations
@@ -36,6 +38,7 @@ def flags() -> list[str]:
         "-shared",
         "-Wall",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-ffp-contract=off",
         "-I", os.path.join(ROOT, "include"),
     ]
 

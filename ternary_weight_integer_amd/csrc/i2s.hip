@@ -243,6 +243,12 @@ __device__ inline float epilogue(int32_t dot, int32_t rsum, float t) {
   return static_cast<float>(dot - rsum) * t;
 }
 
+// Optional F32 bias of a projection (the decoder's q/k/v projections carry
+// one), added to the finished epilogue value as one more IEEE add: the
+// bias tensor add that follows the matmul.  The library is built with FP
+// contraction off, so the multiply above and this add are never fused.
+__device__ inline float add_bias(float v, float b) { return v + b; }
+
 // ---------------------------------------------------------------------------
 // GEMV for N <= 8 columns: streams packed weights with 128-bit loads and
 // accumulates with v_dot4 (4-way int8 dot into int32).
@@ -269,7 +275,7 @@ __global__ void __launch_bounds__(kGemvThreads)
 gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
             const int8_t *__restrict__ qp, const float *__restrict__ act_scale,
             const int32_t *__restrict__ row_sum, float *__restrict__ y,
-            int32_t *__restrict__ dot_out) {
+            int32_t *__restrict__ dot_out, const float *__restrict__ bias) {
   constexpr int kSlots = 64 / L;
   constexpr int kRowsPerWave = kSlots * RPL;
   constexpr int kRowsPerBlock = kRowsPerWave * (kGemvThreads / 64);
@@ -335,7 +341,9 @@ gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       const int total = lanes_sum<L>(acc[m][n]);
       if (r < rows && lam == n % L) {
         const float t = ws * act_scale[n];
-        y[static_cast<int64_t>(n) * rows + r] = epilogue(total, row_sum[n], t);
+        float v = epilogue(total, row_sum[n], t);
+        if (bias) v = add_bias(v, bias[r]);
+        y[static_cast<int64_t>(n) * rows + r] = v;
         if (dot_out) dot_out[static_cast<int64_t>(n) * rows + r] = total;
       }
     }
@@ -364,10 +372,10 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t by
 // (XPT float4 activation loads per thread per row).
 
 template <int NC, int L, int RPL, int CPL, int XPT>
-__global__ void __launch_bounds__(kGemvThreads)
-gemv_fused_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
-                  const float *__restrict__ x, float *__restrict__ y, int32_t *__restrict__ dot_out) {
-  extern __shared__ __attribute__((aligned(16))) int8_t qs[];  // NC x K group-interleaved int8
+__device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
+                                           const float *__restrict__ x, float *__restrict__ y,
+                                           int32_t *__restrict__ dot_out, const float *__restrict__ bias,
+                                           int64_t block, int8_t *qs /* NC x K group-interleaved int8, LDS */) {
   __shared__ float red_f[NC][kGemvThreads / 64];
   __shared__ int red_i[NC][kGemvThreads / 64];
   constexpr int kSlots = 64 / L;
@@ -378,7 +386,7 @@ gemv_fused_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   const int lam = lane % L, slot = lane / L;
   const int C = static_cast<int>(K / 64);  // 16-byte chunks per packed row
   const int64_t row_bytes = K / 4;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave * kRowsPerWave + slot;
+  const int64_t row0 = block * kRowsPerBlock + wave * kRowsPerWave + slot;
 
   // 1. Activation rows first: their absmax is the critical path, and loads
   // retire in order, so they must not queue behind the weights.
@@ -498,11 +506,46 @@ gemv_fused_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       if (r < rows && lam == n % L) {
         const int32_t rs = red_i[n][0] + red_i[n][1] + red_i[n][2] + red_i[n][3];
         const float t = ws * sc[n];
-        y[static_cast<int64_t>(n) * rows + r] = epilogue(total, rs, t);
+        float v = epilogue(total, rs, t);
+        if (bias) v = add_bias(v, bias[r]);
+        y[static_cast<int64_t>(n) * rows + r] = v;
         if (dot_out) dot_out[static_cast<int64_t>(n) * rows + r] = total;
       }
     }
   }
+}
+
+template <int NC, int L, int RPL, int CPL, int XPT>
+__global__ void __launch_bounds__(kGemvThreads)
+gemv_fused_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
+                  const float *__restrict__ x, float *__restrict__ y, int32_t *__restrict__ dot_out,
+                  const float *__restrict__ bias) {
+  extern __shared__ __attribute__((aligned(16))) int8_t qs[];
+  fused_body<NC, L, RPL, CPL, XPT>(packed, rows, K, x, y, dot_out, bias, blockIdx.x, qs);
+}
+
+// Several projections of the same activation rows in one launch (the decoder
+// layer's q/k/v, or gate/up): workgroups are numbered through the
+// projections in order, and each one quantizes the shared rows itself, as
+// above, before its share of one projection.
+struct FusedGroup {
+  int count;
+  int64_t block_end[I2S_GROUP_MAX];  // workgroups of projections 0..p
+  const uint8_t *packed[I2S_GROUP_MAX];
+  int64_t rows[I2S_GROUP_MAX];
+  const float *bias[I2S_GROUP_MAX];
+  float *y[I2S_GROUP_MAX];
+  int32_t *dot[I2S_GROUP_MAX];
+};
+
+template <int NC, int L, int RPL, int CPL, int XPT>
+__global__ void __launch_bounds__(kGemvThreads)
+gemv_fused_group_kernel(const FusedGroup g, int64_t K, const float *__restrict__ x) {
+  extern __shared__ __attribute__((aligned(16))) int8_t qs[];
+  int p = 0;
+  while (p + 1 < g.count && static_cast<int64_t>(blockIdx.x) >= g.block_end[p]) ++p;
+  const int64_t block = static_cast<int64_t>(blockIdx.x) - (p > 0 ? g.block_end[p - 1] : 0);
+  fused_body<NC, L, RPL, CPL, XPT>(g.packed[p], g.rows[p], K, x, g.y[p], g.dot[p], g.bias[p], block, qs);
 }
 
 // ---------------------------------------------------------------------------
@@ -548,7 +591,7 @@ __global__ void __launch_bounds__(Cfg::kThreads)
 gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
             const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
             const int32_t *__restrict__ row_sum, float *__restrict__ y,
-            int32_t *__restrict__ dot_out, int64_t tiles_m) {
+            int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t tiles_m) {
   constexpr int WM = Cfg::kWM, WN = Cfg::kWN;
   __shared__ __attribute__((aligned(16))) int8_t lds[2 * Cfg::kLdsStage];
 
@@ -657,15 +700,22 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       const int64_t o = o_base + 16 * m + 4 * kb;
       float *yr = y + nn * rows;
       if (o + 3 < rows && (rows % 4) == 0) {
-        *reinterpret_cast<float4 *>(yr + o) = make_float4(epilogue(acc[m][n][0], rs, t), epilogue(acc[m][n][1], rs, t),
-                                                         epilogue(acc[m][n][2], rs, t), epilogue(acc[m][n][3], rs, t));
+        float4 v = make_float4(epilogue(acc[m][n][0], rs, t), epilogue(acc[m][n][1], rs, t),
+                               epilogue(acc[m][n][2], rs, t), epilogue(acc[m][n][3], rs, t));
+        if (bias) {
+          const float4 b = *reinterpret_cast<const float4 *>(bias + o);
+          v = make_float4(add_bias(v.x, b.x), add_bias(v.y, b.y), add_bias(v.z, b.z), add_bias(v.w, b.w));
+        }
+        *reinterpret_cast<float4 *>(yr + o) = v;
         if (dot_out)
           *reinterpret_cast<int4 *>(dot_out + nn * rows + o) = make_int4(acc[m][n][0], acc[m][n][1], acc[m][n][2], acc[m][n][3]);
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (o + r < rows) {
-            yr[o + r] = epilogue(acc[m][n][r], rs, t);
+            float v = epilogue(acc[m][n][r], rs, t);
+            if (bias) v = add_bias(v, bias[o + r]);
+            yr[o + r] = v;
             if (dot_out) dot_out[nn * rows + o + r] = acc[m][n][r];
           }
         }
@@ -737,7 +787,7 @@ __global__ void __launch_bounds__(64 * WAVES)
 gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
                 const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
                 const int32_t *__restrict__ row_sum, float *__restrict__ y,
-                int32_t *__restrict__ dot_out, int64_t tiles_m, int ms) {
+                int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t tiles_m, int ms) {
   extern __shared__ __attribute__((aligned(16))) int8_t lds_res[];
   constexpr int BN = 16 * WN;
   static_assert(BN % WAVES == 0, "whole activation rows per wave");
@@ -870,6 +920,28 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 #pragma unroll
   for (int n = 0; n < WN; ++n) tn[n] = ws * sn[n];
 
+  // Bias of the outputs of a group (this lane's 4 consecutive output features
+  // of each subtile), loaded unconditionally ahead of its MFMAs; without a
+  // bias, or past the tensor, it reads 0 and is not added.
+  const bool has_bias = bias != nullptr;
+  const __amdgpu_buffer_rsrc_t bbuf = buffer_of(bias, has_bias ? static_cast<uint32_t>(4 * rows) : 0);
+  v4i bv[G];
+  auto load_bias = [&](int grp) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const uint32_t o = static_cast<uint32_t>(o_tile + 16 * static_cast<int64_t>(wave + WAVES * (grp * G + gi)) + 4 * kb);
+      if constexpr (VEC4) {
+        bv[gi] = __builtin_amdgcn_raw_buffer_load_b128(bbuf, 4 * o, 0, 0);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bv[gi][r] = __builtin_amdgcn_raw_buffer_load_b32(bbuf, 4 * (o + r), 0, 0);
+      }
+    }
+  };
+  auto with_bias = [&](float v, int gi, int r) {
+    return has_bias ? add_bias(v, __int_as_float(bv[gi][r])) : v;
+  };
+
   v4i acc[G][WN];
   // Stores of a finished group, non-temporal (the outputs are not read
   // again by this kernel); subtiles past the group (gi >= gs) and outputs
@@ -885,18 +957,18 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
         const uint32_t base = static_cast<uint32_t>((16 * n + li) * rows);  // element offset of this lane's row
         if constexpr (VEC4) {
           const uint32_t off = sub_ok && o < rows ? 4 * (base + static_cast<uint32_t>(o)) : kOutOfRange;
-          const v4i yv = {__float_as_int(epilogue(acc[gi][n][0], rsn[n], tn[n])),
-                          __float_as_int(epilogue(acc[gi][n][1], rsn[n], tn[n])),
-                          __float_as_int(epilogue(acc[gi][n][2], rsn[n], tn[n])),
-                          __float_as_int(epilogue(acc[gi][n][3], rsn[n], tn[n]))};
+          const v4i yv = {__float_as_int(with_bias(epilogue(acc[gi][n][0], rsn[n], tn[n]), gi, 0)),
+                          __float_as_int(with_bias(epilogue(acc[gi][n][1], rsn[n], tn[n]), gi, 1)),
+                          __float_as_int(with_bias(epilogue(acc[gi][n][2], rsn[n], tn[n]), gi, 2)),
+                          __float_as_int(with_bias(epilogue(acc[gi][n][3], rsn[n], tn[n]), gi, 3))};
           __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, kStreamStore);
           if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b128(acc[gi][n], dbuf, off, 0, kStreamStore);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t off = sub_ok && o + r < rows ? 4 * (base + static_cast<uint32_t>(o + r)) : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(epilogue(acc[gi][n][r], rsn[n], tn[n])), ybuf, off,
-                                                  0, kStreamStore);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(with_bias(epilogue(acc[gi][n][r], rsn[n], tn[n]), gi, r)),
+                                                  ybuf, off, 0, kStreamStore);
             if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(acc[gi][n][r], dbuf, off, 0, kStreamStore);
           }
         }
@@ -933,6 +1005,7 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   auto item = [&](const v4i (&cur)[G][S], v4i (&nxt)[G][S]) {
     const int gs = grp + 1 < groups ? G : mine - grp * G;
     if constexpr (SINGLE) {
+      load_bias(grp);
       load_w(grp + 1 < groups ? grp + 1 : 0, 0, nxt);
       zero_acc();
       mfma_group(cur, gs, lb0);
@@ -941,6 +1014,7 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
     } else {
       const int ngrp = ch + 1 < chunks ? grp : grp + 1;
       const int nch = ch + 1 < chunks ? ch + 1 : 0;
+      load_bias(grp);
       load_w(ngrp < groups ? ngrp : 0, nch, nxt);
       if (ch == 0) zero_acc();
       mfma_group(cur, gs, lb0 + 256 * S * ch);
@@ -954,6 +1028,7 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
     // First group, step by step, interleaved with the activation copy; waves
     // without subtiles (gs0 == 0) still copy and meet every barrier.
     const int gs0 = groups > 1 ? G : mine;
+    load_bias(0);
     zero_acc();
 #pragma unroll
     for (int st = 0; st < S; ++st) {
@@ -1017,8 +1092,8 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 // miss the XCD's L2 on the same lines at once; integer sums do not depend on
 // the order of their terms.  As in gemm_res_kernel, every global access is an
 // unconditional buffer access, so each wait is for exactly the loads it needs.
-// DUAL keeps a second weight register set so that the next group's weights
-// load during the current group; without it they load after its MFMAs.
+// Two weight register sets: the next group's weights load during the current
+// group's MFMAs.
 
 template <int G, int WN>
 __device__ __forceinline__ void pipe_mfma_step(v4i (&acc)[G][WN], const v4i (&w)[G], const int8_t *lb,
@@ -1044,12 +1119,12 @@ __device__ __forceinline__ void pipe_mfma_step(v4i (&acc)[G][WN], const v4i (&w)
   }
 }
 
-template <int G, int WN, int WAVES, int SM, bool DUAL, bool VEC4, bool DOT>
+template <int G, int WN, int WAVES, int SM, bool VEC4, bool DOT>
 __global__ void __launch_bounds__(64 * WAVES)
 gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
                  const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
                  const int32_t *__restrict__ row_sum, float *__restrict__ y,
-                 int32_t *__restrict__ dot_out, int64_t tiles_m, int ms) {
+                 int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t tiles_m, int ms) {
   extern __shared__ __attribute__((aligned(16))) int8_t lds_pipe[];
   constexpr int BN = 16 * WN;
   constexpr int kThreads = 64 * WAVES;
@@ -1108,8 +1183,7 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
     return static_cast<uint32_t>(r >> 2) * group_stride + 64 * (16 * phys(st) + (pc & 15)) + 16 * (r & 3);
   };
 
-  v4i wa[G][SM];
-  v4i wb[DUAL ? G : 1][DUAL ? SM : 1];
+  v4i wa[G][SM], wb[G][SM];
   v4i bst[SM][kPieceLanes];
 #pragma unroll
   for (int st = 0; st < SM; ++st) {
@@ -1118,7 +1192,7 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 #pragma unroll
     for (int j = 0; j < G; ++j) wa[j][st] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, w_off(0, j, st), 0, 0);
   }
-  if constexpr (DUAL) load_w(1, wb);
+  load_w(1, wb);
   // Epilogue constants last: the first group's epilogue needs them only after
   // all of its steps.
   const __amdgpu_buffer_rsrc_t cbuf = buffer_of(packed + rows * static_cast<int64_t>(row_bytes), 4);
@@ -1133,6 +1207,25 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
     sn[n] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, off, 0, 0));
     rsn[n] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, off, 0, 0);
   }
+  // Bias of a group's outputs (this lane's 4 consecutive output features of
+  // each subtile): reads 0 without a bias or past the tensor, and is then
+  // not added.
+  const bool has_bias = bias != nullptr;
+  const __amdgpu_buffer_rsrc_t bbuf = buffer_of(bias, has_bias ? static_cast<uint32_t>(4 * rows) : 0);
+  v4i bv[G];
+  auto load_bias = [&](int grp) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const uint32_t o = static_cast<uint32_t>(o_tile + 16 * static_cast<int64_t>(wave + WAVES * (G * grp + j)) + 4 * kb);
+      if constexpr (VEC4) {
+        bv[j] = __builtin_amdgcn_raw_buffer_load_b128(bbuf, 4 * o, 0, 0);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bv[j][r] = __builtin_amdgcn_raw_buffer_load_b32(bbuf, 4 * (o + r), 0, 0);
+      }
+    }
+  };
+  load_bias(0);
   // Keep every load above ahead of the first wait below.
   __builtin_amdgcn_sched_barrier(0);
 
@@ -1174,7 +1267,10 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
         v4i &yv = yst[j][n];
         v4i &dv = dst[j][DOT ? n : 0];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yv[r] = __float_as_int(epilogue(acc[j][n][r], rsn[n], tn[n]));
+        for (int r = 0; r < 4; ++r) {
+          const float v = epilogue(acc[j][n][r], rsn[n], tn[n]);
+          yv[r] = __float_as_int(has_bias ? add_bias(v, __int_as_float(bv[j][r])) : v);
+        }
         if constexpr (DOT) dv = acc[j][n];
         if constexpr (VEC4) {
           const uint32_t off = ok && o < rows ? 4 * (base + static_cast<uint32_t>(o)) : kOutOfRange;
@@ -1221,34 +1317,26 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
     }
   }
 
-  if constexpr (DUAL) {
-    // Each group's MFMAs are followed by the loads of the group two ahead,
-    // into the register set they have just finished with, then its stores.
-    load_w(2, wa);
+  // Each group's MFMAs are followed by the loads of the group two ahead, into
+  // the register set they have just finished with, then its stores; a
+  // group's bias loads ahead of its MFMAs.
+  load_w(2, wa);
+  __builtin_amdgcn_sched_barrier(0);
+  epilogue_group(0);
+  for (int g = 1; g < groups; g += 2) {
+    load_bias(g);
+    zero_acc();
+    mfma_group(wb);
+    load_w(g + 2, wb);
     __builtin_amdgcn_sched_barrier(0);
-    epilogue_group(0);
-    for (int g = 1; g < groups; g += 2) {
-      zero_acc();
-      mfma_group(wb);
-      load_w(g + 2, wb);
-      __builtin_amdgcn_sched_barrier(0);
-      epilogue_group(g);
-      if (g + 1 >= groups) break;
-      zero_acc();
-      mfma_group(wa);
-      load_w(g + 3, wa);
-      __builtin_amdgcn_sched_barrier(0);
-      epilogue_group(g + 1);
-    }
-  } else {
-    for (int g = 0;; ++g) {
-      load_w(g + 1, wa);
-      __builtin_amdgcn_sched_barrier(0);
-      epilogue_group(g);
-      if (g + 1 >= groups) break;
-      zero_acc();
-      mfma_group(wa);
-    }
+    epilogue_group(g);
+    if (g + 1 >= groups) break;
+    load_bias(g + 1);
+    zero_acc();
+    mfma_group(wa);
+    load_w(g + 3, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    epilogue_group(g + 1);
   }
   // Keep the store registers allocated up to here (see above).
 #pragma unroll
@@ -1280,7 +1368,8 @@ template <int W, int SPW, bool VEC4, bool DOT>
 __global__ void __launch_bounds__(64 * W)
 gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
                  const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
-                 const int32_t *__restrict__ row_sum, float *__restrict__ y, int32_t *__restrict__ dot_out) {
+                 const int32_t *__restrict__ row_sum, float *__restrict__ y, int32_t *__restrict__ dot_out,
+                 const float *__restrict__ bias) {
   __shared__ __attribute__((aligned(16))) v4i part[W][64];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -1358,17 +1447,24 @@ gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + o0, out_bytes);
   const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + o0 : nullptr, DOT ? out_bytes : 0);
   const uint32_t base = static_cast<uint32_t>(li * rows + 4 * kb);  // element offset from y + o0
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = epilogue(tot[r], rs, t);
+  if (bias) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (o + r < rows) v[r] = add_bias(v[r], bias[o + r]);
+  }
   if constexpr (VEC4) {
     const uint32_t off = li < N && o < rows ? 4 * base : kOutOfRange;
-    const v4i yv = {__float_as_int(epilogue(tot[0], rs, t)), __float_as_int(epilogue(tot[1], rs, t)),
-                    __float_as_int(epilogue(tot[2], rs, t)), __float_as_int(epilogue(tot[3], rs, t))};
+    const v4i yv = {__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])};
     __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, 0);
     if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b128(tot, dbuf, off, 0, 0);
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t off = li < N && o + r < rows ? 4 * (base + r) : kOutOfRange;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(epilogue(tot[r], rs, t)), ybuf, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[r]), ybuf, off, 0, 0);
       if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(tot[r], dbuf, off, 0, 0);
     }
   }
@@ -1381,12 +1477,12 @@ inline int hip_status() { return hipGetLastError() == hipSuccess ? I2S_OK : I2S_
 
 template <int NC, int L, int RPL, int CPL>
 int launch_gemv_cfg(const uint8_t *packed, int64_t rows, int64_t K, const ActWorkspace &ws,
-                    float *y, int32_t *dot_out, hipStream_t stream) {
+                    float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
   constexpr int kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
   const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks > kMaxDim) return I2S_ERANGE;
   hipLaunchKernelGGL((gemv_kernel<NC, L, RPL, CPL>), dim3(static_cast<unsigned>(blocks)), dim3(kGemvThreads), 0,
-                     stream, packed, rows, K, ws.q, ws.scale, ws.row_sum, y, dot_out);
+                     stream, packed, rows, K, ws.q, ws.scale, ws.row_sum, y, dot_out, bias);
   return hip_status();
 }
 
@@ -1399,36 +1495,36 @@ int gemv_auto_variant(int64_t K) {
 
 template <int NC>
 int launch_gemv_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K, const ActWorkspace &ws,
-                   float *y, int32_t *dot_out, hipStream_t stream) {
+                   float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
   if (variant == 0) variant = gemv_auto_variant(K);
   switch (variant) {
-    case 1: return launch_gemv_cfg<NC, 4, 1, 2>(packed, rows, K, ws, y, dot_out, stream);
-    case 2: return launch_gemv_cfg<NC, 8, 1, 4>(packed, rows, K, ws, y, dot_out, stream);
-    case 3: return launch_gemv_cfg<NC, 64, 1, 3>(packed, rows, K, ws, y, dot_out, stream);
-    case 4: return launch_gemv_cfg<NC, 8, 2, 3>(packed, rows, K, ws, y, dot_out, stream);
-    case 5: return launch_gemv_cfg<NC, 16, 1, 2>(packed, rows, K, ws, y, dot_out, stream);
+    case 1: return launch_gemv_cfg<NC, 4, 1, 2>(packed, rows, K, ws, y, dot_out, bias, stream);
+    case 2: return launch_gemv_cfg<NC, 8, 1, 4>(packed, rows, K, ws, y, dot_out, bias, stream);
+    case 3: return launch_gemv_cfg<NC, 64, 1, 3>(packed, rows, K, ws, y, dot_out, bias, stream);
+    case 4: return launch_gemv_cfg<NC, 8, 2, 3>(packed, rows, K, ws, y, dot_out, bias, stream);
+    case 5: return launch_gemv_cfg<NC, 16, 1, 2>(packed, rows, K, ws, y, dot_out, bias, stream);
     default: return I2S_EKERNEL;
   }
 }
 constexpr int kGemvVariants = 5;
 
 int launch_gemv(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
-                float *y, int32_t *dot_out, hipStream_t stream) {
+                float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
   switch (N) {
-    case 1: return launch_gemv_nc<1>(variant, packed, rows, K, ws, y, dot_out, stream);
-    case 2: return launch_gemv_nc<2>(variant, packed, rows, K, ws, y, dot_out, stream);
-    case 3: return launch_gemv_nc<3>(variant, packed, rows, K, ws, y, dot_out, stream);
-    case 4: return launch_gemv_nc<4>(variant, packed, rows, K, ws, y, dot_out, stream);
-    case 5: return launch_gemv_nc<5>(variant, packed, rows, K, ws, y, dot_out, stream);
-    case 6: return launch_gemv_nc<6>(variant, packed, rows, K, ws, y, dot_out, stream);
-    case 7: return launch_gemv_nc<7>(variant, packed, rows, K, ws, y, dot_out, stream);
-    case 8: return launch_gemv_nc<8>(variant, packed, rows, K, ws, y, dot_out, stream);
+    case 1: return launch_gemv_nc<1>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
+    case 2: return launch_gemv_nc<2>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
+    case 3: return launch_gemv_nc<3>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
+    case 4: return launch_gemv_nc<4>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
+    case 5: return launch_gemv_nc<5>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
+    case 6: return launch_gemv_nc<6>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
+    case 7: return launch_gemv_nc<7>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
+    case 8: return launch_gemv_nc<8>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
     default: return I2S_EKERNEL;
   }
 }
 
 template <int NC, int L, int RPL, int CPL, int XPT>
-int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float *x, float *y, int32_t *dot_out,
+int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float *x, float *y, int32_t *dot_out, const float *bias,
                      hipStream_t stream) {
   if (K > 64 * L * CPL || K > 4 * kGemvThreads * XPT) return I2S_EKERNEL;
   if (rows * (K / 4) >= (int64_t{1} << 31)) return I2S_EKERNEL;  // 32-bit buffer offsets
@@ -1436,7 +1532,7 @@ int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float
   const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks > kMaxDim) return I2S_ERANGE;
   hipLaunchKernelGGL((gemv_fused_kernel<NC, L, RPL, CPL, XPT>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kGemvThreads), static_cast<size_t>(NC * K), stream, packed, rows, K, x, y, dot_out);
+                     dim3(kGemvThreads), static_cast<size_t>(NC * K), stream, packed, rows, K, x, y, dot_out, bias);
   return hip_status();
 }
 
@@ -1451,25 +1547,67 @@ int fused_auto_variant(int64_t rows, int64_t K) { return K <= 2048 ? (rows <= 20
 
 template <int NC>
 int launch_fused_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K, const float *x, float *y,
-                    int32_t *dot_out, hipStream_t stream) {
+                    int32_t *dot_out, const float *bias, hipStream_t stream) {
   if (variant == 0) variant = fused_auto_variant(rows, K);
   switch (variant) {
-    case 1: return launch_fused_cfg<NC, 8, 2, 3, 2>(packed, rows, K, x, y, dot_out, stream);
-    case 2: return launch_fused_cfg<NC, 8, 1, 4, 2>(packed, rows, K, x, y, dot_out, stream);
-    case 3: return launch_fused_cfg<NC, 16, 1, 2, 2>(packed, rows, K, x, y, dot_out, stream);
-    case 4: return launch_fused_cfg<NC, 64, 1, 3, 9>(packed, rows, K, x, y, dot_out, stream);
-    case 5: return launch_fused_cfg<NC, 32, 1, 5, 9>(packed, rows, K, x, y, dot_out, stream);
+    case 1: return launch_fused_cfg<NC, 8, 2, 3, 2>(packed, rows, K, x, y, dot_out, bias, stream);
+    case 2: return launch_fused_cfg<NC, 8, 1, 4, 2>(packed, rows, K, x, y, dot_out, bias, stream);
+    case 3: return launch_fused_cfg<NC, 16, 1, 2, 2>(packed, rows, K, x, y, dot_out, bias, stream);
+    case 4: return launch_fused_cfg<NC, 64, 1, 3, 9>(packed, rows, K, x, y, dot_out, bias, stream);
+    case 5: return launch_fused_cfg<NC, 32, 1, 5, 9>(packed, rows, K, x, y, dot_out, bias, stream);
     default: return I2S_EKERNEL;
   }
 }
 
 int launch_fused(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const float *x, float *y,
-                 int32_t *dot_out, hipStream_t stream) {
+                 int32_t *dot_out, const float *bias, hipStream_t stream) {
   switch (N) {
-    case 1: return launch_fused_nc<1>(variant, packed, rows, K, x, y, dot_out, stream);
-    case 2: return launch_fused_nc<2>(variant, packed, rows, K, x, y, dot_out, stream);
-    case 3: return launch_fused_nc<3>(variant, packed, rows, K, x, y, dot_out, stream);
-    case 4: return launch_fused_nc<4>(variant, packed, rows, K, x, y, dot_out, stream);
+    case 1: return launch_fused_nc<1>(variant, packed, rows, K, x, y, dot_out, bias, stream);
+    case 2: return launch_fused_nc<2>(variant, packed, rows, K, x, y, dot_out, bias, stream);
+    case 3: return launch_fused_nc<3>(variant, packed, rows, K, x, y, dot_out, bias, stream);
+    case 4: return launch_fused_nc<4>(variant, packed, rows, K, x, y, dot_out, bias, stream);
+    default: return I2S_EKERNEL;
+  }
+}
+
+template <int NC, int L, int RPL, int CPL, int XPT>
+int launch_fused_group_cfg(FusedGroup g, int64_t K, const float *x, hipStream_t stream) {
+  if (K > 64 * L * CPL || K > 4 * kGemvThreads * XPT) return I2S_EKERNEL;
+  constexpr int kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
+  int64_t total = 0;
+  for (int p = 0; p < g.count; ++p) {
+    if (g.rows[p] * (K / 4) >= (int64_t{1} << 31)) return I2S_EKERNEL;  // 32-bit buffer offsets
+    total += (g.rows[p] + kRowsPerBlock - 1) / kRowsPerBlock;
+    g.block_end[p] = total;
+  }
+  if (total == 0) return I2S_OK;
+  if (total > kMaxDim) return I2S_ERANGE;
+  hipLaunchKernelGGL((gemv_fused_group_kernel<NC, L, RPL, CPL, XPT>), dim3(static_cast<unsigned>(total)),
+                     dim3(kGemvThreads), static_cast<size_t>(NC * K), stream, g, K, x);
+  return hip_status();
+}
+
+template <int NC>
+int launch_fused_group_nc(int variant, const FusedGroup &g, int64_t total_rows, int64_t K, const float *x,
+                          hipStream_t stream) {
+  if (variant == 0) variant = fused_auto_variant(total_rows, K);
+  switch (variant) {
+    case 1: return launch_fused_group_cfg<NC, 8, 2, 3, 2>(g, K, x, stream);
+    case 2: return launch_fused_group_cfg<NC, 8, 1, 4, 2>(g, K, x, stream);
+    case 3: return launch_fused_group_cfg<NC, 16, 1, 2, 2>(g, K, x, stream);
+    case 4: return launch_fused_group_cfg<NC, 64, 1, 3, 9>(g, K, x, stream);
+    case 5: return launch_fused_group_cfg<NC, 32, 1, 5, 9>(g, K, x, stream);
+    default: return I2S_EKERNEL;
+  }
+}
+
+int launch_fused_group(int variant, const FusedGroup &g, int64_t total_rows, int64_t K, int64_t N, const float *x,
+                       hipStream_t stream) {
+  switch (N) {
+    case 1: return launch_fused_group_nc<1>(variant, g, total_rows, K, x, stream);
+    case 2: return launch_fused_group_nc<2>(variant, g, total_rows, K, x, stream);
+    case 3: return launch_fused_group_nc<3>(variant, g, total_rows, K, x, stream);
+    case 4: return launch_fused_group_nc<4>(variant, g, total_rows, K, x, stream);
     default: return I2S_EKERNEL;
   }
 }
@@ -1486,13 +1624,13 @@ inline bool fused_auto(int64_t rows, int64_t N, int64_t K) {
 
 template <class Cfg>
 int launch_gemm_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
-                    float *y, int32_t *dot_out, hipStream_t stream) {
+                    float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
   const int64_t tiles_m = (rows + Cfg::kBM - 1) / Cfg::kBM;
   const int64_t tiles_n = (N + Cfg::kBN - 1) / Cfg::kBN;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > kMaxDim) return I2S_ERANGE;
   hipLaunchKernelGGL((gemm_kernel<Cfg>), dim3(static_cast<unsigned>(blocks)), dim3(Cfg::kThreads), 0, stream,
-                     packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out, tiles_m);
+                     packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out, bias, tiles_m);
   return hip_status();
 }
 
@@ -1534,7 +1672,8 @@ int pick_stream_variant(int64_t rows, int64_t N) {
 // 2^31 bytes (else I2S_EKERNEL, and the automatic choice streams instead).
 template <int G, int WN, int S, int WAVES, bool VEC4, bool DOT, bool SINGLE>
 int launch_res_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
-                    const ActWorkspace &ws, float *y, int32_t *dot_out, int64_t tiles_m, int64_t ms,
+                    const ActWorkspace &ws, float *y, int32_t *dot_out, const float *bias, int64_t tiles_m,
+                    int64_t ms,
                     hipStream_t stream) {
   // Allow up to 160 KiB of dynamic LDS, once per device for this instantiation
   // (repeating it from racing threads is harmless).
@@ -1550,13 +1689,13 @@ int launch_res_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t 
   }
   hipLaunchKernelGGL((gemm_res_kernel<G, WN, S, WAVES, VEC4, DOT, SINGLE>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * WAVES), static_cast<size_t>(lds), stream, packed, rows, K, ws.q, N, ws.scale,
-                     ws.row_sum, y, dot_out, tiles_m, static_cast<int>(ms));
+                     ws.row_sum, y, dot_out, bias, tiles_m, static_cast<int>(ms));
   return hip_status();
 }
 
 template <int G, int WN, int S, int WAVES>
 int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
-                   int32_t *dot_out, hipStream_t stream) {
+                   int32_t *dot_out, const float *bias, hipStream_t stream) {
   constexpr int64_t BN = 16 * WN;
   const int64_t lds = BN * res_pitch(K, S);
   if (lds > kResMaxLds) return I2S_EKERNEL;
@@ -1578,7 +1717,7 @@ int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, co
   const bool vec4 = (rows % 4) == 0;
   const bool single = (K + 255) / 256 <= S;
 #define I2S_RES(V, D, SG)                                                                                         \
-  return launch_res_inst<G, WN, S, WAVES, V, D, SG>(blocks, lds, packed, rows, K, N, ws, y, dot_out, tiles_m, ms, \
+  return launch_res_inst<G, WN, S, WAVES, V, D, SG>(blocks, lds, packed, rows, K, N, ws, y, dot_out, bias, tiles_m, ms, \
                                                     stream)
   if (single) {
     if (vec4) {
@@ -1600,29 +1739,30 @@ int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, co
 // Pipelined launch: BN = 16*WN activation rows per block, about one block per
 // compute unit; K must fit in SM steps and the activation tile in LDS, and
 // buffer offsets must stay below 2^31 bytes (else I2S_EKERNEL).
-template <int G, int WN, int WAVES, int SM, bool DUAL, bool VEC4, bool DOT>
+template <int G, int WN, int WAVES, int SM, bool VEC4, bool DOT>
 int launch_pipe_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
-                    const ActWorkspace &ws, float *y, int32_t *dot_out, int64_t tiles_m, int64_t ms,
+                    const ActWorkspace &ws, float *y, int32_t *dot_out, const float *bias, int64_t tiles_m,
+                    int64_t ms,
                     hipStream_t stream) {
   static std::atomic<uint64_t> attr_done{0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return I2S_EHIP;
   const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
   if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_pipe_kernel<G, WN, WAVES, SM, DUAL, VEC4, DOT>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_pipe_kernel<G, WN, WAVES, SM, VEC4, DOT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kResMaxLds) != hipSuccess)
       return I2S_EHIP;
     attr_done.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemm_pipe_kernel<G, WN, WAVES, SM, DUAL, VEC4, DOT>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((gemm_pipe_kernel<G, WN, WAVES, SM, VEC4, DOT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * WAVES), static_cast<size_t>(lds), stream, packed, rows, K, ws.q, N, ws.scale,
-                     ws.row_sum, y, dot_out, tiles_m, static_cast<int>(ms));
+                     ws.row_sum, y, dot_out, bias, tiles_m, static_cast<int>(ms));
   return hip_status();
 }
 
-template <int G, int WN, int WAVES, int SM, bool DUAL>
+template <int G, int WN, int WAVES, int SM>
 int launch_pipe_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
-                   int32_t *dot_out, hipStream_t stream) {
+                   int32_t *dot_out, const float *bias, hipStream_t stream) {
   constexpr int64_t BN = 16 * WN;
   const int64_t steps = (K + 255) / 256;
   const int64_t lds = BN * (256 * steps + 16);
@@ -1641,7 +1781,7 @@ int launch_pipe_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, c
   if (blocks > kMaxDim || ms > kMaxDim) return I2S_ERANGE;
   const bool vec4 = (rows % 4) == 0;
 #define I2S_SEQ(V, D) \
-  return launch_pipe_inst<G, WN, WAVES, SM, DUAL, V, D>(blocks, lds, packed, rows, K, N, ws, y, dot_out, tiles_m, ms, \
+  return launch_pipe_inst<G, WN, WAVES, SM, V, D>(blocks, lds, packed, rows, K, N, ws, y, dot_out, bias, tiles_m, ms, \
                                                          stream)
   if (vec4) {
     if (dot_out) I2S_SEQ(true, true);
@@ -1680,19 +1820,19 @@ int gemm_auto_variant(int64_t rows, int64_t K, int64_t N) {
 }
 
 int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
-                float *y, int32_t *dot_out, hipStream_t stream) {
+                float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
   if (variant == 0) variant = gemm_auto_variant(rows, K, N);
   switch (variant) {
-    case 1: return launch_gemm_cfg<GemmA>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 2: return launch_gemm_cfg<GemmB>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 3: return launch_gemm_cfg<GemmC>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 4: return launch_gemm_cfg<GemmD>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 5: return launch_res_cfg<3, 4, 6, 4>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 6: return launch_res_cfg<2, 4, 6, 8>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 7: return launch_res_cfg<3, 4, 3, 8>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 8: return launch_res_cfg<3, 2, 6, 8>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 9: return launch_res_cfg<3, 1, 6, 8>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 10: return launch_pipe_cfg<2, 2, 4, 6, true>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 1: return launch_gemm_cfg<GemmA>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 2: return launch_gemm_cfg<GemmB>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 3: return launch_gemm_cfg<GemmC>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 4: return launch_gemm_cfg<GemmD>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 5: return launch_res_cfg<3, 4, 6, 4>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 6: return launch_res_cfg<2, 4, 6, 8>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 7: return launch_res_cfg<3, 4, 3, 8>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 8: return launch_res_cfg<3, 2, 6, 8>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 9: return launch_res_cfg<3, 1, 6, 8>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 10: return launch_pipe_cfg<2, 2, 4, 6>(packed, rows, K, N, ws, y, dot_out, bias, stream);
     default: return I2S_EKERNEL;
   }
 }
@@ -1712,31 +1852,31 @@ bool skinny_fits(int64_t rows, int64_t K, int64_t N) {
 
 template <int SPW, bool VEC4, bool DOT>
 int launch_skinny_inst(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
-                       int32_t *dot_out, hipStream_t stream) {
+                       int32_t *dot_out, const float *bias, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_mfma_kernel<8, SPW, VEC4, DOT>), dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(512), 0,
-                     stream, packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out);
+                     stream, packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out, bias);
   return hip_status();
 }
 
 template <int SPW>
 int launch_skinny_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
-                      int32_t *dot_out, hipStream_t stream) {
+                      int32_t *dot_out, const float *bias, hipStream_t stream) {
   // 32-bit buffer offsets: activation rows (N*K), one subtile's weights and
   // the outputs past the block's first row (N*rows*4) stay below 2^31.
   if (!skinny_fits(rows, K, N)) return I2S_EKERNEL;
   const bool vec4 = (rows % 4) == 0;
-  if (vec4) return dot_out ? launch_skinny_inst<SPW, true, true>(packed, rows, K, N, ws, y, dot_out, stream)
-                           : launch_skinny_inst<SPW, true, false>(packed, rows, K, N, ws, y, dot_out, stream);
-  return dot_out ? launch_skinny_inst<SPW, false, true>(packed, rows, K, N, ws, y, dot_out, stream)
-                 : launch_skinny_inst<SPW, false, false>(packed, rows, K, N, ws, y, dot_out, stream);
+  if (vec4) return dot_out ? launch_skinny_inst<SPW, true, true>(packed, rows, K, N, ws, y, dot_out, bias, stream)
+                           : launch_skinny_inst<SPW, true, false>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+  return dot_out ? launch_skinny_inst<SPW, false, true>(packed, rows, K, N, ws, y, dot_out, bias, stream)
+                 : launch_skinny_inst<SPW, false, false>(packed, rows, K, N, ws, y, dot_out, bias, stream);
 }
 
 int launch_skinny(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
-                  float *y, int32_t *dot_out, hipStream_t stream) {
+                  float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
   if (variant == 0) variant = skinny_auto_variant(K);
   switch (variant) {
-    case 1: return launch_skinny_cfg<2>(packed, rows, K, N, ws, y, dot_out, stream);
-    case 2: return launch_skinny_cfg<4>(packed, rows, K, N, ws, y, dot_out, stream);
+    case 1: return launch_skinny_cfg<2>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 2: return launch_skinny_cfg<4>(packed, rows, K, N, ws, y, dot_out, bias, stream);
     default: return I2S_EKERNEL;
   }
 }
@@ -1851,11 +1991,11 @@ int contract_auto_kernel(int64_t rows, int64_t K, int64_t N) {
 }
 
 int contract(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
-             int32_t *dot_out, int kernel, int variant, hipStream_t s) {
+             int32_t *dot_out, const float *bias, int kernel, int variant, hipStream_t s) {
   if (kernel == 0) kernel = contract_auto_kernel(rows, K, N);
-  if (kernel == 4) return launch_skinny(variant, packed, rows, K, N, ws, y, dot_out, s);
-  if (kernel == 1) return launch_gemv(variant, packed, rows, K, N, ws, y, dot_out, s);
-  return launch_gemm(variant, packed, rows, K, N, ws, y, dot_out, s);
+  if (kernel == 4) return launch_skinny(variant, packed, rows, K, N, ws, y, dot_out, bias, s);
+  if (kernel == 1) return launch_gemv(variant, packed, rows, K, N, ws, y, dot_out, bias, s);
+  return launch_gemm(variant, packed, rows, K, N, ws, y, dot_out, bias, s);
 }
 
 }  // namespace
@@ -1882,7 +2022,7 @@ extern "C" int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, in
   int st = check_mul_mat(packed, rows, K, N, workspace, workspace_bytes, y, dot_out, kernel, variant, &noop);
   if (st != I2S_OK || noop) return st;
   ActWorkspace ws = carve_workspace(const_cast<void *>(workspace), N, K);
-  return contract(packed, rows, K, N, ws, y, dot_out, kernel, variant, static_cast<hipStream_t>(stream));
+  return contract(packed, rows, K, N, ws, y, dot_out, nullptr, kernel, variant, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int i2s_mul_mat_ex(const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t N,
@@ -1893,16 +2033,63 @@ extern "C" int i2s_mul_mat_ex(const uint8_t *packed, int64_t rows, int64_t K, co
   if (st != I2S_OK || noop) return st;
   if (!x || !aligned16(x)) return I2S_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (kernel == 3 || (kernel == 0 && fused_auto(rows, N, K))) return launch_fused(variant, packed, rows, K, N, x, y, dot_out, s);
+  if (kernel == 3 || (kernel == 0 && fused_auto(rows, N, K)))
+    return launch_fused(variant, packed, rows, K, N, x, y, dot_out, nullptr, s);
   ActWorkspace ws = carve_workspace(workspace, N, K);
   st = quantize_launch(x, N, K, ws.q, ws.scale, ws.row_sum, true, s);
   if (st != I2S_OK) return st;
-  return contract(packed, rows, K, N, ws, y, dot_out, kernel, variant, s);
+  return contract(packed, rows, K, N, ws, y, dot_out, nullptr, kernel, variant, s);
 }
 
 extern "C" int i2s_mul_mat(const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t N,
                            void *workspace, size_t workspace_bytes, float *y, int32_t *dot_out, void *stream) {
   return i2s_mul_mat_ex(packed, rows, K, x, N, workspace, workspace_bytes, y, dot_out, 0, 0, stream);
+}
+
+extern "C" int i2s_mul_mat_group_ex(const i2s_proj *projs, int count, int64_t K, const float *x, int64_t N,
+                                    void *workspace, size_t workspace_bytes, int kernel, int variant,
+                                    void *stream) {
+  if (!projs || count < 1 || count > I2S_GROUP_MAX) return I2S_EINVAL;
+  bool all_noop = true;
+  int64_t total_rows = 0;
+  bool fits = true;
+  for (int p = 0; p < count; ++p) {
+    bool noop;
+    const int st = check_mul_mat(projs[p].packed, projs[p].rows, K, N, workspace, workspace_bytes, projs[p].y,
+                                 projs[p].dot_out, kernel, variant, &noop);
+    if (st != I2S_OK) return st;
+    if (!noop && projs[p].bias && !aligned16(projs[p].bias)) return I2S_EINVAL;
+    all_noop = all_noop && noop;
+    total_rows += projs[p].rows;
+    fits = fits && projs[p].rows * (K / 4) < (int64_t{1} << 31);
+  }
+  if (all_noop) return I2S_OK;
+  if (!x || !aligned16(x)) return I2S_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kernel == 3 || (kernel == 0 && N <= 3 && K <= kFusedMaxK && fits)) {
+    FusedGroup g{};
+    g.count = count;
+    for (int p = 0; p < count; ++p) {
+      g.packed[p] = projs[p].packed;
+      g.rows[p] = projs[p].rows;
+      g.bias[p] = projs[p].bias;
+      g.y[p] = projs[p].y;
+      g.dot[p] = projs[p].dot_out;
+    }
+    return launch_fused_group(variant, g, total_rows, K, N, x, s);
+  }
+  ActWorkspace ws = carve_workspace(workspace, N, K);
+  int st = quantize_launch(x, N, K, ws.q, ws.scale, ws.row_sum, true, s);
+  for (int p = 0; p < count && st == I2S_OK; ++p)
+    if (projs[p].rows > 0)
+      st = contract(projs[p].packed, projs[p].rows, K, N, ws, projs[p].y, projs[p].dot_out, projs[p].bias, kernel,
+                    variant, s);
+  return st;
+}
+
+extern "C" int i2s_mul_mat_group(const i2s_proj *projs, int count, int64_t K, const float *x, int64_t N,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  return i2s_mul_mat_group_ex(projs, count, K, x, N, workspace, workspace_bytes, 0, 0, stream);
 }
 
 extern "C" int i2s_mul_mat_kernel(int64_t rows, int64_t K, int64_t N) {

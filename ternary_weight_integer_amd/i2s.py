@@ -36,6 +36,15 @@ class I2SError(RuntimeError):
         super().__init__(f"{fn}: {i2s_strerror(status)} (status {status})")
 
 
+class I2SProj(ctypes.Structure):
+    """One projection of a grouped call (struct i2s_proj of include/i2s.h)."""
+    _fields_ = [("packed", ctypes.c_void_p), ("rows", ctypes.c_int64), ("bias", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("dot_out", ctypes.c_void_p)]
+
+
+I2S_GROUP_MAX = 8
+
+
 def declared_symbols() -> list[str]:
     """Names of the functions include/i2s.h declares."""
     with open(HEADER_PATH) as f:
@@ -73,6 +82,10 @@ def lib() -> ctypes.CDLL:
         L.i2s_mul_mat_kernel.argtypes = [i64, i64, i64]
         L.i2s_mul_mat_variant.restype = ci
         L.i2s_mul_mat_variant.argtypes = [i64, i64, i64]
+        L.i2s_mul_mat_group.restype = ci
+        L.i2s_mul_mat_group.argtypes = [ctypes.POINTER(I2SProj), ci, i64, p, i64, p, sz, p]
+        L.i2s_mul_mat_group_ex.restype = ci
+        L.i2s_mul_mat_group_ex.argtypes = [ctypes.POINTER(I2SProj), ci, i64, p, i64, p, sz, ci, ci, p]
         L.i2s_kernel_variants.restype = ci
         L.i2s_kernel_variants.argtypes = [ci]
         L.i2s_strerror.restype = ctypes.c_char_p
@@ -248,3 +261,38 @@ def i2s_mul_mat_ws(packed: torch.Tensor, rows: int, K: int, N: int, workspace: t
         _dev(packed, torch.uint8, "packed"), rows, K, N, _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _dev(y, torch.float32, "y"), dptr, int(kernel), int(variant), _stream(stream)))
     return (y, dot_out) if want_dot else y
+
+
+def i2s_mul_mat_group(weights, K: int, x: torch.Tensor, biases=None, workspace=None, dot_out: bool = False,
+                      kernel: int = KERNEL_AUTO, variant: int = 0, stream=None):
+    """Several projections of one activation x[N][K]: weights is a list of
+    (packed tensor, rows); biases a matching list of F32 [rows] tensors or
+    None.  Returns the list of y[N][rows] (and of the int32 dots if dot_out)."""
+    N = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [N][{K}], got {tuple(x.shape)}")
+    count = len(weights)
+    if biases is None:
+        biases = [None] * count
+    if len(biases) != count:
+        raise ValueError("one bias entry (or None) per projection")
+    dev = x.device
+    workspace = new_workspace(N, K, dev) if workspace is None else workspace
+    projs = (I2SProj * max(count, 1))()
+    ys, dots = [], []
+    for i, ((packed, rows), b) in enumerate(zip(weights, biases)):
+        if packed.numel() < i2s_packed_bytes(rows, K):
+            raise ValueError(f"projection {i}: packed tensor smaller than i2s_packed_bytes(rows, K)")
+        y = torch.empty((N, rows), dtype=torch.float32, device=dev)
+        d = torch.empty((N, rows), dtype=torch.int32, device=dev) if dot_out else None
+        if b is not None and b.numel() < rows:
+            raise ValueError(f"projection {i}: bias shorter than rows")
+        projs[i] = I2SProj(_dev(packed, torch.uint8, "packed"), rows,
+                           _dev(b, torch.float32, "bias") if b is not None else None,
+                           _dev(y, torch.float32, "y"), _dev(d, torch.int32, "dot_out") if dot_out else None)
+        ys.append(y)
+        dots.append(d)
+    _check("i2s_mul_mat_group_ex", lib().i2s_mul_mat_group_ex(
+        projs, count, K, _dev(x, torch.float32, "x"), N, _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), int(kernel), int(variant), _stream(stream)))
+    return (ys, dots) if dot_out else ys

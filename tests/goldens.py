@@ -95,3 +95,13 @@ def headroom():
         "dot": int(d["dot"]),
         "y_bits": int(d["y_hex"], 16),
     }
+
+
+def bias_add():
+    """Hand-worked bias-add values (tests/golden/bias_add.txt), by key; *_hex
+    entries are returned as binary32 bit patterns (int)."""
+    out = {}
+    for line in _lines("bias_add.txt"):
+        k, v = line.split()
+        out[k] = int(v, 16)
+    return out

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from exact import AMAX_FLOOR, epilogue, f32_bits, f32_round, frac, near_tie_rows, quantize_row, round_half_away
-from goldens import headroom, pack_cases, quantize_cases
+from goldens import bias_add, headroom, pack_cases, quantize_cases
 from ternary_weight_integer_amd import workloads
 
 
@@ -265,3 +265,70 @@ def test_dot_on_row_slice_equals_full():
     full = oracle.dot(p, rows, K, q)
     part = oracle.dot(p[3 * K // 4:], 4, K, q)
     assert np.array_equal(part, full[:, 3:7])
+
+
+# --- bias add (grouped decoder projections) ----------------------------------
+
+def _bits_to_f32(b: int) -> np.float32:
+    return np.array([b], dtype=np.uint32).view(np.float32)[0]
+
+
+def test_bias_add_on_headroom_is_exact():
+    g, h = bias_add(), headroom()
+    K = h["K"]
+    p = oracle.pack(np.ones((3, K), np.int8), h["ws"])
+    y = oracle.mul_mat(p, 3, K, np.full((2, K), 127.0, np.float32))
+    yb = oracle.add_bias(y, np.full(3, _bits_to_f32(g["headroom_bias_hex"]), np.float32))
+    assert (yb.view(np.uint32) == g["headroom_y_bias_hex"]).all()
+
+
+def test_bias_added_once_after_the_rounded_epilogue():
+    """The worked case tells the plain reading (round the epilogue product,
+    then one F32 add) from a fused multiply-add, whose result differs."""
+    g = bias_add()
+    K = 128
+    x = np.zeros((1, K), np.float32)
+    x[0, 0], x[0, 1] = 127.0, 3.0
+    w = np.zeros((1, K), np.int8)
+    w[0, 1] = 1
+    p = oracle.pack(w, _bits_to_f32(g["fma_ws_hex"]))
+    y, dot = oracle.mul_mat(p, 1, K, x, with_dot=True)
+    assert int(dot[0, 0]) == 133
+    assert int(y.view(np.uint32)[0, 0]) == g["fma_y_hex"]
+    yn = oracle.add_bias(y, np.array([_bits_to_f32(g["fma_bias_neg_hex"])], np.float32))
+    assert int(yn.view(np.uint32)[0, 0]) == g["fma_y_neg_hex"]
+    assert g["fma_y_neg_hex"] != g["fma_fused_would_be_hex"]
+    yt = oracle.add_bias(y, np.array([_bits_to_f32(g["fma_bias_tiny_hex"])], np.float32))
+    assert int(yt.view(np.uint32)[0, 0]) == g["fma_y_tiny_hex"]
+
+
+def test_bias_on_zero_activation_row():
+    """y = +0 for an all-zero activation row, so y + b = b bitwise, and
+    +0 + (-0) = +0."""
+    rng = np.random.default_rng(29)
+    rows, K = 6, 256
+    p = oracle.pack(workloads.ternary(rng, rows, K), 0.015)
+    y = oracle.mul_mat(p, rows, K, np.zeros((2, K), np.float32))
+    assert (y.view(np.uint32) == 0).all()
+    b = rng.standard_normal(rows).astype(np.float32)
+    b[2] = np.float32(-0.0)
+    yb = oracle.add_bias(y, b)
+    expect = b.view(np.uint32).copy()
+    expect[2] = 0
+    assert (yb.view(np.uint32) == expect[None, :]).all()
+
+
+def test_group_is_each_projection_on_the_same_activation():
+    """A group is its projections one by one (quantization depends on x
+    alone), each followed by its own bias if it has one."""
+    rng = np.random.default_rng(31)
+    K, N = 256, 3
+    x = workloads.normal(rng, N, K)
+    ws = [oracle.pack(workloads.ternary(rng, r, K), 0.02) for r in (8, 4)]
+    b0 = rng.standard_normal(8).astype(np.float32)
+    ys, ds = oracle.mul_mat_group([(ws[0], 8, b0), (ws[1], 4, None)], K, x, with_dot=True)
+    y0, d0 = oracle.mul_mat(ws[0], 8, K, x, with_dot=True)
+    y1, d1 = oracle.mul_mat(ws[1], 4, K, x, with_dot=True)
+    assert np.array_equal(ds[0], d0) and np.array_equal(ds[1], d1)
+    assert np.array_equal(ys[1].view(np.uint32), y1.view(np.uint32))
+    assert np.array_equal(ys[0].view(np.uint32), (y0 + b0[None, :]).astype(np.float32).view(np.uint32))
