@@ -24,6 +24,11 @@ Measurement:
   * cpu_baseline: the CPU oracle (plain scalar C, one thread) on the same
     workload, repeated for about --cpu-seconds.
 
+--workload decode_layer times one Qwen2-1.5B decoder layer's seven ternary
+projections at N = 1 instead (q/k/v grouped with their F32 biases, o,
+gate/up grouped, down: four launches), rotating over 28 layers of weights
+(327.5 MB), beside the same projections as seven separate calls.
+
 Prints one JSON line.
 """
 
@@ -54,7 +59,7 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="decode_up",
-                   choices=["decode_up", "prefill_gate", "down_small_batch", "small"])
+                   choices=["decode_up", "prefill_gate", "down_small_batch", "small", "decode_layer"])
     p.add_argument("--copies", type=int, default=0, help="weight copies to rotate over (0 = enough for 512 MiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -149,6 +154,129 @@ def copy_kernel_only(mib: int):
     print(json.dumps({"copy_kernel_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}), flush=True)
 
 
+LAYER_PROJ = ("q", "k", "v", "o", "gate", "up", "down")
+LAYERS = 28
+
+
+def bench_layer(args, torch, i2s):
+    """One Qwen2-1.5B decoder layer's seven ternary projections at decode time
+    (N = 1) per step, weights rotating over 28 layers (327.5 MB, beyond the
+    Infinity Cache): grouped as q/k/v (one launch, F32 biases), o, gate/up
+    (one launch), down -- four launches -- and, for comparison, as seven
+    separate calls."""
+    from ternary_weight_integer_amd import workloads
+    dev = torch.device("cuda:0")
+    case = workloads.decode_layer_case(N=1)
+    shp = workloads.QWEN2_1P5B_PROJ
+    p0 = {n: i2s.i2s_pack(torch.from_numpy(case.w[n]).to(dev), case.ws) for n in LAYER_PROJ}
+    layers = [p0] + [{n: p0[n].clone() for n in LAYER_PROJ} for _ in range(LAYERS - 1)]
+    bias = {n: torch.from_numpy(case.bias[n]).to(dev) for n in ("q", "k", "v")}
+    xh, xa, xf = (torch.from_numpy(a).to(dev) for a in (case.x_hidden, case.x_attn, case.x_ffn))
+    ws = i2s.new_workspace(1, 8960, dev)
+    y = {n: torch.empty((1, shp[n][0]), dtype=torch.float32, device=dev) for n in LAYER_PROJ}
+    y2 = {n: torch.empty((1, shp[n][0]), dtype=torch.float32, device=dev) for n in LAYER_PROJ}
+    wbytes = sum(shp[n][0] * shp[n][1] // 4 for n in LAYER_PROJ)
+
+    def grouped(i, out=y):
+        lw = layers[i % LAYERS]
+        i2s.i2s_mul_mat_group([(lw["q"], 1536), (lw["k"], 256), (lw["v"], 256)], 1536, xh,
+                              biases=[bias["q"], bias["k"], bias["v"]], workspace=ws, ys=[out["q"], out["k"], out["v"]])
+        i2s.i2s_mul_mat(lw["o"], 1536, 1536, xa, workspace=ws, y=out["o"])
+        i2s.i2s_mul_mat_group([(lw["gate"], 8960), (lw["up"], 8960)], 1536, xa, workspace=ws,
+                              ys=[out["gate"], out["up"]])
+        i2s.i2s_mul_mat(lw["down"], 1536, 8960, xf, workspace=ws, y=out["down"])
+
+    def separate(i, out=y2):
+        lw = layers[i % LAYERS]
+        for n, x in (("q", xh), ("k", xh), ("v", xh), ("o", xa), ("gate", xa), ("up", xa), ("down", xf)):
+            rows, K = shp[n]
+            i2s.i2s_mul_mat_group([(lw[n], rows)], K, x, biases=[bias.get(n)], workspace=ws, ys=[out[n]])
+
+    def gate_up(i):
+        lw = layers[i % LAYERS]
+        i2s.i2s_mul_mat_group([(lw["gate"], 8960), (lw["up"], 8960)], 1536, xa, workspace=ws,
+                              ys=[y["gate"], y["up"]])
+
+    for i in range(args.warmup):
+        grouped(i)
+        separate(i)
+    torch.cuda.synchronize()
+    for n in LAYER_PROJ:  # grouping changes no result bit
+        if not torch.equal(y[n].view(torch.int32), y2[n].view(torch.int32)):
+            raise RuntimeError(f"grouped and separate results differ for {n}")
+    K_steps = args.steps
+    g1 = graph_of(lambda: [grouped(i) for i in range(K_steps)], torch)
+    g2 = graph_of(lambda: [separate(i) for i in range(K_steps)], torch)
+    n_kern = 256
+    g3 = graph_of(lambda: [gate_up(i) for i in range(n_kern)], torch)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    g1.replay()
+    ev[1].record()
+    g2.replay()
+    ev[2].record()
+    g3.replay()
+    ev[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = ev[0].elapsed_time(ev[1]) / K_steps
+    sep_ms = ev[1].elapsed_time(ev[2]) / K_steps
+    kern_us = ev[2].elapsed_time(ev[3]) * 1e3 / n_kern
+    alg = 2 * 8960 * 1536 // 4 + 4 * 1536 + 2 * 4 * 8960 + 8   # gate+up weights, x, outputs, two scales
+    achieved = alg / (kern_us * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(wbytes / (step_ms * 1e-3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": case.name, "layers_rotated": LAYERS, "weight_bytes_per_step": wbytes,
+                   "rotated_bytes": LAYERS * sum(p.numel() for p in p0.values()), "launches_per_step": 4,
+                   "timing": "hip_graph"},
+        "separate_calls": {"launches_per_step": 7, "ms_per_step": round(sep_ms, 6),
+                           "value": round(wbytes / (sep_ms * 1e-3) / 1e9, 3)},
+        "int8_tops": round(2 * (wbytes * 4) / (step_ms * 1e-3) / 1e12, 4),
+        "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                     "kernel": "gemv_fused_group_kernel (gate+up)", "kernel_us": round(kern_us, 4),
+                     "alg_bytes_per_launch": alg},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_layer(case, args.cpu_seconds)
+    return out
+
+
+def cpu_baseline_layer(case, seconds: float):
+    import oracle
+    shp_x = {"q": case.x_hidden, "k": case.x_hidden, "v": case.x_hidden, "o": case.x_attn, "gate": case.x_attn,
+             "up": case.x_attn, "down": case.x_ffn}
+    packed = {n: oracle.pack(case.w[n], case.ws) for n in LAYER_PROJ}
+    wbytes = sum(case.w[n].size // 4 for n in LAYER_PROJ)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        for n in LAYER_PROJ:
+            rows, K = case.w[n].shape
+            oracle.mul_mat_group([(packed[n], rows, case.bias.get(n))], K, shp_x[n])
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(wbytes * calls / el / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full layers (7 projections, N = 1, scalar C, 1 thread) in {el:.1f} s",
+            "cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0)),
+            "ms_per_call": round(el / calls * 1e3, 3)}
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -168,6 +296,9 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.workload == "decode_layer":
+        print(json.dumps(bench_layer(args, torch, i2s)), flush=True)
+        return 0
     dev = torch.device("cuda:0")
     case = make_case(args.workload)
     rows, K, N = case.rows, case.K, case.N

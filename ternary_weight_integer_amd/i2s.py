@@ -264,10 +264,11 @@ def i2s_mul_mat_ws(packed: torch.Tensor, rows: int, K: int, N: int, workspace: t
 
 
 def i2s_mul_mat_group(weights, K: int, x: torch.Tensor, biases=None, workspace=None, dot_out: bool = False,
-                      kernel: int = KERNEL_AUTO, variant: int = 0, stream=None):
+                      kernel: int = KERNEL_AUTO, variant: int = 0, stream=None, ys=None):
     """Several projections of one activation x[N][K]: weights is a list of
     (packed tensor, rows); biases a matching list of F32 [rows] tensors or
-    None.  Returns the list of y[N][rows] (and of the int32 dots if dot_out)."""
+    None; ys optional preallocated outputs.  Returns the list of y[N][rows]
+    (and of the int32 dots if dot_out)."""
     N = x.shape[0]
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError(f"x must be [N][{K}], got {tuple(x.shape)}")
@@ -279,20 +280,22 @@ def i2s_mul_mat_group(weights, K: int, x: torch.Tensor, biases=None, workspace=N
     dev = x.device
     workspace = new_workspace(N, K, dev) if workspace is None else workspace
     projs = (I2SProj * max(count, 1))()
-    ys, dots = [], []
+    outs, dots = [], []
     for i, ((packed, rows), b) in enumerate(zip(weights, biases)):
         if packed.numel() < i2s_packed_bytes(rows, K):
             raise ValueError(f"projection {i}: packed tensor smaller than i2s_packed_bytes(rows, K)")
-        y = torch.empty((N, rows), dtype=torch.float32, device=dev)
+        y = torch.empty((N, rows), dtype=torch.float32, device=dev) if ys is None else ys[i]
+        if y.numel() < N * rows:
+            raise ValueError(f"projection {i}: y too small")
         d = torch.empty((N, rows), dtype=torch.int32, device=dev) if dot_out else None
         if b is not None and b.numel() < rows:
             raise ValueError(f"projection {i}: bias shorter than rows")
         projs[i] = I2SProj(_dev(packed, torch.uint8, "packed"), rows,
                            _dev(b, torch.float32, "bias") if b is not None else None,
                            _dev(y, torch.float32, "y"), _dev(d, torch.int32, "dot_out") if dot_out else None)
-        ys.append(y)
+        outs.append(y)
         dots.append(d)
     _check("i2s_mul_mat_group_ex", lib().i2s_mul_mat_group_ex(
         projs, count, K, _dev(x, torch.float32, "x"), N, _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), int(kernel), int(variant), _stream(stream)))
-    return (ys, dots) if dot_out else ys
+    return (outs, dots) if dot_out else outs

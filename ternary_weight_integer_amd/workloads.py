@@ -152,3 +152,33 @@ def zero_row_case(N: int = 1, zero_row: int = 0, seed: int = 0) -> Case:
     x = normal(rng, N, 1536)
     x[zero_row, :] = 0.0
     return Case(f"zero_row_8960x1536_N{N}_r{zero_row}", w, 0.015, x)
+
+
+@dataclass
+class LayerCase:
+    """One decoder layer's seven ternary projections at decode time: weights
+    (int8 ternary, [out][K]), the q/k/v F32 biases, and the three activation
+    rows they read (the normed hidden state for q/k/v, the attention output
+    for o and gate/up's input, the FFN hidden state for down)."""
+    name: str
+    w: dict
+    ws: float
+    bias: dict
+    x_hidden: np.ndarray
+    x_attn: np.ndarray
+    x_ffn: np.ndarray
+    meta: dict = field(default_factory=dict)
+
+
+def decode_layer_case(seed: int = 0, N: int = 1) -> LayerCase:
+    """Qwen2-1.5B-shaped decoder layer, N activation rows: weights in the
+    order q, k, v, o, gate, up, down, then biases ~ N(0, 0.1) for q, k, v,
+    then x_hidden, x_attn ~ N(0, 1) and x_ffn = ReLU(N(0, 0.5))."""
+    rng = np.random.default_rng(seed)
+    w = {n: ternary(rng, *QWEN2_1P5B_PROJ[n]) for n in ("q", "k", "v", "o", "gate", "up", "down")}
+    bias = {n: (0.1 * rng.standard_normal(QWEN2_1P5B_PROJ[n][0])).astype(np.float32) for n in ("q", "k", "v")}
+    x_hidden = normal(rng, N, 1536)
+    x_attn = normal(rng, N, 1536)
+    x_ffn = relu(normal(rng, N, 8960, std=0.5))
+    return LayerCase(f"decode_layer_qwen2_1p5b_N{N}", w, 0.015, bias, x_hidden, x_attn, x_ffn,
+                     {"layers": 28, "N": N})
