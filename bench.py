@@ -201,6 +201,16 @@ def bench_layer(args, torch, i2s):
         grouped(i)
         separate(i)
     torch.cuda.synchronize()
+    if args.eager:  # launches from Python, one dispatch at a time (counter collection runs)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            grouped(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": round(e0.elapsed_time(e1) / args.steps, 6),
+                "config": {"workload": case.name, "timing": "eager"}}
     for n in LAYER_PROJ:  # grouping changes no result bit
         if not torch.equal(y[n].view(torch.int32), y2[n].view(torch.int32)):
             raise RuntimeError(f"grouped and separate results differ for {n}")

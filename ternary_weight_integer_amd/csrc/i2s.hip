@@ -147,12 +147,13 @@ quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int8_t *__restric
 // sum are block reductions, and each float4 becomes 4 bytes of q (4
 // consecutive positions stay consecutive in the interleaved order).  Same
 // arithmetic as quantize_rowsum_kernel, with a few divisions per thread.
-template <bool kInterleaved, int XPT>
-__global__ void __launch_bounds__(kQuantThreads)
+template <bool kInterleaved, int XPT, int THREADS>
+__global__ void __launch_bounds__(THREADS)
 quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int8_t *__restrict__ q,
                            float *__restrict__ act_scale, int32_t *__restrict__ row_sum) {
-  __shared__ float red_f[kQuantThreads / 64];
-  __shared__ int red_i[kQuantThreads / 64];
+  constexpr int kWaves = THREADS / 64;
+  __shared__ float red_f[kWaves];
+  __shared__ int red_i[kWaves];
   const int64_t n = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -162,21 +163,23 @@ quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int8_t *__res
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
-    const int idx = tid + kQuantThreads * i;
+    const int idx = tid + THREADS * i;
     v[i] = idx < k4 ? xr[idx] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
   }
   amax = wave_max(amax);
   if (lane == 0) red_f[wave] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  amax = red_f[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, red_f[w]);
   amax = fmaxf(amax, 1e-5f);
   const float s = amax / 127.0f;
   int sum = 0;
   int8_t *qr = q + n * K;
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
-    const int idx = tid + kQuantThreads * i;
+    const int idx = tid + THREADS * i;
     if (idx < k4) {
       const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
       uint32_t packed = 0;
@@ -198,8 +201,11 @@ quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int8_t *__res
   if (lane == 0) red_i[wave] = sum;
   __syncthreads();
   if (tid == 0) {
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) total += red_i[w];
     act_scale[n] = s;
-    row_sum[n] = red_i[0] + red_i[1] + red_i[2] + red_i[3];
+    row_sum[n] = total;
   }
 }
 
@@ -1893,19 +1899,21 @@ int check_common(int64_t rows, int64_t K) {
 int quantize_launch(const float *x, int64_t N, int64_t K, int8_t *q, float *s, int32_t *rs, bool interleaved,
                     hipStream_t stream) {
   if (N > kMaxDim) return I2S_ERANGE;
-#define I2S_QREG(XPT)                                                                                      \
+  // The row sits in registers: XPT float4 per thread; longer rows get more
+  // threads (a row is one workgroup), so that each holds few values.
+#define I2S_QREG(XPT, T)                                                                                   \
   do {                                                                                                     \
     if (interleaved)                                                                                       \
-      hipLaunchKernelGGL((quantize_rowsum_reg_kernel<true, XPT>), dim3(static_cast<unsigned>(N)),          \
-                         dim3(kQuantThreads), 0, stream, x, K, q, s, rs);                                  \
+      hipLaunchKernelGGL((quantize_rowsum_reg_kernel<true, XPT, T>), dim3(static_cast<unsigned>(N)),       \
+                         dim3(T), 0, stream, x, K, q, s, rs);                                              \
     else                                                                                                   \
-      hipLaunchKernelGGL((quantize_rowsum_reg_kernel<false, XPT>), dim3(static_cast<unsigned>(N)),         \
-                         dim3(kQuantThreads), 0, stream, x, K, q, s, rs);                                  \
+      hipLaunchKernelGGL((quantize_rowsum_reg_kernel<false, XPT, T>), dim3(static_cast<unsigned>(N)),      \
+                         dim3(T), 0, stream, x, K, q, s, rs);                                              \
     return hip_status();                                                                                   \
   } while (0)
-  if (K <= 4 * kQuantThreads * 2) I2S_QREG(2);
-  if (K <= 4 * kQuantThreads * 4) I2S_QREG(4);
-  if (K <= 4 * kQuantThreads * 9) I2S_QREG(9);
+  if (K <= 4 * 256 * 2) I2S_QREG(2, 256);
+  if (K <= 4 * 512 * 2) I2S_QREG(2, 512);
+  if (K <= 4 * 1024 * 3) I2S_QREG(3, 1024);
 #undef I2S_QREG
   if (interleaved)
     hipLaunchKernelGGL((quantize_rowsum_kernel<true>), dim3(static_cast<unsigned>(N)), dim3(kQuantThreads), 0, stream,
