@@ -150,6 +150,24 @@ int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
                    const void *workspace, size_t workspace_bytes,
                    float *y, int32_t *dot_out, int kernel, int variant, void *stream);
 
+/* i2s_mul_mat_batched: the op on a 3-D activation ("ggml-cpu: ternary I2_S
+ * matmul kernel (VibeASR, 3/4)", Tests: the batched case, whose activation
+ * rows walk a batch stride and whose outputs walk theirs).  For b < B and
+ * n < N, activation row (b, n) is the K floats at x + b*bsx + n*ldx and its
+ * output row is the `rows` floats at y + b*bsy + n*ldy (dot_out, if not NULL,
+ * uses y's strides); the 2-D weight is shared by every batch.  Strides are in
+ * elements: ldx >= K with ldx and bsx multiples of 4 (activation rows start
+ * 16-byte aligned), ldy >= rows, bsy >= 0, and outputs of different batches
+ * must not overlap (bsy >= (N-1)*ldy + rows when B > 1).  x, y and dot_out
+ * themselves are 16-byte aligned.  workspace >= i2s_act_workspace_bytes(N*B, K).
+ * Dense strides run as one i2s_mul_mat of N*B rows; otherwise one quantize
+ * launch (or, for N <= 3, one fused launch per batch) and one contraction per
+ * batch.  Errors: as i2s_mul_mat, I2S_EINVAL for a bad stride. */
+int i2s_mul_mat_batched(const uint8_t *packed, int64_t rows, int64_t K,
+                        const float *x, int64_t N, int64_t B, int64_t ldx, int64_t bsx,
+                        void *workspace, size_t workspace_bytes,
+                        float *y, int64_t ldy, int64_t bsy, int32_t *dot_out, void *stream);
+
 /* Grouped projections sharing one activation ("VibeASR in audio.cpp",
  * Architecture/Decoder: every decoder layer applies the ternary q, k and v
  * projections to one normed hidden state, and gate and up to another; the

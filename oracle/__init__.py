@@ -152,3 +152,13 @@ def mul_mat_group(projs, K: int, x: np.ndarray, with_dot: bool = False):
         ys.append(y)
         ds.append(d)
     return (ys, ds) if with_dot else ys
+
+
+def mul_mat_batched(packed: np.ndarray, rows: int, K: int, x: np.ndarray, with_dot: bool = False):
+    """The op on x[B][N][K]: every batch against the same 2-D weight
+    (y[B][N][rows]); each activation row is quantized on its own."""
+    x = np.asarray(x, dtype=np.float32)
+    outs = [mul_mat(packed, rows, K, x[b], with_dot=True) for b in range(x.shape[0])]
+    y = np.stack([o[0] for o in outs]) if outs else np.zeros((0, x.shape[1], rows), np.float32)
+    d = np.stack([o[1] for o in outs]) if outs else np.zeros((0, x.shape[1], rows), np.int32)
+    return (y, d) if with_dot else y

@@ -84,17 +84,20 @@ __device__ inline int wave_sum(int v) {
 //   amax = max(max|x|, 1e-5f); s = amax / 127 (IEEE division);
 //   q = clamp(roundf(x / s), -127, 127)   (roundf: halfway away from zero).
 // kInterleaved selects the workspace order above; otherwise q is row-major.
+// Activation row n is read from x + (n / n_inner) * bsx + (n % n_inner) * ldx
+// (batches of n_inner rows; contiguous rows have n_inner = N, ldx = K); q,
+// the scales and the row sums are written densely, row n at n.
 
 constexpr int kQuantThreads = 256;
 
 template <bool kInterleaved>
 __global__ void __launch_bounds__(kQuantThreads)
-quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int8_t *__restrict__ q,
-                       float *__restrict__ act_scale, int32_t *__restrict__ row_sum) {
+quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int64_t n_inner, int64_t ldx, int64_t bsx,
+                       int8_t *__restrict__ q, float *__restrict__ act_scale, int32_t *__restrict__ row_sum) {
   __shared__ float red_f[kQuantThreads / 64];
   __shared__ int red_i[kQuantThreads / 64];
   const int64_t n = blockIdx.x;
-  const float *xr = x + n * K;
+  const float *xr = x + (n / n_inner) * bsx + (n % n_inner) * ldx;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
 
@@ -149,15 +152,15 @@ quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int8_t *__restric
 // arithmetic as quantize_rowsum_kernel, with a few divisions per thread.
 template <bool kInterleaved, int XPT, int THREADS>
 __global__ void __launch_bounds__(THREADS)
-quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int8_t *__restrict__ q,
-                           float *__restrict__ act_scale, int32_t *__restrict__ row_sum) {
+quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int64_t n_inner, int64_t ldx, int64_t bsx,
+                           int8_t *__restrict__ q, float *__restrict__ act_scale, int32_t *__restrict__ row_sum) {
   constexpr int kWaves = THREADS / 64;
   __shared__ float red_f[kWaves];
   __shared__ int red_i[kWaves];
   const int64_t n = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const float4 *xr = reinterpret_cast<const float4 *>(x + n * K);
+  const float4 *xr = reinterpret_cast<const float4 *>(x + (n / n_inner) * bsx + (n % n_inner) * ldx);
   const int k4 = static_cast<int>(K / 4);
   float4 v[XPT];
   float amax = 0.0f;
@@ -281,7 +284,7 @@ __global__ void __launch_bounds__(kGemvThreads)
 gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
             const int8_t *__restrict__ qp, const float *__restrict__ act_scale,
             const int32_t *__restrict__ row_sum, float *__restrict__ y,
-            int32_t *__restrict__ dot_out, const float *__restrict__ bias) {
+            int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t ldy) {
   constexpr int kSlots = 64 / L;
   constexpr int kRowsPerWave = kSlots * RPL;
   constexpr int kRowsPerBlock = kRowsPerWave * (kGemvThreads / 64);
@@ -349,8 +352,8 @@ gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
         const float t = ws * act_scale[n];
         float v = epilogue(total, row_sum[n], t);
         if (bias) v = add_bias(v, bias[r]);
-        y[static_cast<int64_t>(n) * rows + r] = v;
-        if (dot_out) dot_out[static_cast<int64_t>(n) * rows + r] = total;
+        y[static_cast<int64_t>(n) * ldy + r] = v;
+        if (dot_out) dot_out[static_cast<int64_t>(n) * ldy + r] = total;
       }
     }
   }
@@ -379,9 +382,10 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t by
 
 template <int NC, int L, int RPL, int CPL, int XPT>
 __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
-                                           const float *__restrict__ x, float *__restrict__ y,
+                                           const float *__restrict__ x, int64_t ldx, float *__restrict__ y,
                                            int32_t *__restrict__ dot_out, const float *__restrict__ bias,
-                                           int64_t block, int8_t *qs /* NC x K group-interleaved int8, LDS */) {
+                                           int64_t ldy, int64_t block,
+                                           int8_t *qs /* NC x K group-interleaved int8, LDS */) {
   __shared__ float red_f[NC][kGemvThreads / 64];
   __shared__ int red_i[NC][kGemvThreads / 64];
   constexpr int kSlots = 64 / L;
@@ -403,7 +407,7 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = tid + kGemvThreads * i;
-      xv[n][i] = idx < k4 ? reinterpret_cast<const float4 *>(x + static_cast<int64_t>(n) * K)[idx]
+      xv[n][i] = idx < k4 ? reinterpret_cast<const float4 *>(x + static_cast<int64_t>(n) * ldx)[idx]
                           : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 
@@ -514,8 +518,8 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
         const float t = ws * sc[n];
         float v = epilogue(total, rs, t);
         if (bias) v = add_bias(v, bias[r]);
-        y[static_cast<int64_t>(n) * rows + r] = v;
-        if (dot_out) dot_out[static_cast<int64_t>(n) * rows + r] = total;
+        y[static_cast<int64_t>(n) * ldy + r] = v;
+        if (dot_out) dot_out[static_cast<int64_t>(n) * ldy + r] = total;
       }
     }
   }
@@ -524,10 +528,10 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
 template <int NC, int L, int RPL, int CPL, int XPT>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_fused_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
-                  const float *__restrict__ x, float *__restrict__ y, int32_t *__restrict__ dot_out,
-                  const float *__restrict__ bias) {
+                  const float *__restrict__ x, int64_t ldx, float *__restrict__ y, int32_t *__restrict__ dot_out,
+                  const float *__restrict__ bias, int64_t ldy) {
   extern __shared__ __attribute__((aligned(16))) int8_t qs[];
-  fused_body<NC, L, RPL, CPL, XPT>(packed, rows, K, x, y, dot_out, bias, blockIdx.x, qs);
+  fused_body<NC, L, RPL, CPL, XPT>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, blockIdx.x, qs);
 }
 
 // Several projections of the same activation rows in one launch (the decoder
@@ -551,7 +555,8 @@ gemv_fused_group_kernel(const FusedGroup g, int64_t K, const float *__restrict__
   int p = 0;
   while (p + 1 < g.count && static_cast<int64_t>(blockIdx.x) >= g.block_end[p]) ++p;
   const int64_t block = static_cast<int64_t>(blockIdx.x) - (p > 0 ? g.block_end[p - 1] : 0);
-  fused_body<NC, L, RPL, CPL, XPT>(g.packed[p], g.rows[p], K, x, g.y[p], g.dot[p], g.bias[p], block, qs);
+  fused_body<NC, L, RPL, CPL, XPT>(g.packed[p], g.rows[p], K, x, K, g.y[p], g.dot[p], g.bias[p], g.rows[p], block,
+                                   qs);
 }
 
 // ---------------------------------------------------------------------------
@@ -597,7 +602,7 @@ __global__ void __launch_bounds__(Cfg::kThreads)
 gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
             const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
             const int32_t *__restrict__ row_sum, float *__restrict__ y,
-            int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t tiles_m) {
+            int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t ldy, int64_t tiles_m) {
   constexpr int WM = Cfg::kWM, WN = Cfg::kWN;
   __shared__ __attribute__((aligned(16))) int8_t lds[2 * Cfg::kLdsStage];
 
@@ -695,6 +700,9 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   // Epilogue: lane l holds C[4*(l/16) + r][l % 16], r = 0..3, of each tile,
   // i.e. four consecutive output features of one activation row.
   const float ws = *reinterpret_cast<const float *>(packed + rows * row_bytes);
+  // 16-byte stores only where every output row starts 16-byte aligned.
+  const bool vec4_out = (rows % 4) == 0 && (ldy % 4) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+                        (reinterpret_cast<uintptr_t>(dot_out) & 15) == 0;
 #pragma unroll
   for (int n = 0; n < WN; ++n) {
     const int64_t nn = n_blk + wn * 16 * WN + 16 * n + li;
@@ -704,8 +712,8 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 #pragma unroll
     for (int m = 0; m < WM; ++m) {
       const int64_t o = o_base + 16 * m + 4 * kb;
-      float *yr = y + nn * rows;
-      if (o + 3 < rows && (rows % 4) == 0) {
+      float *yr = y + nn * ldy;
+      if (o + 3 < rows && vec4_out) {
         float4 v = make_float4(epilogue(acc[m][n][0], rs, t), epilogue(acc[m][n][1], rs, t),
                                epilogue(acc[m][n][2], rs, t), epilogue(acc[m][n][3], rs, t));
         if (bias) {
@@ -714,7 +722,7 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
         }
         *reinterpret_cast<float4 *>(yr + o) = v;
         if (dot_out)
-          *reinterpret_cast<int4 *>(dot_out + nn * rows + o) = make_int4(acc[m][n][0], acc[m][n][1], acc[m][n][2], acc[m][n][3]);
+          *reinterpret_cast<int4 *>(dot_out + nn * ldy + o) = make_int4(acc[m][n][0], acc[m][n][1], acc[m][n][2], acc[m][n][3]);
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -722,7 +730,7 @@ gemm_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
             float v = epilogue(acc[m][n][r], rs, t);
             if (bias) v = add_bias(v, bias[o + r]);
             yr[o + r] = v;
-            if (dot_out) dot_out[nn * rows + o + r] = acc[m][n][r];
+            if (dot_out) dot_out[nn * ldy + o + r] = acc[m][n][r];
           }
         }
       }
@@ -793,7 +801,7 @@ __global__ void __launch_bounds__(64 * WAVES)
 gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
                 const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
                 const int32_t *__restrict__ row_sum, float *__restrict__ y,
-                int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t tiles_m, int ms) {
+                int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t ldy, int64_t tiles_m, int ms) {
   extern __shared__ __attribute__((aligned(16))) int8_t lds_res[];
   constexpr int BN = 16 * WN;
   static_assert(BN % WAVES == 0, "whole activation rows per wave");
@@ -917,9 +925,10 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
     __syncthreads();
   }
 
-  const uint32_t out_bytes = static_cast<uint32_t>(n_here * rows * 4);
-  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + n0 * rows, out_bytes);
-  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + n0 * rows : nullptr, DOT ? out_bytes : 0);
+  // Output rows n0.. of this tile, ldy elements apart.
+  const uint32_t out_bytes = static_cast<uint32_t>(((n_here - 1) * ldy + rows) * 4);
+  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + n0 * ldy, out_bytes);
+  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + n0 * ldy : nullptr, DOT ? out_bytes : 0);
   const int8_t *lb0 = lds_res + li * pitch + 64 * kb;
 
   float tn[WN];
@@ -960,7 +969,7 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       const int64_t o = o_tile + 16 * static_cast<int64_t>(wave + WAVES * (grp * G + gi)) + 4 * kb;
 #pragma unroll
       for (int n = 0; n < WN; ++n) {
-        const uint32_t base = static_cast<uint32_t>((16 * n + li) * rows);  // element offset of this lane's row
+        const uint32_t base = static_cast<uint32_t>((16 * n + li) * ldy);  // element offset of this lane's row
         if constexpr (VEC4) {
           const uint32_t off = sub_ok && o < rows ? 4 * (base + static_cast<uint32_t>(o)) : kOutOfRange;
           const v4i yv = {__float_as_int(with_bias(epilogue(acc[gi][n][0], rsn[n], tn[n]), gi, 0)),
@@ -1130,7 +1139,8 @@ __global__ void __launch_bounds__(64 * WAVES)
 gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
                  const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
                  const int32_t *__restrict__ row_sum, float *__restrict__ y,
-                 int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t tiles_m, int ms) {
+                 int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t ldy, int64_t tiles_m,
+                 int ms) {
   extern __shared__ __attribute__((aligned(16))) int8_t lds_pipe[];
   constexpr int BN = 16 * WN;
   constexpr int kThreads = 64 * WAVES;
@@ -1235,9 +1245,10 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   // Keep every load above ahead of the first wait below.
   __builtin_amdgcn_sched_barrier(0);
 
-  const uint32_t out_bytes = static_cast<uint32_t>(n_here * rows * 4);
-  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + n0 * rows, out_bytes);
-  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + n0 * rows : nullptr, DOT ? out_bytes : 0);
+  // Output rows n0.. of this tile, ldy elements apart.
+  const uint32_t out_bytes = static_cast<uint32_t>(((n_here - 1) * ldy + rows) * 4);
+  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + n0 * ldy, out_bytes);
+  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + n0 * ldy : nullptr, DOT ? out_bytes : 0);
   // This lane's B base: row li of column block 0, piece 4*kb of step 0.
   const int8_t *lb0 = lds_pipe + (li >> 2) * group_stride + 256 * kb + 16 * (li & 3);
 
@@ -1269,7 +1280,7 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       const bool ok = t < mine;
 #pragma unroll
       for (int n = 0; n < WN; ++n) {
-        const uint32_t base = static_cast<uint32_t>((16 * n + li) * rows);  // element offset of this lane's row
+        const uint32_t base = static_cast<uint32_t>((16 * n + li) * ldy);  // element offset of this lane's row
         v4i &yv = yst[j][n];
         v4i &dv = dst[j][DOT ? n : 0];
 #pragma unroll
@@ -1375,7 +1386,7 @@ __global__ void __launch_bounds__(64 * W)
 gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
                  const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
                  const int32_t *__restrict__ row_sum, float *__restrict__ y, int32_t *__restrict__ dot_out,
-                 const float *__restrict__ bias) {
+                 const float *__restrict__ bias, int64_t ldy) {
   __shared__ __attribute__((aligned(16))) v4i part[W][64];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -1449,10 +1460,10 @@ gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   const float t = ws * act_scale[n];
   const int32_t rs = row_sum[n];
   const int64_t o = o0 + 4 * kb;
-  const uint32_t out_bytes = static_cast<uint32_t>(N * rows * 4 - o0 * 4);
+  const uint32_t out_bytes = static_cast<uint32_t>(((N - 1) * ldy + rows - o0) * 4);
   const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + o0, out_bytes);
   const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + o0 : nullptr, DOT ? out_bytes : 0);
-  const uint32_t base = static_cast<uint32_t>(li * rows + 4 * kb);  // element offset from y + o0
+  const uint32_t base = static_cast<uint32_t>(li * ldy + 4 * kb);  // element offset from y + o0
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = epilogue(tot[r], rs, t);
@@ -1483,12 +1494,12 @@ inline int hip_status() { return hipGetLastError() == hipSuccess ? I2S_OK : I2S_
 
 template <int NC, int L, int RPL, int CPL>
 int launch_gemv_cfg(const uint8_t *packed, int64_t rows, int64_t K, const ActWorkspace &ws,
-                    float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
+                    float *y, int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   constexpr int kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
   const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks > kMaxDim) return I2S_ERANGE;
   hipLaunchKernelGGL((gemv_kernel<NC, L, RPL, CPL>), dim3(static_cast<unsigned>(blocks)), dim3(kGemvThreads), 0,
-                     stream, packed, rows, K, ws.q, ws.scale, ws.row_sum, y, dot_out, bias);
+                     stream, packed, rows, K, ws.q, ws.scale, ws.row_sum, y, dot_out, bias, ldy);
   return hip_status();
 }
 
@@ -1501,36 +1512,37 @@ int gemv_auto_variant(int64_t K) {
 
 template <int NC>
 int launch_gemv_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K, const ActWorkspace &ws,
-                   float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
+                   float *y, int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   if (variant == 0) variant = gemv_auto_variant(K);
   switch (variant) {
-    case 1: return launch_gemv_cfg<NC, 4, 1, 2>(packed, rows, K, ws, y, dot_out, bias, stream);
-    case 2: return launch_gemv_cfg<NC, 8, 1, 4>(packed, rows, K, ws, y, dot_out, bias, stream);
-    case 3: return launch_gemv_cfg<NC, 64, 1, 3>(packed, rows, K, ws, y, dot_out, bias, stream);
-    case 4: return launch_gemv_cfg<NC, 8, 2, 3>(packed, rows, K, ws, y, dot_out, bias, stream);
-    case 5: return launch_gemv_cfg<NC, 16, 1, 2>(packed, rows, K, ws, y, dot_out, bias, stream);
+    case 1: return launch_gemv_cfg<NC, 4, 1, 2>(packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 2: return launch_gemv_cfg<NC, 8, 1, 4>(packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 3: return launch_gemv_cfg<NC, 64, 1, 3>(packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 4: return launch_gemv_cfg<NC, 8, 2, 3>(packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 5: return launch_gemv_cfg<NC, 16, 1, 2>(packed, rows, K, ws, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }
 constexpr int kGemvVariants = 5;
 
 int launch_gemv(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
-                float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
+                float *y, int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   switch (N) {
-    case 1: return launch_gemv_nc<1>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
-    case 2: return launch_gemv_nc<2>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
-    case 3: return launch_gemv_nc<3>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
-    case 4: return launch_gemv_nc<4>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
-    case 5: return launch_gemv_nc<5>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
-    case 6: return launch_gemv_nc<6>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
-    case 7: return launch_gemv_nc<7>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
-    case 8: return launch_gemv_nc<8>(variant, packed, rows, K, ws, y, dot_out, bias, stream);
+    case 1: return launch_gemv_nc<1>(variant, packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 2: return launch_gemv_nc<2>(variant, packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 3: return launch_gemv_nc<3>(variant, packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 4: return launch_gemv_nc<4>(variant, packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 5: return launch_gemv_nc<5>(variant, packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 6: return launch_gemv_nc<6>(variant, packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 7: return launch_gemv_nc<7>(variant, packed, rows, K, ws, y, dot_out, bias, ldy, stream);
+    case 8: return launch_gemv_nc<8>(variant, packed, rows, K, ws, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }
 
 template <int NC, int L, int RPL, int CPL, int XPT>
-int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float *x, float *y, int32_t *dot_out, const float *bias,
+int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t ldx, float *y,
+                     int32_t *dot_out, const float *bias, int64_t ldy,
                      hipStream_t stream) {
   if (K > 64 * L * CPL || K > 4 * kGemvThreads * XPT) return I2S_EKERNEL;
   if (rows * (K / 4) >= (int64_t{1} << 31)) return I2S_EKERNEL;  // 32-bit buffer offsets
@@ -1538,7 +1550,7 @@ int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float
   const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks > kMaxDim) return I2S_ERANGE;
   hipLaunchKernelGGL((gemv_fused_kernel<NC, L, RPL, CPL, XPT>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kGemvThreads), static_cast<size_t>(NC * K), stream, packed, rows, K, x, y, dot_out, bias);
+                     dim3(kGemvThreads), static_cast<size_t>(NC * K), stream, packed, rows, K, x, ldx, y, dot_out, bias, ldy);
   return hip_status();
 }
 
@@ -1552,26 +1564,26 @@ constexpr int64_t kFusedMaxK = 9216;
 int fused_auto_variant(int64_t rows, int64_t K) { return K <= 2048 ? (rows <= 2048 ? 3 : 2) : 5; }
 
 template <int NC>
-int launch_fused_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K, const float *x, float *y,
-                    int32_t *dot_out, const float *bias, hipStream_t stream) {
+int launch_fused_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t ldx, float *y,
+                    int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   if (variant == 0) variant = fused_auto_variant(rows, K);
   switch (variant) {
-    case 1: return launch_fused_cfg<NC, 8, 2, 3, 2>(packed, rows, K, x, y, dot_out, bias, stream);
-    case 2: return launch_fused_cfg<NC, 8, 1, 4, 2>(packed, rows, K, x, y, dot_out, bias, stream);
-    case 3: return launch_fused_cfg<NC, 16, 1, 2, 2>(packed, rows, K, x, y, dot_out, bias, stream);
-    case 4: return launch_fused_cfg<NC, 64, 1, 3, 9>(packed, rows, K, x, y, dot_out, bias, stream);
-    case 5: return launch_fused_cfg<NC, 32, 1, 5, 9>(packed, rows, K, x, y, dot_out, bias, stream);
+    case 1: return launch_fused_cfg<NC, 8, 2, 3, 2>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
+    case 2: return launch_fused_cfg<NC, 8, 1, 4, 2>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
+    case 3: return launch_fused_cfg<NC, 16, 1, 2, 2>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
+    case 4: return launch_fused_cfg<NC, 64, 1, 3, 9>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
+    case 5: return launch_fused_cfg<NC, 32, 1, 5, 9>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }
 
-int launch_fused(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const float *x, float *y,
-                 int32_t *dot_out, const float *bias, hipStream_t stream) {
+int launch_fused(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const float *x, int64_t ldx, float *y,
+                 int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   switch (N) {
-    case 1: return launch_fused_nc<1>(variant, packed, rows, K, x, y, dot_out, bias, stream);
-    case 2: return launch_fused_nc<2>(variant, packed, rows, K, x, y, dot_out, bias, stream);
-    case 3: return launch_fused_nc<3>(variant, packed, rows, K, x, y, dot_out, bias, stream);
-    case 4: return launch_fused_nc<4>(variant, packed, rows, K, x, y, dot_out, bias, stream);
+    case 1: return launch_fused_nc<1>(variant, packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
+    case 2: return launch_fused_nc<2>(variant, packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
+    case 3: return launch_fused_nc<3>(variant, packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
+    case 4: return launch_fused_nc<4>(variant, packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }
@@ -1630,13 +1642,13 @@ inline bool fused_auto(int64_t rows, int64_t N, int64_t K) {
 
 template <class Cfg>
 int launch_gemm_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
-                    float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
+                    float *y, int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   const int64_t tiles_m = (rows + Cfg::kBM - 1) / Cfg::kBM;
   const int64_t tiles_n = (N + Cfg::kBN - 1) / Cfg::kBN;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > kMaxDim) return I2S_ERANGE;
   hipLaunchKernelGGL((gemm_kernel<Cfg>), dim3(static_cast<unsigned>(blocks)), dim3(Cfg::kThreads), 0, stream,
-                     packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out, bias, tiles_m);
+                     packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out, bias, ldy, tiles_m);
   return hip_status();
 }
 
@@ -1678,8 +1690,8 @@ int pick_stream_variant(int64_t rows, int64_t N) {
 // 2^31 bytes (else I2S_EKERNEL, and the automatic choice streams instead).
 template <int G, int WN, int S, int WAVES, bool VEC4, bool DOT, bool SINGLE>
 int launch_res_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
-                    const ActWorkspace &ws, float *y, int32_t *dot_out, const float *bias, int64_t tiles_m,
-                    int64_t ms,
+                    const ActWorkspace &ws, float *y, int32_t *dot_out, const float *bias, int64_t ldy,
+                    int64_t tiles_m, int64_t ms,
                     hipStream_t stream) {
   // Allow up to 160 KiB of dynamic LDS, once per device for this instantiation
   // (repeating it from racing threads is harmless).
@@ -1695,13 +1707,13 @@ int launch_res_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t 
   }
   hipLaunchKernelGGL((gemm_res_kernel<G, WN, S, WAVES, VEC4, DOT, SINGLE>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * WAVES), static_cast<size_t>(lds), stream, packed, rows, K, ws.q, N, ws.scale,
-                     ws.row_sum, y, dot_out, bias, tiles_m, static_cast<int>(ms));
+                     ws.row_sum, y, dot_out, bias, ldy, tiles_m, static_cast<int>(ms));
   return hip_status();
 }
 
 template <int G, int WN, int S, int WAVES>
 int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
-                   int32_t *dot_out, const float *bias, hipStream_t stream) {
+                   int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   constexpr int64_t BN = 16 * WN;
   const int64_t lds = BN * res_pitch(K, S);
   if (lds > kResMaxLds) return I2S_EKERNEL;
@@ -1709,7 +1721,7 @@ int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, co
   // Largest weight offset: rows past the tile by up to 16*WAVES*G (re-reads of
   // a short or finished group), plus a chunk padded up to S steps.
   if ((rows + 16 * WAVES * G + 16) * (K / 4) + 64 * S * ((K + 255) / 256 + S) >= lim || BN * K >= lim ||
-      BN * rows * 4 >= lim)
+      BN * ldy * 4 >= lim)
     return I2S_EKERNEL;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t mt = (rows + 15) / 16;
@@ -1720,10 +1732,10 @@ int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, co
   tiles_m = (mt + ms - 1) / ms;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > kMaxDim || ms > kMaxDim) return I2S_ERANGE;
-  const bool vec4 = (rows % 4) == 0;
+  const bool vec4 = (rows % 4) == 0 && (ldy % 4) == 0 && aligned16(y) && (!dot_out || aligned16(dot_out));
   const bool single = (K + 255) / 256 <= S;
 #define I2S_RES(V, D, SG)                                                                                         \
-  return launch_res_inst<G, WN, S, WAVES, V, D, SG>(blocks, lds, packed, rows, K, N, ws, y, dot_out, bias, tiles_m, ms, \
+  return launch_res_inst<G, WN, S, WAVES, V, D, SG>(blocks, lds, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, \
                                                     stream)
   if (single) {
     if (vec4) {
@@ -1747,8 +1759,8 @@ int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, co
 // buffer offsets must stay below 2^31 bytes (else I2S_EKERNEL).
 template <int G, int WN, int WAVES, int SM, bool VEC4, bool DOT>
 int launch_pipe_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
-                    const ActWorkspace &ws, float *y, int32_t *dot_out, const float *bias, int64_t tiles_m,
-                    int64_t ms,
+                    const ActWorkspace &ws, float *y, int32_t *dot_out, const float *bias, int64_t ldy,
+                    int64_t tiles_m, int64_t ms,
                     hipStream_t stream) {
   static std::atomic<uint64_t> attr_done{0};
   int dev = 0;
@@ -1762,19 +1774,19 @@ int launch_pipe_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t
   }
   hipLaunchKernelGGL((gemm_pipe_kernel<G, WN, WAVES, SM, VEC4, DOT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * WAVES), static_cast<size_t>(lds), stream, packed, rows, K, ws.q, N, ws.scale,
-                     ws.row_sum, y, dot_out, bias, tiles_m, static_cast<int>(ms));
+                     ws.row_sum, y, dot_out, bias, ldy, tiles_m, static_cast<int>(ms));
   return hip_status();
 }
 
 template <int G, int WN, int WAVES, int SM>
 int launch_pipe_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
-                   int32_t *dot_out, const float *bias, hipStream_t stream) {
+                   int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   constexpr int64_t BN = 16 * WN;
   const int64_t steps = (K + 255) / 256;
   const int64_t lds = BN * (256 * steps + 16);
   if (steps > SM || lds > kResMaxLds) return I2S_EKERNEL;
   const int64_t lim = int64_t{1} << 31;
-  if ((rows + 16) * (K / 4) >= lim || BN * K >= lim || BN * rows * 4 >= lim || rows >= (int64_t{1} << 24))
+  if ((rows + 16) * (K / 4) >= lim || BN * K >= lim || BN * ldy * 4 >= lim || rows >= (int64_t{1} << 24))
     return I2S_EKERNEL;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t mt = (rows + 15) / 16;
@@ -1785,9 +1797,9 @@ int launch_pipe_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, c
   tiles_m = (mt + ms - 1) / ms;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > kMaxDim || ms > kMaxDim) return I2S_ERANGE;
-  const bool vec4 = (rows % 4) == 0;
+  const bool vec4 = (rows % 4) == 0 && (ldy % 4) == 0 && aligned16(y) && (!dot_out || aligned16(dot_out));
 #define I2S_SEQ(V, D) \
-  return launch_pipe_inst<G, WN, WAVES, SM, V, D>(blocks, lds, packed, rows, K, N, ws, y, dot_out, bias, tiles_m, ms, \
+  return launch_pipe_inst<G, WN, WAVES, SM, V, D>(blocks, lds, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, \
                                                          stream)
   if (vec4) {
     if (dot_out) I2S_SEQ(true, true);
@@ -1826,19 +1838,19 @@ int gemm_auto_variant(int64_t rows, int64_t K, int64_t N) {
 }
 
 int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
-                float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
+                float *y, int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   if (variant == 0) variant = gemm_auto_variant(rows, K, N);
   switch (variant) {
-    case 1: return launch_gemm_cfg<GemmA>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-    case 2: return launch_gemm_cfg<GemmB>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-    case 3: return launch_gemm_cfg<GemmC>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-    case 4: return launch_gemm_cfg<GemmD>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-    case 5: return launch_res_cfg<3, 4, 6, 4>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-    case 6: return launch_res_cfg<2, 4, 6, 8>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-    case 7: return launch_res_cfg<3, 4, 3, 8>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-    case 8: return launch_res_cfg<3, 2, 6, 8>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-    case 9: return launch_res_cfg<3, 1, 6, 8>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-    case 10: return launch_pipe_cfg<2, 2, 4, 6>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 1: return launch_gemm_cfg<GemmA>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 2: return launch_gemm_cfg<GemmB>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 3: return launch_gemm_cfg<GemmC>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 4: return launch_gemm_cfg<GemmD>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 5: return launch_res_cfg<3, 4, 6, 4>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 6: return launch_res_cfg<2, 4, 6, 8>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 7: return launch_res_cfg<3, 4, 3, 8>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 8: return launch_res_cfg<3, 2, 6, 8>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 9: return launch_res_cfg<3, 1, 6, 8>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 10: return launch_pipe_cfg<2, 2, 4, 6>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }
@@ -1858,31 +1870,31 @@ bool skinny_fits(int64_t rows, int64_t K, int64_t N) {
 
 template <int SPW, bool VEC4, bool DOT>
 int launch_skinny_inst(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
-                       int32_t *dot_out, const float *bias, hipStream_t stream) {
+                       int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_mfma_kernel<8, SPW, VEC4, DOT>), dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(512), 0,
-                     stream, packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out, bias);
+                     stream, packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out, bias, ldy);
   return hip_status();
 }
 
 template <int SPW>
 int launch_skinny_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
-                      int32_t *dot_out, const float *bias, hipStream_t stream) {
+                      int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   // 32-bit buffer offsets: activation rows (N*K), one subtile's weights and
   // the outputs past the block's first row (N*rows*4) stay below 2^31.
-  if (!skinny_fits(rows, K, N)) return I2S_EKERNEL;
-  const bool vec4 = (rows % 4) == 0;
-  if (vec4) return dot_out ? launch_skinny_inst<SPW, true, true>(packed, rows, K, N, ws, y, dot_out, bias, stream)
-                           : launch_skinny_inst<SPW, true, false>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-  return dot_out ? launch_skinny_inst<SPW, false, true>(packed, rows, K, N, ws, y, dot_out, bias, stream)
-                 : launch_skinny_inst<SPW, false, false>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+  if (!skinny_fits(rows, K, N) || N * ldy * 4 >= (int64_t{1} << 31)) return I2S_EKERNEL;
+  const bool vec4 = (rows % 4) == 0 && (ldy % 4) == 0 && aligned16(y) && (!dot_out || aligned16(dot_out));
+  if (vec4) return dot_out ? launch_skinny_inst<SPW, true, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream)
+                           : launch_skinny_inst<SPW, true, false>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+  return dot_out ? launch_skinny_inst<SPW, false, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream)
+                 : launch_skinny_inst<SPW, false, false>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
 }
 
 int launch_skinny(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
-                  float *y, int32_t *dot_out, const float *bias, hipStream_t stream) {
+                  float *y, int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   if (variant == 0) variant = skinny_auto_variant(K);
   switch (variant) {
-    case 1: return launch_skinny_cfg<2>(packed, rows, K, N, ws, y, dot_out, bias, stream);
-    case 2: return launch_skinny_cfg<4>(packed, rows, K, N, ws, y, dot_out, bias, stream);
+    case 1: return launch_skinny_cfg<2>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 2: return launch_skinny_cfg<4>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }
@@ -1896,7 +1908,8 @@ int check_common(int64_t rows, int64_t K) {
   return I2S_OK;
 }
 
-int quantize_launch(const float *x, int64_t N, int64_t K, int8_t *q, float *s, int32_t *rs, bool interleaved,
+int quantize_launch(const float *x, int64_t N, int64_t K, int64_t n_inner, int64_t ldx, int64_t bsx, int8_t *q,
+                    float *s, int32_t *rs, bool interleaved,
                     hipStream_t stream) {
   if (N > kMaxDim) return I2S_ERANGE;
   // The row sits in registers: XPT float4 per thread; longer rows get more
@@ -1905,10 +1918,10 @@ int quantize_launch(const float *x, int64_t N, int64_t K, int8_t *q, float *s, i
   do {                                                                                                     \
     if (interleaved)                                                                                       \
       hipLaunchKernelGGL((quantize_rowsum_reg_kernel<true, XPT, T>), dim3(static_cast<unsigned>(N)),       \
-                         dim3(T), 0, stream, x, K, q, s, rs);                                              \
+                         dim3(T), 0, stream, x, K, n_inner, ldx, bsx, q, s, rs);                                              \
     else                                                                                                   \
       hipLaunchKernelGGL((quantize_rowsum_reg_kernel<false, XPT, T>), dim3(static_cast<unsigned>(N)),      \
-                         dim3(T), 0, stream, x, K, q, s, rs);                                              \
+                         dim3(T), 0, stream, x, K, n_inner, ldx, bsx, q, s, rs);                                              \
     return hip_status();                                                                                   \
   } while (0)
   if (K <= 4 * 256 * 2) I2S_QREG(2, 256);
@@ -1917,10 +1930,10 @@ int quantize_launch(const float *x, int64_t N, int64_t K, int8_t *q, float *s, i
 #undef I2S_QREG
   if (interleaved)
     hipLaunchKernelGGL((quantize_rowsum_kernel<true>), dim3(static_cast<unsigned>(N)), dim3(kQuantThreads), 0, stream,
-                       x, K, q, s, rs);
+                       x, K, n_inner, ldx, bsx, q, s, rs);
   else
     hipLaunchKernelGGL((quantize_rowsum_kernel<false>), dim3(static_cast<unsigned>(N)), dim3(kQuantThreads), 0, stream,
-                       x, K, q, s, rs);
+                       x, K, n_inner, ldx, bsx, q, s, rs);
   return hip_status();
 }
 
@@ -1960,7 +1973,7 @@ extern "C" int i2s_quantize_act(const float *x, int64_t N, int64_t K, int8_t *q,
   if (N == 0) return I2S_OK;
   if (!x || !q || !act_scale || !row_sum) return I2S_EINVAL;
   if (!aligned16(x) || !aligned16(q)) return I2S_EINVAL;
-  return quantize_launch(x, N, K, q, act_scale, row_sum, false, static_cast<hipStream_t>(stream));
+  return quantize_launch(x, N, K, N, K, N * K, q, act_scale, row_sum, false, static_cast<hipStream_t>(stream));
 }
 
 namespace {
@@ -1999,11 +2012,11 @@ int contract_auto_kernel(int64_t rows, int64_t K, int64_t N) {
 }
 
 int contract(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
-             int32_t *dot_out, const float *bias, int kernel, int variant, hipStream_t s) {
+             int32_t *dot_out, const float *bias, int64_t ldy, int kernel, int variant, hipStream_t s) {
   if (kernel == 0) kernel = contract_auto_kernel(rows, K, N);
-  if (kernel == 4) return launch_skinny(variant, packed, rows, K, N, ws, y, dot_out, bias, s);
-  if (kernel == 1) return launch_gemv(variant, packed, rows, K, N, ws, y, dot_out, bias, s);
-  return launch_gemm(variant, packed, rows, K, N, ws, y, dot_out, bias, s);
+  if (kernel == 4) return launch_skinny(variant, packed, rows, K, N, ws, y, dot_out, bias, ldy, s);
+  if (kernel == 1) return launch_gemv(variant, packed, rows, K, N, ws, y, dot_out, bias, ldy, s);
+  return launch_gemm(variant, packed, rows, K, N, ws, y, dot_out, bias, ldy, s);
 }
 
 }  // namespace
@@ -2019,7 +2032,7 @@ extern "C" int i2s_quantize_act_ws(const float *x, int64_t N, int64_t K, void *w
   if (!workspace || workspace_bytes < i2s_act_workspace_bytes(N, K)) return I2S_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I2S_EWORKSPACE;
   ActWorkspace ws = carve_workspace(workspace, N, K);
-  return quantize_launch(x, N, K, ws.q, ws.scale, ws.row_sum, true, static_cast<hipStream_t>(stream));
+  return quantize_launch(x, N, K, N, K, N * K, ws.q, ws.scale, ws.row_sum, true, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const void *workspace,
@@ -2030,7 +2043,7 @@ extern "C" int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, in
   int st = check_mul_mat(packed, rows, K, N, workspace, workspace_bytes, y, dot_out, kernel, variant, &noop);
   if (st != I2S_OK || noop) return st;
   ActWorkspace ws = carve_workspace(const_cast<void *>(workspace), N, K);
-  return contract(packed, rows, K, N, ws, y, dot_out, nullptr, kernel, variant, static_cast<hipStream_t>(stream));
+  return contract(packed, rows, K, N, ws, y, dot_out, nullptr, rows, kernel, variant, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int i2s_mul_mat_ex(const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t N,
@@ -2042,11 +2055,11 @@ extern "C" int i2s_mul_mat_ex(const uint8_t *packed, int64_t rows, int64_t K, co
   if (!x || !aligned16(x)) return I2S_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (kernel == 3 || (kernel == 0 && fused_auto(rows, N, K)))
-    return launch_fused(variant, packed, rows, K, N, x, y, dot_out, nullptr, s);
+    return launch_fused(variant, packed, rows, K, N, x, K, y, dot_out, nullptr, rows, s);
   ActWorkspace ws = carve_workspace(workspace, N, K);
-  st = quantize_launch(x, N, K, ws.q, ws.scale, ws.row_sum, true, s);
+  st = quantize_launch(x, N, K, N, K, N * K, ws.q, ws.scale, ws.row_sum, true, s);
   if (st != I2S_OK) return st;
-  return contract(packed, rows, K, N, ws, y, dot_out, nullptr, kernel, variant, s);
+  return contract(packed, rows, K, N, ws, y, dot_out, nullptr, rows, kernel, variant, s);
 }
 
 extern "C" int i2s_mul_mat(const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t N,
@@ -2087,17 +2100,53 @@ extern "C" int i2s_mul_mat_group_ex(const i2s_proj *projs, int count, int64_t K,
     return launch_fused_group(variant, g, total_rows, K, N, x, s);
   }
   ActWorkspace ws = carve_workspace(workspace, N, K);
-  int st = quantize_launch(x, N, K, ws.q, ws.scale, ws.row_sum, true, s);
+  int st = quantize_launch(x, N, K, N, K, N * K, ws.q, ws.scale, ws.row_sum, true, s);
   for (int p = 0; p < count && st == I2S_OK; ++p)
     if (projs[p].rows > 0)
-      st = contract(projs[p].packed, projs[p].rows, K, N, ws, projs[p].y, projs[p].dot_out, projs[p].bias, kernel,
-                    variant, s);
+      st = contract(projs[p].packed, projs[p].rows, K, N, ws, projs[p].y, projs[p].dot_out, projs[p].bias,
+                    projs[p].rows, kernel, variant, s);
   return st;
 }
 
 extern "C" int i2s_mul_mat_group(const i2s_proj *projs, int count, int64_t K, const float *x, int64_t N,
                                  void *workspace, size_t workspace_bytes, void *stream) {
   return i2s_mul_mat_group_ex(projs, count, K, x, N, workspace, workspace_bytes, 0, 0, stream);
+}
+
+extern "C" int i2s_mul_mat_batched(const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t N,
+                                   int64_t B, int64_t ldx, int64_t bsx, void *workspace, size_t workspace_bytes,
+                                   float *y, int64_t ldy, int64_t bsy, int32_t *dot_out, void *stream) {
+  if (N < 0 || B < 0 || N > kMaxDim || B > kMaxDim) return N < 0 || B < 0 ? I2S_EINVAL : I2S_ERANGE;
+  const int64_t NB = N * B;
+  if (NB > kMaxDim) return I2S_ERANGE;
+  bool noop;
+  int st = check_mul_mat(packed, rows, K, NB, workspace, workspace_bytes, y, dot_out, 0, 0, &noop);
+  if (st != I2S_OK || noop) return st;
+  if (!x || !aligned16(x)) return I2S_EINVAL;
+  // Rows of x start 16-byte aligned (float4 loads); outputs never overlap.
+  if (ldx < K || ldx % 4 != 0 || bsx < 0 || bsx % 4 != 0) return I2S_EINVAL;
+  if (ldy < rows || bsy < 0) return I2S_EINVAL;
+  if (B > 1 && bsy < (N - 1) * ldy + rows) return I2S_EINVAL;
+  if (ldx > kMaxDim || ldy > kMaxDim) return I2S_ERANGE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool dense = ldx == K && ldy == rows && (B == 1 || (bsx == N * K && bsy == N * rows));
+  if (dense) return i2s_mul_mat_ex(packed, rows, K, x, NB, workspace, workspace_bytes, y, dot_out, 0, 0, stream);
+  if (fused_auto(rows, N, K)) {
+    for (int64_t b = 0; b < B && st == I2S_OK; ++b)
+      st = launch_fused(0, packed, rows, K, N, x + b * bsx, ldx, y + b * bsy, dot_out ? dot_out + b * bsy : nullptr,
+                        nullptr, ldy, s);
+    return st;
+  }
+  ActWorkspace ws = carve_workspace(workspace, NB, K);
+  st = quantize_launch(x, NB, K, N, ldx, bsx, ws.q, ws.scale, ws.row_sum, true, s);
+  for (int64_t b = 0; b < B && st == I2S_OK; ++b) {
+    ActWorkspace wb;
+    wb.q = ws.q + b * N * K;
+    wb.scale = ws.scale + b * N;
+    wb.row_sum = ws.row_sum + b * N;
+    st = contract(packed, rows, K, N, wb, y + b * bsy, dot_out ? dot_out + b * bsy : nullptr, nullptr, ldy, 0, 0, s);
+  }
+  return st;
 }
 
 extern "C" int i2s_mul_mat_kernel(int64_t rows, int64_t K, int64_t N) {

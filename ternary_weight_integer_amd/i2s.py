@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.i2s_mul_mat_group.argtypes = [ctypes.POINTER(I2SProj), ci, i64, p, i64, p, sz, p]
         L.i2s_mul_mat_group_ex.restype = ci
         L.i2s_mul_mat_group_ex.argtypes = [ctypes.POINTER(I2SProj), ci, i64, p, i64, p, sz, ci, ci, p]
+        L.i2s_mul_mat_batched.restype = ci
+        L.i2s_mul_mat_batched.argtypes = [p, i64, i64, p, i64, i64, i64, i64, p, sz, p, i64, i64, p, p]
         L.i2s_kernel_variants.restype = ci
         L.i2s_kernel_variants.argtypes = [ci]
         L.i2s_strerror.restype = ctypes.c_char_p
@@ -299,3 +301,32 @@ def i2s_mul_mat_group(weights, K: int, x: torch.Tensor, biases=None, workspace=N
         projs, count, K, _dev(x, torch.float32, "x"), N, _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), int(kernel), int(variant), _stream(stream)))
     return (outs, dots) if dot_out else outs
+
+
+def i2s_mul_mat_batched(packed: torch.Tensor, rows: int, K: int, x: torch.Tensor, workspace=None, y=None,
+                        dot_out=None, stream=None):
+    """The op on a 3-D activation x[B][N][K] (any strides whose innermost is 1):
+    y[B][N][rows] (allocated, or a given view with innermost stride 1), and
+    the int32 dots (same strides as y) if dot_out is a tensor or True."""
+    if x.dim() != 3 or x.shape[2] != K or x.stride(2) != 1:
+        raise ValueError(f"x must be [B][N][{K}] with unit innermost stride, got {tuple(x.shape)}")
+    if x.dtype != torch.float32 or not x.is_cuda:
+        raise TypeError("x must be a float32 CUDA (HIP) tensor")
+    B, N = x.shape[0], x.shape[1]
+    if packed.numel() < i2s_packed_bytes(rows, K):
+        raise ValueError("packed tensor smaller than i2s_packed_bytes(rows, K)")
+    dev = x.device
+    workspace = new_workspace(N * B, K, dev) if workspace is None else workspace
+    y = torch.empty((B, N, rows), dtype=torch.float32, device=dev) if y is None else y
+    if y.dim() != 3 or tuple(y.shape) != (B, N, rows) or y.stride(2) != 1 or y.dtype != torch.float32:
+        raise ValueError(f"y must be float32 [B][N][{rows}] with unit innermost stride")
+    want_dot = dot_out is not None and dot_out is not False
+    if dot_out is True:
+        dot_out = torch.empty_strided(y.shape, y.stride(), dtype=torch.int32, device=dev)
+    if want_dot and (dot_out.stride() != y.stride() or dot_out.dtype != torch.int32):
+        raise ValueError("dot_out must be int32 with y's strides")
+    _check("i2s_mul_mat_batched", lib().i2s_mul_mat_batched(
+        _dev(packed, torch.uint8, "packed"), rows, K, x.data_ptr(), N, B, x.stride(1), x.stride(0),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), y.data_ptr(), y.stride(1), y.stride(0),
+        dot_out.data_ptr() if want_dot else None, _stream(stream)))
+    return (y, dot_out) if want_dot else y

@@ -332,3 +332,18 @@ def test_group_is_each_projection_on_the_same_activation():
     assert np.array_equal(ds[0], d0) and np.array_equal(ds[1], d1)
     assert np.array_equal(ys[1].view(np.uint32), y1.view(np.uint32))
     assert np.array_equal(ys[0].view(np.uint32), (y0 + b0[None, :]).astype(np.float32).view(np.uint32))
+
+
+def test_batched_is_the_same_rows_reindexed():
+    """Quantization is per activation row, so a 3-D batch equals the 2-D op on
+    its N*B rows, reshaped (the batched test's indexing, "ggml-cpu: ternary
+    I2_S matmul kernel (VibeASR, 3/4)", Tests)."""
+    rng = np.random.default_rng(37)
+    rows, K, B, N = 9, 256, 3, 4
+    p = oracle.pack(workloads.ternary(rng, rows, K), 0.02)
+    x = workloads.normal(rng, B * N, K).reshape(B, N, K)
+    yb, db = oracle.mul_mat_batched(p, rows, K, x, with_dot=True)
+    y2, d2 = oracle.mul_mat(p, rows, K, x.reshape(B * N, K), with_dot=True)
+    assert yb.shape == (B, N, rows)
+    assert np.array_equal(db.reshape(B * N, rows), d2)
+    assert np.array_equal(yb.reshape(B * N, rows).view(np.uint32), y2.view(np.uint32))
