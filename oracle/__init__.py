@@ -57,6 +57,16 @@ def _load():
         lib.oracle_mul_mat.argtypes = [p, i64, i64, p, i64, p, p]
         lib.oracle_add_bias.restype = None
         lib.oracle_add_bias.argtypes = [p, p, i64, i64]
+        lib.oracle_i8s_bytes.restype = ctypes.c_size_t
+        lib.oracle_i8s_bytes.argtypes = [i64]
+        lib.oracle_i8s_scale.restype = ctypes.c_float
+        lib.oracle_i8s_scale.argtypes = [p, i64]
+        lib.oracle_i8s_quantize.restype = None
+        lib.oracle_i8s_quantize.argtypes = [p, i64, p]
+        lib.oracle_i8s_dequantize.restype = None
+        lib.oracle_i8s_dequantize.argtypes = [p, i64, p]
+        lib.oracle_i8s_mul_mat_add.restype = ctypes.c_int
+        lib.oracle_i8s_mul_mat_add.argtypes = [p, i64, i64, p, i64, p, ctypes.c_int, p, p, p]
         _lib = lib
     return _lib
 
@@ -162,3 +172,71 @@ def mul_mat_batched(packed: np.ndarray, rows: int, K: int, x: np.ndarray, with_d
     y = np.stack([o[0] for o in outs]) if outs else np.zeros((0, x.shape[1], rows), np.float32)
     d = np.stack([o[1] for o in outs]) if outs else np.zeros((0, x.shape[1], rows), np.int32)
     return (y, d) if with_dot else y
+
+
+# ---------------------------------------------------------------------------
+# I8_S: per-tensor int8 payload, then the 32-byte in-band F32 scale slot.
+
+
+def i8s_bytes(n: int) -> int:
+    return int(_load().oracle_i8s_bytes(n))
+
+
+def i8s_make(q: np.ndarray, scale: float) -> np.ndarray:
+    """An I8_S tensor from int8 values (any shape, flattened) and a scale:
+    the payload bytes, the F32 scale, 28 zero bytes."""
+    q = np.ascontiguousarray(q, dtype=np.int8).reshape(-1)
+    out = np.zeros(i8s_bytes(q.size), dtype=np.uint8)
+    out[: q.size] = q.view(np.uint8)
+    out[q.size: q.size + 4] = np.array([scale], dtype="<f4").view(np.uint8)
+    return out
+
+
+def i8s_payload(t: np.ndarray, n: int) -> np.ndarray:
+    return np.ascontiguousarray(t[:n]).view(np.int8)
+
+
+def i8s_scale(t: np.ndarray, n: int) -> np.float32:
+    return np.float32(_load().oracle_i8s_scale(_ptr(np.ascontiguousarray(t, dtype=np.uint8)), n))
+
+
+def i8s_quantize(x: np.ndarray) -> np.ndarray:
+    """I8_S bytes of the F32 tensor x (flattened in C order)."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    out = np.empty(i8s_bytes(x.size), dtype=np.uint8)
+    _load().oracle_i8s_quantize(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def i8s_dequantize(t: np.ndarray, n: int) -> np.ndarray:
+    t = np.ascontiguousarray(t, dtype=np.uint8)
+    assert t.size >= n + 4
+    y = np.empty(n, dtype=np.float32)
+    _load().oracle_i8s_dequantize(_ptr(t), n, _ptr(y))
+    return y
+
+
+def i8s_mul_mat_add(w: np.ndarray, OC: int, IC: int, x: np.ndarray, N: int, bias=None, relu: bool = False,
+                    with_dot: bool = False, with_f: bool = False):
+    """I8_S out[N][OC] (bytes, payload then scale slot) of mul_mat_add, or of
+    mul_mat_add_relu when relu is set; optionally also int32 acc[N][OC] and
+    the F32 values before requantization."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    assert w.size >= OC * IC + 4 and x.size >= N * IC + 4
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    if b is not None:
+        assert b.size >= OC
+    out = np.empty(i8s_bytes(N * OC), dtype=np.uint8)
+    d = np.empty((N, OC), dtype=np.int32)
+    f = np.empty((N, OC), dtype=np.float32)
+    rc = _load().oracle_i8s_mul_mat_add(_ptr(w), OC, IC, _ptr(x), N, None if b is None else _ptr(b), int(bool(relu)),
+                                        _ptr(out), _ptr(d), _ptr(f))
+    if rc != 0:
+        raise MemoryError("oracle_i8s_mul_mat_add: allocation failed")
+    res = [out]
+    if with_dot:
+        res.append(d)
+    if with_f:
+        res.append(f)
+    return res[0] if len(res) == 1 else tuple(res)

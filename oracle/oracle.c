@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the I2_S ternary-weight x int8-activation matmul (W2A8).
+ * CPU oracle for the I2_S ternary-weight x int8-activation matmul (W2A8),
+ * and for the I8_S per-tensor int8 type with its fused mul_mat_add(_relu).
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
  * definition that the GPU library is checked against.  Only the tests, the
@@ -21,8 +22,13 @@
  * rounding vector, the headroom closed form, degenerate scales, sign
  * invariants, exact-rational quantization and Python-integer brute force with
  * signed weights; for the bias add, hand-derived binary32 values that tell
- * one add after the rounded epilogue from a fused multiply-add.  The 28 padding bytes of the in-band scale slot are
- * "parity unpinned": nothing on the pages reads them.
+ * one add after the rounded epilogue from a fused multiply-add.  I8_S
+ * (tests/test_oracle_i8s_pins.py): hand-worked mul_mat_add(_relu) bytes and
+ * scale bits, an exact-rational model, numpy's integer matmul at full scale,
+ * the per-row vectors on one-row tensors, round-trip bounds, equivariances,
+ * and agreement with the I2_S op on ternary weights.  The 28 padding bytes of
+ * the in-band scale slot are "parity unpinned": nothing on the pages reads
+ * them.
  */
 #include <math.h>
 #include <stdint.h>
@@ -197,4 +203,93 @@ void oracle_add_bias(float *y, const float *bias, int64_t N, int64_t rows)
     for (int64_t n = 0; n < N; ++n)
         for (int64_t o = 0; o < rows; ++o)
             y[n * rows + o] = y[n * rows + o] + bias[o];
+}
+
+/* ------------------------------------------------------------------------
+ * I8_S: per-tensor int8 [P1 Two new types: nelements int8 bytes, then one
+ * padded F32 scale, stored as the multiplier amax/127].  The scale occupies
+ * the four bytes right after the payload, followed by 28 zero bytes (the same
+ * 32-byte slot as I2_S; the padding is parity unpinned).
+ */
+
+size_t oracle_i8s_bytes(int64_t n)
+{
+    return (size_t)n + ORACLE_SCALE_SLOT;
+}
+
+float oracle_i8s_scale(const uint8_t *t, int64_t n)
+{
+    float s;
+    memcpy(&s, t + n, sizeof(float));
+    return s;
+}
+
+/* F32 tensor -> I8_S: one amax over the whole tensor, floored at 1e-5
+ * [P3 Architecture/Encoder: the waveform's single scale], s = amax / 127,
+ * q = x / s rounded half away from zero, clamped to [-127, 127]; the same
+ * steps as the per-row activation quantization with the row taken to be the
+ * whole tensor. */
+void oracle_i8s_quantize(const float *x, int64_t n, uint8_t *out)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax < 1e-5f) amax = 1e-5f;
+    float s = amax / 127.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float r = roundf(x[i] / s);
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        out[i] = (uint8_t)(int8_t)r;
+    }
+    memset(out + n, 0, ORACLE_SCALE_SLOT);
+    memcpy(out + n, &s, sizeof(float));
+}
+
+/* I8_S -> F32: y = q * s (dequantize by multiplying [P1 Two new types]). */
+void oracle_i8s_dequantize(const uint8_t *t, int64_t n, float *y)
+{
+    float s = oracle_i8s_scale(t, n);
+    for (int64_t i = 0; i < n; ++i) y[i] = (float)(int8_t)t[i] * s;
+}
+
+/* mul_mat_add (relu = 0) and mul_mat_add_relu (relu = 1)
+ * [P1 Five fused INT8 ops: I8_S x I8_S -> I8_S, the bias added and the
+ * output requantized in the epilogue; the relu form applies ReLU before
+ * requantizing].  w is I8_S [OC][IC] (output channel o is row o), x is I8_S
+ * [N][IC]; per output:
+ *   acc[n][o] = sum_k w[o][k] * x[n][k]                (int32, exact)
+ *   f[n][o]   = (float)acc * (ws * xs)                 (ws * xs first)
+ *   f[n][o]   = f[n][o] + bias[o]                      (if bias != NULL)
+ *   f[n][o]   = f[n][o] > 0 ? f[n][o] : 0              (relu form)
+ * then out = the I8_S quantization of the whole f[N][OC] tensor.  dot and f
+ * (either may be NULL) receive acc and the pre-quantization values.  Returns
+ * 0, or -2 on allocation failure. */
+int oracle_i8s_mul_mat_add(const uint8_t *w, int64_t OC, int64_t IC,
+                           const uint8_t *x, int64_t N, const float *bias, int relu,
+                           uint8_t *out, int32_t *dot, float *f)
+{
+    float ws = oracle_i8s_scale(w, OC * IC);
+    float xs = oracle_i8s_scale(x, N * IC);
+    float t = ws * xs;
+    float *v = (float *)malloc((size_t)(N * OC > 0 ? N * OC : 1) * sizeof(float));
+    if (!v) return -2;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t o = 0; o < OC; ++o) {
+            int32_t acc = 0;
+            for (int64_t k = 0; k < IC; ++k)
+                acc += (int32_t)(int8_t)w[o * IC + k] * (int32_t)(int8_t)x[n * IC + k];
+            float r = (float)acc * t;
+            if (bias) r = r + bias[o];
+            if (relu && !(r > 0.0f)) r = 0.0f;
+            v[n * OC + o] = r;
+            if (dot) dot[n * OC + o] = acc;
+        }
+    }
+    if (f) memcpy(f, v, (size_t)(N * OC) * sizeof(float));
+    oracle_i8s_quantize(v, N * OC, out);
+    free(v);
+    return 0;
 }

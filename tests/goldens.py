@@ -105,3 +105,32 @@ def bias_add():
         k, v = line.split()
         out[k] = int(v, 16)
     return out
+
+
+def i8s_mul_mat_add():
+    """Hand-worked mul_mat_add cases (tests/golden/i8s_mul_mat_add.txt):
+    (shared, cases) where shared holds OC, IC, N, w, ws, x, xs, acc and each
+    case holds name, bias (f32), relu, q and scale_bits."""
+    shared, cases, cur = {}, [], None
+    for line in _lines("i8s_mul_mat_add.txt"):
+        key, *vals = line.split()
+        if key == "case":
+            cur = {"name": vals[0]}
+            cases.append(cur)
+            continue
+        tgt = shared if cur is None else cur
+        if key in ("OC", "IC", "N", "relu"):
+            tgt[key] = int(vals[0])
+        elif key in ("w", "x", "q"):
+            tgt[key] = np.array([int(v) for v in vals], dtype=np.int8)
+        elif key == "acc":
+            tgt[key] = np.array([int(v) for v in vals], dtype=np.int32)
+        elif key in ("ws_hex", "xs_hex"):
+            tgt[key[:2]] = hex_f32(vals[0])
+        elif key == "bias_hex":
+            tgt["bias"] = np.array([hex_f32(v) for v in vals], dtype=np.float32)
+        elif key == "scale_hex":
+            tgt["scale_bits"] = int(vals[0], 16)
+        else:
+            raise ValueError(f"unknown key {key}")
+    return shared, cases
