@@ -16,8 +16,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "i2s.hip")
-HEADER = os.path.join(ROOT, "include", "i2s.h")
+SRCS = [os.path.join(PKG, "csrc", "i2s.hip"), os.path.join(PKG, "csrc", "i8s.hip")]
+HEADERS = [os.path.join(ROOT, "include", "i2s.h"), os.path.join(ROOT, "include", "i8s.h")]
 LIB = os.path.join(PKG, "libi2s.so")
 ARCH = "gfx950"
 
@@ -35,7 +35,6 @@ def flags() -> list[str]:
         "-O3",
         "-std=c++17",
         "-fPIC",
-        "-shared",
         "-Wall",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-ffp-contract=off",
@@ -43,20 +42,41 @@ def flags() -> list[str]:
     ]
 
 
+# hipcc's host pass does not know the packed-fp32 feature and says so; drop that line.
+_NOISE = "-packed-fp32-ops' is not a recognized feature"
+
+
+def _errors(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines() if _NOISE not in l)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile csrc/i2s.hip into libi2s.so next to this file; returns its path."""
+    """Compile csrc/*.hip (in parallel, one object each) and link libi2s.so
+    next to this file; returns its path."""
+    objs = [LIB + "." + os.path.splitext(os.path.basename(src))[0] + ".o" for src in SRCS]
+    procs = []
+    for src, obj in zip(SRCS, objs):
+        cmd = [hipcc(), *flags(), "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    failed = []
+    for src, p in zip(SRCS, procs):
+        _, err = p.communicate()
+        err = _errors(err)
+        if p.returncode != 0:
+            failed.append(f"{os.path.basename(src)} ({p.returncode}):\n{err}")
+        elif err.strip() and verbose:
+            print(err, file=sys.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed: " + "\n".join(failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *flags(), SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line.
-    noise = "-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    for obj in objs:
+        os.remove(obj)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"hipcc link failed ({res.returncode}):\n{_errors(res.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,0 +1,525 @@
+// gfx950 (MI355X) kernels and C ABI for the I8_S per-tensor int8 type and its
+// fused mul_mat_add / mul_mat_add_relu.  The ABI is declared, with its
+// contract, in include/i8s.h.
+//
+// I8_S ("ggml: additive INT8/ternary types, fused CPU ops, and kernels for
+// VibeASR (1/2)", Two new types): n int8 payload bytes, then the F32
+// multiplier scale amax/127 in band, in a 32-byte slot.
+//
+// mul_mat_add (same page, Five fused INT8 ops): int32 acc = w . x, then
+// f = (float)acc * (ws * xs) + bias[o] (ReLU in the relu form), then one
+// per-tensor requantization of f.  The requantization needs max|f| over the
+// whole output before any value can be written, so the op runs the same
+// contraction twice: pass 1 reduces max|f| per workgroup into the workspace,
+// pass 2 reduces those partial maxima to the tensor's scale and writes the
+// int8 values.  Recomputing the integer contraction is cheaper than writing
+// and re-reading the F32 tensor (4 bytes out and 4 back per output against
+// the 1-byte result) for the encoder's shapes, whose IC is small.
+//
+// Every float operation is one IEEE operation: the library is built without
+// fast-math and without FP contraction, and '/' is the correctly rounded
+// division, so results match the definition bit for bit.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "i8s.h"
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;          // every kernel here: 4 wave64s
+constexpr int kMaxParts = 1024;        // workgroups of a two-pass launch (partial maxima)
+constexpr int64_t kMaxBytes = 0x7fff0000;  // largest tensor a buffer descriptor covers here
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // buffer offset beyond every descriptor range
+constexpr int kBufferFlags = 0x00020000;       // raw buffer, 32-bit data format
+constexpr float kAmaxFloor = 1e-5f;
+
+__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           kBufferFlags);
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// max over the workgroup; red is 4 floats of LDS; every thread gets the result.
+__device__ inline float block_max(float v, float *red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+// An in-band F32 scale at any byte address (the payload length need not be a
+// multiple of 4).
+__device__ inline float load_scale(const uint8_t *p) {
+  const uint32_t b = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 8) |
+                     (static_cast<uint32_t>(p[2]) << 16) | (static_cast<uint32_t>(p[3]) << 24);
+  return __uint_as_float(b);
+}
+
+// The tensor scale from the partial maxima: amax floored at 1e-5, s = amax/127.
+__device__ inline float scale_from_parts(const float *parts, int count, float *red) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < count; i += kThreads) m = fmaxf(m, parts[i]);
+  m = block_max(m, red);
+  if (m < kAmaxFloor) m = kAmaxFloor;
+  return m / 127.0f;
+}
+
+// The 32-byte scale slot after the payload: the F32 scale, then 28 zeros.
+// Called by every thread of workgroup 0; threads 0..31 write one byte each.
+__device__ inline void write_slot(uint8_t *slot, float s) {
+  if (threadIdx.x < I8S_SCALE_SLOT) {
+    const uint32_t b = __float_as_uint(s);
+    slot[threadIdx.x] = threadIdx.x < 4 ? static_cast<uint8_t>(b >> (8 * threadIdx.x)) : 0;
+  }
+}
+
+// q = f/s rounded half away from zero (roundf), clamped to [-127, 127].
+__device__ inline int quant(float v, float s) {
+  float r = roundf(v / s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return static_cast<int>(r);
+}
+
+// Four int8 values (each in [-127, 127]) packed little-endian into one dword.
+__device__ inline int pack4(int q0, int q1, int q2, int q3) {
+  return static_cast<int>((static_cast<uint32_t>(q0) & 0xffu) | ((static_cast<uint32_t>(q1) & 0xffu) << 8) |
+                          ((static_cast<uint32_t>(q2) & 0xffu) << 16) | (static_cast<uint32_t>(q3) << 24));
+}
+
+inline int hip_status() { return hipGetLastError() == hipSuccess ? I2S_OK : I2S_EHIP; }
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline int parts_for(int64_t units) {
+  if (units < 1) return 1;
+  return units < kMaxParts ? static_cast<int>(units) : kMaxParts;
+}
+
+// ---------------------------------------------------------------------------
+// F32 -> I8_S over a whole tensor.  Both passes walk the tensor in chunks of
+// 16 values (four float4 loads per thread-step); the last n % 16 values are
+// handled one by one by workgroup 0.
+
+__global__ void __launch_bounds__(kThreads) i8s_absmax_kernel(const float *__restrict__ x, int64_t n,
+                                                              float *__restrict__ parts) {
+  __shared__ float red[4];
+  const int64_t chunks = n / 16;
+  float m = 0.0f;
+  for (int64_t c = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; c < chunks;
+       c += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const float4 *p = reinterpret_cast<const float4 *>(x + 16 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = p[j];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < n - 16 * chunks) m = fmaxf(m, fabsf(x[16 * chunks + threadIdx.x]));
+  m = block_max(m, red);
+  if (threadIdx.x == 0) parts[blockIdx.x] = m;
+}
+
+__global__ void __launch_bounds__(kThreads) i8s_quantize_kernel(const float *__restrict__ x, int64_t n,
+                                                                const float *__restrict__ parts, int nparts,
+                                                                uint8_t *__restrict__ out) {
+  __shared__ float red[4];
+  const float s = scale_from_parts(parts, nparts, red);
+  if (blockIdx.x == 0) write_slot(out + n, s);
+  const int64_t chunks = n / 16;
+  for (int64_t c = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; c < chunks;
+       c += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const float4 *p = reinterpret_cast<const float4 *>(x + 16 * c);
+    v4i pk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = p[j];
+      pk[j] = pack4(quant(v.x, s), quant(v.y, s), quant(v.z, s), quant(v.w, s));
+    }
+    *reinterpret_cast<v4i *>(out + 16 * c) = pk;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < n - 16 * chunks) {
+    const int64_t i = 16 * chunks + threadIdx.x;
+    out[i] = static_cast<uint8_t>(quant(x[i], s));
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) i8s_dequantize_kernel(const uint8_t *__restrict__ t, int64_t n,
+                                                                  float *__restrict__ y) {
+  const float s = load_scale(t + n);
+  const int64_t chunks = n / 16;
+  for (int64_t c = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; c < chunks;
+       c += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const v4i pk = *reinterpret_cast<const v4i *>(t + 16 * c);
+    float4 *p = reinterpret_cast<float4 *>(y + 16 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int w = pk[j];
+      p[j] = make_float4(static_cast<float>(static_cast<int8_t>(w)) * s,
+                         static_cast<float>(static_cast<int8_t>(w >> 8)) * s,
+                         static_cast<float>(static_cast<int8_t>(w >> 16)) * s,
+                         static_cast<float>(static_cast<int8_t>(w >> 24)) * s);
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < n - 16 * chunks) {
+    const int64_t i = 16 * chunks + threadIdx.x;
+    y[i] = static_cast<float>(static_cast<int8_t>(t[i])) * s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// mul_mat_add arguments shared by both passes and both contraction kernels.
+
+struct MatArgs {
+  const int8_t *w;      // [OC][IC] payload
+  const int8_t *x;      // [N][IC] payload
+  const uint8_t *ws;    // in-band scale of w
+  const uint8_t *xs;    // in-band scale of x
+  const float *bias;    // [OC] or null
+  float *parts;         // pass 1 writes parts[blockIdx.x]; pass 2 reads nparts of them
+  int8_t *out;          // [N][OC] payload (pass 2)
+  int32_t *dot;         // [N][OC] or null (pass 2)
+  int64_t OC, IC, N;
+  int nparts;
+  int relu;
+  int vec;              // OC % 16 == 0: 16-byte int8 stores, 16-byte dot stores
+};
+
+// f of one output from its accumulator: (float)acc * t, + bias, ReLU.
+__device__ inline float value_of(int32_t acc, float t, float b, bool has_bias, int relu) {
+  float v = static_cast<float>(acc) * t;
+  if (has_bias) v = v + b;
+  if (relu && !(v > 0.0f)) v = 0.0f;
+  return v;
+}
+
+// Plain per-output contraction for any IC (byte loads); one thread per
+// output, grid-stride.  Used when IC % 16 != 0.
+template <bool QUANT>
+__global__ void __launch_bounds__(kThreads) i8s_mm_plain_kernel(const MatArgs a) {
+  __shared__ float red[4];
+  const float t = load_scale(a.ws) * load_scale(a.xs);
+  float s = 1.0f;
+  if constexpr (QUANT) {
+    s = scale_from_parts(a.parts, a.nparts, red);
+    if (blockIdx.x == 0) write_slot(reinterpret_cast<uint8_t *>(a.out) + a.N * a.OC, s);
+  }
+  float m = 0.0f;
+  const int64_t total = a.N * a.OC;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int64_t n = i / a.OC, o = i - n * a.OC;
+    const int8_t *wr = a.w + o * a.IC;
+    const int8_t *xr = a.x + n * a.IC;
+    int32_t acc = 0;
+    for (int64_t k = 0; k < a.IC; ++k) acc += static_cast<int32_t>(wr[k]) * static_cast<int32_t>(xr[k]);
+    const float v = value_of(acc, t, a.bias ? a.bias[o] : 0.0f, a.bias != nullptr, a.relu);
+    if constexpr (QUANT) {
+      a.out[i] = static_cast<int8_t>(quant(v, s));
+      if (a.dot) a.dot[i] = acc;
+    } else {
+      m = fmaxf(m, fabsf(v));
+    }
+  }
+  if constexpr (!QUANT) {
+    m = block_max(m, red);
+    if (threadIdx.x == 0) a.parts[blockIdx.x] = m;
+  }
+}
+
+// int8 MFMA contraction (v_mfma_i32_16x16x64_i8), IC % 16 == 0.
+//
+// A workgroup owns TM output channels x TN activation rows per tile and walks
+// tiles with a grid stride (the grid is at most kMaxParts workgroups, one
+// partial maximum each).  Four waves; each wave owns 64 channels x TN/WAVES_N
+// rows, i.e. 4 channel blocks x FN row blocks of 16 x 16.  The k loop steps
+// 64 bytes: all 256 threads load the tile's rows (four consecutive lanes read
+// one row's 64 contiguous bytes), store them to LDS, and every wave reads its
+// MFMA operands from LDS; two LDS stages, one barrier per step.
+//
+// LDS layout of a stage: row r's 16-byte chunk c at r*64 + 16*(c ^ sw(r)),
+// sw(r) = ((r >> 2) ^ (r >> 4)) & 3.  Sixteen lanes reading chunk c of rows
+// r0..r0+15 (activation operand) or of rows {16p + 4b + j} (weight operand,
+// below) then touch sixteen different 16-byte bank groups, and four lanes
+// writing one row's four chunks fill 64 contiguous bytes.
+//
+// Channel order inside a wave: MFMA block b's operand row i is channel
+// 16*(i>>2) + 4*b + (i&3) of the wave's 64.  The accumulator element r of
+// lane (li, kq) in block b is MFMA row 4*kq + r, i.e. channel
+// 16*kq + 4*b + r: lane (li, kq) ends up holding the 16 consecutive channels
+// 16*kq .. 16*kq+15 of activation row li -- one 16-byte int8 store.
+template <int TM, int TN, bool QUANT>
+__global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) {
+  constexpr int WAVES_M = TM / 64;
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WTN = TN / WAVES_N;  // activation rows per wave
+  constexpr int FN = WTN / 16;
+  constexpr int LA = TM * 64, LB = TN * 64;
+  constexpr int RA = TM / 64, RB = TN / 64;  // 16-byte loads per thread per step
+  static_assert(WAVES_M * WAVES_N == 4 && FN >= 1 && RA >= 1 && RB >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) int8_t lds[2][LA + LB];
+  __shared__ float red[4];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, kq = lane >> 4;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const float t = load_scale(a.ws) * load_scale(a.xs);
+  float s = 1.0f;
+  if constexpr (QUANT) {
+    s = scale_from_parts(a.parts, a.nparts, red);
+    if (blockIdx.x == 0) write_slot(reinterpret_cast<uint8_t *>(a.out) + a.N * a.OC, s);
+  }
+  const int64_t OC = a.OC, IC = a.IC, N = a.N;
+  const __amdgpu_buffer_rsrc_t wbuf = buffer_of(a.w, static_cast<uint32_t>(OC * IC));
+  const __amdgpu_buffer_rsrc_t xbuf = buffer_of(a.x, static_cast<uint32_t>(N * IC));
+  const __amdgpu_buffer_rsrc_t bbuf = buffer_of(a.bias, a.bias ? static_cast<uint32_t>(OC * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t obuf = buffer_of(a.out, static_cast<uint32_t>(N * OC));
+  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(a.dot, a.dot ? static_cast<uint32_t>(N * OC * 4) : 0u);
+  const bool has_bias = a.bias != nullptr;
+
+  const int64_t tiles_o = (OC + TM - 1) / TM;
+  const int64_t tiles = tiles_o * ((N + TN - 1) / TN);
+  const int ksteps = static_cast<int>((IC + 63) / 64);
+  const int lrow = tid >> 2, lchunk = tid & 3;  // this thread's load slot: row lrow (+64j), chunk lchunk
+
+  auto swz = [](int r, int c) { return r * 64 + 16 * (c ^ (((r >> 2) ^ (r >> 4)) & 3)); };
+
+  float m = 0.0f;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int64_t o0 = (tile % tiles_o) * TM;
+    const int64_t n0 = (tile / tiles_o) * TN;
+    v4i ra[RA], rb[RB];
+    auto gload = [&](int ks) {
+      const int64_t k = static_cast<int64_t>(ks) * 64 + 16 * lchunk;
+      const bool kok = k < IC;
+#pragma unroll
+      for (int j = 0; j < RA; ++j) {
+        const int64_t o = o0 + lrow + 64 * j;
+        ra[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            wbuf, kok && o < OC ? static_cast<uint32_t>(o * IC + k) : kOutOfRange, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        const int64_t n = n0 + lrow + 64 * j;
+        rb[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            xbuf, kok && n < N ? static_cast<uint32_t>(n * IC + k) : kOutOfRange, 0, 0);
+      }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < RA; ++j) *reinterpret_cast<v4i *>(&lds[buf][swz(lrow + 64 * j, lchunk)]) = ra[j];
+#pragma unroll
+      for (int j = 0; j < RB; ++j) *reinterpret_cast<v4i *>(&lds[buf][LA + swz(lrow + 64 * j, lchunk)]) = rb[j];
+    };
+
+    v4i acc[FN][4];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[fn][b] = v4i{0, 0, 0, 0};
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int ks = 0; ks < ksteps; ++ks) {
+      const int buf = ks & 1;
+      const bool more = ks + 1 < ksteps;
+      if (more) gload(ks + 1);
+      v4i af[4], bf[FN];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int r = wm * 64 + 16 * (li >> 2) + 4 * b + (li & 3);
+        af[b] = *reinterpret_cast<const v4i *>(&lds[buf][swz(r, kq)]);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int r = wn * WTN + 16 * fn + li;
+        bf[fn] = *reinterpret_cast<const v4i *>(&lds[buf][LA + swz(r, kq)]);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[fn][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[b], bf[fn], acc[fn][b], 0, 0, 0);
+      if (more) lstore(buf ^ 1);
+      __syncthreads();
+    }
+
+    // Epilogue: lane (li, kq) holds channels og .. og+15 of activation row n.
+    const int64_t og = o0 + wm * 64 + 16 * kq;
+    float bv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      bv[j] = has_bias ? __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                             bbuf, og + j < OC ? static_cast<uint32_t>(4 * (og + j)) : kOutOfRange, 0, 0))
+                       : 0.0f;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int64_t n = n0 + wn * WTN + 16 * fn + li;
+      const bool n_ok = n < N;
+      float v[16];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[4 * b + r] = value_of(acc[fn][b][r], t, bv[4 * b + r], has_bias, a.relu);
+      if constexpr (!QUANT) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (n_ok && og + j < OC) m = fmaxf(m, fabsf(v[j]));
+      } else {
+        if (a.vec) {
+          v4i pk;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            pk[b] = pack4(quant(v[4 * b], s), quant(v[4 * b + 1], s), quant(v[4 * b + 2], s), quant(v[4 * b + 3], s));
+          const uint32_t off = n_ok && og < OC ? static_cast<uint32_t>(n * OC + og) : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(pk, obuf, off, 0, 0);
+          if (a.dot) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              __builtin_amdgcn_raw_buffer_store_b128(acc[fn][b], dbuf, off == kOutOfRange ? kOutOfRange : 4 * (off + 4 * b),
+                                                     0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const uint32_t off = n_ok && og + j < OC ? static_cast<uint32_t>(n * OC + og + j) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(quant(v[j], s)), obuf, off, 0, 0);
+            if (a.dot)
+              __builtin_amdgcn_raw_buffer_store_b32(acc[fn][j >> 2][j & 3], dbuf, off == kOutOfRange ? kOutOfRange : 4 * off,
+                                                    0, 0);
+          }
+        }
+      }
+    }
+  }
+  if constexpr (!QUANT) {
+    m = block_max(m, red);
+    if (threadIdx.x == 0) a.parts[blockIdx.x] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+constexpr int kVariants = 5;
+
+template <int TM, int TN>
+int launch_mfma(MatArgs a, hipStream_t stream) {
+  const int64_t tiles = ((a.OC + TM - 1) / TM) * ((a.N + TN - 1) / TN);
+  const int g = parts_for(tiles);
+  a.nparts = g;
+  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, false>), dim3(g), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, true>), dim3(g), dim3(kThreads), 0, stream, a);
+  return hip_status();
+}
+
+int launch_plain(MatArgs a, hipStream_t stream) {
+  const int g = parts_for((a.N * a.OC + kThreads - 1) / kThreads);
+  a.nparts = g;
+  hipLaunchKernelGGL(i8s_mm_plain_kernel<false>, dim3(g), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(i8s_mm_plain_kernel<true>, dim3(g), dim3(kThreads), 0, stream, a);
+  return hip_status();
+}
+
+// Tile (channels x rows): 2 = 128 x 128, 3 = 64 x 128, 4 = 64 x 256, 5 = 128 x 64.
+int auto_variant(int64_t OC, int64_t IC, int64_t N) {
+  if (IC % 16 != 0) return 1;
+  if (OC <= 64) return N >= 256 ? 4 : 3;
+  const int64_t big = ((OC + 127) / 128) * ((N + 127) / 128);
+  return big >= 256 ? 2 : 5;
+}
+
+int check_mm(const uint8_t *w, int64_t OC, int64_t IC, const uint8_t *x, int64_t N, const float *bias,
+             const uint8_t *out, const int32_t *dot_out, void *workspace, size_t workspace_bytes) {
+  if (!w || !x || !out || OC < 0 || IC < 0 || N < 0) return I2S_EINVAL;
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(out, 16)) return I2S_EINVAL;
+  if ((bias && !aligned(bias, 4)) || (dot_out && !aligned(dot_out, 4))) return I2S_EINVAL;
+  if (IC > I8S_MAX_IC) return I2S_ERANGE;
+  if (OC * IC >= kMaxBytes || N * IC >= kMaxBytes || N * OC >= kMaxBytes / 4) return I2S_ERANGE;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < kMaxParts * sizeof(float)) return I2S_EWORKSPACE;
+  return I2S_OK;
+}
+
+}  // namespace
+
+extern "C" size_t i8s_bytes(int64_t n) { return n < 0 ? 0 : static_cast<size_t>(n) + I8S_SCALE_SLOT; }
+
+extern "C" size_t i8s_workspace_bytes(void) { return kMaxParts * sizeof(float); }
+
+extern "C" int i8s_variants(void) { return kVariants; }
+
+extern "C" int i8s_mul_mat_add_variant(int64_t OC, int64_t IC, int64_t N) { return auto_variant(OC, IC, N); }
+
+extern "C" int i8s_quantize(const float *x, int64_t n, uint8_t *out, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  if ((!x && n != 0) || !out || n < 0 || !aligned(x, 16) || !aligned(out, 16)) return I2S_EINVAL;
+  if (n >= kMaxBytes) return I2S_ERANGE;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < kMaxParts * sizeof(float)) return I2S_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int g = parts_for((n / 16 + kThreads - 1) / kThreads);
+  float *parts = static_cast<float *>(workspace);
+  hipLaunchKernelGGL(i8s_absmax_kernel, dim3(g), dim3(kThreads), 0, s, x, n, parts);
+  hipLaunchKernelGGL(i8s_quantize_kernel, dim3(g), dim3(kThreads), 0, s, x, n, parts, g, out);
+  return hip_status();
+}
+
+extern "C" int i8s_dequantize(const uint8_t *t, int64_t n, float *y, void *stream) {
+  if (!t || (!y && n != 0) || n < 0 || !aligned(t, 16) || !aligned(y, 16)) return I2S_EINVAL;
+  if (n >= kMaxBytes / 4) return I2S_ERANGE;
+  const int g = parts_for((n / 16 + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(i8s_dequantize_kernel, dim3(g), dim3(kThreads), 0, static_cast<hipStream_t>(stream), t, n, y);
+  return hip_status();
+}
+
+extern "C" int i8s_mul_mat_add_ex(const uint8_t *w, int64_t OC, int64_t IC, const uint8_t *x, int64_t N,
+                                  const float *bias, int relu, uint8_t *out, int32_t *dot_out, int variant,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  const int st = check_mm(w, OC, IC, x, N, bias, out, dot_out, workspace, workspace_bytes);
+  if (st != I2S_OK) return st;
+  if (variant < 0 || variant > kVariants) return I2S_EKERNEL;
+  if (variant == 0) variant = auto_variant(OC, IC, N);
+  if (variant >= 2 && IC % 16 != 0) return I2S_EKERNEL;
+  MatArgs a;
+  a.w = reinterpret_cast<const int8_t *>(w);
+  a.x = reinterpret_cast<const int8_t *>(x);
+  a.ws = w + OC * IC;
+  a.xs = x + N * IC;
+  a.bias = bias;
+  a.parts = static_cast<float *>(workspace);
+  a.out = reinterpret_cast<int8_t *>(out);
+  a.dot = dot_out;
+  a.OC = OC;
+  a.IC = IC;
+  a.N = N;
+  a.nparts = 0;
+  a.relu = relu ? 1 : 0;
+  a.vec = (OC % 16 == 0) && (!dot_out || aligned(dot_out, 16));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (variant) {
+    case 1: return launch_plain(a, s);
+    case 2: return launch_mfma<128, 128>(a, s);
+    case 3: return launch_mfma<64, 128>(a, s);
+    case 4: return launch_mfma<64, 256>(a, s);
+    default: return launch_mfma<128, 64>(a, s);
+  }
+}
+
+extern "C" int i8s_mul_mat_add(const uint8_t *w, int64_t OC, int64_t IC, const uint8_t *x, int64_t N,
+                               const float *bias, uint8_t *out, void *workspace, size_t workspace_bytes, void *stream) {
+  return i8s_mul_mat_add_ex(w, OC, IC, x, N, bias, 0, out, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+extern "C" int i8s_mul_mat_add_relu(const uint8_t *w, int64_t OC, int64_t IC, const uint8_t *x, int64_t N,
+                                    const float *bias, uint8_t *out, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  return i8s_mul_mat_add_ex(w, OC, IC, x, N, bias, 1, out, nullptr, 0, workspace, workspace_bytes, stream);
+}
