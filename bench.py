@@ -24,6 +24,12 @@ Measurement:
   * cpu_baseline: the CPU oracle (plain scalar C, one thread) on the same
     workload, repeated for about --cpu-seconds.
 
+--workload encoder_mlp times one I8_S encoder block MLP instead (stage 3 of a
+4-second clip: FC1 256 -> 1024 with bias and ReLU, then FC2 1024 -> 256 with
+bias, 6000 positions, I8_S in and out: i8s_mul_mat_add_relu then
+i8s_mul_mat_add, four launches); its roofline line is the FC1 op (both of its
+passes) against HBM.
+
 --workload decode_layer times one Qwen2-1.5B decoder layer's seven ternary
 projections at N = 1 instead (q/k/v grouped with their F32 biases, o,
 gate/up grouped, down: four launches), rotating over 28 layers of weights
@@ -51,6 +57,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8.0 TB/s
 INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
 ROTATE_BYTES = 512 << 20
 KERNEL_SRC = os.path.join(ROOT, "ternary_weight_integer_amd", "csrc", "i2s.hip")
+KERNEL_SRC_I8S = os.path.join(ROOT, "ternary_weight_integer_amd", "csrc", "i8s.hip")
 
 
 def parse_args(argv=None):
@@ -59,7 +66,8 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="decode_up",
-                   choices=["decode_up", "prefill_gate", "down_small_batch", "small", "decode_layer"])
+                   choices=["decode_up", "prefill_gate", "down_small_batch", "small", "decode_layer", "encoder_mlp"])
+    p.add_argument("--stage", type=int, default=3, help="encoder stage of --workload encoder_mlp (0..6)")
     p.add_argument("--copies", type=int, default=0, help="weight copies to rotate over (0 = enough for 512 MiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -80,8 +88,8 @@ def make_case(name):
     }[name]()
 
 
-def kernel_source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_digest(workload: str = "") -> str:
+    with open(KERNEL_SRC_I8S if workload == "encoder_mlp" else KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -94,7 +102,7 @@ def measured_traffic(workload: str):
     text = open(path).read()
     m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9.]+)", text, re.M)
     m_h = re.search(r"^kernel_source_sha256_16:\s*([0-9a-f]+)", text, re.M)
-    if not m_b or not m_h or m_h.group(1) != kernel_source_digest():
+    if not m_b or not m_h or m_h.group(1) != kernel_source_digest(workload):
         return None
     return float(m_b.group(1))
 
@@ -266,6 +274,121 @@ def bench_layer(args, torch, i2s):
     return out
 
 
+def bench_encoder(args, torch):
+    """One I8_S encoder block MLP per step: FC1 (+bias, ReLU, requantize) then
+    FC2 (+bias, requantize), FC2 reading FC1's I8_S output.  The inputs stay
+    hot in the Infinity Cache across steps, as they are when the previous op
+    of the block has just written them."""
+    from ternary_weight_integer_amd import i8s, workloads
+    dev = torch.device("cuda:0")
+    case = workloads.encoder_mlp_case(stage=args.stage)
+    C, N, H = case.C, case.N, case.w1.shape[0]
+    W1 = i8s.i8s_tensor(case.w1, case.w1_scale, dev)
+    W2 = i8s.i8s_tensor(case.w2, case.w2_scale, dev)
+    X = i8s.i8s_tensor(case.x, case.x_scale, dev)
+    b1, b2 = torch.from_numpy(case.b1).to(dev), torch.from_numpy(case.b2).to(dev)
+    Hb = torch.empty(i8s.i8s_bytes(N * H), dtype=torch.uint8, device=dev)
+    Yb = torch.empty(i8s.i8s_bytes(N * C), dtype=torch.uint8, device=dev)
+    ws1, ws2 = i8s.new_workspace(dev), i8s.new_workspace(dev)
+
+    def step():
+        i8s.i8s_mul_mat_add_relu(W1, H, C, X, N, b1, out=Hb, workspace=ws1)
+        i8s.i8s_mul_mat_add(W2, C, H, Hb, N, b2, out=Yb, workspace=ws2)
+
+    def fc1():
+        i8s.i8s_mul_mat_add_relu(W1, H, C, X, N, b1, out=Hb, workspace=ws1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    h_eager, y_eager = Hb.clone(), Yb.clone()
+    K_steps = args.steps
+    if args.eager:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K_steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        step_ms, kern_us, wall = e0.elapsed_time(e1) / K_steps, None, None
+    else:
+        g_step = graph_of(lambda: [step() for _ in range(K_steps)], torch)
+        n_kern = 256
+        g_kern = graph_of(lambda: [fc1() for _ in range(n_kern)], torch)
+        g_step.replay()
+        g_kern.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        t0 = time.perf_counter()
+        ev[0].record()
+        g_step.replay()
+        ev[1].record()
+        g_kern.replay()
+        ev[2].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = ev[0].elapsed_time(ev[1]) / K_steps
+        kern_us = ev[1].elapsed_time(ev[2]) * 1e3 / n_kern
+    if not (torch.equal(Hb, h_eager) and torch.equal(Yb, y_eager)):
+        raise RuntimeError("graph replay result differs from the eager result")
+    slot = i8s.I8S_SCALE_SLOT
+    fc1_bytes = H * C + N * C + 4 * H + N * H + 3 * slot
+    fc2_bytes = C * H + N * H + 4 * C + N * C + 3 * slot
+    ops = 2 * 2 * N * H * C
+    out = {
+        "metric": METRIC,
+        "value": round((fc1_bytes + fc2_bytes) / (step_ms * 1e-3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": case.name, "stage": case.stage, "C": C, "hidden": H, "N": N,
+                   "launches_per_step": 4, "variant_fc1": i8s.i8s_mul_mat_add_variant(H, C, N),
+                   "variant_fc2": i8s.i8s_mul_mat_add_variant(C, H, N),
+                   "timing": "eager" if args.eager else "hip_graph",
+                   "value_is": "algorithmic bytes (weights, I8_S input and output, biases) per second"},
+        "int8_tops": round(ops / (step_ms * 1e-3) / 1e12, 4),
+        "wall_s": None if wall is None else round(wall, 4),
+    }
+    if kern_us is not None:
+        achieved = fc1_bytes / (kern_us * 1e-6) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                           "kernel": "i8s_mm_mfma_kernel (FC1: max|f| pass + requantize pass)",
+                           "kernel_us": round(kern_us, 4), "alg_bytes_per_launch": fc1_bytes,
+                           "int8_tops": round(2 * N * H * C / (kern_us * 1e-6) / 1e12, 3)}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_encoder(case, args.cpu_seconds, fc1_bytes + fc2_bytes)
+    return out
+
+
+def cpu_baseline_encoder(case, seconds: float, step_bytes: int):
+    import oracle
+    H, C, N = case.w1.shape[0], case.C, case.N
+    W1 = oracle.i8s_make(case.w1, case.w1_scale)
+    W2 = oracle.i8s_make(case.w2, case.w2_scale)
+    X = oracle.i8s_make(case.x, case.x_scale)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        h = oracle.i8s_mul_mat_add(W1, H, C, X, N, case.b1, True)
+        oracle.i8s_mul_mat_add(W2, C, H, h, N, case.b2, False)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(step_bytes * calls / el / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full block MLPs ({case.name}, FC1+ReLU and FC2 with requantization, scalar C, "
+                      f"1 thread) in {el:.1f} s",
+            "cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0)),
+            "ms_per_call": round(el / calls * 1e3, 3)}
+
+
 def cpu_baseline_layer(case, seconds: float):
     import oracle
     shp_x = {"q": case.x_hidden, "k": case.x_hidden, "v": case.x_hidden, "o": case.x_attn, "gate": case.x_attn,
@@ -308,6 +431,9 @@ def main(argv=None):
         return 1
     if args.workload == "decode_layer":
         print(json.dumps(bench_layer(args, torch, i2s)), flush=True)
+        return 0
+    if args.workload == "encoder_mlp":
+        print(json.dumps(bench_encoder(args, torch)), flush=True)
         return 0
     dev = torch.device("cuda:0")
     case = make_case(args.workload)

@@ -32,6 +32,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;          // every kernel here: 4 wave64s
 constexpr int kMaxParts = 1024;        // workgroups of a two-pass launch (partial maxima)
+constexpr int kResidentGroups = 512;   // MFMA contraction grid: 2 workgroups per CU
 constexpr int64_t kMaxBytes = 0x7fff0000;  // largest tensor a buffer descriptor covers here
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // buffer offset beyond every descriptor range
 constexpr int kBufferFlags = 0x00020000;       // raw buffer, 32-bit data format
@@ -89,6 +90,31 @@ __device__ inline int quant(float v, float s) {
   float r = roundf(v / s);
   r = fminf(fmaxf(r, -127.0f), 127.0f);
   return static_cast<int>(r);
+}
+
+// The same q for 16 values at once, with the division replaced by a multiply
+// by inv = 1/s (correctly rounded) wherever that provably gives the same q.
+// The values are within the tensor's range (|v| <= amax, so |v/s| <= 127.0001;
+// ReLU is applied before), r = fl(v * inv) is within |v/s| * 2^-23 (1.6e-5)
+// of v/s, and fl(v/s) within 2^-18 of it.  So if the fraction of |r| is more
+// than 2^-14 from 1/2, r and fl(v/s) lie strictly between the same two
+// half-integers: both round to the integer nearest r, whatever the tie rule,
+// and rint(r) (ties to even, one instruction) gives q, already within +-127.
+// A group with any value nearer a tie takes the exact division for all 16.
+constexpr float kTieMargin = 6.103515625e-05f;  // 2^-14
+
+__device__ inline void quant16(const float (&v)[16], float s, float inv, int (&q)[16]) {
+  bool near = false;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float r = v[j] * inv;
+    near |= fabsf(__builtin_amdgcn_fractf(fabsf(r)) - 0.5f) <= kTieMargin;
+    q[j] = static_cast<int>(rintf(r));
+  }
+  if (near) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) q[j] = quant(v[j], s);
+  }
 }
 
 // Four int8 values (each in [-127, 127]) packed little-endian into one dword.
@@ -240,13 +266,20 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_plain_kernel(const MatArgs a)
 //
 // A workgroup owns TM output channels x TN activation rows per tile and walks
 // tiles with a grid stride (the grid is at most kMaxParts workgroups, one
-// partial maximum each).  Four waves; each wave owns 64 channels x TN/WAVES_N
-// rows, i.e. 4 channel blocks x FN row blocks of 16 x 16.  The k loop steps
-// 64 bytes: all 256 threads load the tile's rows (four consecutive lanes read
-// one row's 64 contiguous bytes), store them to LDS, and every wave reads its
-// MFMA operands from LDS; two LDS stages, one barrier per step.
+// partial maximum each; the host makes it a multiple of the number of channel
+// blocks when it can, so that a workgroup keeps one channel block).  Four
+// waves; each wave owns 64 channels x TN/WAVES_N rows, i.e. 4 channel blocks x
+// FN row blocks of 16 x 16.
 //
-// LDS layout of a stage: row r's 16-byte chunk c at r*64 + 16*(c ^ sw(r)),
+// Work items are (tile, K chunk) pairs, a chunk being KS steps of 64 bytes.
+// For each item all 256 threads load the chunk's rows into registers (four
+// consecutive lanes read one row's 64 contiguous bytes of a step), then store
+// them to LDS; right after the store they issue the next item's loads -- the
+// next chunk, or the first chunk of the next tile -- so that memory latency
+// overlaps this item's MFMAs and the epilogue.  One LDS buffer, two barriers
+// per item.
+//
+// LDS layout of a step: row r's 16-byte chunk c at r*64 + 16*(c ^ sw(r)),
 // sw(r) = ((r >> 2) ^ (r >> 4)) & 3.  Sixteen lanes reading chunk c of rows
 // r0..r0+15 (activation operand) or of rows {16p + 4b + j} (weight operand,
 // below) then touch sixteen different 16-byte bank groups, and four lanes
@@ -257,130 +290,241 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_plain_kernel(const MatArgs a)
 // lane (li, kq) in block b is MFMA row 4*kq + r, i.e. channel
 // 16*kq + 4*b + r: lane (li, kq) ends up holding the 16 consecutive channels
 // 16*kq .. 16*kq+15 of activation row li -- one 16-byte int8 store.
-template <int TM, int TN, bool QUANT>
+//
+// Pass 1 needs max|f| only.  For a fixed channel, f = max(fl(fl(acc) * t) +
+// b, lo) is a monotone function of acc (every rounding is monotone; the
+// direction is the sign of t), so max|f| over a set of rows is reached at the
+// smallest or the largest acc among them.  Each lane therefore keeps, per
+// channel, the min and max of its valid accumulators (two integer operations
+// per output) and evaluates f at those two points when its channel block
+// changes or at the end -- exactly the maximum the definition asks for.
+//
+// The bias is always added (0 for a missing bias: adding +0 only turns a -0
+// into +0, which neither |f| nor q can see), and lo is 0 for the relu form and
+// -inf otherwise, so the value has no data-dependent branch.
+template <int TM, int TN, int KS, bool QUANT>
 __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) {
   constexpr int WAVES_M = TM / 64;
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WTN = TN / WAVES_N;  // activation rows per wave
   constexpr int FN = WTN / 16;
-  constexpr int LA = TM * 64, LB = TN * 64;
+  constexpr int LA = TM * 64, LB = TN * 64;  // bytes of one 64-byte step of each operand
+  constexpr int LS = LA + LB;
   constexpr int RA = TM / 64, RB = TN / 64;  // 16-byte loads per thread per step
   static_assert(WAVES_M * WAVES_N == 4 && FN >= 1 && RA >= 1 && RB >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) int8_t lds[2][LA + LB];
+  __shared__ __attribute__((aligned(16))) int8_t lds[KS * LS];
+  __shared__ __attribute__((aligned(16))) float lbias[TM];  // bias of the item's channel block
   __shared__ float red[4];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kq = lane >> 4;
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
-  const float t = load_scale(a.ws) * load_scale(a.xs);
-  float s = 1.0f;
-  if constexpr (QUANT) {
-    s = scale_from_parts(a.parts, a.nparts, red);
-    if (blockIdx.x == 0) write_slot(reinterpret_cast<uint8_t *>(a.out) + a.N * a.OC, s);
-  }
-  const int64_t OC = a.OC, IC = a.IC, N = a.N;
-  const __amdgpu_buffer_rsrc_t wbuf = buffer_of(a.w, static_cast<uint32_t>(OC * IC));
-  const __amdgpu_buffer_rsrc_t xbuf = buffer_of(a.x, static_cast<uint32_t>(N * IC));
-  const __amdgpu_buffer_rsrc_t bbuf = buffer_of(a.bias, a.bias ? static_cast<uint32_t>(OC * 4) : 0u);
-  const __amdgpu_buffer_rsrc_t obuf = buffer_of(a.out, static_cast<uint32_t>(N * OC));
-  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(a.dot, a.dot ? static_cast<uint32_t>(N * OC * 4) : 0u);
-  const bool has_bias = a.bias != nullptr;
+  const int OC = static_cast<int>(a.OC), IC = static_cast<int>(a.IC), N = static_cast<int>(a.N);
+  const __amdgpu_buffer_rsrc_t wbuf = buffer_of(a.w, static_cast<uint32_t>(a.OC * a.IC));
+  const __amdgpu_buffer_rsrc_t xbuf = buffer_of(a.x, static_cast<uint32_t>(a.N * a.IC));
+  const __amdgpu_buffer_rsrc_t bbuf = buffer_of(a.bias, a.bias ? static_cast<uint32_t>(a.OC * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t obuf = buffer_of(a.out, static_cast<uint32_t>(a.N * a.OC));
+  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(a.dot, a.dot ? static_cast<uint32_t>(a.N * a.OC * 4) : 0u);
 
-  const int64_t tiles_o = (OC + TM - 1) / TM;
-  const int64_t tiles = tiles_o * ((N + TN - 1) / TN);
-  const int ksteps = static_cast<int>((IC + 63) / 64);
+  // Tiles: channel block ob = tile % tiles_o, row block nb = tile / tiles_o;
+  // this workgroup takes tiles blockIdx.x, +G, +2G, ...  Cursors step through
+  // them (and through the K chunks of each) without divisions.
+  const int tiles_o = (OC + TM - 1) / TM;
+  const int tiles = tiles_o * ((N + TN - 1) / TN);
+  const int G = static_cast<int>(gridDim.x);
+  const int step_o = G % tiles_o, step_n = G / tiles_o;
+  const int kchunks = IC > 0 ? (IC + 64 * KS - 1) / (64 * KS) : 1;
+  const int my_tiles = static_cast<int>(blockIdx.x) < tiles ? (tiles - static_cast<int>(blockIdx.x) + G - 1) / G : 0;
+  const int items = my_tiles * kchunks;
+  struct Cursor {
+    int ob, nb, kc;
+  };
+  auto advance = [&](Cursor &c) {
+    if (++c.kc < kchunks) return;
+    c.kc = 0;
+    c.ob += step_o;
+    c.nb += step_n;
+    if (c.ob >= tiles_o) {
+      c.ob -= tiles_o;
+      c.nb += 1;
+    }
+  };
+  const Cursor first = {static_cast<int>(blockIdx.x) % tiles_o, static_cast<int>(blockIdx.x) / tiles_o, 0};
   const int lrow = tid >> 2, lchunk = tid & 3;  // this thread's load slot: row lrow (+64j), chunk lchunk
 
   auto swz = [](int r, int c) { return r * 64 + 16 * (c ^ (((r >> 2) ^ (r >> 4)) & 3)); };
 
-  float m = 0.0f;
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    const int64_t o0 = (tile % tiles_o) * TM;
-    const int64_t n0 = (tile / tiles_o) * TN;
-    v4i ra[RA], rb[RB];
-    auto gload = [&](int ks) {
-      const int64_t k = static_cast<int64_t>(ks) * 64 + 16 * lchunk;
+  // Each item's loads include the bias of its channel block (thread t < TM
+  // loads channel o0 + t; 0 past OC or without a bias), staged through LDS
+  // with the operands so that no epilogue waits on global memory.
+  v4i ra[KS][RA], rb[KS][RB];
+  float rbias = 0.0f;
+  auto gload = [&](const Cursor &c) {
+    const int o0 = c.ob * TM, n0 = c.nb * TN;
+    if (tid < TM)
+      rbias = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          bbuf, o0 + tid < OC ? static_cast<uint32_t>(4 * (o0 + tid)) : kOutOfRange, 0, 0));
+    const int kbase = c.kc * (64 * KS) + 16 * lchunk;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const int k = kbase + 64 * st;
       const bool kok = k < IC;
 #pragma unroll
       for (int j = 0; j < RA; ++j) {
-        const int64_t o = o0 + lrow + 64 * j;
-        ra[j] = __builtin_amdgcn_raw_buffer_load_b128(
-            wbuf, kok && o < OC ? static_cast<uint32_t>(o * IC + k) : kOutOfRange, 0, 0);
+        const int o = o0 + lrow + 64 * j;
+        ra[st][j] = __builtin_amdgcn_raw_buffer_load_b128(
+            wbuf, kok && o < OC ? static_cast<uint32_t>(o) * static_cast<uint32_t>(IC) + k : kOutOfRange, 0, 0);
       }
 #pragma unroll
       for (int j = 0; j < RB; ++j) {
-        const int64_t n = n0 + lrow + 64 * j;
-        rb[j] = __builtin_amdgcn_raw_buffer_load_b128(
-            xbuf, kok && n < N ? static_cast<uint32_t>(n * IC + k) : kOutOfRange, 0, 0);
+        const int n = n0 + lrow + 64 * j;
+        rb[st][j] = __builtin_amdgcn_raw_buffer_load_b128(
+            xbuf, kok && n < N ? static_cast<uint32_t>(n) * static_cast<uint32_t>(IC) + k : kOutOfRange, 0, 0);
       }
-    };
-    auto lstore = [&](int buf) {
+    }
+  };
+  auto lstore = [&]() {
+    if (tid < TM) lbias[tid] = rbias;
 #pragma unroll
-      for (int j = 0; j < RA; ++j) *reinterpret_cast<v4i *>(&lds[buf][swz(lrow + 64 * j, lchunk)]) = ra[j];
+    for (int st = 0; st < KS; ++st) {
 #pragma unroll
-      for (int j = 0; j < RB; ++j) *reinterpret_cast<v4i *>(&lds[buf][LA + swz(lrow + 64 * j, lchunk)]) = rb[j];
-    };
+      for (int j = 0; j < RA; ++j) *reinterpret_cast<v4i *>(&lds[st * LS + swz(lrow + 64 * j, lchunk)]) = ra[st][j];
+#pragma unroll
+      for (int j = 0; j < RB; ++j) *reinterpret_cast<v4i *>(&lds[st * LS + LA + swz(lrow + 64 * j, lchunk)]) = rb[st][j];
+    }
+  };
+  // Bias of this lane's 16 channels, from LDS (the current item's block).
+  auto lds_bias = [&](float (&bv)[16]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 b4 = *reinterpret_cast<const float4 *>(&lbias[wm * 64 + 16 * kq + 4 * j]);
+      bv[4 * j] = b4.x;
+      bv[4 * j + 1] = b4.y;
+      bv[4 * j + 2] = b4.z;
+      bv[4 * j + 3] = b4.w;
+    }
+  };
 
-    v4i acc[FN][4];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[fn][b] = v4i{0, 0, 0, 0};
+  // Prologue: the first item's loads go out before anything waits on memory
+  // (the in-band scales, and in pass 2 the partial maxima), so that those
+  // latencies overlap.
+  Cursor lc = first, cc = first;
+  if (items > 0) gload(lc);
+  const float ws = load_scale(a.ws), xs = load_scale(a.xs);
+  const float lo = a.relu ? 0.0f : -INFINITY;
+  float s = 1.0f, inv = 1.0f;
+  if constexpr (QUANT) {
+    s = scale_from_parts(a.parts, a.nparts, red);
+    inv = 1.0f / s;
+    if (blockIdx.x == 0) write_slot(reinterpret_cast<uint8_t *>(a.out) + a.N * a.OC, s);
+  }
+  const float t = ws * xs;
 
-    gload(0);
-    lstore(0);
+  v4i acc[FN][4];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[fn][b] = v4i{0, 0, 0, 0};
+
+  // Pass 1 state: per-channel extremes of the valid accumulators of the
+  // current channel block, and the running max|f|.
+  int32_t amx[16], amn[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    amx[j] = INT32_MIN;
+    amn[j] = INT32_MAX;
+  }
+  int cur_ob = -1;
+  float m = 0.0f;
+  float bcur[16];  // bias of the channel block being accumulated
+  auto flush = [&]() {
+    const float(&bv)[16] = bcur;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (amx[j] >= amn[j]) {  // the lane saw a valid row of this channel
+        const float f1 = fmaxf(static_cast<float>(amx[j]) * t + bv[j], lo);
+        const float f2 = fmaxf(static_cast<float>(amn[j]) * t + bv[j], lo);
+        m = fmaxf(m, fmaxf(fabsf(f1), fabsf(f2)));
+      }
+      amx[j] = INT32_MIN;
+      amn[j] = INT32_MAX;
+    }
+  };
+
+  for (int it = 0; it < items; ++it) {
+    __syncthreads();  // every wave is done reading the previous item from LDS
+    lstore();
     __syncthreads();
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const int buf = ks & 1;
-      const bool more = ks + 1 < ksteps;
-      if (more) gload(ks + 1);
+    if (it + 1 < items) {
+      advance(lc);
+      gload(lc);
+    }
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
       v4i af[4], bf[FN];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int r = wm * 64 + 16 * (li >> 2) + 4 * b + (li & 3);
-        af[b] = *reinterpret_cast<const v4i *>(&lds[buf][swz(r, kq)]);
+        af[b] = *reinterpret_cast<const v4i *>(&lds[st * LS + swz(r, kq)]);
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int r = wn * WTN + 16 * fn + li;
-        bf[fn] = *reinterpret_cast<const v4i *>(&lds[buf][LA + swz(r, kq)]);
+        bf[fn] = *reinterpret_cast<const v4i *>(&lds[st * LS + LA + swz(r, kq)]);
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[fn][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[b], bf[fn], acc[fn][b], 0, 0, 0);
-      if (more) lstore(buf ^ 1);
-      __syncthreads();
     }
+    const Cursor ec = cc;
+    advance(cc);
+    if (ec.kc + 1 < kchunks) continue;
 
-    // Epilogue: lane (li, kq) holds channels og .. og+15 of activation row n.
-    const int64_t og = o0 + wm * 64 + 16 * kq;
-    float bv[16];
+    // Epilogue of the tile: lane (li, kq) holds channels og .. og+15 of
+    // activation row n.
+    const int o0 = ec.ob * TM, n0 = ec.nb * TN;
+    const int og = o0 + wm * 64 + 16 * kq;
+    if constexpr (!QUANT) {
+      if (ec.ob != cur_ob) {
+        if (cur_ob >= 0) flush();
+        cur_ob = ec.ob;
+        lds_bias(bcur);
+      }
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      bv[j] = has_bias ? __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                             bbuf, og + j < OC ? static_cast<uint32_t>(4 * (og + j)) : kOutOfRange, 0, 0))
-                       : 0.0f;
+      for (int fn = 0; fn < FN; ++fn) {
+        if (n0 + wn * WTN + 16 * fn + li < N) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int64_t n = n0 + wn * WTN + 16 * fn + li;
-      const bool n_ok = n < N;
-      float v[16];
+          for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+            for (int r = 0; r < 4; ++r) {
+              amx[4 * b + r] = max(amx[4 * b + r], acc[fn][b][r]);
+              amn[4 * b + r] = min(amn[4 * b + r], acc[fn][b][r]);
+            }
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[4 * b + r] = value_of(acc[fn][b][r], t, bv[4 * b + r], has_bias, a.relu);
-      if constexpr (!QUANT) {
+        for (int b = 0; b < 4; ++b) acc[fn][b] = v4i{0, 0, 0, 0};
+      }
+    } else {
+      float bv[16];
+      lds_bias(bv);
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (n_ok && og + j < OC) m = fmaxf(m, fabsf(v[j]));
-      } else {
+      for (int fn = 0; fn < FN; ++fn) {
+        const int n = n0 + wn * WTN + 16 * fn + li;
+        const bool n_ok = n < N;
+        float v[16];
+        int q[16];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[4 * b + r] = fmaxf(static_cast<float>(acc[fn][b][r]) * t + bv[4 * b + r], lo);
+        quant16(v, s, inv, q);
+        const uint32_t row = static_cast<uint32_t>(n) * static_cast<uint32_t>(OC);
         if (a.vec) {
           v4i pk;
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            pk[b] = pack4(quant(v[4 * b], s), quant(v[4 * b + 1], s), quant(v[4 * b + 2], s), quant(v[4 * b + 3], s));
-          const uint32_t off = n_ok && og < OC ? static_cast<uint32_t>(n * OC + og) : kOutOfRange;
+          for (int b = 0; b < 4; ++b) pk[b] = pack4(q[4 * b], q[4 * b + 1], q[4 * b + 2], q[4 * b + 3]);
+          const uint32_t off = n_ok && og < OC ? row + og : kOutOfRange;
           __builtin_amdgcn_raw_buffer_store_b128(pk, obuf, off, 0, 0);
           if (a.dot) {
 #pragma unroll
@@ -391,17 +535,20 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
         } else {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const uint32_t off = n_ok && og + j < OC ? static_cast<uint32_t>(n * OC + og + j) : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(quant(v[j], s)), obuf, off, 0, 0);
+            const uint32_t off = n_ok && og + j < OC ? row + og + j : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(q[j]), obuf, off, 0, 0);
             if (a.dot)
               __builtin_amdgcn_raw_buffer_store_b32(acc[fn][j >> 2][j & 3], dbuf, off == kOutOfRange ? kOutOfRange : 4 * off,
                                                     0, 0);
           }
         }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[fn][b] = v4i{0, 0, 0, 0};
       }
     }
   }
   if constexpr (!QUANT) {
+    if (cur_ob >= 0) flush();
     m = block_max(m, red);
     if (threadIdx.x == 0) a.parts[blockIdx.x] = m;
   }
@@ -410,15 +557,25 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
 // ---------------------------------------------------------------------------
 // Host side.
 
-constexpr int kVariants = 5;
+constexpr int kVariants = 8;
 
-template <int TM, int TN>
+template <int TM, int TN, int KS>
 int launch_mfma(MatArgs a, hipStream_t stream) {
-  const int64_t tiles = ((a.OC + TM - 1) / TM) * ((a.N + TN - 1) / TN);
-  const int g = parts_for(tiles);
+  // A multiple of the channel-block count when possible: each workgroup then
+  // keeps one channel block over all of its tiles.
+  // The grid stays within what is resident at once (kResidentGroups), so each
+  // workgroup's prologue is paid once and its tiles stream through the
+  // pipeline.
+  const int64_t tiles_o = (a.OC + TM - 1) / TM, tiles_n = (a.N + TN - 1) / TN;
+  const int64_t cap = kResidentGroups;
+  int g = static_cast<int>(tiles_o * tiles_n < cap ? (tiles_o * tiles_n > 0 ? tiles_o * tiles_n : 1) : cap);
+  if (tiles_o >= 1 && tiles_o <= cap) {
+    const int64_t per = tiles_n < cap / tiles_o ? tiles_n : cap / tiles_o;
+    g = static_cast<int>(tiles_o * (per > 0 ? per : 1));
+  }
   a.nparts = g;
-  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, false>), dim3(g), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, true>), dim3(g), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, false>), dim3(g), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, true>), dim3(g), dim3(kThreads), 0, stream, a);
   return hip_status();
 }
 
@@ -430,12 +587,15 @@ int launch_plain(MatArgs a, hipStream_t stream) {
   return hip_status();
 }
 
-// Tile (channels x rows): 2 = 128 x 128, 3 = 64 x 128, 4 = 64 x 256, 5 = 128 x 64.
+// Tile (channels x rows, 64-byte steps per K chunk): 2 = 128 x 128 x 1, 3 = 64 x 128 x 1,
+// 4 = 128 x 64 x 1, 5 = 128 x 64 x 2, 6 = 64 x 128 x 2, 7 = 128 x 64 x 4, 8 = 64 x 64 x 1.
 int auto_variant(int64_t OC, int64_t IC, int64_t N) {
+  (void)N;
   if (IC % 16 != 0) return 1;
-  if (OC <= 64) return N >= 256 ? 4 : 3;
-  const int64_t big = ((OC + 127) / 128) * ((N + 127) / 128);
-  return big >= 256 ? 2 : 5;
+  if (OC <= 64) return 6;   // 64 x 128 x 2: few channels, many rows
+  if (IC <= 64) return 2;   // 128 x 128 x 1
+  if (IC <= 128) return 5;  // 128 x 64 x 2
+  return 7;                 // 128 x 64 x 4
 }
 
 int check_mm(const uint8_t *w, int64_t OC, int64_t IC, const uint8_t *x, int64_t N, const float *bias,
@@ -506,10 +666,13 @@ extern "C" int i8s_mul_mat_add_ex(const uint8_t *w, int64_t OC, int64_t IC, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
     case 1: return launch_plain(a, s);
-    case 2: return launch_mfma<128, 128>(a, s);
-    case 3: return launch_mfma<64, 128>(a, s);
-    case 4: return launch_mfma<64, 256>(a, s);
-    default: return launch_mfma<128, 64>(a, s);
+    case 8: return launch_mfma<64, 64, 1>(a, s);
+    case 2: return launch_mfma<128, 128, 1>(a, s);
+    case 3: return launch_mfma<64, 128, 1>(a, s);
+    case 4: return launch_mfma<128, 64, 1>(a, s);
+    case 5: return launch_mfma<128, 64, 2>(a, s);
+    case 6: return launch_mfma<64, 128, 2>(a, s);
+    default: return launch_mfma<128, 64, 4>(a, s);
   }
 }
 

@@ -81,6 +81,18 @@ def new_workspace(device) -> torch.Tensor:
     return torch.empty(i8s_workspace_bytes(), dtype=torch.uint8, device=device)
 
 
+def i8s_tensor(q, scale: float, device) -> torch.Tensor:
+    """An I8_S tensor on `device` holding the given int8 values (any shape,
+    C order) and scale: the payload bytes, the F32 scale, 28 zero bytes (the
+    layout of an I8_S tensor read from a checkpoint)."""
+    import numpy as np
+    q = np.ascontiguousarray(q, dtype=np.int8).reshape(-1)
+    buf = np.zeros(q.size + I8S_SCALE_SLOT, dtype=np.uint8)
+    buf[: q.size] = q.view(np.uint8)
+    buf[q.size: q.size + 4] = np.array([scale], dtype="<f4").view(np.uint8)
+    return torch.from_numpy(buf).to(device)
+
+
 def _i8s_tensor(t: torch.Tensor, n: int, name: str) -> int:
     ptr = _dev(t, torch.uint8, name)
     if t.numel() < i8s_bytes(n):

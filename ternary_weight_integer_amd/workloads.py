@@ -182,3 +182,65 @@ def decode_layer_case(seed: int = 0, N: int = 1) -> LayerCase:
     x_ffn = relu(normal(rng, N, 8960, std=0.5))
     return LayerCase(f"decode_layer_qwen2_1p5b_N{N}", w, 0.015, bias, x_hidden, x_attn, x_ffn,
                      {"layers": 28, "N": N})
+
+
+# ---------------------------------------------------------------------------
+# I8_S encoder block MLP ("VibeASR in audio.cpp", Architecture / Encoder):
+# seven stages with strides 1, 2, 2, 4, 5, 5, 8 (3200 samples per frame at
+# 24 kHz) and widths 32 .. 2048; each ConvNeXt-style block ends in
+# FC1 -> ReLU -> FC2.  The FC1 expansion is not given on the pages; the
+# ConvNeXt design's 4x is taken.  Stage s sees samples / (s1 * ... * s_s)
+# positions of a 4-second clip.
+
+ENCODER_CHANNELS = (32, 64, 128, 256, 512, 1024, 2048)
+ENCODER_STRIDES = (1, 2, 2, 4, 5, 5, 8)
+ENCODER_MLP_RATIO = 4
+
+
+@dataclass
+class EncoderMlpCase:
+    name: str
+    stage: int
+    C: int
+    N: int
+    w1: np.ndarray      # int8 [4C][C]  (FC1, output channel = row)
+    w1_scale: float
+    b1: np.ndarray      # f32 [4C]
+    w2: np.ndarray      # int8 [C][4C]  (FC2)
+    w2_scale: float
+    b2: np.ndarray      # f32 [C]
+    x: np.ndarray       # int8 [N][C]   (the block's normed input, already I8_S)
+    x_scale: float
+
+
+def _int8_bell(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    """Bell-shaped int8 values (a normal draw rounded and clipped to +-127)."""
+    return np.clip(np.rint(rng.normal(0.0, std, size=shape)), -127, 127).astype(np.int8)
+
+
+def encoder_positions(stage: int, seconds: float = 4.0, sample_rate: int = 24000) -> int:
+    n = int(round(seconds * sample_rate))
+    for s in ENCODER_STRIDES[: stage + 1]:
+        n //= s
+    return n
+
+
+def encoder_mlp_case(stage: int = 3, seed: int = 0, seconds: float = 4.0) -> EncoderMlpCase:
+    """One block MLP of encoder stage `stage` (default 3: C = 256, 6000
+    positions): int8 weights with std 24 (scales 0.004 / 0.003), biases
+    ~ N(0, 0.1), the input int8 with std 40 plus 0.1% of entries at +-127
+    (scale 0.03); weights drawn before activations."""
+    rng = np.random.default_rng(seed)
+    C = ENCODER_CHANNELS[stage]
+    H = ENCODER_MLP_RATIO * C
+    N = encoder_positions(stage, seconds)
+    w1 = _int8_bell(rng, (H, C), 24.0)
+    b1 = rng.normal(0.0, 0.1, size=H).astype(np.float32)
+    w2 = _int8_bell(rng, (C, H), 24.0)
+    b2 = rng.normal(0.0, 0.1, size=C).astype(np.float32)
+    x = _int8_bell(rng, (N, C), 40.0)
+    k = max(1, x.size // 1000)
+    idx = rng.choice(x.size, size=k, replace=False)
+    x.flat[idx] = np.where(rng.random(k) < 0.5, -127, 127).astype(np.int8)
+    return EncoderMlpCase(name=f"encoder_mlp_stage{stage}_C{C}_N{N}", stage=stage, C=C, N=N,
+                          w1=w1, w1_scale=0.004, b1=b1, w2=w2, w2_scale=0.003, b2=b2, x=x, x_scale=0.03)

@@ -219,3 +219,29 @@ def test_chained_block_mlp():
     assert host(X).tobytes() == rX.tobytes()
     assert host(H).tobytes() == rH.tobytes()
     assert host(Y).tobytes() == rY.tobytes()
+
+
+def test_requantize_near_ties():
+    # Zero activations make every accumulator 0, so f = bias[o] exactly; the
+    # biases sit on and a few floats either side of (k + 1/2) * s for the
+    # tensor scale s = f32(100 / 127) fixed by bias[0] = 100, where the
+    # rounding of the division decides q.
+    OC, IC, N = 1024, 64, 3
+    s = np.float32(np.float32(100.0) / np.float32(127.0))
+    vals = [np.float32(100.0)]
+    rng = np.random.default_rng(2)
+    while len(vals) < OC:
+        k = int(rng.integers(-127, 127))
+        c = np.float32((k + 0.5) * float(s))
+        for d in range(-3, 4):
+            v = c
+            step = np.float32(np.inf) if d > 0 else np.float32(-np.inf)
+            for _ in range(abs(d)):
+                v = np.nextafter(v, step)
+            vals.append(np.float32(v))
+    bias = np.array(vals[:OC], np.float32)
+    W = rand_i8s(rng, OC, IC, 0.01)
+    X = oracle.i8s_make(np.zeros((N, IC), np.int8), 0.5)
+    for v in range(1, i8s.i8s_variants() + 1):
+        for relu in (0, 1):
+            check_mm(W, OC, IC, X, N, bias, relu, v, tag="near ties")
