@@ -67,6 +67,14 @@ def _load():
         lib.oracle_i8s_dequantize.argtypes = [p, i64, p]
         lib.oracle_i8s_mul_mat_add.restype = ctypes.c_int
         lib.oracle_i8s_mul_mat_add.argtypes = [p, i64, i64, p, i64, p, ctypes.c_int, p, p, p]
+        lib.oracle_w8a8_quantize_weight.restype = None
+        lib.oracle_w8a8_quantize_weight.argtypes = [p, i64, i64, p, p]
+        lib.oracle_w8a8_quantize_act.restype = None
+        lib.oracle_w8a8_quantize_act.argtypes = [p, i64, i64, p, p]
+        lib.oracle_w8a8_matmul.restype = None
+        lib.oracle_w8a8_matmul.argtypes = [p, p, i64, p, p, i64, i64, p, p]
+        lib.oracle_w8a8_mul_mat.restype = ctypes.c_int
+        lib.oracle_w8a8_mul_mat.argtypes = [p, p, i64, i64, p, i64, p, p]
         _lib = lib
     return _lib
 
@@ -240,3 +248,57 @@ def i8s_mul_mat_add(w: np.ndarray, OC: int, IC: int, x: np.ndarray, N: int, bias
     if with_f:
         res.append(f)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+# ---------------------------------------------------------------------------
+# Per-channel W8A8 (the NPU page's scheme): int8 weights with per-channel
+# scales, per-row int8 activations, d = aScale * bScale * C.
+
+
+def w8a8_quantize_weight(w: np.ndarray):
+    """(q int8[OC][K], scale f32[OC]) of F32 w[OC][K]."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    OC, K = w.shape
+    q = np.empty((OC, K), dtype=np.int8)
+    s = np.empty(OC, dtype=np.float32)
+    _load().oracle_w8a8_quantize_weight(_ptr(w), OC, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def w8a8_quantize_act(x: np.ndarray):
+    """(q int8[M][K], scale f32[M]) of F32 x[M][K]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.int8)
+    s = np.empty(M, dtype=np.float32)
+    _load().oracle_w8a8_quantize_act(_ptr(x), M, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def w8a8_matmul(a: np.ndarray, ascale: np.ndarray, w: np.ndarray, wscale: np.ndarray, with_c: bool = False):
+    a = np.ascontiguousarray(a, dtype=np.int8)
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    ascale = np.ascontiguousarray(ascale, dtype=np.float32)
+    wscale = np.ascontiguousarray(wscale, dtype=np.float32)
+    M, K = a.shape
+    OC = w.shape[0]
+    assert w.shape[1] == K
+    d = np.empty((M, OC), dtype=np.float32)
+    c = np.empty((M, OC), dtype=np.int32)
+    _load().oracle_w8a8_matmul(_ptr(a), _ptr(ascale), M, _ptr(w), _ptr(wscale), OC, K, _ptr(d), _ptr(c))
+    return (d, c) if with_c else d
+
+
+def w8a8_mul_mat(wq: np.ndarray, wscale: np.ndarray, x: np.ndarray, with_c: bool = False):
+    """F32 d[M][OC] of the whole op on F32 x[M][K] (activations quantized here)."""
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    wscale = np.ascontiguousarray(wscale, dtype=np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    M, K = x.shape
+    OC = wq.shape[0]
+    d = np.empty((M, OC), dtype=np.float32)
+    c = np.empty((M, OC), dtype=np.int32)
+    rc = _load().oracle_w8a8_mul_mat(_ptr(wq), _ptr(wscale), OC, K, _ptr(x), M, _ptr(d), _ptr(c))
+    if rc != 0:
+        raise MemoryError("oracle_w8a8_mul_mat: allocation failed")
+    return (d, c) if with_c else d

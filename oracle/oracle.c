@@ -1,6 +1,7 @@
 /*
  * CPU oracle for the I2_S ternary-weight x int8-activation matmul (W2A8),
- * and for the I8_S per-tensor int8 type with its fused mul_mat_add(_relu).
+ * for the I8_S per-tensor int8 type with its fused mul_mat_add(_relu), and
+ * for the per-channel W8A8 matmul.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
  * definition that the GPU library is checked against.  Only the tests, the
@@ -17,6 +18,7 @@
  *        VibeASR (1/2)"
  *   [P2] "ggml-cpu: ternary I2_S matmul kernel (VibeASR, 3/4)"
  *   [P3] "VibeASR in audio.cpp"
+ *   [P4] "Experiment - int8 W8A8 path (the practical default)"
  *
  * Parity pins (tests/test_oracle_pins.py): hand-decoded pack bytes, the
  * rounding vector, the headroom closed form, degenerate scales, sign
@@ -26,7 +28,11 @@
  * (tests/test_oracle_i8s_pins.py): hand-worked mul_mat_add(_relu) bytes and
  * scale bits, an exact-rational model, numpy's integer matmul at full scale,
  * the per-row vectors on one-row tensors, round-trip bounds, equivariances,
- * and agreement with the I2_S op on ternary weights.  The 28 padding bytes of
+ * and agreement with the I2_S op on ternary weights.  Per-channel W8A8
+ * (tests/test_oracle_w8a8_pins.py): the hand-worked rounding row, exact-
+ * rational models of both quantizers (near ties included) and of the
+ * left-to-right dequantization, numpy's integer matmul, the 1e-9 start of the
+ * running maximum.  The 28 padding bytes of
  * the in-band scale slot are "parity unpinned": nothing on the pages reads
  * them.
  */
@@ -291,5 +297,99 @@ int oracle_i8s_mul_mat_add(const uint8_t *w, int64_t OC, int64_t IC,
     if (f) memcpy(f, v, (size_t)(N * OC) * sizeof(float));
     oracle_i8s_quantize(v, N * OC, out);
     free(v);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Per-channel W8A8 ["Experiment - int8 W8A8 path (the practical default)",
+ * Hypothesis and Implementation]: int8 weights with one F32 scale per output
+ * channel, int8 activations with one F32 scale per row, an int32 product,
+ * and the dequantization d[m][n] = aScale[m] * bScale[n] * C[m][n].  Each
+ * quantizer follows the page's own arithmetic, which differs from the I2_S
+ * activation quantizer in three places: the running maximum starts at 1e-9
+ * instead of being floored at 1e-5, weights round with lrintf (ties to
+ * even), and activations multiply by the reciprocal 127/max and then add
+ * copysign(0.5) and truncate.  Weights are kept as w[n][k] (K contiguous);
+ * the page transposes them for its NPU, which changes no value.
+ */
+
+/* Weight quantization, per output channel n of w[OC][K]:
+ *   mx = max(1e-9, max_k |w|), s = mx / 127, q = lrintf(w / s) clamped to
+ *   [-127, 127]. */
+void oracle_w8a8_quantize_weight(const float *w, int64_t OC, int64_t K, int8_t *q, float *scale)
+{
+    for (int64_t n = 0; n < OC; ++n) {
+        float mx = 1e-9f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf(w[n * K + k]);
+            if (v > mx) mx = v;
+        }
+        float s = mx / 127.0f;
+        scale[n] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            long r = lrintf(w[n * K + k] / s); /* current rounding mode: to nearest, ties to even */
+            if (r > 127) r = 127;
+            if (r < -127) r = -127;
+            q[n * K + k] = (int8_t)r;
+        }
+    }
+}
+
+/* Activation quantization, per row m of x[M][K]:
+ *   mx = max(1e-9, max_k |x|), aScale = mx / 127, inv = 127 / mx,
+ *   v = x * inv, q = (int)(v + copysign(0.5, v)) (the sum rounded to F32,
+ *   then truncated toward zero), clamped to [-127, 127]. */
+void oracle_w8a8_quantize_act(const float *x, int64_t M, int64_t K, int8_t *q, float *scale)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        float mx = 1e-9f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf(x[m * K + k]);
+            if (v > mx) mx = v;
+        }
+        scale[m] = mx / 127.0f;
+        float inv = 127.0f / mx;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = x[m * K + k] * inv;
+            float h = v + copysignf(0.5f, v);
+            int qi = (int)h;
+            if (qi > 127) qi = 127;
+            if (qi < -127) qi = -127;
+            q[m * K + k] = (int8_t)qi;
+        }
+    }
+}
+
+/* C[m][n] = sum_k a[m][k] * w[n][k] (int32), then
+ * d[m][n] = aScale[m] * bScale[n] * (float)C[m][n], multiplied left to
+ * right. */
+void oracle_w8a8_matmul(const int8_t *a, const float *ascale, int64_t M,
+                        const int8_t *w, const float *wscale, int64_t OC, int64_t K,
+                        float *d, int32_t *c)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < OC; ++n) {
+            int32_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int32_t)a[m * K + k] * (int32_t)w[n * K + k];
+            if (c) c[m * OC + n] = acc;
+            d[m * OC + n] = ascale[m] * wscale[n] * (float)acc;
+        }
+    }
+}
+
+/* The whole op on F32 activations x[M][K] and pre-quantized weights. */
+int oracle_w8a8_mul_mat(const int8_t *w, const float *wscale, int64_t OC, int64_t K,
+                        const float *x, int64_t M, float *d, int32_t *c)
+{
+    int8_t *a = (int8_t *)malloc((size_t)(M * K > 0 ? M * K : 1));
+    float *as = (float *)malloc((size_t)(M > 0 ? M : 1) * sizeof(float));
+    if (!a || !as) {
+        free(a); free(as);
+        return -2;
+    }
+    oracle_w8a8_quantize_act(x, M, K, a, as);
+    oracle_w8a8_matmul(a, as, M, w, wscale, OC, K, d, c);
+    free(a); free(as);
     return 0;
 }

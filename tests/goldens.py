@@ -134,3 +134,19 @@ def i8s_mul_mat_add():
         else:
             raise ValueError(f"unknown key {key}")
     return shared, cases
+
+
+def w8a8_rounding():
+    """The hand-worked W8A8 rounding row (tests/golden/w8a8_rounding.txt):
+    x (f32[16]), weight_q, act_q (int8[16]) and the scale (f32)."""
+    d = {}
+    for line in _lines("w8a8_rounding.txt"):
+        key, *vals = line.split()
+        d[key] = vals
+    x = np.zeros(16, np.float32)
+    x[: len(d["x_hex"])] = [hex_f32(v) for v in d["x_hex"]]
+    wq = np.zeros(16, np.int8)
+    wq[: len(d["weight_q"])] = [int(v) for v in d["weight_q"]]
+    aq = np.zeros(16, np.int8)
+    aq[: len(d["act_q"])] = [int(v) for v in d["act_q"]]
+    return {"x": x, "weight_q": wq, "act_q": aq, "scale": hex_f32(d["scale_hex"][0])}
