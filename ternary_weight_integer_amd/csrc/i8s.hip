@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include "i8s.h"
+#include "w8a8.h"
 
 namespace {
 
@@ -218,7 +219,15 @@ struct MatArgs {
   int nparts;
   int relu;
   int vec;              // OC % 16 == 0: 16-byte int8 stores, 16-byte dot stores
+                        // (W8A8: OC % 4 == 0 and y, dot 16-byte aligned)
+  const float *cscale;  // W8A8: per-channel weight scales [OC]
+  const float *rscale;  // W8A8: per-row activation scales [N]
+  float *y;             // W8A8: [N][OC] F32 output
 };
+
+// Epilogues of the MFMA contraction: the two passes of mul_mat_add, and the
+// F32 dequantization of the per-channel W8A8 product.
+constexpr int kModeMax = 0, kModeQuant = 1, kModeF32 = 2;
 
 // f of one output from its accumulator: (float)acc * t, + bias, ReLU.
 __device__ inline float value_of(int32_t acc, float t, float b, bool has_bias, int relu) {
@@ -302,8 +311,9 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_plain_kernel(const MatArgs a)
 // The bias is always added (0 for a missing bias: adding +0 only turns a -0
 // into +0, which neither |f| nor q can see), and lo is 0 for the relu form and
 // -inf otherwise, so the value has no data-dependent branch.
-template <int TM, int TN, int KS, bool QUANT>
+template <int TM, int TN, int KS, int MODE>
 __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) {
+  constexpr bool QUANT = MODE == kModeQuant;
   constexpr int WAVES_M = TM / 64;
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WTN = TN / WAVES_N;  // activation rows per wave
@@ -313,7 +323,8 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
   constexpr int RA = TM / 64, RB = TN / 64;  // 16-byte loads per thread per step
   static_assert(WAVES_M * WAVES_N == 4 && FN >= 1 && RA >= 1 && RB >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) int8_t lds[KS * LS];
-  __shared__ __attribute__((aligned(16))) float lbias[TM];  // bias of the item's channel block
+  __shared__ __attribute__((aligned(16))) float lbias[TM];  // bias (W8A8: weight scales) of the item's channels
+  __shared__ float lrs[MODE == kModeF32 ? TN : 1];           // W8A8: activation scales of the item's rows
   __shared__ float red[4];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -322,7 +333,10 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
   const int OC = static_cast<int>(a.OC), IC = static_cast<int>(a.IC), N = static_cast<int>(a.N);
   const __amdgpu_buffer_rsrc_t wbuf = buffer_of(a.w, static_cast<uint32_t>(a.OC * a.IC));
   const __amdgpu_buffer_rsrc_t xbuf = buffer_of(a.x, static_cast<uint32_t>(a.N * a.IC));
-  const __amdgpu_buffer_rsrc_t bbuf = buffer_of(a.bias, a.bias ? static_cast<uint32_t>(a.OC * 4) : 0u);
+  const float *cvec = MODE == kModeF32 ? a.cscale : a.bias;
+  const __amdgpu_buffer_rsrc_t bbuf = buffer_of(cvec, cvec ? static_cast<uint32_t>(a.OC * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t rbuf = buffer_of(a.rscale, MODE == kModeF32 ? static_cast<uint32_t>(a.N * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(a.y, MODE == kModeF32 ? static_cast<uint32_t>(a.N * a.OC * 4) : 0u);
   const __amdgpu_buffer_rsrc_t obuf = buffer_of(a.out, static_cast<uint32_t>(a.N * a.OC));
   const __amdgpu_buffer_rsrc_t dbuf = buffer_of(a.dot, a.dot ? static_cast<uint32_t>(a.N * a.OC * 4) : 0u);
 
@@ -364,6 +378,9 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
     if (tid < TM)
       rbias = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           bbuf, o0 + tid < OC ? static_cast<uint32_t>(4 * (o0 + tid)) : kOutOfRange, 0, 0));
+    else if (MODE == kModeF32 && tid < TM + TN)
+      rbias = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rbuf, n0 + tid - TM < N ? static_cast<uint32_t>(4 * (n0 + tid - TM)) : kOutOfRange, 0, 0));
     const int kbase = c.kc * (64 * KS) + 16 * lchunk;
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
@@ -385,6 +402,7 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
   };
   auto lstore = [&]() {
     if (tid < TM) lbias[tid] = rbias;
+    else if (MODE == kModeF32 && tid < TM + TN) lrs[tid - TM] = rbias;
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
 #pragma unroll
@@ -410,7 +428,7 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
   // latencies overlap.
   Cursor lc = first, cc = first;
   if (items > 0) gload(lc);
-  const float ws = load_scale(a.ws), xs = load_scale(a.xs);
+  const float ws = MODE == kModeF32 ? 1.0f : load_scale(a.ws), xs = MODE == kModeF32 ? 1.0f : load_scale(a.xs);
   const float lo = a.relu ? 0.0f : -INFINITY;
   float s = 1.0f, inv = 1.0f;
   if constexpr (QUANT) {
@@ -485,7 +503,41 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
     // activation row n.
     const int o0 = ec.ob * TM, n0 = ec.nb * TN;
     const int og = o0 + wm * 64 + 16 * kq;
-    if constexpr (!QUANT) {
+    if constexpr (MODE == kModeF32) {
+      float cs[16];
+      lds_bias(cs);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int nl = wn * WTN + 16 * fn + li;
+        const int n = n0 + nl;
+        const float rs = lrs[nl];
+        v4i yv[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            yv[b][r] = __float_as_int(rs * cs[4 * b + r] * static_cast<float>(acc[fn][b][r]));
+        const uint32_t row = static_cast<uint32_t>(n) * static_cast<uint32_t>(OC);
+        const bool n_ok = n < N;
+        if (a.vec) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t off = n_ok && og + 4 * b < OC ? 4 * (row + og + 4 * b) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(yv[b], ybuf, off, 0, 0);
+            if (a.dot) __builtin_amdgcn_raw_buffer_store_b128(acc[fn][b], dbuf, off, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const uint32_t off = n_ok && og + j < OC ? 4 * (row + og + j) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(yv[j >> 2][j & 3], ybuf, off, 0, 0);
+            if (a.dot) __builtin_amdgcn_raw_buffer_store_b32(acc[fn][j >> 2][j & 3], dbuf, off, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[fn][b] = v4i{0, 0, 0, 0};
+      }
+    } else if constexpr (MODE == kModeMax) {
       if (ec.ob != cur_ob) {
         if (cur_ob >= 0) flush();
         cur_ob = ec.ob;
@@ -547,10 +599,43 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
       }
     }
   }
-  if constexpr (!QUANT) {
+  if constexpr (MODE == kModeMax) {
     if (cur_ob >= 0) flush();
     m = block_max(m, red);
     if (threadIdx.x == 0) a.parts[blockIdx.x] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-channel W8A8 row quantizers: one workgroup per row (a weight channel or
+// an activation row); the row maximum starts at 1e-9.  Weights: s = mx/127,
+// q = rint(w / s) (lrintf's ties to even).  Activations: s = mx/127,
+// inv = 127/mx, v = x * inv, q = trunc(v + copysign(0.5, v)).
+
+template <bool WEIGHT>
+__global__ void __launch_bounds__(kThreads) w8a8_quant_rows_kernel(const float *__restrict__ x, int64_t K,
+                                                                   int8_t *__restrict__ q, float *__restrict__ scale) {
+  __shared__ float red[4];
+  const float *xr = x + blockIdx.x * K;
+  int8_t *qr = q + blockIdx.x * K;
+  float mx = 1e-9f;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) mx = fmaxf(mx, fabsf(xr[k]));
+  mx = block_max(mx, red);
+  const float s = mx / 127.0f;
+  if (threadIdx.x == 0) scale[blockIdx.x] = s;
+  if constexpr (WEIGHT) {
+    for (int64_t k = threadIdx.x; k < K; k += kThreads) {
+      const float r = fminf(fmaxf(rintf(xr[k] / s), -127.0f), 127.0f);
+      qr[k] = static_cast<int8_t>(static_cast<int>(r));
+    }
+  } else {
+    const float inv = 127.0f / mx;
+    for (int64_t k = threadIdx.x; k < K; k += kThreads) {
+      const float v = xr[k] * inv;
+      const float h = v + copysignf(0.5f, v);
+      const int qi = static_cast<int>(fminf(fmaxf(h, -127.0f), 127.0f));
+      qr[k] = static_cast<int8_t>(qi);
+    }
   }
 }
 
@@ -574,8 +659,12 @@ int launch_mfma(MatArgs a, hipStream_t stream) {
     g = static_cast<int>(tiles_o * (per > 0 ? per : 1));
   }
   a.nparts = g;
-  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, false>), dim3(g), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, true>), dim3(g), dim3(kThreads), 0, stream, a);
+  if (a.y) {  // W8A8: one pass, F32 out
+    hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, kModeF32>), dim3(g), dim3(kThreads), 0, stream, a);
+    return hip_status();
+  }
+  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, kModeMax>), dim3(g), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, kModeQuant>), dim3(g), dim3(kThreads), 0, stream, a);
   return hip_status();
 }
 
@@ -685,4 +774,110 @@ extern "C" int i8s_mul_mat_add_relu(const uint8_t *w, int64_t OC, int64_t IC, co
                                     const float *bias, uint8_t *out, void *workspace, size_t workspace_bytes,
                                     void *stream) {
   return i8s_mul_mat_add_ex(w, OC, IC, x, N, bias, 1, out, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Per-channel W8A8 (include/w8a8.h).
+
+namespace {
+
+int w8a8_auto_variant(int64_t OC, int64_t K, int64_t M) {
+  (void)K;
+  if (OC <= 64) return 6;
+  return M <= 64 ? 8 : (M <= 256 ? 4 : 2);
+}
+
+int check_rows(const void *x, int64_t rows, int64_t K, const void *q, const float *scale) {
+  if (!x || !q || !scale || rows < 0 || K < 0) return I2S_EINVAL;
+  if (rows * K >= kMaxBytes) return I2S_ERANGE;
+  return I2S_OK;
+}
+
+}  // namespace
+
+extern "C" size_t w8a8_act_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  const size_t q = (static_cast<size_t>(M) * static_cast<size_t>(K) + 255) / 256 * 256;
+  return q + (static_cast<size_t>(M) * 4 + 255) / 256 * 256;
+}
+
+extern "C" int w8a8_quantize_weight(const float *w, int64_t OC, int64_t K, int8_t *wq, float *wscale, void *stream) {
+  const int st = check_rows(w, OC, K, wq, wscale);
+  if (st != I2S_OK) return st;
+  if (OC == 0) return I2S_OK;
+  hipLaunchKernelGGL(w8a8_quant_rows_kernel<true>, dim3(static_cast<uint32_t>(OC)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), w, K, wq, wscale);
+  return hip_status();
+}
+
+extern "C" int w8a8_quantize_act(const float *x, int64_t M, int64_t K, int8_t *q, float *ascale, void *stream) {
+  const int st = check_rows(x, M, K, q, ascale);
+  if (st != I2S_OK) return st;
+  if (M == 0) return I2S_OK;
+  hipLaunchKernelGGL(w8a8_quant_rows_kernel<false>, dim3(static_cast<uint32_t>(M)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), x, K, q, ascale);
+  return hip_status();
+}
+
+extern "C" int w8a8_mul_mat_variant(int64_t OC, int64_t K, int64_t M) { return w8a8_auto_variant(OC, K, M); }
+
+extern "C" int w8a8_matmul(const int8_t *wq, const float *wscale, int64_t OC, int64_t K, const int8_t *aq,
+                           const float *ascale, int64_t M, float *y, int32_t *dot_out, int variant, void *stream) {
+  if (!wq || !wscale || !aq || !ascale || !y || OC < 0 || K < 0 || M < 0) return I2S_EINVAL;
+  if (!aligned(wq, 16) || !aligned(aq, 16) || !aligned(y, 16) || !aligned(wscale, 4) || !aligned(ascale, 4))
+    return I2S_EINVAL;
+  if (dot_out && !aligned(dot_out, 16)) return I2S_EINVAL;
+  if (K == 0 || K % 16 != 0) return I2S_EALIGN;
+  if (OC * K >= kMaxBytes || M * K >= kMaxBytes || M * OC >= kMaxBytes / 4) return I2S_ERANGE;
+  if (variant < 0 || variant == 1 || variant > kVariants) return I2S_EKERNEL;
+  if (variant == 0) variant = w8a8_auto_variant(OC, K, M);
+  if (OC == 0 || M == 0) return I2S_OK;
+  MatArgs a = {};
+  a.w = wq;
+  a.x = aq;
+  a.dot = dot_out;
+  a.OC = OC;
+  a.IC = K;
+  a.N = M;
+  a.vec = OC % 4 == 0;
+  a.cscale = wscale;
+  a.rscale = ascale;
+  a.y = y;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (variant) {
+    case 2: return launch_mfma<128, 128, 1>(a, s);
+    case 3: return launch_mfma<64, 128, 1>(a, s);
+    case 4: return launch_mfma<128, 64, 1>(a, s);
+    case 5: return launch_mfma<128, 64, 2>(a, s);
+    case 6: return launch_mfma<64, 128, 2>(a, s);
+    case 7: return launch_mfma<128, 64, 4>(a, s);
+    default: return launch_mfma<64, 64, 1>(a, s);
+  }
+}
+
+extern "C" int w8a8_mul_mat_ex(const int8_t *wq, const float *wscale, int64_t OC, int64_t K, const float *x, int64_t M,
+                               void *workspace, size_t workspace_bytes, float *y, int32_t *dot_out, int variant,
+                               void *stream) {
+  if (!x || !aligned(x, 16)) return I2S_EINVAL;
+  if (M < 0 || K < 0) return I2S_EINVAL;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < w8a8_act_workspace_bytes(M, K))
+    return I2S_EWORKSPACE;
+  int8_t *aq = static_cast<int8_t *>(workspace);
+  float *as = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                        (static_cast<size_t>(M) * static_cast<size_t>(K) + 255) / 256 * 256);
+  // Validate the contraction's arguments before launching anything.
+  if (!wq || !wscale || !y || OC < 0) return I2S_EINVAL;
+  if (!aligned(wq, 16) || !aligned(y, 16) || !aligned(wscale, 4) || (dot_out && !aligned(dot_out, 16)))
+    return I2S_EINVAL;
+  if (K == 0 || K % 16 != 0) return I2S_EALIGN;
+  if (OC * K >= kMaxBytes || M * K >= kMaxBytes || M * OC >= kMaxBytes / 4) return I2S_ERANGE;
+  if (variant < 0 || variant == 1 || variant > kVariants) return I2S_EKERNEL;
+  int st = w8a8_quantize_act(x, M, K, aq, as, stream);
+  if (st != I2S_OK) return st;
+  return w8a8_matmul(wq, wscale, OC, K, aq, as, M, y, dot_out, variant, stream);
+}
+
+extern "C" int w8a8_mul_mat(const int8_t *wq, const float *wscale, int64_t OC, int64_t K, const float *x, int64_t M,
+                            void *workspace, size_t workspace_bytes, float *y, void *stream) {
+  return w8a8_mul_mat_ex(wq, wscale, OC, K, x, M, workspace, workspace_bytes, y, nullptr, 0, stream);
 }
