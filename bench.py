@@ -30,6 +30,11 @@ bias, 6000 positions, I8_S in and out: i8s_mul_mat_add_relu then
 i8s_mul_mat_add, four launches); its roofline line is the FC1 op (both of its
 passes) against HBM.
 
+--workload w8a8_prefill / w8a8_decode time the per-channel W8A8 matmul of
+the NPU page on the gate projection's shape (8960 x 1536; 512 rows, or one):
+quantize the activation rows, then the int8-MFMA contraction with its F32
+dequantizing epilogue (two launches); weights quantized once beforehand.
+
 --workload decode_layer times one Qwen2-1.5B decoder layer's seven ternary
 projections at N = 1 instead (q/k/v grouped with their F32 biases, o,
 gate/up grouped, down: four launches), rotating over 28 layers of weights
@@ -66,7 +71,8 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="decode_up",
-                   choices=["decode_up", "prefill_gate", "down_small_batch", "small", "decode_layer", "encoder_mlp"])
+                   choices=["decode_up", "prefill_gate", "down_small_batch", "small", "decode_layer", "encoder_mlp",
+                            "w8a8_prefill", "w8a8_decode"])
     p.add_argument("--stage", type=int, default=3, help="encoder stage of --workload encoder_mlp (0..6)")
     p.add_argument("--copies", type=int, default=0, help="weight copies to rotate over (0 = enough for 512 MiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -368,6 +374,116 @@ def bench_encoder(args, torch):
     return out
 
 
+def bench_w8a8(args, torch):
+    """Per-channel W8A8: quantize the activation rows and contract (two
+    launches); weight copies rotate through >= 512 MiB as for I2_S."""
+    from ternary_weight_integer_amd import w8a8, workloads
+    dev = torch.device("cuda:0")
+    case = workloads.w8a8_case(args.workload.split("_", 1)[1])
+    OC, K, M = case.OC, case.K, case.M
+    wq0, ws0 = w8a8.w8a8_quantize_weight(torch.from_numpy(case.w).to(dev))
+    R = args.copies or max(1, -(-ROTATE_BYTES // wq0.numel()))
+    copies = [(wq0, ws0)] + [(wq0.clone(), ws0.clone()) for _ in range(R - 1)]
+    x = torch.from_numpy(case.x).to(dev)
+    ws = w8a8.new_workspace(M, K, dev)
+    y = torch.empty((M, OC), dtype=torch.float32, device=dev)
+    aq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    asc = torch.empty(M, dtype=torch.float32, device=dev)
+    w8a8.w8a8_quantize_act(x, aq, asc)
+    variant = w8a8.w8a8_mul_mat_variant(OC, K, M)
+
+    def step(i):
+        wq, wsc = copies[i % R]
+        w8a8.w8a8_mul_mat(wq, wsc, x, workspace=ws, y=y)
+
+    def contraction(i):
+        wq, wsc = copies[i % R]
+        w8a8.w8a8_matmul(wq, wsc, aq, asc, y=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    K_steps = args.steps
+    g_step = graph_of(lambda: [step(i) for i in range(K_steps)], torch)
+    n_kern = max(R, 64)
+    g_kern = graph_of(lambda: [contraction(i) for i in range(n_kern)], torch)
+    g_step.replay()
+    g_kern.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    g_step.replay()
+    ev[1].record()
+    g_kern.replay()
+    ev[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if not torch.equal(y.view(torch.int32), y_eager.view(torch.int32)):
+        raise RuntimeError("graph replay result differs from the eager result")
+    step_ms = ev[0].elapsed_time(ev[1]) / K_steps
+    kern_us = ev[1].elapsed_time(ev[2]) * 1e3 / n_kern
+    ops = 2 * OC * K * M
+    wbytes = OC * K + 4 * OC
+    alg_bytes = wbytes + M * K + 4 * M + 4 * M * OC
+    out = {
+        "metric": METRIC,
+        "value": round(wbytes / (step_ms * 1e-3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": case.name, "OC": OC, "K": K, "M": M, "weight_copies_rotated": R,
+                   "variant": variant, "timing": "hip_graph",
+                   "value_is": "int8 weight bytes (+ channel scales) per second"},
+        "int8_tops": round(ops / (step_ms * 1e-3) / 1e12, 4),
+        "wall_s": round(wall, 4),
+    }
+    kname = "i8s_mm_mfma_kernel (F32 dequantizing epilogue)"
+    if M >= 64:
+        achieved = ops / (kern_us * 1e-6) / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_MFMA_PEAK_TOPS,
+                           "unit": "TOP/s", "frac": round(achieved / INT8_MFMA_PEAK_TOPS, 4),
+                           "traffic": measured_traffic(args.workload), "kernel": kname, "kernel_variant": variant,
+                           "kernel_us": round(kern_us, 4), "alg_ops_per_launch": ops, "alg_bytes_per_launch": alg_bytes}
+    else:
+        achieved = alg_bytes / (kern_us * 1e-6) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                           "kernel": kname, "kernel_variant": variant, "kernel_us": round(kern_us, 4),
+                           "alg_bytes_per_launch": alg_bytes}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_w8a8(case, args.cpu_seconds)
+    return out
+
+
+def cpu_baseline_w8a8(case, seconds: float):
+    import oracle
+    wq, wsc = oracle.w8a8_quantize_weight(case.w)
+    rows = min(case.M, 8)   # a bounded sample: rows are independent
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.w8a8_mul_mat(wq, wsc, case.x[:rows])
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    wbytes = case.OC * case.K + 4 * case.OC
+    per_step = el / calls * case.M / rows
+    return {"value": round(wbytes / per_step / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} calls on {rows} of the {case.M} activation rows ({case.name}, scalar C, 1 thread) "
+                      f"in {el:.1f} s, scaled to the full {case.M} rows",
+            "cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0)),
+            "ms_per_step": round(per_step * 1e3, 3)}
+
+
 def cpu_baseline_encoder(case, seconds: float, step_bytes: int):
     import oracle
     H, C, N = case.w1.shape[0], case.C, case.N
@@ -434,6 +550,9 @@ def main(argv=None):
         return 0
     if args.workload == "encoder_mlp":
         print(json.dumps(bench_encoder(args, torch)), flush=True)
+        return 0
+    if args.workload.startswith("w8a8_"):
+        print(json.dumps(bench_w8a8(args, torch)), flush=True)
         return 0
     dev = torch.device("cuda:0")
     case = make_case(args.workload)

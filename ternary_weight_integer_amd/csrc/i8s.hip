@@ -781,10 +781,12 @@ extern "C" int i8s_mul_mat_add_relu(const uint8_t *w, int64_t OC, int64_t IC, co
 
 namespace {
 
+// 128 x 64 tiles with 4-step K chunks measured fastest on every Qwen2-1.5B
+// projection shape, from one row to 512.
 int w8a8_auto_variant(int64_t OC, int64_t K, int64_t M) {
   (void)K;
-  if (OC <= 64) return 6;
-  return M <= 64 ? 8 : (M <= 256 ? 4 : 2);
+  (void)M;
+  return OC <= 64 ? 6 : 7;
 }
 
 int check_rows(const void *x, int64_t rows, int64_t K, const void *q, const float *scale) {

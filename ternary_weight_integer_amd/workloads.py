@@ -244,3 +244,37 @@ def encoder_mlp_case(stage: int = 3, seed: int = 0, seconds: float = 4.0) -> Enc
     x.flat[idx] = np.where(rng.random(k) < 0.5, -127, 127).astype(np.int8)
     return EncoderMlpCase(name=f"encoder_mlp_stage{stage}_C{C}_N{N}", stage=stage, C=C, N=N,
                           w1=w1, w1_scale=0.004, b1=b1, w2=w2, w2_scale=0.003, b2=b2, x=x, x_scale=0.03)
+
+
+# ---------------------------------------------------------------------------
+# Per-channel W8A8 ("Experiment - int8 W8A8 path (the practical default)"):
+# the same Qwen2-1.5B projection shapes with F32 weights ~ N(0, 0.02) (to be
+# quantized per channel) and the I2_S workloads' activations.
+
+
+@dataclass
+class W8A8Case:
+    name: str
+    OC: int
+    K: int
+    M: int
+    w: np.ndarray   # f32 [OC][K]
+    x: np.ndarray   # f32 [M][K]
+
+
+def w8a8_case(which: str = "prefill", seed: int = 0) -> W8A8Case:
+    """'prefill': gate projection 8960 x 1536 against 512 rows ~ N(0,1);
+    'decode': the same weight against one row ~ N(0,1) with 1% of entries
+    scaled by 20.  Weights drawn before activations."""
+    rng = np.random.default_rng(seed)
+    OC, K = QWEN2_1P5B_PROJ["gate"]
+    w = rng.normal(0.0, 0.02, size=(OC, K)).astype(np.float32)
+    if which == "prefill":
+        M = 512
+        x = normal(rng, M, K)
+    elif which == "decode":
+        M = 1
+        x = with_outliers(rng, normal(rng, M, K))
+    else:
+        raise ValueError(which)
+    return W8A8Case(name=f"w8a8_{which}_gate_{OC}x{K}_M{M}", OC=OC, K=K, M=M, w=w, x=x)
