@@ -405,6 +405,16 @@ def bench_w8a8(args, torch):
     torch.cuda.synchronize()
     y_eager = y.clone()
     K_steps = args.steps
+    if args.eager:  # launches from Python, one dispatch at a time (counter collection runs)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(K_steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": K_steps,
+                "warmup": args.warmup, "ms_per_step": round(e0.elapsed_time(e1) / K_steps, 6),
+                "config": {"workload": case.name, "timing": "eager"}}
     g_step = graph_of(lambda: [step(i) for i in range(K_steps)], torch)
     n_kern = max(R, 64)
     g_kern = graph_of(lambda: [contraction(i) for i in range(n_kern)], torch)

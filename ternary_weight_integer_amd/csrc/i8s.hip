@@ -644,8 +644,10 @@ __global__ void __launch_bounds__(kThreads) w8a8_quant_rows_kernel(const float *
 
 constexpr int kVariants = 8;
 
+// f32 selects the W8A8 epilogue (one pass into a.y); otherwise the two
+// passes of mul_mat_add.
 template <int TM, int TN, int KS>
-int launch_mfma(MatArgs a, hipStream_t stream) {
+int launch_mfma(MatArgs a, bool f32, hipStream_t stream) {
   // A multiple of the channel-block count when possible: each workgroup then
   // keeps one channel block over all of its tiles.
   // The grid stays within what is resident at once (kResidentGroups), so each
@@ -659,7 +661,7 @@ int launch_mfma(MatArgs a, hipStream_t stream) {
     g = static_cast<int>(tiles_o * (per > 0 ? per : 1));
   }
   a.nparts = g;
-  if (a.y) {  // W8A8: one pass, F32 out
+  if (f32) {  // W8A8: one pass, F32 out
     hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, kModeF32>), dim3(g), dim3(kThreads), 0, stream, a);
     return hip_status();
   }
@@ -737,7 +739,7 @@ extern "C" int i8s_mul_mat_add_ex(const uint8_t *w, int64_t OC, int64_t IC, cons
   if (variant < 0 || variant > kVariants) return I2S_EKERNEL;
   if (variant == 0) variant = auto_variant(OC, IC, N);
   if (variant >= 2 && IC % 16 != 0) return I2S_EKERNEL;
-  MatArgs a;
+  MatArgs a = {};  // every field not set below (the W8A8 ones) stays null
   a.w = reinterpret_cast<const int8_t *>(w);
   a.x = reinterpret_cast<const int8_t *>(x);
   a.ws = w + OC * IC;
@@ -755,13 +757,13 @@ extern "C" int i8s_mul_mat_add_ex(const uint8_t *w, int64_t OC, int64_t IC, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
     case 1: return launch_plain(a, s);
-    case 8: return launch_mfma<64, 64, 1>(a, s);
-    case 2: return launch_mfma<128, 128, 1>(a, s);
-    case 3: return launch_mfma<64, 128, 1>(a, s);
-    case 4: return launch_mfma<128, 64, 1>(a, s);
-    case 5: return launch_mfma<128, 64, 2>(a, s);
-    case 6: return launch_mfma<64, 128, 2>(a, s);
-    default: return launch_mfma<128, 64, 4>(a, s);
+    case 8: return launch_mfma<64, 64, 1>(a, false, s);
+    case 2: return launch_mfma<128, 128, 1>(a, false, s);
+    case 3: return launch_mfma<64, 128, 1>(a, false, s);
+    case 4: return launch_mfma<128, 64, 1>(a, false, s);
+    case 5: return launch_mfma<128, 64, 2>(a, false, s);
+    case 6: return launch_mfma<64, 128, 2>(a, false, s);
+    default: return launch_mfma<128, 64, 4>(a, false, s);
   }
 }
 
@@ -847,13 +849,13 @@ extern "C" int w8a8_matmul(const int8_t *wq, const float *wscale, int64_t OC, in
   a.y = y;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
-    case 2: return launch_mfma<128, 128, 1>(a, s);
-    case 3: return launch_mfma<64, 128, 1>(a, s);
-    case 4: return launch_mfma<128, 64, 1>(a, s);
-    case 5: return launch_mfma<128, 64, 2>(a, s);
-    case 6: return launch_mfma<64, 128, 2>(a, s);
-    case 7: return launch_mfma<128, 64, 4>(a, s);
-    default: return launch_mfma<64, 64, 1>(a, s);
+    case 2: return launch_mfma<128, 128, 1>(a, true, s);
+    case 3: return launch_mfma<64, 128, 1>(a, true, s);
+    case 4: return launch_mfma<128, 64, 1>(a, true, s);
+    case 5: return launch_mfma<128, 64, 2>(a, true, s);
+    case 6: return launch_mfma<64, 128, 2>(a, true, s);
+    case 7: return launch_mfma<128, 64, 4>(a, true, s);
+    default: return launch_mfma<64, 64, 1>(a, true, s);
   }
 }
 
