@@ -24,6 +24,8 @@
 
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "i8s.h"
 #include "w8a8.h"
 
@@ -223,7 +225,21 @@ struct MatArgs {
   const float *cscale;  // W8A8: per-channel weight scales [OC]
   const float *rscale;  // W8A8: per-row activation scales [N]
   float *y;             // W8A8: [N][OC] F32 output
+  int map;              // tile assignment: kMapStride, kMapXLocal or kMapWLocal
+  int rep;              // XCD-local maps: workgroups per XCD per block of the local operand
 };
+
+// Tile assignment of the MFMA contraction.  Workgroup b runs on XCD b % 8
+// (workgroups are dealt round-robin over the 8 XCDs, each with its own L2).
+//   kMapStride: tiles b, b + G, b + 2G, ... (channel block fastest).
+//   kMapXLocal: XCD x takes the row blocks nb = x (mod 8) with every channel
+//     block, so each block of activations is fetched by one XCD only and the
+//     (smaller) weights are fetched once per XCD; a workgroup keeps one channel
+//     block and steps its row block by 8 * rep.
+//   kMapWLocal: the same with the roles swapped, for weights larger than the
+//     activations.
+constexpr int kMapStride = 0, kMapXLocal = 1, kMapWLocal = 2;
+constexpr int kXcds = 8;
 
 // Epilogues of the MFMA contraction: the two passes of mul_mat_add, and the
 // F32 dequantization of the per-channel W8A8 product.
@@ -343,27 +359,49 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
   // Tiles: channel block ob = tile % tiles_o, row block nb = tile / tiles_o;
   // this workgroup takes tiles blockIdx.x, +G, +2G, ...  Cursors step through
   // them (and through the K chunks of each) without divisions.
-  const int tiles_o = (OC + TM - 1) / TM;
-  const int tiles = tiles_o * ((N + TN - 1) / TN);
-  const int G = static_cast<int>(gridDim.x);
-  const int step_o = G % tiles_o, step_n = G / tiles_o;
+  const int tiles_o = (OC + TM - 1) / TM, tiles_n = (N + TN - 1) / TN;
+  const int tiles = tiles_o * tiles_n;
+  const int G = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
   const int kchunks = IC > 0 ? (IC + 64 * KS - 1) / (64 * KS) : 1;
-  const int my_tiles = static_cast<int>(blockIdx.x) < tiles ? (tiles - static_cast<int>(blockIdx.x) + G - 1) / G : 0;
-  const int items = my_tiles * kchunks;
   struct Cursor {
     int ob, nb, kc;
   };
+  Cursor first = {0, 0, 0};
+  int my_tiles = 0, step_o = 0, step_n = 0;
+  if (tiles == 0) {
+    // empty output: no tile (pass 1 still writes its partial, pass 2 the scale slot)
+  } else if (a.map == kMapStride) {
+    first = {b % tiles_o, b / tiles_o, 0};
+    step_o = G % tiles_o;
+    step_n = G / tiles_o;
+    my_tiles = b < tiles ? (tiles - b + G - 1) / G : 0;
+  } else {
+    const int xcd = b % kXcds, sl = b / kXcds, stride = kXcds * a.rep;
+    const int fixed_n = a.map == kMapXLocal ? tiles_o : tiles_n;  // blocks of the replicated operand
+    const int fixed = sl % fixed_n, start = xcd + kXcds * (sl / fixed_n);
+    const int local_n = a.map == kMapXLocal ? tiles_n : tiles_o;
+    my_tiles = start < local_n ? (local_n - start + stride - 1) / stride : 0;
+    if (a.map == kMapXLocal) {
+      first = {fixed, start, 0};
+      step_o = 0;
+      step_n = stride;
+    } else {
+      first = {start, fixed, 0};
+      step_o = stride;
+      step_n = 0;
+    }
+  }
+  const int items = my_tiles * kchunks;
   auto advance = [&](Cursor &c) {
     if (++c.kc < kchunks) return;
     c.kc = 0;
     c.ob += step_o;
     c.nb += step_n;
-    if (c.ob >= tiles_o) {
+    if (a.map == kMapStride && c.ob >= tiles_o) {
       c.ob -= tiles_o;
       c.nb += 1;
     }
   };
-  const Cursor first = {static_cast<int>(blockIdx.x) % tiles_o, static_cast<int>(blockIdx.x) / tiles_o, 0};
   const int lrow = tid >> 2, lchunk = tid & 3;  // this thread's load slot: row lrow (+64j), chunk lchunk
 
   auto swz = [](int r, int c) { return r * 64 + 16 * (c ^ (((r >> 2) ^ (r >> 4)) & 3)); };
@@ -652,13 +690,32 @@ int launch_mfma(MatArgs a, bool f32, hipStream_t stream) {
   // keeps one channel block over all of its tiles.
   // The grid stays within what is resident at once (kResidentGroups), so each
   // workgroup's prologue is paid once and its tiles stream through the
-  // pipeline.
+  // pipeline.  The larger operand is made XCD-local when the tile counts
+  // allow it; otherwise tiles are dealt with a plain grid stride (a multiple
+  // of the channel-block count when possible, so that a workgroup keeps one
+  // channel block).
   const int64_t tiles_o = (a.OC + TM - 1) / TM, tiles_n = (a.N + TN - 1) / TN;
   const int64_t cap = kResidentGroups;
-  int g = static_cast<int>(tiles_o * tiles_n < cap ? (tiles_o * tiles_n > 0 ? tiles_o * tiles_n : 1) : cap);
-  if (tiles_o >= 1 && tiles_o <= cap) {
-    const int64_t per = tiles_n < cap / tiles_o ? tiles_n : cap / tiles_o;
-    g = static_cast<int>(tiles_o * (per > 0 ? per : 1));
+  const bool x_larger = a.N >= a.OC;  // both operands have IC bytes per row
+  int g;
+  if (x_larger && tiles_o >= 1 && tiles_n >= kXcds && kXcds * tiles_o <= cap) {
+    const int64_t r = std::min((tiles_n + kXcds - 1) / kXcds, cap / (kXcds * tiles_o));
+    a.map = kMapXLocal;
+    a.rep = static_cast<int>(r);
+    g = static_cast<int>(kXcds * tiles_o * r);
+  } else if (!x_larger && tiles_n >= 1 && tiles_o >= kXcds && kXcds * tiles_n <= cap) {
+    const int64_t r = std::min((tiles_o + kXcds - 1) / kXcds, cap / (kXcds * tiles_n));
+    a.map = kMapWLocal;
+    a.rep = static_cast<int>(r);
+    g = static_cast<int>(kXcds * tiles_n * r);
+  } else {
+    a.map = kMapStride;
+    a.rep = 1;
+    g = static_cast<int>(tiles_o * tiles_n < cap ? (tiles_o * tiles_n > 0 ? tiles_o * tiles_n : 1) : cap);
+    if (tiles_o >= 1 && tiles_o <= cap) {
+      const int64_t per = tiles_n < cap / tiles_o ? tiles_n : cap / tiles_o;
+      g = static_cast<int>(tiles_o * (per > 0 ? per : 1));
+    }
   }
   a.nparts = g;
   if (f32) {  // W8A8: one pass, F32 out
