@@ -645,6 +645,160 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+// Skinny int8 MFMA contraction for few activation rows (the encoder's last
+// stages and connector, W8A8 decode): the tile kernel above would have only a
+// few dozen tiles there.  A workgroup of W waves owns 16 output channels and
+// up to 16 * FN activation rows; its waves take the 64-byte K-steps
+// round-robin, SPW steps per batch with the next batch's loads in flight,
+// and sum their int32 partial tiles through LDS.  Lane (li, kq) loads row li
+// of each operand block at bytes 16 * kq of a step (the MFMA operand order).
+// Wave 0 finishes: it holds channels o0 + 4 * kq + r (r = 0..3) of row
+// n0 + 16 * fn + li, and applies the same epilogue as the tile kernel (max|f|,
+// requantization with the exact division, or the W8A8 dequantization).
+// Items (16-channel block, 16*FN-row block) are walked with a grid stride.
+
+template <int W>
+__device__ inline float wave_group_max(float v, float *red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+template <int W, int FN, int SPW, int MODE>
+__global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(const MatArgs a) {
+  __shared__ __attribute__((aligned(16))) v4i part[W][FN][64];
+  __shared__ float red[W];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, kq = lane >> 4;
+  const int OC = static_cast<int>(a.OC), IC = static_cast<int>(a.IC), N = static_cast<int>(a.N);
+  const __amdgpu_buffer_rsrc_t wbuf = buffer_of(a.w, static_cast<uint32_t>(a.OC * a.IC));
+  const __amdgpu_buffer_rsrc_t xbuf = buffer_of(a.x, static_cast<uint32_t>(a.N * a.IC));
+  const __amdgpu_buffer_rsrc_t obuf = buffer_of(a.out, static_cast<uint32_t>(a.N * a.OC));
+  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(a.dot, a.dot ? static_cast<uint32_t>(a.N * a.OC * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(a.y, MODE == kModeF32 ? static_cast<uint32_t>(a.N * a.OC * 4) : 0u);
+  const float *cvec = MODE == kModeF32 ? a.cscale : a.bias;
+  const __amdgpu_buffer_rsrc_t bbuf = buffer_of(cvec, cvec ? static_cast<uint32_t>(a.OC * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t rbuf = buffer_of(a.rscale, MODE == kModeF32 ? static_cast<uint32_t>(a.N * 4) : 0u);
+
+  const float ws = MODE == kModeF32 ? 1.0f : load_scale(a.ws), xs = MODE == kModeF32 ? 1.0f : load_scale(a.xs);
+  const float t = ws * xs;
+  const float lo = a.relu ? 0.0f : -INFINITY;
+  float s = 1.0f;
+  if constexpr (MODE == kModeQuant) {
+    float pm = 0.0f;
+    for (int i = tid; i < a.nparts; i += 64 * W) pm = fmaxf(pm, a.parts[i]);
+    pm = wave_group_max<W>(pm, red);
+    if (pm < kAmaxFloor) pm = kAmaxFloor;
+    s = pm / 127.0f;
+    if (blockIdx.x == 0) write_slot(reinterpret_cast<uint8_t *>(a.out) + a.N * a.OC, s);
+  }
+
+  const int blocks_o = (OC + 15) / 16, blocks_n = (N + 16 * FN - 1) / (16 * FN);
+  const int items = blocks_o * blocks_n;
+  const int steps = (IC + 63) / 64;
+  float m = 0.0f;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int o0 = (item % blocks_o) * 16, n0 = (item / blocks_o) * (16 * FN);
+    const bool o_ok = o0 + li < OC;
+    const uint32_t wrow = static_cast<uint32_t>(o0 + li) * static_cast<uint32_t>(IC) + 16 * kq;
+    uint32_t xrow[FN];
+    bool n_ok[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      n_ok[fn] = n0 + 16 * fn + li < N;
+      xrow[fn] = static_cast<uint32_t>(n0 + 16 * fn + li) * static_cast<uint32_t>(IC) + 16 * kq;
+    }
+    // Step slot i of batch g of this wave: K-step wave + W * (SPW * g + i).
+    auto load = [&](int g, v4i (&av)[SPW], v4i (&bv)[SPW][FN]) {
+#pragma unroll
+      for (int i = 0; i < SPW; ++i) {
+        const int st = wave + W * (SPW * g + i);
+        const bool kok = st < steps && 64 * st + 16 * kq < IC;
+        av[i] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, kok && o_ok ? wrow + 64 * st : kOutOfRange, 0, 0);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          bv[i][fn] = __builtin_amdgcn_raw_buffer_load_b128(xbuf, kok && n_ok[fn] ? xrow[fn] + 64 * st : kOutOfRange,
+                                                            0, 0);
+      }
+    };
+    v4i acc[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fn] = v4i{0, 0, 0, 0};
+    auto compute = [&](const v4i (&av)[SPW], const v4i (&bv)[SPW][FN]) {
+#pragma unroll
+      for (int i = 0; i < SPW; ++i)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i], bv[i][fn], acc[fn], 0, 0, 0);
+    };
+    const int mine = steps > wave ? (steps - wave + W - 1) / W : 0;
+    const int batches = (mine + SPW - 1) / SPW;
+    v4i aa[SPW], ab[SPW], ba[SPW][FN], bb[SPW][FN];
+    if (batches > 0) load(0, aa, ba);
+    for (int g = 0; g < batches; g += 2) {
+      if (g + 1 < batches) load(g + 1, ab, bb);
+      compute(aa, ba);
+      if (g + 1 >= batches) break;
+      if (g + 2 < batches) load(g + 2, aa, ba);
+      compute(ab, bb);
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) part[wave][fn][lane] = acc[fn];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        v4i tot = part[0][fn][lane];
+#pragma unroll
+        for (int w = 1; w < W; ++w) tot += part[w][fn][lane];
+        acc[fn] = tot;
+      }
+      // Lane (li, kq): channels o0 + 4*kq + r of row n0 + 16*fn + li.
+      const int oc = o0 + 4 * kq;
+      float cv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        cv[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            bbuf, oc + r < OC ? static_cast<uint32_t>(4 * (oc + r)) : kOutOfRange, 0, 0));
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int n = n0 + 16 * fn + li;
+        const uint32_t row = static_cast<uint32_t>(n) * static_cast<uint32_t>(OC);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = n < N && oc + r < OC;
+          const uint32_t off = ok ? row + oc + r : kOutOfRange;
+          if constexpr (MODE == kModeF32) {
+            const float rs = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rbuf, n < N ? static_cast<uint32_t>(4 * n) : kOutOfRange, 0, 0));
+            const float y = rs * cv[r] * static_cast<float>(acc[fn][r]);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(y), ybuf, ok ? 4 * off : kOutOfRange, 0, 0);
+          } else {
+            const float v = fmaxf(static_cast<float>(acc[fn][r]) * t + cv[r], lo);
+            if constexpr (MODE == kModeMax) {
+              if (ok) m = fmaxf(m, fabsf(v));
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(quant(v, s)), obuf, off, 0, 0);
+            }
+          }
+          if (a.dot && MODE != kModeMax)
+            __builtin_amdgcn_raw_buffer_store_b32(acc[fn][r], dbuf, ok ? 4 * off : kOutOfRange, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // part[] is reused by the next item
+  }
+  if constexpr (MODE == kModeMax) {
+    m = wave_group_max<W>(m, red);
+    if (threadIdx.x == 0) a.parts[blockIdx.x] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Per-channel W8A8 row quantizers: one workgroup per row (a weight channel or
 // an activation row); the row maximum starts at 1e-9.  Weights: s = mx/127,
 // q = rint(w / s) (lrintf's ties to even).  Activations: s = mx/127,
@@ -680,7 +834,7 @@ __global__ void __launch_bounds__(kThreads) w8a8_quant_rows_kernel(const float *
 // ---------------------------------------------------------------------------
 // Host side.
 
-constexpr int kVariants = 8;
+constexpr int kVariants = 9;
 
 // f32 selects the W8A8 epilogue (one pass into a.y); otherwise the two
 // passes of mul_mat_add.
@@ -727,6 +881,28 @@ int launch_mfma(MatArgs a, bool f32, hipStream_t stream) {
   return hip_status();
 }
 
+template <int FN>
+int launch_skinny_fn(MatArgs a, bool f32, hipStream_t stream) {
+  constexpr int W = 8, SPW = 2;
+  const int64_t items = ((a.OC + 15) / 16) * ((a.N + 16 * FN - 1) / (16 * FN));
+  const int g = parts_for(items);
+  a.nparts = g;
+  if (f32) {
+    hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeF32>), dim3(g), dim3(64 * W), 0, stream, a);
+    return hip_status();
+  }
+  hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeMax>), dim3(g), dim3(64 * W), 0, stream, a);
+  hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeQuant>), dim3(g), dim3(64 * W), 0, stream, a);
+  return hip_status();
+}
+
+// Row blocks of 16, 32 or 64 rows, by N.
+int launch_skinny(MatArgs a, bool f32, hipStream_t stream) {
+  if (a.N <= 16) return launch_skinny_fn<1>(a, f32, stream);
+  if (a.N <= 32) return launch_skinny_fn<2>(a, f32, stream);
+  return launch_skinny_fn<4>(a, f32, stream);
+}
+
 int launch_plain(MatArgs a, hipStream_t stream) {
   const int g = parts_for((a.N * a.OC + kThreads - 1) / kThreads);
   a.nparts = g;
@@ -736,10 +912,19 @@ int launch_plain(MatArgs a, hipStream_t stream) {
 }
 
 // Tile (channels x rows, 64-byte steps per K chunk): 2 = 128 x 128 x 1, 3 = 64 x 128 x 1,
-// 4 = 128 x 64 x 1, 5 = 128 x 64 x 2, 6 = 64 x 128 x 2, 7 = 128 x 64 x 4, 8 = 64 x 64 x 1.
+// 4 = 128 x 64 x 1, 5 = 128 x 64 x 2, 6 = 64 x 128 x 2, 7 = 128 x 64 x 4, 8 = 64 x 64 x 1;
+// 9 = the skinny kernel (16 channels x up to 64 rows per workgroup, waves split K).
+// The skinny kernel when the tile kernel would have too few tiles: up to 64
+// rows, or up to 256 rows with fewer than 128 tiles of 128 x 64 (measured on
+// the encoder, connector and decoder shapes).
+bool skinny_wins(int64_t OC, int64_t N) {
+  const int64_t tiles = ((OC + 127) / 128) * ((N + 63) / 64);
+  return N <= 64 || (N <= 256 && tiles < 128);
+}
+
 int auto_variant(int64_t OC, int64_t IC, int64_t N) {
-  (void)N;
   if (IC % 16 != 0) return 1;
+  if (skinny_wins(OC, N)) return 9;
   if (OC <= 64) return 6;   // 64 x 128 x 2: few channels, many rows
   if (IC <= 64) return 2;   // 128 x 128 x 1
   if (IC <= 128) return 5;  // 128 x 64 x 2
@@ -814,6 +999,7 @@ extern "C" int i8s_mul_mat_add_ex(const uint8_t *w, int64_t OC, int64_t IC, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
     case 1: return launch_plain(a, s);
+    case 9: return launch_skinny(a, false, s);
     case 8: return launch_mfma<64, 64, 1>(a, false, s);
     case 2: return launch_mfma<128, 128, 1>(a, false, s);
     case 3: return launch_mfma<64, 128, 1>(a, false, s);
@@ -840,11 +1026,11 @@ extern "C" int i8s_mul_mat_add_relu(const uint8_t *w, int64_t OC, int64_t IC, co
 
 namespace {
 
-// 128 x 64 tiles with 4-step K chunks measured fastest on every Qwen2-1.5B
-// projection shape, from one row to 512.
+// The skinny kernel for few rows (as for I8_S); otherwise 128 x 64 tiles with
+// 4-step K chunks, measured fastest on the Qwen2-1.5B projection shapes.
 int w8a8_auto_variant(int64_t OC, int64_t K, int64_t M) {
   (void)K;
-  (void)M;
+  if (skinny_wins(OC, M)) return 9;
   return OC <= 64 ? 6 : 7;
 }
 
@@ -912,6 +1098,7 @@ extern "C" int w8a8_matmul(const int8_t *wq, const float *wscale, int64_t OC, in
     case 5: return launch_mfma<128, 64, 2>(a, true, s);
     case 6: return launch_mfma<64, 128, 2>(a, true, s);
     case 7: return launch_mfma<128, 64, 4>(a, true, s);
+    case 9: return launch_skinny(a, true, s);
     default: return launch_mfma<64, 64, 1>(a, true, s);
   }
 }
