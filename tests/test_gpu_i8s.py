@@ -245,3 +245,34 @@ def test_requantize_near_ties():
     for v in range(1, i8s.i8s_variants() + 1):
         for relu in (0, 1):
             check_mm(W, OC, IC, X, N, bias, relu, v, tag="near ties")
+
+
+@pytest.mark.parametrize("OC,IC,N,relu", [(1024, 256, 600, 1), (2048, 512, 30, 0)])
+def test_graph_replay_matches_eager(OC, IC, N, relu):
+    # Both passes captured in a HIP graph; every replay, with eager work and
+    # synchronizations in between, must give the eager bytes (the partial
+    # maxima are written by the kernels themselves, no memset is captured).
+    say(f"graph replay mul_mat_add OC={OC} IC={IC} N={N}")
+    rng = np.random.default_rng(OC + N)
+    W, X = dev(rand_i8s(rng, OC, IC, 0.01)), dev(rand_i8s(rng, N, IC, 0.02))
+    b = dev(rng.normal(0, 1, size=OC).astype(np.float32))
+    ws = i8s.new_workspace(DEV)
+    out = torch.empty(i8s.i8s_bytes(N * OC), dtype=torch.uint8, device=DEV)
+    fn = i8s.i8s_mul_mat_add_relu if relu else i8s.i8s_mul_mat_add
+    fn(W, OC, IC, X, N, b, out=out, workspace=ws)
+    eager = host(out).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(W, OC, IC, X, N, b, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(W, OC, IC, X, N, b, out=out, workspace=ws)
+    for r in range(4):
+        out.zero_()
+        ws.fill_(0xFF)   # stale partial maxima must not leak into the next replay
+        torch.cuda.synchronize()
+        g.replay()
+        assert host(out).tobytes() == eager.tobytes(), f"replay {r}"

@@ -135,3 +135,30 @@ def test_whole_op_zero_rows_and_streams():
     yh = host(y)
     assert not yh[4].any()
     assert np.array_equal(bits(yh), bits(oracle.w8a8_mul_mat(wq, ws, x)))
+
+
+@pytest.mark.parametrize("OC,K,M", [(8960, 1536, 64), (1536, 8960, 4)])
+def test_graph_replay_matches_eager(OC, K, M):
+    say(f"graph replay w8a8_mul_mat OC={OC} K={K} M={M}")
+    rng = np.random.default_rng(M)
+    wq, ws_ = w8a8.w8a8_quantize_weight(dev(rng.normal(0, 0.02, size=(OC, K)).astype(np.float32)))
+    x = dev(rng.normal(0, 1, size=(M, K)).astype(np.float32))
+    wsp = w8a8.new_workspace(M, K, DEV)
+    y = torch.empty((M, OC), dtype=torch.float32, device=DEV)
+    w8a8.w8a8_mul_mat(wq, ws_, x, workspace=wsp, y=y)
+    eager = host(y).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w8a8.w8a8_mul_mat(wq, ws_, x, workspace=wsp, y=y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w8a8.w8a8_mul_mat(wq, ws_, x, workspace=wsp, y=y)
+    for r in range(4):
+        y.zero_()
+        wsp.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        assert np.array_equal(bits(host(y)), bits(eager)), f"replay {r}"
