@@ -279,6 +279,17 @@ __device__ inline int lanes_sum(int v) {
   return v;
 }
 
+// Raw buffer accesses: the descriptor bounds the tensor, out-of-range loads
+// read 0 and out-of-range stores are dropped by the hardware.
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // buffer offset beyond every descriptor's range
+constexpr int kBufferFlags = 0x00020000;       // raw buffer, 32-bit data format
+
+__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           kBufferFlags);
+}
+
 template <int NC, int L, int RPL, int CPL>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
@@ -294,6 +305,31 @@ gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   const int64_t C = K / 64;               // 16-byte chunks per packed row
   const int64_t row_bytes = K / 4;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave * kRowsPerWave + slot;
+
+  // Epilogue constants first (buffer loads keep their place): the weight
+  // scale from the in-band slot, the activation scales and row sums, and this
+  // lane's biases.  Loaded at their use they would cost one more memory round
+  // trip before the stores.
+  const float ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_of(packed + rows * row_bytes, 4), 0, 0, 0));
+  float asc[NC];
+  int32_t rsum[NC];
+  float bv[RPL];
+  {
+    const __amdgpu_buffer_rsrc_t sbuf = buffer_of(act_scale, 4 * NC);
+    const __amdgpu_buffer_rsrc_t rbuf = buffer_of(row_sum, 4 * NC);
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      asc[n] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, 4 * n, 0, 0));
+      rsum[n] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, 4 * n, 0, 0);
+    }
+    const __amdgpu_buffer_rsrc_t bbuf = buffer_of(bias, bias ? static_cast<uint32_t>(rows * 4) : 0u);
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+      const int64_t r = row0 + static_cast<int64_t>(m) * kSlots;
+      bv[m] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          bbuf, r < rows ? static_cast<uint32_t>(4 * r) : kOutOfRange, 0, 0));
+    }
+  }
 
   int acc[RPL][NC];
 #pragma unroll
@@ -341,7 +377,6 @@ gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
     }
   }
 
-  const float ws = *reinterpret_cast<const float *>(packed + rows * row_bytes);
 #pragma unroll
   for (int m = 0; m < RPL; ++m) {
     const int64_t r = row0 + static_cast<int64_t>(m) * kSlots;
@@ -349,9 +384,9 @@ gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
     for (int n = 0; n < NC; ++n) {
       const int total = lanes_sum<L>(acc[m][n]);
       if (r < rows && lam == n % L) {
-        const float t = ws * act_scale[n];
-        float v = epilogue(total, row_sum[n], t);
-        if (bias) v = add_bias(v, bias[r]);
+        const float t = ws * asc[n];
+        float v = epilogue(total, rsum[n], t);
+        if (bias) v = add_bias(v, bv[m]);
         y[static_cast<int64_t>(n) * ldy + r] = v;
         if (dot_out) dot_out[static_cast<int64_t>(n) * ldy + r] = total;
       }
@@ -359,16 +394,6 @@ gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   }
 }
 
-// Raw buffer accesses: the descriptor bounds the tensor, out-of-range loads
-// read 0 and out-of-range stores are dropped by the hardware.
-typedef int v4i __attribute__((ext_vector_type(4)));
-constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // buffer offset beyond every descriptor's range
-constexpr int kBufferFlags = 0x00020000;       // raw buffer, 32-bit data format
-
-__device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0), static_cast<int>(bytes),
-                                           kBufferFlags);
-}
 
 // ---------------------------------------------------------------------------
 // Fused quantize + GEMV for small N*K (the decode shapes): one launch per
@@ -410,6 +435,22 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
       xv[n][i] = idx < k4 ? reinterpret_cast<const float4 *>(x + static_cast<int64_t>(n) * ldx)[idx]
                           : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
+
+  // Epilogue constants next, ahead of the weights (buffer loads keep their
+  // place; loaded at their use they would cost one more memory round trip
+  // before the stores): the weight scale from the in-band slot and this
+  // lane's biases.
+  const float ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_of(packed + rows * row_bytes, 4), 0, 0, 0));
+  float bv[RPL];
+  {
+    const __amdgpu_buffer_rsrc_t bbuf = buffer_of(bias, bias ? static_cast<uint32_t>(rows * 4) : 0u);
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+      const int64_t r = row0 + static_cast<int64_t>(m) * kSlots;
+      bv[m] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          bbuf, r < rows ? static_cast<uint32_t>(4 * r) : kOutOfRange, 0, 0));
+    }
+  }
 
   // 2. Weight loads for every row and chunk of this lane, unconditional:
   // rows past the end read as 0x00 bytes (all codes 0, which add nothing to
@@ -506,7 +547,6 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
   }
 
   // 5. Epilogue.
-  const float ws = *reinterpret_cast<const float *>(packed + rows * row_bytes);
 #pragma unroll
   for (int m = 0; m < RPL; ++m) {
     const int64_t r = row0 + static_cast<int64_t>(m) * kSlots;
@@ -517,7 +557,7 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
         const int32_t rs = red_i[n][0] + red_i[n][1] + red_i[n][2] + red_i[n][3];
         const float t = ws * sc[n];
         float v = epilogue(total, rs, t);
-        if (bias) v = add_bias(v, bias[r]);
+        if (bias) v = add_bias(v, bv[m]);
         y[static_cast<int64_t>(n) * ldy + r] = v;
         if (dot_out) dot_out[static_cast<int64_t>(n) * ldy + r] = total;
       }
@@ -1402,6 +1442,26 @@ gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   const bool q_row_ok = li < N;
   const int perm = 4 * (4 * li + kb);  // ds_bpermute source lane (bytes) of MFMA lane (li, kb)
 
+  // Epilogue constants of this lane (activation row li, weight rows
+  // o0 + 4*kb + r), loaded before the weight stream: the weight scale from
+  // the in-band slot, the row's scale and sum, the biases.  Buffer loads keep
+  // their place; loaded at their use they would add a memory round trip
+  // before the stores.
+  const float ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_of(packed + rows * static_cast<int64_t>(row_bytes), 4), 0, 0, 0));
+  const uint32_t n_off = li < N ? static_cast<uint32_t>(4 * li) : kOutOfRange;
+  const float asc = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_of(act_scale, static_cast<uint32_t>(4 * N)), n_off, 0, 0));
+  const int32_t rsm = __builtin_amdgcn_raw_buffer_load_b32(buffer_of(row_sum, static_cast<uint32_t>(4 * N)), n_off, 0, 0);
+  float bvr[4];
+  {
+    const __amdgpu_buffer_rsrc_t bbuf = buffer_of(bias, bias ? static_cast<uint32_t>(rows * 4) : 0u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t o = o0 + 4 * kb + r;
+      bvr[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(bbuf, o < rows ? static_cast<uint32_t>(4 * o) : kOutOfRange, 0, 0));
+    }
+  }
+
   // Step slot i of batch g of this wave: K-step wave + W*(SPW*g + i).
   auto load = [&](int g, v4i (&wv)[SPW], v4i (&qv)[SPW][4]) {
 #pragma unroll
@@ -1454,11 +1514,8 @@ gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 
   // Lane (li, kb) holds the dots of weight rows o0 + 4*kb + r (r = 0..3) with
   // activation row li.
-  const float ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-      buffer_of(packed + rows * static_cast<int64_t>(row_bytes), 4), 0, 0, 0));
-  const int n = li < N ? li : 0;
-  const float t = ws * act_scale[n];
-  const int32_t rs = row_sum[n];
+  const float t = ws * asc;
+  const int32_t rs = rsm;
   const int64_t o = o0 + 4 * kb;
   const uint32_t out_bytes = static_cast<uint32_t>(((N - 1) * ldy + rows - o0) * 4);
   const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + o0, out_bytes);
@@ -1470,7 +1527,7 @@ gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   if (bias) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (o + r < rows) v[r] = add_bias(v[r], bias[o + r]);
+      if (o + r < rows) v[r] = add_bias(v[r], bvr[r]);
   }
   if constexpr (VEC4) {
     const uint32_t off = li < N && o < rows ? 4 * base : kOutOfRange;

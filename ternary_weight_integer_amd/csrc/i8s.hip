@@ -705,6 +705,22 @@ __global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(const MatArgs a) 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int o0 = (item % blocks_o) * 16, n0 = (item / blocks_o) * (16 * FN);
     const bool o_ok = o0 + li < OC;
+    // Epilogue constants of this lane (channels o0 + 4*kq + r; rows
+    // n0 + 16*fn + li), loaded ahead of the operand stream so that wave 0
+    // does not wait on memory before its stores.
+    const int oc = o0 + 4 * kq;
+    float cv[4], rsv[FN];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      cv[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          bbuf, oc + r < OC ? static_cast<uint32_t>(4 * (oc + r)) : kOutOfRange, 0, 0));
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int n = n0 + 16 * fn + li;
+      rsv[fn] = MODE == kModeF32 ? __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                       rbuf, n < N ? static_cast<uint32_t>(4 * n) : kOutOfRange, 0, 0))
+                                 : 0.0f;
+    }
     const uint32_t wrow = static_cast<uint32_t>(o0 + li) * static_cast<uint32_t>(IC) + 16 * kq;
     uint32_t xrow[FN];
     bool n_ok[FN];
@@ -758,12 +774,6 @@ __global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(const MatArgs a) 
         acc[fn] = tot;
       }
       // Lane (li, kq): channels o0 + 4*kq + r of row n0 + 16*fn + li.
-      const int oc = o0 + 4 * kq;
-      float cv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        cv[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            bbuf, oc + r < OC ? static_cast<uint32_t>(4 * (oc + r)) : kOutOfRange, 0, 0));
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int n = n0 + 16 * fn + li;
@@ -773,9 +783,7 @@ __global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(const MatArgs a) 
           const bool ok = n < N && oc + r < OC;
           const uint32_t off = ok ? row + oc + r : kOutOfRange;
           if constexpr (MODE == kModeF32) {
-            const float rs = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                rbuf, n < N ? static_cast<uint32_t>(4 * n) : kOutOfRange, 0, 0));
-            const float y = rs * cv[r] * static_cast<float>(acc[fn][r]);
+            const float y = rsv[fn] * cv[r] * static_cast<float>(acc[fn][r]);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(y), ybuf, ok ? 4 * off : kOutOfRange, 0, 0);
           } else {
             const float v = fmaxf(static_cast<float>(acc[fn][r]) * t + cv[r], lo);
