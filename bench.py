@@ -21,8 +21,9 @@ Measurement:
   * the dominant kernel's average launch duration comes from a second graph of
     back-to-back launches of that kernel alone, timed the same way inside the
     same bracket; roofline.achieved = algorithmic bytes per launch / that time;
-  * cpu_baseline: the CPU oracle (plain scalar C, one thread) on the same
-    workload, repeated for about --cpu-seconds.
+  * cpu_baseline: the CPU oracle (plain scalar C) on the same workload,
+    repeated for about --cpu-seconds: half of it on all host cores (up to
+    16 threads, output features split), half on one thread.
 
 --workload encoder_mlp times one I8_S encoder block MLP instead (stage 3 of a
 4-second clip: FC1 256 -> 1024 with bias and ReLU, then FC2 1024 -> 256 with
@@ -114,21 +115,44 @@ def measured_traffic(workload: str):
 
 
 def cpu_baseline(case, seconds: float):
+    """The oracle, unchanged, on all host cores: the output features are split
+    into one row slice per thread (a row slice of the packed payload plus the
+    scale slot is itself a packed tensor), each thread calls the scalar C
+    oracle on its slice (ctypes releases the GIL), as the pages' schedule
+    splits output features over threads.  Also timed on one thread."""
+    import concurrent.futures
+
     import numpy as np
 
     import oracle
     packed = oracle.pack(case.w, case.ws)
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        oracle.mul_mat(packed, case.rows, case.K, case.x)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    rb = case.K // 4
+    slot = packed[case.rows * rb:]
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    bounds = [case.rows * i // cores for i in range(cores + 1)]
+    slices = [(np.concatenate([packed[a * rb:b * rb], slot]), b - a) for a, b in zip(bounds, bounds[1:]) if b > a]
+
+    def run(sl):
+        oracle.mul_mat(sl[0], sl[1], case.K, case.x)
+
+    def timed(fn, budget):
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return calls, el
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(slices)) as pool:
+        calls, el = timed(lambda: list(pool.map(run, slices)), seconds / 2)
+    calls1, el1 = timed(lambda: oracle.mul_mat(packed, case.rows, case.K, case.x), seconds / 2)
     wbytes = case.rows * case.K // 4
-    return {"value": round(wbytes * calls / el / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{calls} full calls of the same workload ({case.name}, quantize+contract+epilogue, "
-                      f"scalar C, 1 thread) in {el:.1f} s",
+    return {"value": round(wbytes * calls / el / 1e9, 6), "unit": "GB/s", "cores": len(slices), "kind": "oracle",
+            "sample": f"{calls} full calls of the same workload ({case.name}, quantize+contract+epilogue, scalar C) "
+                      f"on {len(slices)} threads, output features split, in {el:.1f} s",
+            "one_thread": {"value": round(wbytes * calls1 / el1 / 1e9, 6), "calls": calls1,
+                           "ms_per_call": round(el1 / calls1 * 1e3, 3)},
             "cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0)),
             "ms_per_call": round(el / calls * 1e3, 3)}
 
