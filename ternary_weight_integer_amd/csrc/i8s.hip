@@ -923,11 +923,12 @@ int launch_plain(MatArgs a, hipStream_t stream) {
 // 4 = 128 x 64 x 1, 5 = 128 x 64 x 2, 6 = 64 x 128 x 2, 7 = 128 x 64 x 4, 8 = 64 x 64 x 1;
 // 9 = the skinny kernel (16 channels x up to 64 rows per workgroup, waves split K).
 // The skinny kernel when the tile kernel would have too few tiles: up to 64
-// rows, or up to 256 rows with fewer than 128 tiles of 128 x 64 (measured on
-// the encoder, connector and decoder shapes).
+// rows, up to 256 rows with fewer than 128 tiles of 128 x 64, or up to 512
+// rows with fewer than 64 (measured on the encoder, connector and decoder
+// shapes).
 bool skinny_wins(int64_t OC, int64_t N) {
   const int64_t tiles = ((OC + 127) / 128) * ((N + 63) / 64);
-  return N <= 64 || (N <= 256 && tiles < 128);
+  return N <= 64 || (N <= 256 && tiles < 128) || (N <= 512 && tiles < 64);
 }
 
 int auto_variant(int64_t OC, int64_t IC, int64_t N) {
