@@ -41,6 +41,11 @@ projections at N = 1 instead (q/k/v grouped with their F32 biases, o,
 gate/up grouped, down: four launches), rotating over 28 layers of weights
 (327.5 MB), beside the same projections as seven separate calls.
 
+--workload layer_sweep times each of the seven projections on its own at
+N = 1 and at N = 64 (fourteen i2s_mul_mat calls per step, each weight
+rotating over >= 512 MiB of copies) and reports every one of them: step and
+dominant-kernel time, weight GB/s, int8 TOPS and its roofline fraction.
+
 Prints one JSON line.
 """
 
@@ -73,7 +78,7 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="decode_up",
                    choices=["decode_up", "prefill_gate", "down_small_batch", "small", "decode_layer", "encoder_mlp",
-                            "w8a8_prefill", "w8a8_decode"])
+                            "w8a8_prefill", "w8a8_decode", "layer_sweep"])
     p.add_argument("--stage", type=int, default=3, help="encoder stage of --workload encoder_mlp (0..6)")
     p.add_argument("--copies", type=int, default=0, help="weight copies to rotate over (0 = enough for 512 MiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -190,6 +195,48 @@ def copy_kernel_only(mib: int):
         torch.mul(a, 1.0, out=b)
     torch.cuda.synchronize()
     print(json.dumps({"copy_kernel_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}), flush=True)
+
+
+def kernel_name_of(kind: int, variant: int) -> str:
+    if kind == 2:
+        return "gemm_pipe_kernel" if variant == 10 else ("gemm_res_kernel" if variant >= 5 else "gemm_kernel")
+    return {1: "gemv_kernel", 3: "gemv_fused_kernel", 4: "gemv_mfma_kernel"}[kind]
+
+
+def alg_bytes_of(kind: int, rows: int, K: int, N: int) -> int:
+    """Algorithmic bytes of one launch of the dominant kernel.  Fused: packed
+    weights + F32 activations + F32 outputs + the weight scale.  Otherwise:
+    packed weights + int8 activations + F32 outputs + per-row scale and row
+    sum + the weight scale."""
+    if kind == 3:
+        return rows * K // 4 + 4 * N * K + 4 * N * rows + 4
+    return rows * K // 4 + N * K + 4 * N * rows + 8 * N + 4
+
+
+def copy_ceiling(torch, nbytes: int):
+    """A plain copy kernel moving the same number of bytes as one launch of
+    the dominant kernel (half read, half written; F32 elementwise copy),
+    sources rotating over >= 512 MiB so reads come from HBM: the attainable
+    time of a memory-bound kernel this short on this GPU."""
+    dev = torch.device("cuda:0")
+    n = max(64, (nbytes // 2 + 255) // 256 * 64)   # floats per copy, 256-byte multiple
+    R = max(1, -(-ROTATE_BYTES // (4 * n)))
+    src = torch.ones(R * n, dtype=torch.float32, device=dev)
+    dst = torch.empty(n, dtype=torch.float32, device=dev)
+    launches = max(R, 256)
+    g = graph_of(lambda: [torch.mul(src[(i % R) * n:(i % R + 1) * n], 1.0, out=dst) for i in range(launches)], torch)
+    g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    moved = 8 * n
+    del g, src, dst
+    return {"bytes_moved": moved, "us": round(us, 4), "gbs": round(moved / (us * 1e-6) / 1e9, 2),
+            "frac_of_hbm": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "sources_rotated": R}
 
 
 LAYER_PROJ = ("q", "k", "v", "o", "gate", "up", "down")
@@ -498,6 +545,151 @@ def bench_w8a8(args, torch):
     return out
 
 
+def bench_sweep(args, torch, i2s):
+    """Each Qwen2-1.5B projection alone at N = 1 and N = 64 (ws 0.015, x ~
+    N(0,1)).  A step is the fourteen i2s_mul_mat calls once each; every
+    projection's packed weight is replicated into >= 512 MiB of copies and
+    call i of a case uses copy i mod R, so weights come from HBM.  Per case,
+    its own graph of the whole call (max(R, 256) launches) and one of the
+    dominant kernel alone give the step and kernel times."""
+    from ternary_weight_integer_amd import workloads
+    dev = torch.device("cuda:0")
+    cases = workloads.layer_sweep_cases()
+    ws = i2s.new_workspace(64, 8960, dev)
+    copies = {}
+    prepared = []
+    for c in cases:
+        proj = c.meta["proj"]
+        if proj not in copies:
+            p0 = i2s.i2s_pack(torch.from_numpy(c.w).to(dev), c.ws)
+            R = max(1, -(-ROTATE_BYTES // p0.numel()))
+            copies[proj] = [p0] + [p0.clone() for _ in range(R - 1)]
+        x = torch.from_numpy(c.x).to(dev)
+        y = torch.empty((c.N, c.rows), dtype=torch.float32, device=dev)
+        prepared.append((c, copies[proj], x, y))
+    torch.cuda.synchronize()
+
+    def call(pc, i):
+        c, cp, x, y = pc
+        i2s.i2s_mul_mat(cp[i % len(cp)], c.rows, c.K, x, workspace=ws, y=y)
+
+    def timed_graph(fn, n):
+        g = graph_of(lambda: [fn(i) for i in range(n)], torch)
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n  # us per launch
+
+    for i in range(args.warmup):
+        for pc in prepared:
+            call(pc, i)
+    torch.cuda.synchronize()
+    eager = [pc[3].clone() for pc in prepared]
+    K_steps = args.steps
+    g = graph_of(lambda: [call(pc, i) for i in range(K_steps) for pc in prepared], torch)
+    g.replay()
+    torch.cuda.synchronize()
+    for pc, ye in zip(prepared, eager):
+        if not torch.equal(pc[3].view(torch.int32), ye.view(torch.int32)):
+            raise RuntimeError(f"graph replay result differs from the eager result for {pc[0].name}")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / K_steps
+
+    rows_out, wbytes_step, ops_step, kern_total = [], 0, 0, {}
+    for j, pc in enumerate(prepared):
+        c, cp, x, y = pc
+        rows, K, N = c.rows, c.K, c.N
+        n = max(len(cp), 256)
+        call_us = timed_graph(lambda i: call(pc, i), n)
+        kind = i2s.i2s_mul_mat_kernel(rows, K, N)
+        variant = i2s.i2s_mul_mat_variant(rows, K, N)
+        if kind == i2s.KERNEL_FUSED:
+            kern = lambda i: i2s.i2s_mul_mat_ex(cp[i % len(cp)], rows, K, x, workspace=ws, y=y, kernel=kind)
+        else:
+            i2s.i2s_quantize_act_ws(x, ws)
+            kern = lambda i: i2s.i2s_mul_mat_ws(cp[i % len(cp)], rows, K, N, ws, y=y, kernel=kind)
+        kern_us = timed_graph(kern, n)
+        if not torch.equal(y.view(torch.int32), eager[j].view(torch.int32)):
+            raise RuntimeError(f"kernel-only result differs from the eager result for {c.name}")
+        wb = rows * K // 4
+        alg = alg_bytes_of(kind, rows, K, N)
+        gbs = alg / (kern_us * 1e-6) / 1e9
+        name = kernel_name_of(kind, variant)
+        wbytes_step += wb
+        ops_step += 2 * rows * K * N
+        kern_total[name] = kern_total.get(name, 0.0) + kern_us
+        ceiling = copy_ceiling(torch, alg)
+        rows_out.append({"case": c.name, "rows": rows, "K": K, "N": N, "copies_rotated": len(cp),
+                         "call_us": round(call_us, 3), "weight_gbs": round(wb / (call_us * 1e-6) / 1e9, 2),
+                         "int8_tops": round(2 * rows * K * N / (call_us * 1e-6) / 1e12, 3),
+                         "kernel": name, "kernel_variant": variant, "kernel_us": round(kern_us, 3),
+                         "kernel_alg_bytes": alg, "kernel_gbs": round(gbs, 2),
+                         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "mfma_frac": round(2 * rows * K * N / (kern_us * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
+                         "copy_ceiling_us": ceiling["us"]})
+    # The dominant kernel of the sweep: the one with the most time summed over
+    # the cases; its roofline line is its largest single case.
+    dom = max(kern_total, key=kern_total.get)
+    big = max((r for r in rows_out if r["kernel"] == dom), key=lambda r: r["kernel_us"])
+    out = {
+        "metric": METRIC,
+        "value": round(wbytes_step / (step_ms * 1e-3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "qwen2_1p5b_projection_sweep_N1_N64", "calls_per_step": len(prepared),
+                   "weight_bytes_per_step": wbytes_step, "timing": "hip_graph"},
+        "int8_tops": round(ops_step / (step_ms * 1e-3) / 1e12, 4),
+        "wall_s": round(wall, 4),
+        "sweep": rows_out,
+        "roofline": {"bound": "hbm", "achieved": big["kernel_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": big["hbm_frac"], "traffic": None, "kernel": f"{dom} ({big['case']})",
+                     "kernel_us": big["kernel_us"], "alg_bytes_per_launch": big["kernel_alg_bytes"]},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_sweep(cases, args.cpu_seconds)
+    return out
+
+
+def cpu_baseline_sweep(cases, seconds: float):
+    import oracle
+    packed = {}
+    for c in cases:
+        packed.setdefault(c.meta["proj"], oracle.pack(c.w, c.ws))
+    wbytes = sum(c.rows * c.K // 4 for c in cases)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        for c in cases:
+            oracle.mul_mat(packed[c.meta["proj"]], c.rows, c.K, c.x)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(wbytes * calls / el / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full sweeps (14 calls: 7 projections at N = 1 and 64, scalar C, 1 thread) "
+                      f"in {el:.1f} s",
+            "cpu_model": cpu_model(), "host_cores": len(os.sched_getaffinity(0)),
+            "ms_per_call": round(el / calls * 1e3, 3)}
+
+
 def cpu_baseline_w8a8(case, seconds: float):
     import oracle
     wq, wsc = oracle.w8a8_quantize_weight(case.w)
@@ -588,6 +780,9 @@ def main(argv=None):
     if args.workload.startswith("w8a8_"):
         print(json.dumps(bench_w8a8(args, torch)), flush=True)
         return 0
+    if args.workload == "layer_sweep":
+        print(json.dumps(bench_sweep(args, torch, i2s)), flush=True)
+        return 0
     dev = torch.device("cuda:0")
     case = make_case(args.workload)
     rows, K, N = case.rows, case.K, case.N
@@ -660,19 +855,9 @@ def main(argv=None):
 
     ops = 2 * rows * K * N
     value = wbytes / (step_ms * 1e-3) / 1e9
-    # Algorithmic bytes of one launch of the dominant kernel.  Fused: packed
-    # weights + F32 activations + F32 outputs + the weight scale.  Otherwise:
-    # packed weights + int8 activations + F32 outputs + per-row scale and row
-    # sum + the weight scale.
-    if kernel_kind == i2s.KERNEL_FUSED:
-        alg_bytes = wbytes + 4 * N * K + 4 * N * rows + 4
-    else:
-        alg_bytes = wbytes + N * K + 4 * N * rows + 8 * N + 4
+    alg_bytes = alg_bytes_of(kernel_kind, rows, K, N)
     variant = i2s.i2s_mul_mat_variant(rows, K, N)
-    if kernel_kind == 2:
-        kernel_name = "gemm_pipe_kernel" if variant == 10 else ("gemm_res_kernel" if variant >= 5 else "gemm_kernel")
-    else:
-        kernel_name = {1: "gemv_kernel", 3: "gemv_fused_kernel", 4: "gemv_mfma_kernel"}[kernel_kind]
+    kernel_name = kernel_name_of(kernel_kind, variant)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -706,11 +891,14 @@ def main(argv=None):
                                "traffic": measured_traffic(args.workload), "kernel": kernel_name, "kernel_variant": variant,
                                "kernel_us": round(kern_us, 4), "alg_ops_per_launch": ops,
                                "alg_bytes_per_launch": alg_bytes}
+    if kern_us is not None and kernel_kind != 2:
+        out["roofline"]["copy_ceiling"] = copy_ceiling(torch, alg_bytes)
     props = torch.cuda.get_device_properties(0)
     out["gpu"] = {"name": props.name, "cus": props.multi_processor_count,
                   "arch": getattr(props, "gcnArchName", "")}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        out["cpu_baseline"]["gpu_over_cpu"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
     return 0
 

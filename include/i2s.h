@@ -121,7 +121,7 @@ int i2s_mul_mat(const uint8_t *packed, int64_t rows, int64_t K,
  * on its own.  kernel: 0 = automatic (as i2s_mul_mat), 1 = GEMV (N <= 8),
  * 2 = MFMA GEMM (any N >= 1), 3 = fused quantize + GEMV in one launch
  * (N <= 4, K <= 9216; it does not use the workspace), 4 = skinny MFMA
- * (N <= 16).  variant: 0 =
+ * (N <= 64).  variant: 0 =
  * automatic, else a 1-based index into the kernel's tile configurations
  * (i2s_kernel_variants).  Returns I2S_EKERNEL for an unknown pair or a kernel
  * that does not accept this N or K.  After any matmul call the workspace

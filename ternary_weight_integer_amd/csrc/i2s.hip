@@ -23,6 +23,15 @@
 // chunk j of packed weights (row bytes 16j..16j+15) pairs with the 64
 // contiguous qp bytes 64j..64j+63.  Integer sums do not depend on the order
 // of their terms, so this permutation changes no result bit.
+//
+// The workspace also has room for an MFMA-tiled copy qt of qp, the operand
+// order of the skinny int8-MFMA kernel, filled when a contraction has at most
+// 64 rows: for each block b of 16 activation rows, each 256-position step st
+// and each chunk d = 0..3, one KiB in which lane l = i + 16*kb (i, kb: 0..15,
+// 0..3) holds at 16*l the 16 bytes qp[16b + i][256*st + 64*kb + 16*d ..], so
+// one 16-byte load per lane reads a whole operand from contiguous memory.
+// Slots of rows >= N and of positions >= K are never written (the kernel
+// does not read them).
 
 #include <hip/hip_runtime.h>
 
@@ -40,6 +49,7 @@ constexpr int kScaleSlot = 32;
 constexpr unsigned kCodeMask = 0x03030303u;
 constexpr int64_t kMaxK = 8454528;  // 2*127*K stays below 2^31 (int32 accumulators)
 constexpr int64_t kMaxDim = 0x7fffffff;
+constexpr int64_t kTiledMaxN = 64;  // largest contraction N for which the quantizer fills the tiled copy
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -47,9 +57,20 @@ struct ActWorkspace {
   int8_t *q;
   float *scale;
   int32_t *row_sum;
+  int8_t *qt;          // the MFMA-tiled copy of q, or nullptr where it is not filled
+  int64_t qt_row0;     // tiled-copy row of q's row 0 (a batch's first row)
 };
 
-inline ActWorkspace carve_workspace(void *base, int64_t N, int64_t K) {
+// Bytes of the MFMA-tiled copy: ceil(N/16) blocks x ceil(K/256) steps x 4 KiB.
+inline size_t tiled_bytes(int64_t N, int64_t K) {
+  if (N < 1) return 0;
+  return static_cast<size_t>((N + 15) / 16) * static_cast<size_t>((K + 255) / 256) * 4096;
+}
+
+// The workspace of N activation rows of length K; the tiled copy is used
+// (qt set) when the contractions that read it have at most kTiledMaxN rows
+// (contraction_n: N, or a batch's rows).
+inline ActWorkspace carve_workspace(void *base, int64_t N, int64_t K, int64_t contraction_n) {
   char *p = static_cast<char *>(base);
   size_t q_bytes = align_up(static_cast<size_t>(N) * static_cast<size_t>(K), 256);
   size_t s_bytes = align_up(static_cast<size_t>(N) * 4, 256);
@@ -57,7 +78,15 @@ inline ActWorkspace carve_workspace(void *base, int64_t N, int64_t K) {
   ws.q = reinterpret_cast<int8_t *>(p);
   ws.scale = reinterpret_cast<float *>(p + q_bytes);
   ws.row_sum = reinterpret_cast<int32_t *>(p + q_bytes + s_bytes);
+  ws.qt = contraction_n <= kTiledMaxN && tiled_bytes(N, K) ? reinterpret_cast<int8_t *>(p + q_bytes + 2 * s_bytes)
+                                                            : nullptr;
+  ws.qt_row0 = 0;
   return ws;
+}
+
+// Offset in the tiled copy of byte p (group-interleaved order) of activation row n.
+__device__ inline int64_t tiled_offset(int64_t n, int64_t p, int64_t steps) {
+  return ((((n >> 4) * steps + (p >> 8)) * 4 + ((p >> 4) & 3)) << 10) + 16 * ((n & 15) + 16 * ((p >> 6) & 3)) + (p & 15);
 }
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -86,14 +115,16 @@ __device__ inline int wave_sum(int v) {
 // kInterleaved selects the workspace order above; otherwise q is row-major.
 // Activation row n is read from x + (n / n_inner) * bsx + (n % n_inner) * ldx
 // (batches of n_inner rows; contiguous rows have n_inner = N, ldx = K); q,
-// the scales and the row sums are written densely, row n at n.
+// the scales and the row sums are written densely, row n at n, and q also
+// into the MFMA-tiled copy qt when it is given (interleaved order only).
 
 constexpr int kQuantThreads = 256;
 
 template <bool kInterleaved>
 __global__ void __launch_bounds__(kQuantThreads)
 quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int64_t n_inner, int64_t ldx, int64_t bsx,
-                       int8_t *__restrict__ q, float *__restrict__ act_scale, int32_t *__restrict__ row_sum) {
+                       int8_t *__restrict__ q, float *__restrict__ act_scale, int32_t *__restrict__ row_sum,
+                       int8_t *__restrict__ qt) {
   __shared__ float red_f[kQuantThreads / 64];
   __shared__ int red_i[kQuantThreads / 64];
   const int64_t n = blockIdx.x;
@@ -135,6 +166,8 @@ quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int64_t n_inner, 
       out[sl] = packed;
     }
     *reinterpret_cast<uint4 *>(qr + 16 * u) = make_uint4(out[0], out[1], out[2], out[3]);
+    if (kInterleaved && qt)
+      *reinterpret_cast<uint4 *>(qt + tiled_offset(n, 16 * u, (K + 255) / 256)) = make_uint4(out[0], out[1], out[2], out[3]);
   }
   sum = wave_sum(sum);
   if (lane == 0) red_i[wave] = sum;
@@ -153,7 +186,8 @@ quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int64_t n_inner, 
 template <bool kInterleaved, int XPT, int THREADS>
 __global__ void __launch_bounds__(THREADS)
 quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int64_t n_inner, int64_t ldx, int64_t bsx,
-                           int8_t *__restrict__ q, float *__restrict__ act_scale, int32_t *__restrict__ row_sum) {
+                           int8_t *__restrict__ q, float *__restrict__ act_scale, int32_t *__restrict__ row_sum,
+                           int8_t *__restrict__ qt) {
   constexpr int kWaves = THREADS / 64;
   __shared__ float red_f[kWaves];
   __shared__ int red_i[kWaves];
@@ -198,6 +232,7 @@ quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int64_t n_inn
       const int jj = p & 127;
       const int off = kInterleaved ? (p & ~127) + 16 * ((jj & 31) >> 2) + 4 * (jj >> 5) : p;
       *reinterpret_cast<uint32_t *>(qr + off) = packed;
+      if (kInterleaved && qt) *reinterpret_cast<uint32_t *>(qt + tiled_offset(n, off, (K + 255) / 256)) = packed;
     }
   }
   sum = wave_sum(sum);
@@ -1406,7 +1441,7 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 }
 
 // ---------------------------------------------------------------------------
-// Skinny int8-MFMA contraction for 1 <= N <= 16 activation rows (the small
+// Skinny int8-MFMA contraction for 1 <= N <= 64 activation rows (the small
 // batches).  At N = 8 the v_dot4 GEMV spends most of its time on VALU work
 // (one v_dot4 per 4 codes per activation row); one v_mfma_i32_16x16x64_i8
 // does the same for 16 weight rows x 64 positions x 16 activation rows.
@@ -1416,18 +1451,24 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 // subtile's weights, and their int32 partial dots are summed through LDS.
 // The weights go in as operand A (lane i + 16*kb: row i; loaded
 // row-contiguous -- lane l reads row l/4, bytes 16*(l%4) of the step -- and
-// moved into that order by ds_bpermute), the group-interleaved activation
-// rows as operand B (lane j + 16*kb: activation row j, zero for j >= N).  A
-// wave issues the loads of SPW steps at a time, into one of two register
-// sets, before computing the previous SPW steps.
+// moved into that order by ds_bpermute), the activations as operand B, NB
+// blocks of 16 rows (lane j + 16*kb of block b: activation row 16*b + j,
+// zero for rows >= N) read from the workspace's MFMA-tiled copy, one
+// contiguous KiB per operand when the rows start on a 16-row block (a
+// batch's rows may not; each lane's address is computed on its own): each
+// unpacked weight operand feeds NB MFMAs.  A wave issues the loads of SPW steps at a time, into one of two
+// register sets, before computing the previous SPW steps.  After the LDS
+// reduction, wave b writes the outputs of activation block b.
 
-template <int W, int SPW, bool VEC4, bool DOT>
+template <int W, int NB, int SPW, bool VEC4, bool DOT>
 __global__ void __launch_bounds__(64 * W)
 gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
-                 const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
+                 const int8_t *__restrict__ qt, int64_t qt_row0, int64_t qt_bytes, int64_t N,
+                 const float *__restrict__ act_scale,
                  const int32_t *__restrict__ row_sum, float *__restrict__ y, int32_t *__restrict__ dot_out,
                  const float *__restrict__ bias, int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) v4i part[W][64];
+  static_assert(NB >= 1 && NB <= W, "one epilogue wave per activation block");
+  __shared__ __attribute__((aligned(16))) v4i part[W][NB][64];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, kb = lane >> 4;
@@ -1436,20 +1477,27 @@ gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   const int steps = static_cast<int>((K + 255) / 256);
   const int64_t rows_here = rows - o0 < 16 ? rows - o0 : 16;
   const __amdgpu_buffer_rsrc_t wbuf = buffer_of(packed + o0 * row_bytes, static_cast<uint32_t>(rows_here * row_bytes));
-  const __amdgpu_buffer_rsrc_t qbuf = buffer_of(qp, static_cast<uint32_t>(N * K));
+  const __amdgpu_buffer_rsrc_t qbuf = buffer_of(qt, static_cast<uint32_t>(qt_bytes));
   const uint32_t w_lane = (lane >> 2) * row_bytes + 16 * (lane & 3);
-  const uint32_t q_lane = static_cast<uint32_t>(li * K) + 64 * kb;
-  const bool q_row_ok = li < N;
   const int perm = 4 * (4 * li + kb);  // ds_bpermute source lane (bytes) of MFMA lane (li, kb)
+  // Tiled-copy offset of this lane's 16 bytes of block b, step 0, chunk 0;
+  // step st adds 4 KiB, chunk d adds 1 KiB.
+  uint32_t q_lane[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int64_t ng = qt_row0 + 16 * b + li;
+    q_lane[b] = static_cast<uint32_t>(((ng >> 4) * steps * 4 << 10) + 16 * ((ng & 15) + 16 * kb));
+  }
 
-  // Epilogue constants of this lane (activation row li, weight rows
-  // o0 + 4*kb + r), loaded before the weight stream: the weight scale from
-  // the in-band slot, the row's scale and sum, the biases.  Buffer loads keep
-  // their place; loaded at their use they would add a memory round trip
-  // before the stores.
+  // Epilogue constants of this lane as an epilogue wave (activation row
+  // 16*wave + li, weight rows o0 + 4*kb + r), loaded before the weight
+  // stream: the weight scale from the in-band slot, the row's scale and sum,
+  // the biases.  Buffer loads keep their place; loaded at their use they
+  // would add a memory round trip before the stores.
+  const int64_t n_ep = 16 * static_cast<int64_t>(wave) + li;
   const float ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
       buffer_of(packed + rows * static_cast<int64_t>(row_bytes), 4), 0, 0, 0));
-  const uint32_t n_off = li < N ? static_cast<uint32_t>(4 * li) : kOutOfRange;
+  const uint32_t n_off = wave < NB && n_ep < N ? static_cast<uint32_t>(4 * n_ep) : kOutOfRange;
   const float asc = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_of(act_scale, static_cast<uint32_t>(4 * N)), n_off, 0, 0));
   const int32_t rsm = __builtin_amdgcn_raw_buffer_load_b32(buffer_of(row_sum, static_cast<uint32_t>(4 * N)), n_off, 0, 0);
   float bvr[4];
@@ -1458,27 +1506,36 @@ gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t o = o0 + 4 * kb + r;
-      bvr[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(bbuf, o < rows ? static_cast<uint32_t>(4 * o) : kOutOfRange, 0, 0));
+      bvr[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(bbuf, wave < NB && o < rows ? static_cast<uint32_t>(4 * o) : kOutOfRange, 0, 0));
     }
   }
 
-  // Step slot i of batch g of this wave: K-step wave + W*(SPW*g + i).
-  auto load = [&](int g, v4i (&wv)[SPW], v4i (&qv)[SPW][4]) {
+  // Step slot i of batch g of this wave: K-step wave + W*(SPW*g + i).  Slots
+  // past the last step and blocks past row N issue no loads and no MFMAs
+  // (wave-uniform branches; their registers are never read).
+  auto load = [&](int g, v4i (&wv)[SPW], v4i (&qv)[SPW][NB][4]) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int st = wave + W * (SPW * g + i);
-      const bool ok = st < steps;
-      wv[i] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, ok ? w_lane + 64 * st : kOutOfRange, 0, 0);
+      if (st >= steps) continue;
+      wv[i] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, w_lane + 64 * st, 0, 0);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t qo = q_lane + 256 * st + 16 * d;  // past K (the half step of an odd group count) reads 0
-        qv[i][d] = __builtin_amdgcn_raw_buffer_load_b128(qbuf, ok && q_row_ok && 256 * st + 64 * kb + 16 * d < K ? qo : kOutOfRange,
-                                                         0, 0);
+      for (int b = 0; b < NB; ++b) {
+        if (16 * b >= N) continue;
+        const bool row_ok = 16 * b + li < N;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t qo = q_lane[b] + (4 * st + d) * 1024;  // past K (the half step of an odd group count) reads 0
+          qv[i][b][d] = __builtin_amdgcn_raw_buffer_load_b128(
+              qbuf, row_ok && 256 * st + 64 * kb + 16 * d < K ? qo : kOutOfRange, 0, 0);
+        }
       }
     }
   };
-  v4i acc[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
-  auto compute = [&](const v4i (&wv)[SPW], const v4i (&qv)[SPW][4]) {
+  v4i acc[NB][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b][0] = acc[b][1] = v4i{0, 0, 0, 0};
+  auto compute = [&](int g, const v4i (&wv)[SPW], const v4i (&qv)[SPW][NB][4]) {
     v4i a4[SPW];
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
@@ -1486,41 +1543,48 @@ gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       for (int e = 0; e < 4; ++e) a4[i][e] = __builtin_amdgcn_ds_bpermute(perm, wv[i][e]);
     __builtin_amdgcn_sched_barrier(0);  // all permutes in flight before the first use
 #pragma unroll
-    for (int i = 0; i < SPW; ++i)
+    for (int i = 0; i < SPW; ++i) {
+      if (wave + W * (SPW * g + i) >= steps) continue;
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        acc[d & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_codes(static_cast<uint32_t>(a4[i][d])), qv[i][d],
-                                                           acc[d & 1], 0, 0, 0);
+      for (int d = 0; d < 4; ++d) {
+        const v4i a = unpack_codes(static_cast<uint32_t>(a4[i][d]));
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (16 * b < N) acc[b][d & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qv[i][b][d], acc[b][d & 1], 0, 0, 0);
+      }
+    }
   };
 
   const int mine = steps > wave ? (steps - wave + W - 1) / W : 0;  // this wave's steps
   const int batches = (mine + SPW - 1) / SPW;
-  v4i wa[SPW], wb[SPW], qa[SPW][4], qb[SPW][4];
+  v4i wa[SPW], wb[SPW], qa[SPW][NB][4], qb[SPW][NB][4];
   load(0, wa, qa);
   for (int g = 0; g < batches; g += 2) {
     load(g + 1, wb, qb);
-    compute(wa, qa);
+    compute(g, wa, qa);
     if (g + 1 >= batches) break;
     load(g + 2, wa, qa);
-    compute(wb, qb);
+    compute(g + 1, wb, qb);
   }
 
-  part[wave][lane] = acc[0] + acc[1];
-  __syncthreads();
-  if (wave != 0) return;
-  v4i tot = part[0][lane];
 #pragma unroll
-  for (int w = 1; w < W; ++w) tot += part[w][lane];
+  for (int b = 0; b < NB; ++b) part[wave][b][lane] = acc[b][0] + acc[b][1];
+  __syncthreads();
+  if (wave >= NB) return;
+  v4i tot = part[0][wave][lane];
+#pragma unroll
+  for (int w = 1; w < W; ++w) tot += part[w][wave][lane];
 
-  // Lane (li, kb) holds the dots of weight rows o0 + 4*kb + r (r = 0..3) with
-  // activation row li.
+  // Lane (li, kb) of wave b holds the dots of weight rows o0 + 4*kb + r
+  // (r = 0..3) with activation row n_ep = 16*b + li.
   const float t = ws * asc;
   const int32_t rs = rsm;
   const int64_t o = o0 + 4 * kb;
   const uint32_t out_bytes = static_cast<uint32_t>(((N - 1) * ldy + rows - o0) * 4);
   const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + o0, out_bytes);
   const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + o0 : nullptr, DOT ? out_bytes : 0);
-  const uint32_t base = static_cast<uint32_t>(li * ldy + 4 * kb);  // element offset from y + o0
+  const bool n_ok = n_ep < N;
+  const uint32_t base = n_ok ? static_cast<uint32_t>(n_ep * ldy + 4 * kb) : 0u;  // element offset from y + o0
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = epilogue(tot[r], rs, t);
@@ -1530,14 +1594,14 @@ gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       if (o + r < rows) v[r] = add_bias(v[r], bvr[r]);
   }
   if constexpr (VEC4) {
-    const uint32_t off = li < N && o < rows ? 4 * base : kOutOfRange;
+    const uint32_t off = n_ok && o < rows ? 4 * base : kOutOfRange;
     const v4i yv = {__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])};
     __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, 0);
     if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b128(tot, dbuf, off, 0, 0);
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t off = li < N && o + r < rows ? 4 * (base + r) : kOutOfRange;
+      const uint32_t off = n_ok && o + r < rows ? 4 * (base + r) : kOutOfRange;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[r]), ybuf, off, 0, 0);
       if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(tot[r], dbuf, off, 0, 0);
     }
@@ -1912,11 +1976,16 @@ int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int
   }
 }
 
-// Skinny MFMA launch (kernel 4): one block per 16-row subtile, 8 waves.
-// Variant 1 issues 2 steps per batch, variant 2 issues 4 (measured slower on
-// the decoder shapes; kept for parity coverage of deeper batches).
+// Skinny MFMA launch (kernel 4): one block per 16-row subtile, NB = 1, 2 or 4
+// blocks of 16 activation rows (N <= 16, 32, 64); 8 waves, except 4 at
+// NB = 4 with more than 256 subtiles (its ~170 registers per lane allow one
+// 8-wave block per compute unit, or two 4-wave blocks: with more blocks than
+// compute units the shorter blocks win, measured on the decoder shapes).  Variant 1 issues
+// 2 steps per batch at NB = 1 and 1 step otherwise, variant 2 twice as many
+// where the activation registers allow (4, 2, 1; measured slower on the
+// decoder shapes, kept for parity coverage of deeper batches).
 constexpr int kSkinnyVariants = 2;
-constexpr int kSkinnyMaxN = 16;
+constexpr int kSkinnyMaxN = 64;
 
 int skinny_auto_variant(int64_t) { return 1; }
 
@@ -1925,35 +1994,54 @@ bool skinny_fits(int64_t rows, int64_t K, int64_t N) {
   return N <= kSkinnyMaxN && N * rows * 4 < lim && N * K < lim && 16 * (K / 4) + 64 < lim && (rows + 15) / 16 <= kMaxDim;
 }
 
-template <int SPW, bool VEC4, bool DOT>
+template <int NB, int SPW, bool VEC4, bool DOT>
 int launch_skinny_inst(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
                        int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_mfma_kernel<8, SPW, VEC4, DOT>), dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(512), 0,
-                     stream, packed, rows, K, ws.q, N, ws.scale, ws.row_sum, y, dot_out, bias, ldy);
+  // The tiled copy from the 16-row block holding this call's first row: the
+  // kernel's offsets stay 32-bit however many batches precede it.
+  const int64_t row0 = ws.qt_row0 & 15;
+  const int8_t *qt = ws.qt + (ws.qt_row0 >> 4) * ((K + 255) / 256) * 4096;
+  const int64_t tiles = (rows + 15) / 16;
+  const int64_t qbytes = static_cast<int64_t>(tiled_bytes(row0 + N, K));
+  if constexpr (NB == 4) {
+    if (tiles > 256) {
+      hipLaunchKernelGGL((gemv_mfma_kernel<4, NB, SPW, VEC4, DOT>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
+                         stream, packed, rows, K, qt, row0, qbytes, N, ws.scale, ws.row_sum, y, dot_out, bias, ldy);
+      return hip_status();
+    }
+  }
+  hipLaunchKernelGGL((gemv_mfma_kernel<8, NB, SPW, VEC4, DOT>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, stream,
+                     packed, rows, K, qt, row0, qbytes, N, ws.scale, ws.row_sum, y, dot_out, bias, ldy);
   return hip_status();
 }
 
-template <int SPW>
+template <int NB, int SPW>
 int launch_skinny_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
                       int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   // 32-bit buffer offsets: activation rows (N*K), one subtile's weights and
   // the outputs past the block's first row (N*rows*4) stay below 2^31.
-  if (!skinny_fits(rows, K, N) || N * ldy * 4 >= (int64_t{1} << 31)) return I2S_EKERNEL;
+  if (!skinny_fits(rows, K, N) || N > 16 * NB || N * ldy * 4 >= (int64_t{1} << 31) || !ws.qt ||
+      tiled_bytes(15 + N, K) >= (size_t{1} << 31))
+    return I2S_EKERNEL;
   const bool vec4 = (rows % 4) == 0 && (ldy % 4) == 0 && aligned16(y) && (!dot_out || aligned16(dot_out));
-  if (vec4) return dot_out ? launch_skinny_inst<SPW, true, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream)
-                           : launch_skinny_inst<SPW, true, false>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
-  return dot_out ? launch_skinny_inst<SPW, false, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream)
-                 : launch_skinny_inst<SPW, false, false>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+  if (vec4) return dot_out ? launch_skinny_inst<NB, SPW, true, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream)
+                           : launch_skinny_inst<NB, SPW, true, false>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+  return dot_out ? launch_skinny_inst<NB, SPW, false, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream)
+                 : launch_skinny_inst<NB, SPW, false, false>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
 }
 
 int launch_skinny(int variant, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
                   float *y, int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   if (variant == 0) variant = skinny_auto_variant(K);
-  switch (variant) {
-    case 1: return launch_skinny_cfg<2>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
-    case 2: return launch_skinny_cfg<4>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
-    default: return I2S_EKERNEL;
-  }
+  if (variant < 1 || variant > kSkinnyVariants) return I2S_EKERNEL;
+  const bool deep = variant == 2;
+  if (N <= 16)
+    return deep ? launch_skinny_cfg<1, 4>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream)
+                : launch_skinny_cfg<1, 2>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+  if (N <= 32)
+    return deep ? launch_skinny_cfg<2, 2>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream)
+                : launch_skinny_cfg<2, 1>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+  return launch_skinny_cfg<4, 1>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
 }
 
 inline bool k_ok(int64_t K) { return K > 0 && K % kGroupValues == 0; }
@@ -1966,7 +2054,7 @@ int check_common(int64_t rows, int64_t K) {
 }
 
 int quantize_launch(const float *x, int64_t N, int64_t K, int64_t n_inner, int64_t ldx, int64_t bsx, int8_t *q,
-                    float *s, int32_t *rs, bool interleaved,
+                    float *s, int32_t *rs, bool interleaved, int8_t *qt,
                     hipStream_t stream) {
   if (N > kMaxDim) return I2S_ERANGE;
   // The row sits in registers: XPT float4 per thread; longer rows get more
@@ -1975,10 +2063,10 @@ int quantize_launch(const float *x, int64_t N, int64_t K, int64_t n_inner, int64
   do {                                                                                                     \
     if (interleaved)                                                                                       \
       hipLaunchKernelGGL((quantize_rowsum_reg_kernel<true, XPT, T>), dim3(static_cast<unsigned>(N)),       \
-                         dim3(T), 0, stream, x, K, n_inner, ldx, bsx, q, s, rs);                                              \
+                         dim3(T), 0, stream, x, K, n_inner, ldx, bsx, q, s, rs, qt);                              \
     else                                                                                                   \
       hipLaunchKernelGGL((quantize_rowsum_reg_kernel<false, XPT, T>), dim3(static_cast<unsigned>(N)),      \
-                         dim3(T), 0, stream, x, K, n_inner, ldx, bsx, q, s, rs);                                              \
+                         dim3(T), 0, stream, x, K, n_inner, ldx, bsx, q, s, rs, nullptr);                         \
     return hip_status();                                                                                   \
   } while (0)
   if (K <= 4 * 256 * 2) I2S_QREG(2, 256);
@@ -1987,10 +2075,10 @@ int quantize_launch(const float *x, int64_t N, int64_t K, int64_t n_inner, int64
 #undef I2S_QREG
   if (interleaved)
     hipLaunchKernelGGL((quantize_rowsum_kernel<true>), dim3(static_cast<unsigned>(N)), dim3(kQuantThreads), 0, stream,
-                       x, K, n_inner, ldx, bsx, q, s, rs);
+                       x, K, n_inner, ldx, bsx, q, s, rs, qt);
   else
     hipLaunchKernelGGL((quantize_rowsum_kernel<false>), dim3(static_cast<unsigned>(N)), dim3(kQuantThreads), 0, stream,
-                       x, K, n_inner, ldx, bsx, q, s, rs);
+                       x, K, n_inner, ldx, bsx, q, s, rs, nullptr);
   return hip_status();
 }
 
@@ -2006,7 +2094,8 @@ extern "C" size_t i2s_packed_bytes(int64_t rows, int64_t K) {
 
 extern "C" size_t i2s_act_workspace_bytes(int64_t N, int64_t K) {
   if (N < 0 || !k_ok(K)) return 0;
-  return align_up(static_cast<size_t>(N) * static_cast<size_t>(K), 256) + 2 * align_up(static_cast<size_t>(N) * 4, 256);
+  return align_up(static_cast<size_t>(N) * static_cast<size_t>(K), 256) + 2 * align_up(static_cast<size_t>(N) * 4, 256) +
+         tiled_bytes(N, K);
 }
 
 extern "C" int i2s_pack(const int8_t *w, float weight_scale, int64_t rows, int64_t K, uint8_t *packed, void *stream) {
@@ -2030,7 +2119,7 @@ extern "C" int i2s_quantize_act(const float *x, int64_t N, int64_t K, int8_t *q,
   if (N == 0) return I2S_OK;
   if (!x || !q || !act_scale || !row_sum) return I2S_EINVAL;
   if (!aligned16(x) || !aligned16(q)) return I2S_EINVAL;
-  return quantize_launch(x, N, K, N, K, N * K, q, act_scale, row_sum, false, static_cast<hipStream_t>(stream));
+  return quantize_launch(x, N, K, N, K, N * K, q, act_scale, row_sum, false, nullptr, static_cast<hipStream_t>(stream));
 }
 
 namespace {
@@ -2062,9 +2151,16 @@ int check_mul_mat(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, con
   return I2S_OK;
 }
 
+// The skinny kernel up to N = 32, and up to N = 64 with at most 256 weight
+// subtiles (rows <= 4096); measured on the decoder shapes against the GEMM.
+bool skinny_auto(int64_t rows, int64_t K, int64_t N) {
+  if (!skinny_fits(rows, K, N)) return false;
+  return N <= 32 || (N <= kSkinnyMaxN && (rows + 15) / 16 <= 256);
+}
+
 int contract_auto_kernel(int64_t rows, int64_t K, int64_t N) {
   if (N == 1 || (N == 2 && K <= 2048)) return 1;
-  if (N <= kSkinnyMaxN && skinny_fits(rows, K, N)) return 4;
+  if (skinny_auto(rows, K, N)) return 4;
   return N <= 8 ? 1 : 2;
 }
 
@@ -2088,8 +2184,8 @@ extern "C" int i2s_quantize_act_ws(const float *x, int64_t N, int64_t K, void *w
   if (!x || !aligned16(x)) return I2S_EINVAL;
   if (!workspace || workspace_bytes < i2s_act_workspace_bytes(N, K)) return I2S_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I2S_EWORKSPACE;
-  ActWorkspace ws = carve_workspace(workspace, N, K);
-  return quantize_launch(x, N, K, N, K, N * K, ws.q, ws.scale, ws.row_sum, true, static_cast<hipStream_t>(stream));
+  ActWorkspace ws = carve_workspace(workspace, N, K, N);
+  return quantize_launch(x, N, K, N, K, N * K, ws.q, ws.scale, ws.row_sum, true, ws.qt, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const void *workspace,
@@ -2099,7 +2195,7 @@ extern "C" int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, in
   if (kernel == 3) return I2S_EKERNEL;  // the fused kernel quantizes x itself; x is not an argument here
   int st = check_mul_mat(packed, rows, K, N, workspace, workspace_bytes, y, dot_out, kernel, variant, &noop);
   if (st != I2S_OK || noop) return st;
-  ActWorkspace ws = carve_workspace(const_cast<void *>(workspace), N, K);
+  ActWorkspace ws = carve_workspace(const_cast<void *>(workspace), N, K, N);
   return contract(packed, rows, K, N, ws, y, dot_out, nullptr, rows, kernel, variant, static_cast<hipStream_t>(stream));
 }
 
@@ -2113,8 +2209,8 @@ extern "C" int i2s_mul_mat_ex(const uint8_t *packed, int64_t rows, int64_t K, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (kernel == 3 || (kernel == 0 && fused_auto(rows, N, K)))
     return launch_fused(variant, packed, rows, K, N, x, K, y, dot_out, nullptr, rows, s);
-  ActWorkspace ws = carve_workspace(workspace, N, K);
-  st = quantize_launch(x, N, K, N, K, N * K, ws.q, ws.scale, ws.row_sum, true, s);
+  ActWorkspace ws = carve_workspace(workspace, N, K, N);
+  st = quantize_launch(x, N, K, N, K, N * K, ws.q, ws.scale, ws.row_sum, true, ws.qt, s);
   if (st != I2S_OK) return st;
   return contract(packed, rows, K, N, ws, y, dot_out, nullptr, rows, kernel, variant, s);
 }
@@ -2156,8 +2252,8 @@ extern "C" int i2s_mul_mat_group_ex(const i2s_proj *projs, int count, int64_t K,
     }
     return launch_fused_group(variant, g, total_rows, K, N, x, s);
   }
-  ActWorkspace ws = carve_workspace(workspace, N, K);
-  int st = quantize_launch(x, N, K, N, K, N * K, ws.q, ws.scale, ws.row_sum, true, s);
+  ActWorkspace ws = carve_workspace(workspace, N, K, N);
+  int st = quantize_launch(x, N, K, N, K, N * K, ws.q, ws.scale, ws.row_sum, true, ws.qt, s);
   for (int p = 0; p < count && st == I2S_OK; ++p)
     if (projs[p].rows > 0)
       st = contract(projs[p].packed, projs[p].rows, K, N, ws, projs[p].y, projs[p].dot_out, projs[p].bias,
@@ -2194,13 +2290,14 @@ extern "C" int i2s_mul_mat_batched(const uint8_t *packed, int64_t rows, int64_t 
                         nullptr, ldy, s);
     return st;
   }
-  ActWorkspace ws = carve_workspace(workspace, NB, K);
-  st = quantize_launch(x, NB, K, N, ldx, bsx, ws.q, ws.scale, ws.row_sum, true, s);
+  ActWorkspace ws = carve_workspace(workspace, NB, K, N);
+  st = quantize_launch(x, NB, K, N, ldx, bsx, ws.q, ws.scale, ws.row_sum, true, ws.qt, s);
   for (int64_t b = 0; b < B && st == I2S_OK; ++b) {
-    ActWorkspace wb;
+    ActWorkspace wb = ws;
     wb.q = ws.q + b * N * K;
     wb.scale = ws.scale + b * N;
     wb.row_sum = ws.row_sum + b * N;
+    wb.qt_row0 = b * N;
     st = contract(packed, rows, K, N, wb, y + b * bsy, dot_out ? dot_out + b * bsy : nullptr, nullptr, ldy, 0, 0, s);
   }
   return st;

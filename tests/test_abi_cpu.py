@@ -26,9 +26,12 @@ def test_size_queries():
     assert i2s.i2s_packed_bytes(0, 128) == 32
     assert i2s.i2s_packed_bytes(4, 100) == 0
     assert i2s.i2s_packed_bytes(-1, 128) == 0
-    # q (N*K, 256-aligned) + scales + row sums (each 256-aligned)
-    assert i2s.i2s_act_workspace_bytes(1, 1536) == 1536 + 256 + 256
-    assert i2s.i2s_act_workspace_bytes(512, 1536) == 512 * 1536 + 2048 + 2048
+    # q (N*K, 256-aligned) + scales + row sums (each 256-aligned) + the
+    # MFMA-tiled copy (ceil(N/16) blocks x ceil(K/256) steps x 4 KiB)
+    assert i2s.i2s_act_workspace_bytes(1, 1536) == 1536 + 256 + 256 + 1 * 6 * 4096
+    assert i2s.i2s_act_workspace_bytes(512, 1536) == 512 * 1536 + 2048 + 2048 + 32 * 6 * 4096
+    assert i2s.i2s_act_workspace_bytes(17, 1152) == 19712 + 256 + 256 + 2 * 5 * 4096  # 17*1152 rounded up to 256
+    assert i2s.i2s_act_workspace_bytes(0, 1536) == 0
     assert i2s.i2s_act_workspace_bytes(3, 200) == 0
 
 
@@ -69,7 +72,7 @@ FAKE = 1 << 20  # a 16- and 256-byte aligned non-null address; never dereference
     ((FAKE, 4, 128, FAKE, 1, FAKE + 16, 1 << 20, FAKE, None, 0, 0), i2s.I2S_EWORKSPACE),
     ((FAKE, 4, 128, FAKE, 9, FAKE, 1 << 20, FAKE, None, 1, 0), i2s.I2S_EKERNEL),
     ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 5, 0), i2s.I2S_EKERNEL),
-    ((FAKE, 4, 128, FAKE, 17, FAKE, 1 << 20, FAKE, None, 4, 0), i2s.I2S_EKERNEL),
+    ((FAKE, 4, 128, FAKE, 65, FAKE, 1 << 20, FAKE, None, 4, 0), i2s.I2S_EKERNEL),
     ((FAKE, 4, 128, FAKE, 1, FAKE, 1 << 20, FAKE, None, 4, 9), i2s.I2S_EKERNEL),
     ((FAKE, 4, 128, FAKE, 5, FAKE, 1 << 20, FAKE, None, 3, 0), i2s.I2S_EKERNEL),
     ((FAKE, 4, 9344, FAKE, 1, FAKE, 1 << 20, FAKE, None, 3, 0), i2s.I2S_EKERNEL),
@@ -111,7 +114,13 @@ def test_mul_mat_kernel_choice():
     assert i2s.i2s_mul_mat_kernel(1536, 8960, 4) == i2s.KERNEL_SKINNY
     assert i2s.i2s_mul_mat_kernel(1536, 8960, 8) == i2s.KERNEL_SKINNY
     assert i2s.i2s_mul_mat_kernel(8960, 1536, 16) == i2s.KERNEL_SKINNY
-    assert i2s.i2s_mul_mat_kernel(8960, 1536, 17) == i2s.KERNEL_GEMM
+    assert i2s.i2s_mul_mat_kernel(8960, 1536, 32) == i2s.KERNEL_SKINNY   # N <= 32
+    assert i2s.i2s_mul_mat_kernel(8960, 1536, 33) == i2s.KERNEL_GEMM     # N > 32, 560 subtiles
+    assert i2s.i2s_mul_mat_kernel(4096, 1536, 64) == i2s.KERNEL_SKINNY   # 256 subtiles
+    assert i2s.i2s_mul_mat_kernel(4112, 1536, 64) == i2s.KERNEL_GEMM     # 257 subtiles
+    assert i2s.i2s_mul_mat_kernel(1536, 8960, 64) == i2s.KERNEL_SKINNY
+    assert i2s.i2s_mul_mat_kernel(256, 1536, 64) == i2s.KERNEL_SKINNY
+    assert i2s.i2s_mul_mat_kernel(256, 1536, 65) == i2s.KERNEL_GEMM
     assert i2s.i2s_mul_mat_kernel(8960, 1536, 512) == i2s.KERNEL_GEMM
     with pytest.raises(i2s.I2SError):
         i2s.i2s_mul_mat_kernel(4, 100, 1)
@@ -125,6 +134,6 @@ def test_mul_mat_variant_choice():
         v = i2s.i2s_mul_mat_variant(rows, K, N)
         assert 1 <= v <= i2s.i2s_kernel_variants(k), (rows, K, N, k, v)
     assert i2s.i2s_mul_mat_variant(8960, 1536, 512) == 7    # the resident GEMM
-    assert i2s.i2s_mul_mat_variant(1536, 1536, 64) == 10    # the pipelined GEMM
+    assert i2s.i2s_mul_mat_variant(1536, 1536, 128) == 10   # the pipelined GEMM
     with pytest.raises(i2s.I2SError):
         i2s.i2s_mul_mat_variant(4, 100, 1)

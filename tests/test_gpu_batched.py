@@ -62,9 +62,17 @@ def test_dense_batches(N):
     run_case(70, 1152, 3, N)
 
 
-@pytest.mark.parametrize("N", [1, 3, 8, 40])
+@pytest.mark.parametrize("N", [1, 3, 5, 8, 24, 40])
 def test_strided_batches(N):
     run_case(70, 1152, 3, N, pad_x=(2, 128), pad_y=(1, 8))
+
+
+def test_strided_batches_past_64_rows_in_all():
+    """Five batches of 17 rows (85 in all, batches starting inside a 16-row
+    block of the workspace's tiled activation copy) through the skinny MFMA
+    kernel."""
+    assert i2s.i2s_mul_mat_kernel(70, 1152, 17) == i2s.KERNEL_SKINNY
+    run_case(70, 1152, 5, 17, pad_x=(1, 0), pad_y=(1, 0), seed=7)
 
 
 def test_strided_single_batch_and_long_k():

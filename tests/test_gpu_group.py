@@ -119,7 +119,7 @@ def test_group_every_kernel_and_variant(K):
             combos += [(1, v) for v in range(1, i2s.i2s_kernel_variants(1) + 1)]
         if N <= 4:
             combos += [(3, v) for v in range(0, i2s.i2s_kernel_variants(3) + 1)]
-        if N <= 16:
+        if N <= 64:
             combos += [(4, v) for v in range(0, i2s.i2s_kernel_variants(4) + 1)]
         for kern, var in combos:
             check_group(ws, b, x, K, kernel=kern, variant=var)

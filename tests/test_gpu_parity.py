@@ -191,7 +191,7 @@ def test_grid_all_kernels_and_variants(K):
                 combos += [(1, v) for v in range(1, nv1 + 1)]
             if N <= 4:
                 combos += [(3, v) for v in range(1, i2s.i2s_kernel_variants(3) + 1)]
-            if N <= 16:
+            if N <= 64:
                 combos += [(4, v) for v in range(0, i2s.i2s_kernel_variants(4) + 1)]
             say(f"[grid] K={K} rows={rows} N={N} combos={len(combos)}")
             xg = dev(x)
@@ -233,6 +233,21 @@ def test_all_gemv_variants_full_decode_shapes(N):
                                            np.random.default_rng(2).choice(rows, 48, replace=False)]))
         for v in range(1, i2s.i2s_kernel_variants(1) + 1):
             check_mul_mat(case, kernel=1, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
+
+
+@pytest.mark.parametrize("N", [16, 17, 32, 33, 48, 64])
+def test_all_skinny_variants_decode_shapes(N):
+    """Skinny MFMA variants at every activation-block count (N <= 16, 32, 64)
+    on the decoder shapes against the oracle, with a ragged weight-row count
+    (not a multiple of 16 or of 4) for the scalar store path."""
+    for rows, K in [(8960, 1536), (1536, 8960), (256, 1536), (1501, 1536)]:
+        case = workloads.random_case(29 + N, rows, K, N)
+        pnp = oracle.pack(case.w, case.ws)
+        pg = gpu_pack(case.w, case.ws)
+        sample = np.unique(np.concatenate([np.arange(0, 24), np.arange(rows - 24, rows),
+                                           np.random.default_rng(4).choice(rows, 48, replace=False)]))
+        for v in range(1, i2s.i2s_kernel_variants(4) + 1):
+            check_mul_mat(case, kernel=4, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
 
 
 def test_all_gemm_variants_prefill_shape():
