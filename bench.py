@@ -101,7 +101,8 @@ def make_case(name):
 
 
 def kernel_source_digest(workload: str = "") -> str:
-    with open(KERNEL_SRC_I8S if workload == "encoder_mlp" else KERNEL_SRC, "rb") as f:
+    i8s = workload == "encoder_mlp" or workload.startswith("w8a8_")
+    with open(KERNEL_SRC_I8S if i8s else KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 

@@ -66,8 +66,10 @@ size_t i2s_packed_bytes(int64_t rows, int64_t K);
 /* Bytes of the activation workspace i2s_mul_mat needs for N rows of length K:
  * the int8 activations, then N F32 activation scales, then N int32 row sums
  * (the sidecar of "ggml-cpu: ternary I2_S matmul kernel (VibeASR, 3/4)",
- * Interface).  The layout inside is private to the library.  0 if K is not a
- * positive multiple of 128 or N < 0. */
+ * Interface), then a second copy of the int8 activations in the skinny
+ * MFMA kernel's operand order (ceil(N/16) * ceil(K/256) * 4096 bytes).  The
+ * layout inside is private to the library.  0 if K is not a positive
+ * multiple of 128 or N < 0. */
 size_t i2s_act_workspace_bytes(int64_t N, int64_t K);
 
 /* Pack ternary weights into I2_S.
@@ -100,8 +102,8 @@ int i2s_quantize_act(const float *x, int64_t N, int64_t K,
  * device from the packed tensor's scale slot.  Quantizes x into `workspace`,
  * then runs the contraction with the epilogue fused: for N <= 3 (K <= 9216)
  * one fused quantize + v_dot4 GEMV launch; otherwise a weight-streaming v_dot4
- * GEMV for N = 1, a skinny int8-MFMA kernel up to N = 16, an int8-MFMA GEMM
- * above (i2s_mul_mat_kernel tells which).
+ * GEMV for N = 1, a skinny int8-MFMA kernel up to N = 32 (N = 64 for at most
+ * 4096 rows), an int8-MFMA GEMM above (i2s_mul_mat_kernel tells which).
  *   packed     I2_S tensor of rows x K (as written by i2s_pack).
  *   x          [N][K] F32 activations, finite.
  *   workspace  >= i2s_act_workspace_bytes(N, K) bytes, 256-byte aligned;
