@@ -75,6 +75,22 @@ def test_strided_batches_past_64_rows_in_all():
     run_case(70, 1152, 5, 17, pad_x=(1, 0), pad_y=(1, 0), seed=7)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_random_batched_shapes(seed):
+    """Seeded random batch counts, row counts, K and padded strides (every
+    contraction path: fused, GEMV, skinny MFMA with batches starting inside
+    a 16-row block, GEMM)."""
+    rng = np.random.default_rng(2000 + seed)
+    for _ in range(4):
+        rows = int(rng.integers(1, 300))
+        K = 128 * int(rng.integers(1, 13))
+        B = int(rng.integers(1, 5))
+        N = int(rng.integers(1, 70))
+        pad_x = (int(rng.integers(0, 3)), 4 * int(rng.integers(0, 40)))
+        pad_y = (int(rng.integers(0, 3)), int(rng.integers(0, 20)))
+        run_case(rows, K, B, N, pad_x=pad_x, pad_y=pad_y, seed=int(rng.integers(1 << 30)))
+
+
 def test_strided_single_batch_and_long_k():
     run_case(64, 8960, 1, 4, pad_x=(0, 64), pad_y=(0, 4))
     run_case(36, 9344, 2, 2, pad_x=(1, 4), pad_y=(2, 0))    # beyond the fused K limit

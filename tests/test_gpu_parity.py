@@ -295,6 +295,36 @@ def test_ragged_shapes(rows, K, N):
         check_mul_mat(case, kernel=2, variant=1, sample=sample)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_every_kernel(seed):
+    """Seeded random shapes (rows 1..600, K a multiple of 128 up to 2560,
+    N 1..80) through every kernel and variant that accepts them, against the
+    oracle, bit for bit; every refusal must be I2S_EKERNEL."""
+    rng = np.random.default_rng(1000 + seed)
+    for _ in range(5):
+        rows = int(rng.integers(1, 601))
+        K = 128 * int(rng.integers(1, 21))
+        N = int(rng.integers(1, 81))
+        case = workloads.random_case(int(rng.integers(1 << 30)), rows, K, N, ws=float(rng.uniform(0.001, 0.1)))
+        pnp = oracle.pack(case.w, case.ws)
+        pg = gpu_pack(case.w, case.ws)
+        ye, de = oracle.mul_mat(pnp, rows, K, case.x, with_dot=True)
+        xg = dev(case.x)
+        combos = [(0, 0)] + [(k, v) for k in (1, 2, 3, 4) for v in range(1, i2s.i2s_kernel_variants(k) + 1)]
+        say(f"[random] seed={seed} rows={rows} K={K} N={N} combos={len(combos)}")
+        ran = 0
+        for kern, var in combos:
+            try:
+                y, d = i2s.i2s_mul_mat_ex(pg, rows, K, xg, dot_out=True, kernel=kern, variant=var)
+            except i2s.I2SError as e:
+                assert e.status == i2s.I2S_EKERNEL, (rows, K, N, kern, var, e.status)
+                continue
+            ran += 1
+            assert np.array_equal(host(d), de), (rows, K, N, kern, var)
+            assert np.array_equal(bits(host(y)), bits(ye)), (rows, K, N, kern, var)
+        assert ran >= 2
+
+
 def test_empty_inputs_are_noops():
     pg = gpu_pack(np.zeros((4, 128), np.int8), 1.0)
     y = torch.full((1, 4), 7.0, device=DEV)
