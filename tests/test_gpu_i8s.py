@@ -129,6 +129,29 @@ def test_every_variant_ragged(OC, IC, N):
             check_mm(W, OC, IC, X, N, None if relu else bias, relu, v)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shapes_every_variant(seed):
+    """Seeded random OC, IC (any, so the plain kernel is covered too), N,
+    scales and biases through every variant that accepts them; refusals must
+    be I2S_EKERNEL (an MFMA variant with IC % 16 != 0)."""
+    rng = np.random.default_rng(3000 + seed)
+    for _ in range(4):
+        OC = int(rng.integers(1, 260))
+        IC = int(rng.integers(1, 400))
+        N = int(rng.integers(1, 300))
+        W = rand_i8s(rng, OC, IC, float(rng.uniform(1e-4, 0.05)), full=True)
+        X = rand_i8s(rng, N, IC, float(rng.uniform(1e-3, 0.1)))
+        bias = rng.normal(0, float(rng.uniform(0.1, 50)), size=OC).astype(np.float32)
+        relu = int(rng.integers(0, 2))
+        for v in range(0, i8s.i8s_variants() + 1):
+            if v >= 2 and IC % 16:
+                with pytest.raises(i8s.I2SError) as ei:
+                    run_mm(W, OC, IC, X, N, bias, relu, v)
+                assert ei.value.status == i2s.I2S_EKERNEL
+                continue
+            check_mm(W, OC, IC, X, N, bias, relu, v, tag=f"random seed {seed}")
+
+
 @pytest.mark.parametrize("OC,IC,N", [(3, 7, 5), (33, 40, 21), (8, 1, 3), (5, 100, 2)])
 def test_plain_kernel_any_ic(OC, IC, N):
     rng = np.random.default_rng(IC)

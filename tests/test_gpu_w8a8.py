@@ -92,6 +92,27 @@ def test_matmul_every_variant(OC, K, M):
         assert np.array_equal(bits(host(y)), bits(rd))
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_random_shapes_every_variant(seed):
+    """Seeded random OC, K (a multiple of 16), M and scales through every
+    contraction variant, against the oracle bit for bit."""
+    rng = np.random.default_rng(4000 + seed)
+    for _ in range(4):
+        OC = int(rng.integers(1, 400))
+        K = 16 * int(rng.integers(1, 100))
+        M = int(rng.integers(1, 300))
+        wq = rng.integers(-127, 128, size=(OC, K), dtype=np.int8)
+        aq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+        ws = rng.uniform(1e-5, 0.05, size=OC).astype(np.float32)
+        as_ = rng.uniform(1e-4, 0.2, size=M).astype(np.float32)
+        rd, rc = oracle.w8a8_matmul(aq, as_, wq, ws, with_c=True)
+        for v in [0] + list(range(2, i8s.i8s_variants() + 1)):
+            say(f"w8a8_matmul random seed={seed} OC={OC} K={K} M={M} variant={v}")
+            y, c = w8a8.w8a8_matmul(dev(wq), dev(ws), dev(aq), dev(as_), dot_out=True, variant=v)
+            assert np.array_equal(host(c), rc)
+            assert np.array_equal(bits(host(y)), bits(rd))
+
+
 def test_matmul_full_scale():
     K = 8192
     wq = np.full((64, K), 127, np.int8)
