@@ -135,6 +135,32 @@ def test_quantize_matches_oracle(name, x):
     assert np.array_equal(host(rs), rse)
 
 
+def test_near_ties_through_every_kernel():
+    """Activation rows on and around the .5 boundaries of x/s, quantized
+    inside each contraction path (the fused kernels quantize for themselves):
+    any q off by one shows in dot (random codes over 96 weight rows) and y."""
+    ties = near_tie_rows()
+    K = max(r.size for r in ties)
+    x = np.stack([np.pad(r, (0, K - r.size)) for r in ties])
+    N = x.shape[0]
+    rng = np.random.default_rng(17)
+    w = workloads.ternary(rng, 96, K)
+    pnp = oracle.pack(w, 0.015)
+    pg = gpu_pack(w, 0.015)
+    ye, de = oracle.mul_mat(pnp, 96, K, x, with_dot=True)
+    xg = dev(x)
+    for kern in (0, 1, 2, 3, 4):
+        for var in range(0 if kern == 0 else 1, (1 if kern == 0 else i2s.i2s_kernel_variants(kern)) + 1):
+            try:
+                y, d = i2s.i2s_mul_mat_ex(pg, 96, K, xg, dot_out=True, kernel=kern, variant=var)
+            except i2s.I2SError as e:
+                assert e.status == i2s.I2S_EKERNEL
+                continue
+            say(f"[near ties] K={K} N={N} kernel={kern} variant={var}")
+            assert np.array_equal(host(d), de), (kern, var)
+            assert np.array_equal(bits(host(y)), bits(ye)), (kern, var)
+
+
 # --- the five workloads, through the automatic dispatch that the benchmark uses -------
 
 def test_small_case():
