@@ -94,17 +94,49 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 // ---------------------------------------------------------------------------
 // Block-wide reductions (256 threads = 4 wave64s).
 
+// Cross-lane steps as DPP moves (VALU, a few cycles each) instead of
+// ds_bpermute (an LDS round trip each, which nothing hides at one wave per
+// SIMD): within each quad, then each 8 and each 16 lanes by mirroring, then
+// across the four rows of 16 by reading one lane of each.  Max and integer
+// sums do not depend on the order of their terms.
+template <int CTRL>
+__device__ inline int dpp_move(int v) { return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false); }
+constexpr int kDppXor1 = 0xB1;         // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4E;         // quad_perm(2,3,0,1)
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within each 16
+
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppXor1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppXor2>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppHalfMirror>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppMirror>(__float_as_int(v))));
+  const int b = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+
+// Sum over each group of L consecutive lanes (L a power of two up to 64),
+// the result in every lane of the group.
+template <int L>
+__device__ inline int lanes_sum(int v) {
+  static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "power-of-two lane group");
+  if constexpr (L >= 2) v += dpp_move<kDppXor1>(v);
+  if constexpr (L >= 4) v += dpp_move<kDppXor2>(v);
+  if constexpr (L >= 8) v += dpp_move<kDppHalfMirror>(v);
+  if constexpr (L >= 16) v += dpp_move<kDppMirror>(v);
+  if constexpr (L == 32) {
+    const int lo = __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16);
+    const int hi = __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+    v = (threadIdx.x & 32) ? hi : lo;
+  }
+  if constexpr (L == 64)
+    v = (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+        (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
   return v;
 }
 
-__device__ inline int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
+__device__ inline int wave_sum(int v) { return lanes_sum<64>(v); }
 
 // ---------------------------------------------------------------------------
 // Activation quantization + row sum: one workgroup per activation row (the
@@ -307,12 +339,7 @@ __device__ inline float add_bias(float v, float b) { return v + b; }
 
 constexpr int kGemvThreads = 256;
 
-template <int L>
-__device__ inline int lanes_sum(int v) {
-#pragma unroll
-  for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
+
 
 // Raw buffer accesses: the descriptor bounds the tensor, out-of-range loads
 // read 0 and out-of-range stores are dropped by the hardware.
@@ -525,16 +552,41 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
     float a = fmaxf(fmaxf(red_f[n][0], red_f[n][1]), fmaxf(red_f[n][2], red_f[n][3]));
     a = fmaxf(a, 1e-5f);
     sc[n] = a / 127.0f;
+    // x / s as x * (1/s): |x / s| < 128, so the product is within 2^-15 of
+    // the correctly rounded quotient and rounds the same way unless that
+    // quotient lies within 2^-15 of a half-integer.  If any value of the wave
+    // comes within 2^-14 of one, the whole wave divides (a wave-uniform
+    // branch; per-value branches would serialize the values).
+    const float inv = 1.0f / sc[n];
+    float rq[XPT][4];
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const float e[4] = {xv[n][i].x, xv[n][i].y, xv[n][i].z, xv[n][i].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        rq[i][t] = e[t] * inv;
+        const float m = fabsf(rq[i][t]);
+        near = near || fabsf(m - truncf(m) - 0.5f) <= 0x1p-14f;
+      }
+    }
+    if (__any(near)) {
+#pragma unroll
+      for (int i = 0; i < XPT; ++i) {
+        const float e[4] = {xv[n][i].x, xv[n][i].y, xv[n][i].z, xv[n][i].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rq[i][t] = e[t] / sc[n];
+      }
+    }
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = tid + kGemvThreads * i;
       if (idx < k4) {
-        const float e[4] = {xv[n][i].x, xv[n][i].y, xv[n][i].z, xv[n][i].w};
         uint32_t packed4 = 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          float r = roundf(e[t] / sc[n]);
+          float r = roundf(rq[i][t]);
           r = fminf(fmaxf(r, -127.0f), 127.0f);
           const int qi = static_cast<int>(r);
           sum += qi;
