@@ -46,10 +46,21 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t by
                                            kBufferFlags);
 }
 
+// Max over the wave, in every lane: DPP moves within each quad, 8 and 16
+// lanes (VALU, a few cycles each, where ds_bpermute shuffles would be an LDS
+// round trip each), then one lane of each row of 16.  Max does not depend on
+// the order of its terms.
+template <int CTRL>
+__device__ inline int dpp_move(int v) { return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false); }
+
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, __int_as_float(dpp_move<0xB1>(__float_as_int(v))));   // quad_perm(1,0,3,2)
+  v = fmaxf(v, __int_as_float(dpp_move<0x4E>(__float_as_int(v))));   // quad_perm(2,3,0,1)
+  v = fmaxf(v, __int_as_float(dpp_move<0x141>(__float_as_int(v))));  // row_half_mirror
+  v = fmaxf(v, __int_as_float(dpp_move<0x140>(__float_as_int(v))));  // row_mirror
+  const int b = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }
 
 // max over the workgroup; red is 4 floats of LDS; every thread gets the result.
