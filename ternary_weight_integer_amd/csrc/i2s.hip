@@ -244,17 +244,40 @@ quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int64_t n_inn
   for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, red_f[w]);
   amax = fmaxf(amax, 1e-5f);
   const float s = amax / 127.0f;
+  // x / s as x * (1/s), with the whole wave dividing when any of its
+  // values comes within 2^-14 of a half-integer (the argument of the fused
+  // GEMV's quantizer: the result is roundf(x / s) bit for bit).
+  const float inv = 1.0f / s;
+  float rq[XPT][4];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      rq[i][t] = e[t] * inv;
+      const float m = fabsf(rq[i][t]);
+      near = near || fabsf(m - truncf(m) - 0.5f) <= 0x1p-14f;
+    }
+  }
+  if (__any(near)) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) rq[i][t] = e[t] / s;
+    }
+  }
   int sum = 0;
   int8_t *qr = q + n * K;
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const int idx = tid + THREADS * i;
     if (idx < k4) {
-      const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
       uint32_t packed = 0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        float r = roundf(e[t] / s);
+        float r = roundf(rq[i][t]);
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         const int qi = static_cast<int>(r);
         sum += qi;
