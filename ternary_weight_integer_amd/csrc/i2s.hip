@@ -249,7 +249,7 @@ quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int64_t n_inn
   // GEMV's quantizer: the result is roundf(x / s) bit for bit).
   const float inv = 1.0f / s;
   float rq[XPT][4];
-  bool near = false;
+  float dmin = 1.0f;  // nearest distance of a product to a half-integer
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
@@ -257,10 +257,10 @@ quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int64_t n_inn
     for (int t = 0; t < 4; ++t) {
       rq[i][t] = e[t] * inv;
       const float m = fabsf(rq[i][t]);
-      near = near || fabsf(m - truncf(m) - 0.5f) <= 0x1p-14f;
+      dmin = fminf(dmin, fabsf(m - truncf(m) - 0.5f));
     }
   }
-  if (__any(near)) {
+  if (__any(dmin <= 0x1p-14f)) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
@@ -582,7 +582,7 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
     // branch; per-value branches would serialize the values).
     const float inv = 1.0f / sc[n];
     float rq[XPT][4];
-    bool near = false;
+    float dmin = 1.0f;  // nearest distance of a product to a half-integer
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const float e[4] = {xv[n][i].x, xv[n][i].y, xv[n][i].z, xv[n][i].w};
@@ -590,10 +590,10 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
       for (int t = 0; t < 4; ++t) {
         rq[i][t] = e[t] * inv;
         const float m = fabsf(rq[i][t]);
-        near = near || fabsf(m - truncf(m) - 0.5f) <= 0x1p-14f;
+        dmin = fminf(dmin, fabsf(m - truncf(m) - 0.5f));
       }
     }
-    if (__any(near)) {
+    if (__any(dmin <= 0x1p-14f)) {
 #pragma unroll
       for (int i = 0; i < XPT; ++i) {
         const float e[4] = {xv[n][i].x, xv[n][i].y, xv[n][i].z, xv[n][i].w};
