@@ -510,16 +510,19 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
 
   // 1. Activation rows first: their absmax is the critical path, and loads
   // retire in order, so they must not queue behind the weights.
+  // Buffer loads: past the row they read 0, with no branch around them.
   const int k4 = static_cast<int>(K / 4);
   float4 xv[NC][XPT];
 #pragma unroll
-  for (int n = 0; n < NC; ++n)
+  for (int n = 0; n < NC; ++n) {
+    const __amdgpu_buffer_rsrc_t xbuf = buffer_of(x + static_cast<int64_t>(n) * ldx, static_cast<uint32_t>(16 * k4));
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = tid + kGemvThreads * i;
-      xv[n][i] = idx < k4 ? reinterpret_cast<const float4 *>(x + static_cast<int64_t>(n) * ldx)[idx]
-                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(xbuf, idx < k4 ? static_cast<uint32_t>(16 * idx) : kOutOfRange, 0, 0);
+      xv[n][i] = make_float4(__int_as_float(v[0]), __int_as_float(v[1]), __int_as_float(v[2]), __int_as_float(v[3]));
     }
+  }
 
   // Epilogue constants next, ahead of the weights (buffer loads keep their
   // place; loaded at their use they would cost one more memory round trip
@@ -626,12 +629,16 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
   }
   __syncthreads();
 
-  // 4. Contraction from LDS.
-  int acc[RPL][NC];
+  // 4. Contraction from LDS: four independent int32 partial sums per
+  // (row, activation row) -- one per dword of a chunk -- so that consecutive
+  // v_dot4 do not wait on each other; integer sums are exact in any order.
+  int acc[RPL][NC][4];
 #pragma unroll
   for (int m = 0; m < RPL; ++m)
 #pragma unroll
-    for (int n = 0; n < NC; ++n) acc[m][n] = 0;
+    for (int n = 0; n < NC; ++n)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) acc[m][n][d] = 0;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int j = lam + L * c;
@@ -642,16 +649,16 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
       const uint4 qd[4] = {qv[0], qv[1], qv[2], qv[3]};
 #pragma unroll
       for (int m = 0; m < RPL; ++m) {
-        int a = acc[m][n];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const uint32_t w = static_cast<uint32_t>(wv[m][c][d]);
+          int a = acc[m][n][d];
           a = __builtin_amdgcn_sdot4(static_cast<int>((w >> 6) & kCodeMask), static_cast<int>(qd[d].x), a, false);
           a = __builtin_amdgcn_sdot4(static_cast<int>((w >> 4) & kCodeMask), static_cast<int>(qd[d].y), a, false);
           a = __builtin_amdgcn_sdot4(static_cast<int>((w >> 2) & kCodeMask), static_cast<int>(qd[d].z), a, false);
           a = __builtin_amdgcn_sdot4(static_cast<int>(w & kCodeMask), static_cast<int>(qd[d].w), a, false);
+          acc[m][n][d] = a;
         }
-        acc[m][n] = a;
       }
     }
   }
@@ -662,7 +669,7 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
     const int64_t r = row0 + static_cast<int64_t>(m) * kSlots;
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-      const int total = lanes_sum<L>(acc[m][n]);
+      const int total = lanes_sum<L>((acc[m][n][0] + acc[m][n][1]) + (acc[m][n][2] + acc[m][n][3]));
       if (r < rows && lam == n % L) {
         const int32_t rs = red_i[n][0] + red_i[n][1] + red_i[n][2] + red_i[n][3];
         const float t = ws * sc[n];
