@@ -528,7 +528,8 @@ def bench_w8a8(args, torch):
         "int8_tops": round(ops / (step_ms * 1e-3) / 1e12, 4),
         "wall_s": round(wall, 4),
     }
-    kname = ("i8s_mm_skinny_kernel" if variant == 9 else "i8s_mm_mfma_kernel") + " (F32 dequantizing epilogue)"
+    kname = {9: "i8s_mm_skinny_kernel", 10: "w8a8_res_kernel"}.get(variant, "i8s_mm_mfma_kernel") + \
+        " (F32 dequantizing epilogue)"
     if M >= 64:
         achieved = ops / (kern_us * 1e-6) / 1e12
         out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_MFMA_PEAK_TOPS,

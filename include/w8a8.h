@@ -52,8 +52,11 @@ int w8a8_quantize_act(const float *x, int64_t M, int64_t K,
  * [M][OC]) receives C.  K % 16 == 0 and K > 0; wq, aq, y and dot_out 16-byte
  * aligned, the scales 4-byte aligned; OC*K and M*K below 2^31 - 2^16, M*OC
  * below 2^29 - 2^14.  variant 0 = automatic, else an MFMA tile configuration
- * 2..i8s_variants() of the I8_S contraction.  Errors: I2S_EINVAL,
- * I2S_EALIGN (K), I2S_ERANGE, I2S_EKERNEL (variant), I2S_EHIP. */
+ * 2..i8s_variants() of the I8_S contraction, or 10: the activation-resident
+ * kernel (64 activation rows in LDS, the int8 weights streamed; needs
+ * K % 64 == 0 and K <= 2544).  Errors: I2S_EINVAL, I2S_EALIGN (K),
+ * I2S_ERANGE, I2S_EKERNEL (variant, or variant 10 with K it does not take),
+ * I2S_EHIP. */
 int w8a8_matmul(const int8_t *wq, const float *wscale, int64_t OC, int64_t K,
                 const int8_t *aq, const float *ascale, int64_t M,
                 float *y, int32_t *dot_out, int variant, void *stream);
@@ -73,6 +76,10 @@ int w8a8_mul_mat_ex(const int8_t *wq, const float *wscale, int64_t OC, int64_t K
 
 /* The tile variant the automatic choice takes for this shape. */
 int w8a8_mul_mat_variant(int64_t OC, int64_t K, int64_t M);
+
+/* The largest valid variant number of w8a8_matmul (variant 1 and variants
+ * beyond it are refused). */
+int w8a8_variants(void);
 
 #ifdef __cplusplus
 }

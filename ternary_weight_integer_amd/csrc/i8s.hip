@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "i8s.h"
 #include "w8a8.h"
@@ -656,6 +657,184 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+// W8A8 activation-resident int8-MFMA contraction (the prefill shapes, W8A8
+// variant 10).  A workgroup of 8 waves copies its tile of 64 activation rows
+// (K bytes each, row pitch K + 16) into LDS once; each wave then streams the
+// int8 weights of its 16-row subtiles (wave, wave + 8, ..., G at a time) in
+// batches of KST 64-position chunks, the next batch's loads in flight while
+// the current one's MFMAs run, with no further barrier.  Weights are loaded
+// row-contiguously (lane l: row l/4, bytes 16*(l%4) of the chunk: 4
+// consecutive lanes read 64 contiguous bytes) and moved into MFMA lane order
+// by ds_bpermute; each weight operand feeds 4 MFMAs (the 4 blocks of 16
+// activation rows) whose B operands come from LDS.  Epilogue as the tile
+// kernel's F32 mode: y = (aScale * wScale) * (float)acc.
+
+template <int G, int KST, bool VEC4>
+__global__ void __launch_bounds__(512)
+w8a8_res_kernel(const int8_t *__restrict__ wq, const float *__restrict__ wscale, int OC, int K,
+                const int8_t *__restrict__ aq, const float *__restrict__ ascale, int M, float *__restrict__ y,
+                int32_t *__restrict__ dot, int tiles_m, int ms) {
+  constexpr int WN = 4, BN = 64, W = 8;
+  extern __shared__ __attribute__((aligned(16))) int8_t lt[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, kb = lane >> 4;
+  const int tile_m = static_cast<int>(blockIdx.x) % tiles_m, tile_n = static_cast<int>(blockIdx.x) / tiles_m;
+  const int o_tile = tile_m * ms * 16, n0 = tile_n * BN;
+  const int n_here = M - n0 < BN ? M - n0 : BN;
+  const int pitch = K + 16;
+  const int sub_total = (OC - o_tile + 15) / 16;
+  const int present = sub_total < ms ? sub_total : ms;  // 16-row subtiles of this tile
+  const int mine = present > wave ? (present - wave + W - 1) / W : 0;
+  const int groups = (mine + G - 1) / G;
+  const int chunks = K / 64;
+  const int batches = (chunks + KST - 1) / KST;
+  const __amdgpu_buffer_rsrc_t wbuf = buffer_of(wq, static_cast<uint32_t>(OC) * static_cast<uint32_t>(K));
+  const __amdgpu_buffer_rsrc_t abuf = buffer_of(aq + static_cast<int64_t>(n0) * K,
+                                                static_cast<uint32_t>(n_here) * static_cast<uint32_t>(K));
+
+  // Activation scales of this lane's rows n0 + 16*n + li (0 past M; never stored).
+  float asc[WN];
+  {
+    const __amdgpu_buffer_rsrc_t sbuf = buffer_of(ascale + n0, static_cast<uint32_t>(4 * n_here));
+#pragma unroll
+    for (int n = 0; n < WN; ++n)
+      asc[n] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, static_cast<uint32_t>(4 * (16 * n + li)), 0, 0));
+  }
+
+  // The activation tile into LDS, 8 pieces of 16 bytes per thread in flight;
+  // rows past M read as zero.
+  {
+    const int ppr = K / 16;  // pieces per row
+    const int pieces = BN * ppr;
+    for (int p0 = 0; p0 < pieces; p0 += 512 * 8) {
+      v4i t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int p = p0 + 512 * j + tid;
+        const int r = p / ppr, c = p - (p / ppr) * ppr;
+        t[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            abuf, p < pieces && r < n_here ? static_cast<uint32_t>(r * K + 16 * c) : kOutOfRange, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int p = p0 + 512 * j + tid;
+        if (p < pieces) {
+          const int r = p / ppr, c = p - (p / ppr) * ppr;
+          *reinterpret_cast<v4i *>(lt + r * pitch + 16 * c) = t[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const int perm = 4 * (4 * li + kb);  // ds_bpermute source lane (bytes) of MFMA lane (li, kb)
+  const int8_t *lb = lt + li * pitch + 16 * kb;
+  const __amdgpu_buffer_rsrc_t cbuf = buffer_of(wscale, static_cast<uint32_t>(4 * OC));
+  const uint32_t out_bytes = static_cast<uint32_t>(M) * static_cast<uint32_t>(OC) * 4u;
+  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y, out_bytes);
+  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(dot, dot ? out_bytes : 0u);
+
+  for (int grp = 0; grp < groups; ++grp) {
+    // Row of this lane's loads in subtile gi of the group (past OC or past
+    // the tile: an out-of-range offset, reads 0, never stored).
+    uint32_t wrow[G];
+    bool wok[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const int sub = wave + W * (grp * G + gi);
+      const int row = o_tile + 16 * sub + (lane >> 2);
+      wok[gi] = sub < present && row < OC;
+      wrow[gi] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + 16u * static_cast<uint32_t>(lane & 3);
+    }
+    auto load = [&](int bt, v4i (&w)[G][KST]) {
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+        for (int kk = 0; kk < KST; ++kk) {
+          const int chunk = bt * KST + kk;
+          w[gi][kk] = __builtin_amdgcn_raw_buffer_load_b128(
+              wbuf, wok[gi] && chunk < chunks ? wrow[gi] + 64u * static_cast<uint32_t>(chunk) : kOutOfRange, 0, 0);
+        }
+    };
+    v4i acc[G][WN];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int n = 0; n < WN; ++n) acc[gi][n] = v4i{0, 0, 0, 0};
+    // Permutes one chunk ahead of its MFMAs (G operands at a time), so that
+    // only two chunks' worth of permuted registers are live.
+    auto compute = [&](int bt, const v4i (&w)[G][KST]) {
+      v4i pw[2][G];
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pw[0][gi][e] = __builtin_amdgcn_ds_bpermute(perm, w[gi][0][e]);
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk) {
+        if (kk + 1 < KST) {
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pw[(kk + 1) & 1][gi][e] = __builtin_amdgcn_ds_bpermute(perm, w[gi][kk + 1][e]);
+        }
+        const int chunk = bt * KST + kk;
+        if (chunk >= chunks) continue;  // wave-uniform
+#pragma unroll
+        for (int n = 0; n < WN; ++n) {
+          const v4i b = *reinterpret_cast<const v4i *>(lb + 16 * n * pitch + 64 * chunk);
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi)
+            acc[gi][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pw[kk & 1][gi], b, acc[gi][n], 0, 0, 0);
+        }
+      }
+    };
+    v4i wa[G][KST], wb[G][KST];
+    load(0, wa);
+    for (int bt = 0; bt < batches; bt += 2) {
+      load(bt + 1, wb);
+      compute(bt, wa);
+      if (bt + 1 >= batches) break;
+      load(bt + 2, wa);
+      compute(bt + 1, wb);
+    }
+
+    // Lane (li, kb) holds, per subtile gi, weight rows o + r (o = o_tile +
+    // 16*sub + 4*kb, r = 0..3) of activation rows n0 + 16*n + li.
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const int sub = wave + W * (grp * G + gi);
+      if (sub >= present) continue;  // wave-uniform
+      const int o = o_tile + 16 * sub + 4 * kb;
+      float cs[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        cs[r] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(cbuf, o + r < OC ? static_cast<uint32_t>(4 * (o + r)) : kOutOfRange, 0, 0));
+#pragma unroll
+      for (int n = 0; n < WN; ++n) {
+        const int m = n0 + 16 * n + li;
+        const bool m_ok = m < M;
+        const uint32_t row = static_cast<uint32_t>(m_ok ? m : 0) * static_cast<uint32_t>(OC);
+        v4i yv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yv[r] = __float_as_int(asc[n] * cs[r] * static_cast<float>(acc[gi][n][r]));
+        if constexpr (VEC4) {
+          const uint32_t off = m_ok && o < OC ? 4u * (row + static_cast<uint32_t>(o)) : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, 0);
+          if (dot) __builtin_amdgcn_raw_buffer_store_b128(acc[gi][n], dbuf, off, 0, 0);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t off = m_ok && o + r < OC ? 4u * (row + static_cast<uint32_t>(o + r)) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(yv[r], ybuf, off, 0, 0);
+            if (dot) __builtin_amdgcn_raw_buffer_store_b32(acc[gi][n][r], dbuf, off, 0, 0);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Skinny int8 MFMA contraction for few activation rows (the encoder's last
 // stages and connector, W8A8 decode): the tile kernel above would have only a
 // few dozen tiles there.  A workgroup of W waves owns 16 output channels and
@@ -854,6 +1033,51 @@ __global__ void __launch_bounds__(kThreads) w8a8_quant_rows_kernel(const float *
 // Host side.
 
 constexpr int kVariants = 9;
+constexpr int kW8a8Variants = 10;  // the I8_S variants, and 10: activation-resident (W8A8 only)
+constexpr int64_t kW8a8ResMaxLds = 160 * 1024;
+
+// Variant 10 needs K a multiple of 64 and the 64-row activation tile (pitch
+// K + 16) within the LDS of a CU.
+bool w8a8_res_fits(int64_t K) { return K % 64 == 0 && 64 * (K + 16) <= kW8a8ResMaxLds; }
+
+template <int G, int KST, bool VEC4>
+int launch_w8a8_res_inst(int64_t blocks, int64_t lds, const MatArgs &a, int tiles_m, int ms, hipStream_t stream) {
+  // Allow the large dynamic LDS once per device for this instantiation
+  // (repeating it from racing threads is harmless).
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return I2S_EHIP;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&w8a8_res_kernel<G, KST, VEC4>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kW8a8ResMaxLds)) != hipSuccess)
+      return I2S_EHIP;
+    attr_done.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL((w8a8_res_kernel<G, KST, VEC4>), dim3(static_cast<unsigned>(blocks)), dim3(512),
+                     static_cast<size_t>(lds), stream, static_cast<const int8_t *>(a.w), a.cscale,
+                     static_cast<int>(a.OC), static_cast<int>(a.IC), static_cast<const int8_t *>(a.x), a.rscale,
+                     static_cast<int>(a.N), a.y, a.dot, tiles_m, ms);
+  return hipGetLastError() == hipSuccess ? I2S_OK : I2S_EHIP;
+}
+
+// Tiles of 64 activation rows; weight tiles of ms 16-row subtiles, ms chosen
+// so that the grid is about one workgroup per compute unit.
+int launch_w8a8_res(const MatArgs &a, hipStream_t stream) {
+  if (!w8a8_res_fits(a.IC)) return I2S_EKERNEL;
+  const int64_t tiles_n = (a.N + 63) / 64;
+  const int64_t mt = (a.OC + 15) / 16;
+  int64_t per = 256 / tiles_n;
+  if (per < 1) per = 1;
+  int64_t ms = (mt + per - 1) / per;
+  if (ms < 1) ms = 1;
+  const int64_t tiles_m = (mt + ms - 1) / ms;
+  const int64_t blocks = tiles_m * tiles_n;
+  if (blocks > 0x7fffffff || ms > 0x7fffffff) return I2S_ERANGE;
+  const int64_t lds = 64 * (a.IC + 16);
+  if (a.OC % 4 == 0) return launch_w8a8_res_inst<3, 4, true>(blocks, lds, a, static_cast<int>(tiles_m), static_cast<int>(ms), stream);
+  return launch_w8a8_res_inst<3, 4, false>(blocks, lds, a, static_cast<int>(tiles_m), static_cast<int>(ms), stream);
+}
 
 // f32 selects the W8A8 epilogue (one pass into a.y); otherwise the two
 // passes of mul_mat_add.
@@ -1048,10 +1272,15 @@ namespace {
 
 // The skinny kernel for few rows (as for I8_S); otherwise 128 x 64 tiles with
 // 4-step K chunks, measured fastest on the Qwen2-1.5B projection shapes.
+// Measured on MI355X (the Qwen2 gate, q and k shapes, M 1..1024): the skinny
+// kernel while it wins, the activation-resident kernel from 128 rows where K
+// fits it (gate 8960 x 1536, M = 512: 22 against 31 us with weights from
+// HBM), the tile kernels otherwise.
 int w8a8_auto_variant(int64_t OC, int64_t K, int64_t M) {
-  (void)K;
   if (skinny_wins(OC, M)) return 9;
-  return OC <= 64 ? 6 : 7;
+  if (OC <= 64) return 6;
+  if (M >= 128 && w8a8_res_fits(K)) return 10;
+  return 7;
 }
 
 int check_rows(const void *x, int64_t rows, int64_t K, const void *q, const float *scale) {
@@ -1088,6 +1317,8 @@ extern "C" int w8a8_quantize_act(const float *x, int64_t M, int64_t K, int8_t *q
 
 extern "C" int w8a8_mul_mat_variant(int64_t OC, int64_t K, int64_t M) { return w8a8_auto_variant(OC, K, M); }
 
+extern "C" int w8a8_variants(void) { return kW8a8Variants; }
+
 extern "C" int w8a8_matmul(const int8_t *wq, const float *wscale, int64_t OC, int64_t K, const int8_t *aq,
                            const float *ascale, int64_t M, float *y, int32_t *dot_out, int variant, void *stream) {
   if (!wq || !wscale || !aq || !ascale || !y || OC < 0 || K < 0 || M < 0) return I2S_EINVAL;
@@ -1096,7 +1327,8 @@ extern "C" int w8a8_matmul(const int8_t *wq, const float *wscale, int64_t OC, in
   if (dot_out && !aligned(dot_out, 16)) return I2S_EINVAL;
   if (K == 0 || K % 16 != 0) return I2S_EALIGN;
   if (OC * K >= kMaxBytes || M * K >= kMaxBytes || M * OC >= kMaxBytes / 4) return I2S_ERANGE;
-  if (variant < 0 || variant == 1 || variant > kVariants) return I2S_EKERNEL;
+  if (variant < 0 || variant == 1 || variant > kW8a8Variants) return I2S_EKERNEL;
+  if (variant == 10 && !w8a8_res_fits(K)) return I2S_EKERNEL;
   if (variant == 0) variant = w8a8_auto_variant(OC, K, M);
   if (OC == 0 || M == 0) return I2S_OK;
   MatArgs a = {};
@@ -1119,6 +1351,7 @@ extern "C" int w8a8_matmul(const int8_t *wq, const float *wscale, int64_t OC, in
     case 6: return launch_mfma<64, 128, 2>(a, true, s);
     case 7: return launch_mfma<128, 64, 4>(a, true, s);
     case 9: return launch_skinny(a, true, s);
+    case 10: return launch_w8a8_res(a, s);
     default: return launch_mfma<64, 64, 1>(a, true, s);
   }
 }
@@ -1139,7 +1372,8 @@ extern "C" int w8a8_mul_mat_ex(const int8_t *wq, const float *wscale, int64_t OC
     return I2S_EINVAL;
   if (K == 0 || K % 16 != 0) return I2S_EALIGN;
   if (OC * K >= kMaxBytes || M * K >= kMaxBytes || M * OC >= kMaxBytes / 4) return I2S_ERANGE;
-  if (variant < 0 || variant == 1 || variant > kVariants) return I2S_EKERNEL;
+  if (variant < 0 || variant == 1 || variant > kW8a8Variants) return I2S_EKERNEL;
+  if (variant == 10 && !w8a8_res_fits(K)) return I2S_EKERNEL;
   int st = w8a8_quantize_act(x, M, K, aq, as, stream);
   if (st != I2S_OK) return st;
   return w8a8_matmul(wq, wscale, OC, K, aq, as, M, y, dot_out, variant, stream);

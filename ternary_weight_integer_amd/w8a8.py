@@ -48,12 +48,18 @@ def lib() -> ctypes.CDLL:
         L.w8a8_mul_mat_ex.argtypes = [p, p, i64, i64, p, i64, p, sz, p, p, ci, p]
         L.w8a8_mul_mat_variant.restype = ci
         L.w8a8_mul_mat_variant.argtypes = [i64, i64, i64]
+        L.w8a8_variants.restype = ci
+        L.w8a8_variants.argtypes = []
         _ready = True
     return L
 
 
 def w8a8_act_workspace_bytes(M: int, K: int) -> int:
     return int(lib().w8a8_act_workspace_bytes(M, K))
+
+
+def w8a8_variants() -> int:
+    return int(lib().w8a8_variants())
 
 
 def w8a8_mul_mat_variant(OC: int, K: int, M: int) -> int:
@@ -136,5 +142,5 @@ def w8a8_mul_mat(wq: torch.Tensor, wscale: torch.Tensor, x: torch.Tensor, worksp
     return y
 
 
-__all__ = ["I2SError", "w8a8_act_workspace_bytes", "w8a8_mul_mat_variant", "w8a8_quantize_weight",
+__all__ = ["w8a8_variants", "I2SError", "w8a8_act_workspace_bytes", "w8a8_mul_mat_variant", "w8a8_quantize_weight",
            "w8a8_quantize_act", "w8a8_matmul", "w8a8_mul_mat", "w8a8_mul_mat_ex"]

@@ -27,7 +27,11 @@ def test_workspace_and_variant():
     assert w8a8.w8a8_act_workspace_bytes(1, 1536) == 1536 + 256
     assert w8a8.w8a8_act_workspace_bytes(-1, 16) == 0
     for shape in [(8960, 1536, 512), (1536, 8960, 1), (256, 1536, 64), (32, 64, 1000)]:
-        assert 2 <= w8a8.w8a8_mul_mat_variant(*shape) <= i8s.i8s_variants()
+        assert 2 <= w8a8.w8a8_mul_mat_variant(*shape) <= w8a8.w8a8_variants()
+    assert w8a8.w8a8_variants() == i8s.i8s_variants() + 1  # variant 10: W8A8 only
+    assert w8a8.w8a8_mul_mat_variant(8960, 1536, 512) == 10   # activation-resident
+    assert w8a8.w8a8_mul_mat_variant(1536, 8960, 512) == 7    # K beyond its LDS tile
+    assert w8a8.w8a8_mul_mat_variant(8960, 1536, 1) == 9      # skinny
 
 
 def _mm(wq=FAKE, ws=FAKE, OC=64, K=64, aq=FAKE, as_=FAKE, M=8, y=FAKE, dot=None, variant=0):
@@ -46,6 +50,9 @@ def _mm(wq=FAKE, ws=FAKE, OC=64, K=64, aq=FAKE, as_=FAKE, M=8, y=FAKE, dot=None,
     (dict(OC=1 << 20, K=4096), i2s.I2S_ERANGE),
     (dict(variant=1), i2s.I2S_EKERNEL),
     (dict(variant=99), i2s.I2S_EKERNEL),
+    (dict(variant=11), i2s.I2S_EKERNEL),
+    (dict(K=48, variant=10), i2s.I2S_EKERNEL),      # K % 64 != 0
+    (dict(K=2560, variant=10), i2s.I2S_EKERNEL),    # activation tile beyond the LDS
 ])
 def test_matmul_rejects_on_host(kw, expect):
     assert _mm(**kw) == expect
