@@ -1029,6 +1029,104 @@ __global__ void __launch_bounds__(kThreads) w8a8_quant_rows_kernel(const float *
   }
 }
 
+// The activation rounding of the kernel above, for one value.
+__device__ inline int w8a8_round_act(float x, float inv) {
+  const float v = x * inv;
+  const float h = v + copysignf(0.5f, v);
+  return static_cast<int>(fminf(fmaxf(h, -127.0f), 127.0f));
+}
+
+// The activation quantizer with the row held in registers: W waves per row,
+// thread t loads the float4s at 4 * (t + 64 W j), j < R (64 W R >= K / 4),
+// all before the first use, takes the row maximum with DPP moves (and, for
+// W > 1, through LDS) and writes four codes as one 32-bit store.  Same
+// arithmetic as w8a8_quant_rows_kernel<false>, so the same codes and scales.
+// Needs K % 4 == 0, x 16-byte and q 4-byte aligned.
+template <int R, int W>
+__global__ void __launch_bounds__(64 * W) w8a8_quant_act_reg_kernel(const float *__restrict__ x, int64_t K,
+                                                                    int8_t *__restrict__ q, float *__restrict__ scale) {
+  const int t = threadIdx.x;
+  const int K4 = static_cast<int>(K >> 2);
+  const float4 *xr = reinterpret_cast<const float4 *>(x + blockIdx.x * K);
+  uint32_t *qr = reinterpret_cast<uint32_t *>(q + blockIdx.x * K);
+  float4 v[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = t + 64 * W * j;
+    v[j] = i < K4 ? xr[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  float mx = 1e-9f;
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+  if constexpr (W == 1) {
+    mx = wave_max(mx);
+  } else {
+    __shared__ float red[W];
+    mx = wave_max(mx);
+    if ((t & 63) == 0) red[t >> 6] = mx;
+    __syncthreads();
+    mx = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) mx = fmaxf(mx, red[w]);
+  }
+  if (t == 0) scale[blockIdx.x] = mx / 127.0f;
+  const float inv = 127.0f / mx;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = t + 64 * W * j;
+    if (i < K4) {
+      const uint32_t b0 = static_cast<uint32_t>(w8a8_round_act(v[j].x, inv)) & 0xFFu;
+      const uint32_t b1 = static_cast<uint32_t>(w8a8_round_act(v[j].y, inv)) & 0xFFu;
+      const uint32_t b2 = static_cast<uint32_t>(w8a8_round_act(v[j].z, inv)) & 0xFFu;
+      const uint32_t b3 = static_cast<uint32_t>(w8a8_round_act(v[j].w, inv)) & 0xFFu;
+      qr[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    }
+  }
+}
+
+constexpr int kActRegMaxR = 36;          // float4s a thread holds at most
+constexpr int64_t kActRegRowsOneWave = 1024;  // rows from which each row gets one wave
+
+template <int R, int W>
+void launch_act_reg(const float *x, int64_t M, int64_t K, int8_t *q, float *scale, hipStream_t stream) {
+  hipLaunchKernelGGL((w8a8_quant_act_reg_kernel<R, W>), dim3(static_cast<uint32_t>(M)), dim3(64 * W), 0, stream, x,
+                     K, q, scale);
+}
+
+template <int W>
+void launch_act_reg_w(int64_t r, const float *x, int64_t M, int64_t K, int8_t *q, float *scale, hipStream_t stream) {
+  if (r <= 2) launch_act_reg<2, W>(x, M, K, q, scale, stream);
+  else if (r <= 4) launch_act_reg<4, W>(x, M, K, q, scale, stream);
+  else if (r <= 6) launch_act_reg<6, W>(x, M, K, q, scale, stream);
+  else if (r <= 9) launch_act_reg<9, W>(x, M, K, q, scale, stream);
+  else if (r <= 12) launch_act_reg<12, W>(x, M, K, q, scale, stream);
+  else if (r <= 18) launch_act_reg<18, W>(x, M, K, q, scale, stream);
+  else if (r <= 24) launch_act_reg<24, W>(x, M, K, q, scale, stream);
+  else launch_act_reg<36, W>(x, M, K, q, scale, stream);
+}
+
+// Waves per row, as measured on the Qwen2-1.5B row lengths: from 1024 rows
+// one wave each fills the chip; fewer rows split each row over four waves,
+// and a few long rows (K > 4096, at most 64 rows) over eight.
+int act_reg_waves(int64_t M, int64_t K) {
+  if (M >= kActRegRowsOneWave) return 1;
+  return (K > 4096 && M <= 64) ? 8 : 4;
+}
+
+// false where the register quantizer does not take the row (then the
+// workgroup-per-row kernel runs).
+bool launch_act_reg_fit(const float *x, int64_t M, int64_t K, int8_t *q, float *scale, hipStream_t stream) {
+  if (K % 4 != 0 || !aligned(x, 16) || !aligned(q, 4)) return false;
+  const int W = act_reg_waves(M, K);
+  const int64_t r = (K / 4 + 64 * W - 1) / (64 * W);
+  if (r > kActRegMaxR) return false;
+  if (W == 1) launch_act_reg_w<1>(r, x, M, K, q, scale, stream);
+  else if (W == 4) launch_act_reg_w<4>(r, x, M, K, q, scale, stream);
+  else launch_act_reg_w<8>(r, x, M, K, q, scale, stream);
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 
@@ -1310,8 +1408,9 @@ extern "C" int w8a8_quantize_act(const float *x, int64_t M, int64_t K, int8_t *q
   const int st = check_rows(x, M, K, q, ascale);
   if (st != I2S_OK) return st;
   if (M == 0) return I2S_OK;
-  hipLaunchKernelGGL(w8a8_quant_rows_kernel<false>, dim3(static_cast<uint32_t>(M)), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), x, K, q, ascale);
+  if (!launch_act_reg_fit(x, M, K, q, ascale, static_cast<hipStream_t>(stream)))
+    hipLaunchKernelGGL(w8a8_quant_rows_kernel<false>, dim3(static_cast<uint32_t>(M)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), x, K, q, ascale);
   return hip_status();
 }
 

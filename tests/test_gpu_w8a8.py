@@ -69,6 +69,44 @@ def test_quantizers_random(rows, K):
     check_quantizers(x, "random")
 
 
+# (rows, K) through every (float4s per thread, waves per row) instance of the
+# register quantizer: four waves under 1024 rows (eight for K > 4096 and at
+# most 64 rows), one wave from 1024 rows; ragged tails; and rows past the
+# register limit of their wave count (the workgroup-per-row kernel).
+ACT_REG_CASES = [(3, 512), (4, 2048), (3, 3000), (2, 4096), (70, 260), (65, 8960), (100, 6100), (200, 9000),
+                 (70, 12000), (65, 36864), (2, 6000), (3, 9216), (2, 20000), (1, 36864), (2, 49152), (1, 73728),
+                 (1, 73732), (66, 36868), (1024, 256), (1024, 1000), (1024, 1536), (1024, 2200), (1024, 3000),
+                 (1024, 4600), (1024, 6000), (1024, 9216), (1030, 9220), (2, 18000), (70, 16000), (80, 24000)]
+
+
+@pytest.mark.parametrize("rows,K", ACT_REG_CASES)
+def test_act_quantizer_every_register_width(rows, K):
+    rng = np.random.default_rng(K)
+    x = rng.standard_t(3, size=(rows, K)).astype(np.float32)
+    x[0, K - 1] = 1e3   # the maximum in the last float4 of the row
+    say(f"w8a8 act quantizer rows={rows} K={K}")
+    aq, as_ = w8a8.w8a8_quantize_act(dev(x))
+    raq, ras = oracle.w8a8_quantize_act(x)
+    assert np.array_equal(host(aq), raq) and np.array_equal(bits(host(as_)), bits(ras))
+
+
+@pytest.mark.parametrize("x_off,q_off", [(1, 0), (0, 1), (2, 2)])
+def test_act_quantizer_unaligned_buffers(x_off, q_off):
+    rows, K = 9, 1536
+    x = np.random.default_rng(x_off * 3 + q_off).normal(0, 2, size=(rows, K)).astype(np.float32)
+    xb = torch.zeros(rows * K + x_off, dtype=torch.float32, device=DEV)
+    xv = xb[x_off:].view(rows, K)
+    xv.copy_(dev(x))
+    qb = torch.zeros(rows * K + q_off, dtype=torch.int8, device=DEV)
+    qv = qb[q_off:].view(rows, K)
+    say(f"w8a8 act quantizer unaligned x+{4 * x_off} B q+{q_off} B")
+    aq, as_ = w8a8.w8a8_quantize_act(xv, q=qv)
+    raq, ras = oracle.w8a8_quantize_act(x)
+    assert np.array_equal(host(aq), raq) and np.array_equal(bits(host(as_)), bits(ras))
+    if q_off:
+        assert not host(qb[:q_off]).any()   # nothing written before q
+
+
 def test_quantizers_near_ties():
     for row in near_tie_rows((3.3, 0.77, 100.0)):
         check_quantizers(row[None, :], "near ties")
