@@ -39,6 +39,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "i2s.h"
 
@@ -989,19 +990,24 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   // its MFMA operand directly (16 rows x 64 bytes per instruction).
   const uint32_t lane_off = PERM ? (lane >> 2) * row_bytes + 16 * (lane & 3) : li * row_bytes + 16 * kb;
   const int perm_addr = 4 * (4 * li + kb);
-  auto permute_step = [&](const v4i (&src)[G][S], v4i (&dst)[G][S], int st) {
+  auto permute_step = [&](const v4i (&src)[G][S], v4i (&dst)[G][S], int st, auto gsc) {
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi)
+    for (int gi = 0; gi < decltype(gsc)::value; ++gi)
 #pragma unroll
       for (int e = 0; e < 4; ++e) dst[gi][st][e] = __builtin_amdgcn_ds_bpermute(perm_addr, src[gi][st][e]);
   };
+  // Subtiles of a short group past this wave's last one read nothing (an
+  // out-of-range offset: no memory traffic, and the same number of loads in
+  // flight, so every wait below stays as it is).
   auto load_w = [&](int grp, int ch, v4i (&wv)[G][S]) {
+    const int gs = grp + 1 < groups ? G : mine - grp * G;
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       const uint32_t sub_off = static_cast<uint32_t>(16 * (wave + WAVES * (grp * G + gi))) * row_bytes + 64 * S * ch;
 #pragma unroll
       for (int st = 0; st < S; ++st)
-        wv[gi][st] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lane_off + sub_off + 64 * st, 0, 0);
+        wv[gi][st] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, gi < gs ? lane_off + sub_off + 64 * st : kOutOfRange,
+                                                           0, 0);
     }
   };
 
@@ -1058,7 +1064,8 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         const uint32_t sub_off = static_cast<uint32_t>(16 * (wave + WAVES * gi)) * row_bytes;
-        wa[gi][st] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, lane_off + sub_off + 64 * st, 0, 0);
+        wa[gi][st] = __builtin_amdgcn_raw_buffer_load_b128(
+            wbuf, gi < (groups > 1 ? G : mine) ? lane_off + sub_off + 64 * st : kOutOfRange, 0, 0);
       }
     }
     load_w(groups > 1 ? 1 : 0, 0, wb);
@@ -1166,22 +1173,27 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       for (int n = 0; n < WN; ++n) acc[gi][n] = v4i{0, 0, 0, 0};
   };
 
+  // The MFMAs (and, with PERM, the permutes) of the group's gs subtiles only.
   auto mfma_group = [&](const v4i (&cur_in)[G][S], int gs, const int8_t *lb) {
-    v4i pm[G][S];
-    if constexpr (PERM) {
+    auto run = [&](auto gsc) {
+      constexpr int GS = decltype(gsc)::value;
+      v4i pm[G][S];
+      if constexpr (PERM) {
 #pragma unroll
-      for (int st = 0; st < S; ++st) permute_step(cur_in, pm, st);
-      __builtin_amdgcn_sched_barrier(0);  // all permutes in flight before the first use
-    }
-    const v4i(&cur)[G][S] = PERM ? pm : cur_in;
+        for (int st = 0; st < S; ++st) permute_step(cur_in, pm, st, gsc);
+        __builtin_amdgcn_sched_barrier(0);  // all permutes in flight before the first use
+      }
+      const v4i(&cur)[G][S] = PERM ? pm : cur_in;
+      res_mfma_chunk<GS, G, WN, S>(acc, cur, lb, pitch);
+    };
     if (gs == G) {
-      res_mfma_chunk<G, G, WN, S>(acc, cur, lb, pitch);
+      run(std::integral_constant<int, G>{});
     } else {
       switch (gs) {
-        case 1: res_mfma_chunk<1, G, WN, S>(acc, cur, lb, pitch); break;
-        case 2: if constexpr (G > 2) res_mfma_chunk<2, G, WN, S>(acc, cur, lb, pitch); break;
-        case 3: if constexpr (G > 3) res_mfma_chunk<3, G, WN, S>(acc, cur, lb, pitch); break;
-        case 4: if constexpr (G > 4) res_mfma_chunk<4, G, WN, S>(acc, cur, lb, pitch); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: if constexpr (G > 2) run(std::integral_constant<int, 2>{}); break;
+        case 3: if constexpr (G > 3) run(std::integral_constant<int, 3>{}); break;
+        case 4: if constexpr (G > 4) run(std::integral_constant<int, 4>{}); break;
         default: break;
       }
     }
@@ -1226,17 +1238,21 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       for (int p = 0; p < kPieceLanes; ++p)
         if (64 * p + lane < kStepPieces) *reinterpret_cast<v4i *>(lds_res + step_loff(st, p)) = bst[st][p];
       __syncthreads();
-      v4i pw[G][S];
-      if constexpr (PERM) permute_step(wa, pw, st);
-      const v4i(&w0)[G][S] = PERM ? pw : wa;
+      auto run0 = [&](auto gsc) {
+        constexpr int GS = decltype(gsc)::value;
+        v4i pw[G][S];
+        if constexpr (PERM) permute_step(wa, pw, st, gsc);
+        const v4i(&w0)[G][S] = PERM ? pw : wa;
+        res_mfma_step<GS, G, WN, S>(acc, w0, st, lb0, pitch);
+      };
       if (gs0 == G) {
-        res_mfma_step<G, G, WN, S>(acc, w0, st, lb0, pitch);
+        run0(std::integral_constant<int, G>{});
       } else {
         switch (gs0) {
-          case 1: res_mfma_step<1, G, WN, S>(acc, w0, st, lb0, pitch); break;
-          case 2: if constexpr (G > 2) res_mfma_step<2, G, WN, S>(acc, w0, st, lb0, pitch); break;
-          case 3: if constexpr (G > 3) res_mfma_step<3, G, WN, S>(acc, w0, st, lb0, pitch); break;
-          case 4: if constexpr (G > 4) res_mfma_step<4, G, WN, S>(acc, w0, st, lb0, pitch); break;
+          case 1: run0(std::integral_constant<int, 1>{}); break;
+          case 2: if constexpr (G > 2) run0(std::integral_constant<int, 2>{}); break;
+          case 3: if constexpr (G > 3) run0(std::integral_constant<int, 3>{}); break;
+          case 4: if constexpr (G > 4) run0(std::integral_constant<int, 4>{}); break;
           default: break;
         }
       }
@@ -2038,27 +2054,35 @@ int launch_pipe_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, c
 // (G, WN, S, waves) = (3,4,6,4), (2,4,6,8), (3,4,3,8), (3,2,6,8), (3,1,6,8), 10 pipelined
 // (G, WN, waves, steps) = (2,2,4,6), 11 = 7 with row-contiguous weight loads
 // permuted into MFMA lane order.
-constexpr int kGemmVariants = 11;
+constexpr int kGemmVariants = 14;
 
 int gemm_auto_variant(int64_t rows, int64_t K, int64_t N) {
   int variant;
   // Measured on MI355X (rows 256 .. 8960, K 1024 .. 8960, N 64 .. 2048):
-  // the 8-wave, 3-subtile, 3-step resident kernel is fastest while each of
-  // its blocks holds at least one 16-row subtile per wave; with fewer (few
-  // rows or small N) the 4-wave pipelined kernel is, where K fits it.
-  // Narrower resident tiles for longer K.
+  // the 8-wave resident kernel with row-contiguous weight loads is fastest
+  // from 4 subtiles per block; with fewer (few rows or large N) the 4-wave
+  // pipelined kernel is, where K fits it.  Narrower resident tiles for longer
+  // K.
   const int64_t tiles_n = (N + 63) / 64;
   const int64_t tiles_m = tiles_n < 256 ? 256 / tiles_n : 1;
   const int64_t ms7 = ((rows + 15) / 16 + tiles_m - 1) / tiles_m;  // subtiles per block of variant 7
   const bool fits7 = 64 * res_pitch(K, 3) <= kResMaxLds && N > 16;
-  if ((K + 255) / 256 <= 6 && (!fits7 || ms7 < 8))
+  const bool fits2 = 64 * res_pitch(K, 2) <= kResMaxLds && N > 16;
+  if ((K + 255) / 256 <= 6 && (!fits7 || ms7 < (fits2 ? 4 : 8))) {
     variant = 10;
-  else if (fits7)
+  } else if (fits2) {
+    // Row-contiguous weight loads and 2-step chunks; the group size follows
+    // the subtiles each wave holds (spw): whole groups with few, one or two
+    // groups for 3-5, groups of 3 beyond.
+    const int64_t spw = (ms7 + 7) / 8;
+    variant = spw <= 2 ? 12 : (spw <= 5 ? 13 : 14);
+  } else if (fits7) {
     variant = 11;  // variant 7's tiles with row-contiguous weight loads: 4-6% faster, measured
-  else if (16 * res_pitch(K, 6) <= kResMaxLds)
+  } else if (16 * res_pitch(K, 6) <= kResMaxLds) {
     variant = 9;
-  else
+  } else {
     variant = pick_stream_variant(rows, N);
+  }
   return variant;
 }
 
@@ -2077,6 +2101,9 @@ int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int
     case 9: return launch_res_cfg<3, 1, 6, 8>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     case 10: return launch_pipe_cfg<2, 2, 4, 6>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     case 11: return launch_res_cfg<3, 4, 3, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 12: return launch_res_cfg<2, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 13: return launch_res_cfg<4, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 14: return launch_res_cfg<3, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }

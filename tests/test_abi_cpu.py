@@ -133,7 +133,16 @@ def test_mul_mat_variant_choice():
         k = i2s.i2s_mul_mat_kernel(rows, K, N)
         v = i2s.i2s_mul_mat_variant(rows, K, N)
         assert 1 <= v <= i2s.i2s_kernel_variants(k), (rows, K, N, k, v)
-    assert i2s.i2s_mul_mat_variant(8960, 1536, 512) == 11   # the resident GEMM, row-contiguous weight loads
-    assert i2s.i2s_mul_mat_variant(1536, 1536, 128) == 10   # the pipelined GEMM
+    # the resident GEMM with row-contiguous weight loads; its group size by
+    # the 16-row subtiles each wave holds
+    assert i2s.i2s_mul_mat_variant(8960, 1536, 128) == 12   # 1 subtile per wave: groups of 2
+    assert i2s.i2s_mul_mat_variant(8960, 1536, 256) == 12   # 2
+    assert i2s.i2s_mul_mat_variant(8960, 1536, 512) == 13   # 3: groups of 4
+    assert i2s.i2s_mul_mat_variant(8960, 1536, 1024) == 13  # 5
+    assert i2s.i2s_mul_mat_variant(8960, 1536, 2048) == 14  # 9: groups of 3
+    assert i2s.i2s_mul_mat_variant(8960, 2304, 512) == 11   # past the 2-step chunks' LDS limit: 3-step chunks
+    assert i2s.i2s_mul_mat_variant(1536, 1536, 128) == 10   # the pipelined GEMM: 1 subtile per block
+    assert i2s.i2s_mul_mat_variant(1536, 1536, 512) == 10   # 3 subtiles per block
+    assert i2s.i2s_mul_mat_variant(2048, 1536, 512) == 12   # 4
     with pytest.raises(i2s.I2SError):
         i2s.i2s_mul_mat_variant(4, 100, 1)
