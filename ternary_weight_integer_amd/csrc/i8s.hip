@@ -26,6 +26,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "i8s.h"
 #include "w8a8.h"
@@ -746,56 +747,72 @@ w8a8_res_kernel(const int8_t *__restrict__ wq, const float *__restrict__ wscale,
       wok[gi] = sub < present && row < OC;
       wrow[gi] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) + 16u * static_cast<uint32_t>(lane & 3);
     }
-    auto load = [&](int bt, v4i (&w)[G][KST]) {
-#pragma unroll
-      for (int gi = 0; gi < G; ++gi)
-#pragma unroll
-        for (int kk = 0; kk < KST; ++kk) {
-          const int chunk = bt * KST + kk;
-          w[gi][kk] = __builtin_amdgcn_raw_buffer_load_b128(
-              wbuf, wok[gi] && chunk < chunks ? wrow[gi] + 64u * static_cast<uint32_t>(chunk) : kOutOfRange, 0, 0);
-        }
-    };
     v4i acc[G][WN];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi)
 #pragma unroll
       for (int n = 0; n < WN; ++n) acc[gi][n] = v4i{0, 0, 0, 0};
-    // Permutes one chunk ahead of its MFMAs (G operands at a time), so that
-    // only two chunks' worth of permuted registers are live.
-    auto compute = [&](int bt, const v4i (&w)[G][KST]) {
-      v4i pw[2][G];
+    // The group's loads, permutes and MFMAs for its GS subtiles only (a
+    // short last group runs none for the subtiles it lacks).
+    auto run = [&](auto gsc) {
+      constexpr int GS = decltype(gsc)::value;
+      auto load = [&](int bt, v4i (&w)[G][KST]) {
 #pragma unroll
-      for (int gi = 0; gi < G; ++gi)
+        for (int gi = 0; gi < GS; ++gi)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pw[0][gi][e] = __builtin_amdgcn_ds_bpermute(perm, w[gi][0][e]);
+          for (int kk = 0; kk < KST; ++kk) {
+            const int chunk = bt * KST + kk;
+            w[gi][kk] = __builtin_amdgcn_raw_buffer_load_b128(
+                wbuf, wok[gi] && chunk < chunks ? wrow[gi] + 64u * static_cast<uint32_t>(chunk) : kOutOfRange, 0, 0);
+          }
+      };
+      // Permutes one chunk ahead of its MFMAs (GS operands at a time), so that
+      // only two chunks' worth of permuted registers are live.
+      auto compute = [&](int bt, const v4i (&w)[G][KST]) {
+        v4i pw[2][G];
 #pragma unroll
-      for (int kk = 0; kk < KST; ++kk) {
-        if (kk + 1 < KST) {
+        for (int gi = 0; gi < GS; ++gi)
 #pragma unroll
-          for (int gi = 0; gi < G; ++gi)
+          for (int e = 0; e < 4; ++e) pw[0][gi][e] = __builtin_amdgcn_ds_bpermute(perm, w[gi][0][e]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pw[(kk + 1) & 1][gi][e] = __builtin_amdgcn_ds_bpermute(perm, w[gi][kk + 1][e]);
+        for (int kk = 0; kk < KST; ++kk) {
+          if (kk + 1 < KST) {
+#pragma unroll
+            for (int gi = 0; gi < GS; ++gi)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) pw[(kk + 1) & 1][gi][e] = __builtin_amdgcn_ds_bpermute(perm, w[gi][kk + 1][e]);
+          }
+          const int chunk = bt * KST + kk;
+          if (chunk >= chunks) continue;  // wave-uniform
+#pragma unroll
+          for (int n = 0; n < WN; ++n) {
+            const v4i b = *reinterpret_cast<const v4i *>(lb + 16 * n * pitch + 64 * chunk);
+#pragma unroll
+            for (int gi = 0; gi < GS; ++gi)
+              acc[gi][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pw[kk & 1][gi], b, acc[gi][n], 0, 0, 0);
+          }
         }
-        const int chunk = bt * KST + kk;
-        if (chunk >= chunks) continue;  // wave-uniform
-#pragma unroll
-        for (int n = 0; n < WN; ++n) {
-          const v4i b = *reinterpret_cast<const v4i *>(lb + 16 * n * pitch + 64 * chunk);
-#pragma unroll
-          for (int gi = 0; gi < G; ++gi)
-            acc[gi][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pw[kk & 1][gi], b, acc[gi][n], 0, 0, 0);
-        }
+      };
+      v4i wa[G][KST], wb[G][KST];
+      load(0, wa);
+      for (int bt = 0; bt < batches; bt += 2) {
+        load(bt + 1, wb);
+        compute(bt, wa);
+        if (bt + 1 >= batches) break;
+        load(bt + 2, wa);
+        compute(bt + 1, wb);
       }
     };
-    v4i wa[G][KST], wb[G][KST];
-    load(0, wa);
-    for (int bt = 0; bt < batches; bt += 2) {
-      load(bt + 1, wb);
-      compute(bt, wa);
-      if (bt + 1 >= batches) break;
-      load(bt + 2, wa);
-      compute(bt + 1, wb);
+    const int gs = mine - grp * G < G ? mine - grp * G : G;
+    if (gs == G) {
+      run(std::integral_constant<int, G>{});
+    } else {
+      switch (gs) {
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: if constexpr (G > 2) run(std::integral_constant<int, 2>{}); break;
+        case 3: if constexpr (G > 3) run(std::integral_constant<int, 3>{}); break;
+        default: break;
+      }
     }
 
     // Lane (li, kb) holds, per subtile gi, weight rows o + r (o = o_tile +
