@@ -1304,12 +1304,12 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 // Two weight register sets: the next group's weights load during the current
 // group's MFMAs.
 
-template <int G, int WN>
+template <int G, int WN, int GS = G>
 __device__ __forceinline__ void pipe_mfma_step(v4i (&acc)[G][WN], const v4i (&w)[G], const int8_t *lb,
                                                uint32_t group_stride, int perm) {
   v4i a4[G];
 #pragma unroll
-  for (int j = 0; j < G; ++j)
+  for (int j = 0; j < GS; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) a4[j][e] = __builtin_amdgcn_ds_bpermute(perm, w[j][e]);
   // All permutes in flight before the first use (else they go out one by one).
@@ -1320,7 +1320,7 @@ __device__ __forceinline__ void pipe_mfma_step(v4i (&acc)[G][WN], const v4i (&w)
 #pragma unroll
     for (int n = 0; n < WN; ++n) b[n] = *reinterpret_cast<const v4i *>(lb + 4 * n * group_stride + 64 * d);
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
+    for (int j = 0; j < GS; ++j) {
       const v4i a = unpack_codes(static_cast<uint32_t>(a4[j][d]));
 #pragma unroll
       for (int n = 0; n < WN; ++n) acc[j][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[j][n], 0, 0, 0);
@@ -1500,14 +1500,30 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   };
 
   auto step_ptr = [&](int st) { return lb0 + 1024 * phys(st); };
-  auto mfma_group = [&](const v4i (&cur)[G][SM]) {
+  // One step's permutes and MFMAs for the gs subtiles a group has (a short
+  // last group runs none for the subtiles it lacks).
+  auto mfma_step_gs = [&](const v4i (&w)[G], const int8_t *lb, int gs) {
+    if (gs >= G) {
+      pipe_mfma_step<G, WN>(acc, w, lb, group_stride, perm);
+    } else {
+      switch (gs) {
+        case 1: pipe_mfma_step<G, WN, 1>(acc, w, lb, group_stride, perm); break;
+        case 2: if constexpr (G > 2) pipe_mfma_step<G, WN, 2>(acc, w, lb, group_stride, perm); break;
+        case 3: if constexpr (G > 3) pipe_mfma_step<G, WN, 3>(acc, w, lb, group_stride, perm); break;
+        default: break;
+      }
+    }
+  };
+  auto group_size = [&](int grp) { return mine - G * grp < G ? mine - G * grp : G; };
+  auto mfma_group = [&](const v4i (&cur)[G][SM], int grp) {
+    const int gs = group_size(grp);
 #pragma unroll
     for (int st = 0; st < SM; ++st)
       if (st < steps) {
         v4i w[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) w[j] = cur[j][st];
-        pipe_mfma_step<G, WN>(acc, w, step_ptr(st), group_stride, perm);
+        mfma_step_gs(w, step_ptr(st), gs);
       }
   };
 
@@ -1524,7 +1540,7 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       v4i w[G];
 #pragma unroll
       for (int j = 0; j < G; ++j) w[j] = wa[j][st];
-      pipe_mfma_step<G, WN>(acc, w, step_ptr(st), group_stride, perm);
+      mfma_step_gs(w, step_ptr(st), group_size(0));
     }
   }
 
@@ -1537,14 +1553,14 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   for (int g = 1; g < groups; g += 2) {
     load_bias(g);
     zero_acc();
-    mfma_group(wb);
+    mfma_group(wb, g);
     load_w(g + 2, wb);
     __builtin_amdgcn_sched_barrier(0);
     epilogue_group(g);
     if (g + 1 >= groups) break;
     load_bias(g + 1);
     zero_acc();
-    mfma_group(wa);
+    mfma_group(wa, g + 1);
     load_w(g + 3, wa);
     __builtin_amdgcn_sched_barrier(0);
     epilogue_group(g + 1);
