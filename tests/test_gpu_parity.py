@@ -286,6 +286,19 @@ def test_all_gemm_variants_prefill_shape():
         check_mul_mat(case, kernel=2, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
 
 
+def test_gemm_variants_many_groups_per_wave():
+    """N = 2048 on the gate shape: 9 subtiles per wave, so every resident
+    variant runs several groups and a short last one (groups of 2, 3 and 4);
+    checked on sampled output features."""
+    case = workloads.prefill_gate_case(seed=5, N=2048)
+    pnp = oracle.pack(case.w, case.ws)
+    pg = gpu_pack(case.w, case.ws)
+    sample = np.unique(np.concatenate([np.arange(0, 24), np.arange(8960 - 24, 8960),
+                                       np.random.default_rng(8).choice(8960, 24, replace=False)]))
+    for v in (0, 11, 12, 13, 14):
+        check_mul_mat(case, kernel=2, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
+
+
 # --- edge cases -----------------------------------------------------------------------
 
 @pytest.mark.parametrize("N", [1, 8, 64])
