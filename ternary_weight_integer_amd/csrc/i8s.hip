@@ -38,6 +38,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;          // every kernel here: 4 wave64s
 constexpr int kMaxParts = 1024;        // workgroups of a two-pass launch (partial maxima)
 constexpr int kResidentGroups = 512;   // MFMA contraction grid: 2 workgroups per CU
+constexpr int64_t kSkinnyFewWavesItems = 256;  // skinny items from which a workgroup has 4 waves
 constexpr int64_t kMaxBytes = 0x7fff0000;  // largest tensor a buffer descriptor covers here
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // buffer offset beyond every descriptor range
 constexpr int kBufferFlags = 0x00020000;       // raw buffer, 32-bit data format
@@ -1239,10 +1240,9 @@ int launch_mfma(MatArgs a, bool f32, hipStream_t stream) {
   return hip_status();
 }
 
-template <int FN>
-int launch_skinny_fn(MatArgs a, bool f32, hipStream_t stream) {
-  constexpr int W = 8, SPW = 2;
-  const int64_t items = ((a.OC + 15) / 16) * ((a.N + 16 * FN - 1) / (16 * FN));
+template <int FN, int W>
+int launch_skinny_fn_w(MatArgs a, bool f32, int64_t items, hipStream_t stream) {
+  constexpr int SPW = 2;
   const int g = parts_for(items);
   a.nparts = g;
   if (f32) {
@@ -1252,6 +1252,17 @@ int launch_skinny_fn(MatArgs a, bool f32, hipStream_t stream) {
   hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeMax>), dim3(g), dim3(64 * W), 0, stream, a);
   hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeQuant>), dim3(g), dim3(64 * W), 0, stream, a);
   return hip_status();
+}
+
+// Waves per workgroup, measured on MI355X: with at least one item per
+// compute unit, 4 waves (gate 8960 x 1536 at one row: 6.2 against 6.9 us);
+// with fewer items, 8 waves split each item's K-steps further (down
+// 1536 x 8960: 9.1 against 11.8 us with 4).
+template <int FN>
+int launch_skinny_fn(MatArgs a, bool f32, hipStream_t stream) {
+  const int64_t items = ((a.OC + 15) / 16) * ((a.N + 16 * FN - 1) / (16 * FN));
+  return items >= kSkinnyFewWavesItems ? launch_skinny_fn_w<FN, 4>(a, f32, items, stream)
+                                       : launch_skinny_fn_w<FN, 8>(a, f32, items, stream);
 }
 
 // Row blocks of 16, 32 or 64 rows, by N.
