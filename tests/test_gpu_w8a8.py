@@ -120,7 +120,8 @@ def variant_takes(v: int, K: int) -> bool:
     return v != 10 or (K % 64 == 0 and K <= 2544)
 
 
-@pytest.mark.parametrize("OC,K,M", SHAPES + [(2048, 1536, 256), (1536, 2496, 130), (513, 1600, 64)])
+@pytest.mark.parametrize("OC,K,M", SHAPES + [(2048, 1536, 256), (1536, 2496, 130), (513, 1600, 64), (4100, 640, 130),
+                                           (4097, 576, 70)])
 def test_matmul_every_variant(OC, K, M):
     rng = np.random.default_rng(OC + K + M)
     wq = rng.integers(-127, 128, size=(OC, K), dtype=np.int8)
