@@ -62,8 +62,9 @@ static unsigned oracle_code(int8_t w)
 }
 
 /* Where value number f of the flat tensor lives: a group holds 128 values in
- * 32 bytes; byte gp of a group holds the group-relative positions gp, 32+gp,
- * 64+gp and 96+gp in the bit pairs at shifts 6, 4, 2 and 0
+ * 32 bytes, split into four slices of 32; the value at offset j of its group
+ * goes to byte j mod 32 of the group, in the bit pair of slice j / 32, the
+ * first slice in the top two bits and the last in the bottom two
  * [P1 Kernels; P2 Kernels; P3 Architecture/Decoder: packed over the whole
  * flat tensor]. */
 static void oracle_locate(int64_t f, int64_t *byte, int *shift)
@@ -304,76 +305,94 @@ int oracle_i8s_mul_mat_add(const uint8_t *w, int64_t OC, int64_t IC,
  * Per-channel W8A8 ["Experiment - int8 W8A8 path (the practical default)",
  * Hypothesis and Implementation]: int8 weights with one F32 scale per output
  * channel, int8 activations with one F32 scale per row, an int32 product,
- * and the dequantization d[m][n] = aScale[m] * bScale[n] * C[m][n].  Each
- * quantizer follows the page's own arithmetic, which differs from the I2_S
- * activation quantizer in three places: the running maximum starts at 1e-9
- * instead of being floored at 1e-5, weights round with lrintf (ties to
- * even), and activations multiply by the reciprocal 127/max and then add
- * copysign(0.5) and truncate.  Weights are kept as w[n][k] (K contiguous);
+ * and a dequantization that multiplies the activation row's scale, the
+ * channel's scale and the converted int32 product, in that order.  Its
+ * rounding differs from the I2_S activation quantizer in three places: the
+ * maximum is never below 1e-9 (instead of a 1e-5 floor), weight codes round
+ * ties to even, and activation codes multiply by the reciprocal of the
+ * scale, step half a unit away from zero and drop the fraction.  Weights are kept as w[n][k] (K contiguous);
  * the page transposes them for its NPU, which changes no value.
  */
 
-/* Weight quantization, per output channel n of w[OC][K]:
- *   mx = max(1e-9, max_k |w|), s = mx / 127, q = lrintf(w / s) clamped to
- *   [-127, 127]. */
+/* The largest magnitude of v[0..K), but never below the page's starting
+ * value 1e-9 (so an all-zero row still has a finite, nonzero scale). */
+static float w8a8_max_mag(const float *v, int64_t K)
+{
+    float m = 0.0f;
+    for (int64_t k = 0; k < K; ++k)
+        m = fmaxf(m, fabsf(v[k]));
+    return m < 1e-9f ? 1e-9f : m;
+}
+
+static int8_t w8a8_clamp127(float r)
+{
+    return (int8_t)(r > 127.0f ? 127 : (r < -127.0f ? -127 : (int)r));
+}
+
+/* Weight code: the F32 quotient w / s rounded to the nearest integer, ties
+ * to the even neighbour (the default rounding mode, as lrintf uses). */
+static int8_t w8a8_weight_code(float w, float s)
+{
+    return w8a8_clamp127(rintf(w / s));
+}
+
+/* Activation code: the F32 product v = x * inv, moved half a unit away from
+ * zero (that sum is itself rounded to F32), then the fraction dropped.  For
+ * v = -0 the sign makes no difference: both +-0.5 truncate to 0. */
+static int8_t w8a8_act_code(float x, float inv)
+{
+    float v = x * inv;
+    float moved = v < 0.0f ? v - 0.5f : v + 0.5f;
+    return w8a8_clamp127(truncf(moved));
+}
+
+/* Per output channel n of w[OC][K]: scale[n] = max / 127 and each weight's
+ * code from w8a8_weight_code. */
 void oracle_w8a8_quantize_weight(const float *w, int64_t OC, int64_t K, int8_t *q, float *scale)
 {
     for (int64_t n = 0; n < OC; ++n) {
-        float mx = 1e-9f;
-        for (int64_t k = 0; k < K; ++k) {
-            float v = fabsf(w[n * K + k]);
-            if (v > mx) mx = v;
-        }
-        float s = mx / 127.0f;
-        scale[n] = s;
-        for (int64_t k = 0; k < K; ++k) {
-            long r = lrintf(w[n * K + k] / s); /* current rounding mode: to nearest, ties to even */
-            if (r > 127) r = 127;
-            if (r < -127) r = -127;
-            q[n * K + k] = (int8_t)r;
-        }
+        const float *row = w + n * K;
+        scale[n] = w8a8_max_mag(row, K) / 127.0f;
+        for (int64_t k = 0; k < K; ++k)
+            q[n * K + k] = w8a8_weight_code(row[k], scale[n]);
     }
 }
 
-/* Activation quantization, per row m of x[M][K]:
- *   mx = max(1e-9, max_k |x|), aScale = mx / 127, inv = 127 / mx,
- *   v = x * inv, q = (int)(v + copysign(0.5, v)) (the sum rounded to F32,
- *   then truncated toward zero), clamped to [-127, 127]. */
+/* Per activation row m of x[M][K]: scale[m] = max / 127, and the codes use
+ * the reciprocal 127 / max (not the division by the stored scale). */
 void oracle_w8a8_quantize_act(const float *x, int64_t M, int64_t K, int8_t *q, float *scale)
 {
     for (int64_t m = 0; m < M; ++m) {
-        float mx = 1e-9f;
-        for (int64_t k = 0; k < K; ++k) {
-            float v = fabsf(x[m * K + k]);
-            if (v > mx) mx = v;
-        }
-        scale[m] = mx / 127.0f;
+        const float *row = x + m * K;
+        float mx = w8a8_max_mag(row, K);
         float inv = 127.0f / mx;
-        for (int64_t k = 0; k < K; ++k) {
-            float v = x[m * K + k] * inv;
-            float h = v + copysignf(0.5f, v);
-            int qi = (int)h;
-            if (qi > 127) qi = 127;
-            if (qi < -127) qi = -127;
-            q[m * K + k] = (int8_t)qi;
-        }
+        scale[m] = mx / 127.0f;
+        for (int64_t k = 0; k < K; ++k)
+            q[m * K + k] = w8a8_act_code(row[k], inv);
     }
 }
 
-/* C[m][n] = sum_k a[m][k] * w[n][k] (int32), then
- * d[m][n] = aScale[m] * bScale[n] * (float)C[m][n], multiplied left to
- * right. */
+static int32_t w8a8_int_dot(const int8_t *u, const int8_t *v, int64_t K)
+{
+    int32_t s = 0;
+    for (int64_t k = 0; k < K; ++k)
+        s += (int32_t)u[k] * (int32_t)v[k];
+    return s;
+}
+
+/* C[m][n] = the int32 dot of activation row m and weight row n; the
+ * dequantized value multiplies the two scales first (activation scale on
+ * the left) and then the converted C. */
 void oracle_w8a8_matmul(const int8_t *a, const float *ascale, int64_t M,
                         const int8_t *w, const float *wscale, int64_t OC, int64_t K,
                         float *d, int32_t *c)
 {
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < OC; ++n) {
-            int32_t acc = 0;
-            for (int64_t k = 0; k < K; ++k)
-                acc += (int32_t)a[m * K + k] * (int32_t)w[n * K + k];
-            if (c) c[m * OC + n] = acc;
-            d[m * OC + n] = ascale[m] * wscale[n] * (float)acc;
+            int32_t cv = w8a8_int_dot(a + m * K, w + n * K, K);
+            float t = ascale[m] * wscale[n];
+            if (c) c[m * OC + n] = cv;
+            d[m * OC + n] = t * (float)cv;
         }
     }
 }

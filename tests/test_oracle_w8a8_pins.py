@@ -137,3 +137,18 @@ def test_full_scale_integer_part():
     w[1] = 127
     _, c = oracle.w8a8_matmul(a, np.ones(2, np.float32), w, np.ones(3, np.float32), with_c=True)
     assert c[0, 0] == -127 * 127 * K and c[1, 1] == 127 * 127 * K
+
+
+def test_sliced_oracle_is_the_whole_call():
+    """The row-sliced W8A8 oracle calls give the whole calls' bits."""
+    rng = np.random.default_rng(78)
+    for OC, K, M, threads in ((33, 96, 19, 4), (7, 64, 3, 16), (40, 48, 1, 0)):
+        w = rng.normal(0, 0.05, size=(OC, K)).astype(np.float32)
+        x = rng.normal(0, 1, size=(M, K)).astype(np.float32)
+        wq, ws = oracle.w8a8_quantize_weight(w)
+        d, c = oracle.w8a8_mul_mat(wq, ws, x, with_c=True)
+        d2, c2 = oracle.w8a8_mul_mat_sliced(wq, ws, x, with_c=True, threads=threads)
+        assert np.array_equal(c2, c) and np.array_equal(d2.view(np.uint32), d.view(np.uint32))
+        aq, as_ = oracle.w8a8_quantize_act(x)
+        d3, c3 = oracle.w8a8_matmul_sliced(aq, as_, wq, ws, with_c=True, threads=threads)
+        assert np.array_equal(c3, c) and np.array_equal(d3.view(np.uint32), d.view(np.uint32))
