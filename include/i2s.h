@@ -14,8 +14,9 @@
  *   "ggml: additive INT8/ternary types, fused CPU ops, and kernels for VibeASR
  *     (1/2)", section Two new types: I2_S holds 128 values per 32-byte group,
  *     then one padded F32 absmax in band, after the payload;
- *   same page, section Kernels: byte gp of a group holds the group-relative
- *     positions gp, 32+gp, 64+gp, 96+gp in the bit pairs at shifts 6/4/2/0;
+ *   same page, section Kernels: byte i of a group carries the codes of the
+ *     group's positions i, i+32, i+64 and i+96, the first in the top bit pair
+ *     (shift 6) and the last in the bottom one (shift 0);
  *   "VibeASR in audio.cpp", Architecture / Decoder: packed over the whole flat
  *     tensor; the kernel asserts K % 128 == 0;
  *   "VibeASR in audio.cpp", Architecture / Encoder: amax floored at 1e-5.

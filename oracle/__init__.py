@@ -148,6 +148,44 @@ def mul_mat(packed: np.ndarray, rows: int, K: int, x: np.ndarray, with_dot: bool
     return (y, d) if with_dot else y
 
 
+def host_threads() -> int:
+    """Threads for the row-sliced oracle calls: the host cores this process
+    may use, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def mul_mat_sliced(packed: np.ndarray, rows: int, K: int, x: np.ndarray, with_dot: bool = False,
+                   threads: int = 0):
+    """mul_mat over slices of the output features, one slice per thread.
+    A row slice of the payload followed by the scale slot is itself an I2_S
+    tensor (groups never straddle rows), and every output feature depends on
+    its own weight row only, so the concatenated slices are mul_mat's result
+    exactly; this is the same oracle call, run in parallel (ctypes releases
+    the GIL) so that whole outputs of the large shapes are checked in
+    seconds."""
+    import concurrent.futures
+
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rb = K // 4
+    slot = packed[rows * rb: rows * rb + 32]
+    n = max(1, min(threads or host_threads(), rows))
+    bounds = [rows * i // n for i in range(n + 1)]
+    parts = [(a, b) for a, b in zip(bounds, bounds[1:]) if b > a]
+    if len(parts) <= 1:
+        return mul_mat(packed, rows, K, x, with_dot=with_dot)
+
+    def run(ab):
+        a, b = ab
+        return mul_mat(np.concatenate([packed[a * rb:b * rb], slot]), b - a, K, x, with_dot=True)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(parts)) as pool:
+        outs = list(pool.map(run, parts))
+    y = np.concatenate([o[0] for o in outs], axis=1)
+    d = np.concatenate([o[1] for o in outs], axis=1)
+    return (y, d) if with_dot else y
+
+
 def add_bias(y: np.ndarray, bias: np.ndarray) -> np.ndarray:
     """y[N][rows] + bias[rows], one F32 add per element (oracle_add_bias)."""
     out = np.array(y, dtype=np.float32, order="C", copy=True)
@@ -301,4 +339,43 @@ def w8a8_mul_mat(wq: np.ndarray, wscale: np.ndarray, x: np.ndarray, with_c: bool
     rc = _load().oracle_w8a8_mul_mat(_ptr(wq), _ptr(wscale), OC, K, _ptr(x), M, _ptr(d), _ptr(c))
     if rc != 0:
         raise MemoryError("oracle_w8a8_mul_mat: allocation failed")
+    return (d, c) if with_c else d
+
+
+def _split_rows(M: int, threads: int):
+    n = max(1, min(threads or host_threads(), M))
+    bounds = [M * i // n for i in range(n + 1)]
+    return [(a, b) for a, b in zip(bounds, bounds[1:]) if b > a]
+
+
+def w8a8_matmul_sliced(a: np.ndarray, ascale: np.ndarray, w: np.ndarray, wscale: np.ndarray,
+                       with_c: bool = False, threads: int = 0):
+    """w8a8_matmul over slices of the activation rows, one slice per thread:
+    each output row depends on its own activation row only, so the stacked
+    slices are the whole result exactly (the same oracle call, in parallel)."""
+    import concurrent.futures
+
+    parts = _split_rows(a.shape[0], threads)
+    if len(parts) <= 1:
+        return w8a8_matmul(a, ascale, w, wscale, with_c=with_c)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(parts)) as pool:
+        outs = list(pool.map(lambda ab: w8a8_matmul(a[ab[0]:ab[1]], ascale[ab[0]:ab[1]], w, wscale, with_c=True),
+                             parts))
+    d = np.concatenate([o[0] for o in outs], axis=0)
+    c = np.concatenate([o[1] for o in outs], axis=0)
+    return (d, c) if with_c else d
+
+
+def w8a8_mul_mat_sliced(wq: np.ndarray, wscale: np.ndarray, x: np.ndarray, with_c: bool = False, threads: int = 0):
+    """w8a8_mul_mat over slices of the activation rows (each row is quantized
+    on its own), one slice per thread."""
+    import concurrent.futures
+
+    parts = _split_rows(x.shape[0], threads)
+    if len(parts) <= 1:
+        return w8a8_mul_mat(wq, wscale, x, with_c=with_c)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(parts)) as pool:
+        outs = list(pool.map(lambda ab: w8a8_mul_mat(wq, wscale, x[ab[0]:ab[1]], with_c=True), parts))
+    d = np.concatenate([o[0] for o in outs], axis=0)
+    c = np.concatenate([o[1] for o in outs], axis=0)
     return (d, c) if with_c else d

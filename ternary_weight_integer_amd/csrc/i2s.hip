@@ -9,8 +9,9 @@
 //
 // Packed layout ("ggml: additive INT8/ternary types, fused CPU ops, and kernels
 // for VibeASR (1/2)", Two new types and Kernels): 128 values per 32-byte group;
-// byte gp of a group holds group-relative positions gp, 32+gp, 64+gp, 96+gp in
-// the bit pairs at shifts 6/4/2/0; one F32 scale in band after the payload.
+// within a group, byte i carries the codes of positions i, i+32, i+64 and i+96
+// (counted from the group's start), from the high bit pair down to the low
+// one; the tensor's F32 scale follows the payload in band.
 // A packed dword (bytes gp..gp+3 of a group) therefore yields, for slice s,
 // (dword >> (6-2s)) & 0x03030303 = the codes of the four consecutive positions
 // 32s+gp .. 32s+gp+3, one per byte, ready for a 4-way int8 dot.
@@ -55,11 +56,11 @@ constexpr int64_t kTiledMaxN = 64;  // largest contraction N for which the quant
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct ActWorkspace {
-  int8_t *q;
-  float *scale;
-  int32_t *row_sum;
-  int8_t *qt;          // the MFMA-tiled copy of q, or nullptr where it is not filled
-  int64_t qt_row0;     // tiled-copy row of q's row 0 (a batch's first row)
+  int8_t *q = nullptr;
+  float *scale = nullptr;
+  int32_t *row_sum = nullptr;
+  int8_t *qt = nullptr;  // the MFMA-tiled copy of q, or nullptr where it is not filled
+  int64_t qt_row0 = 0;   // tiled-copy row of q's row 0 (a batch's first row)
 };
 
 // Bytes of the MFMA-tiled copy: ceil(N/16) blocks x ceil(K/256) steps x 4 KiB.
@@ -697,13 +698,13 @@ gemv_fused_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 // projections in order, and each one quantizes the shared rows itself, as
 // above, before its share of one projection.
 struct FusedGroup {
-  int count;
-  int64_t block_end[I2S_GROUP_MAX];  // workgroups of projections 0..p
-  const uint8_t *packed[I2S_GROUP_MAX];
-  int64_t rows[I2S_GROUP_MAX];
-  const float *bias[I2S_GROUP_MAX];
-  float *y[I2S_GROUP_MAX];
-  int32_t *dot[I2S_GROUP_MAX];
+  int count = 0;
+  int64_t block_end[I2S_GROUP_MAX] = {};  // workgroups of projections 0..p
+  const uint8_t *packed[I2S_GROUP_MAX] = {};
+  int64_t rows[I2S_GROUP_MAX] = {};
+  const float *bias[I2S_GROUP_MAX] = {};
+  float *y[I2S_GROUP_MAX] = {};
+  int32_t *dot[I2S_GROUP_MAX] = {};
 };
 
 template <int NC, int L, int RPL, int CPL, int XPT>

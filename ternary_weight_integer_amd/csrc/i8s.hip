@@ -223,24 +223,26 @@ __global__ void __launch_bounds__(kThreads) i8s_dequantize_kernel(const uint8_t 
 // mul_mat_add arguments shared by both passes and both contraction kernels.
 
 struct MatArgs {
-  const int8_t *w;      // [OC][IC] payload
-  const int8_t *x;      // [N][IC] payload
-  const uint8_t *ws;    // in-band scale of w
-  const uint8_t *xs;    // in-band scale of x
-  const float *bias;    // [OC] or null
-  float *parts;         // pass 1 writes parts[blockIdx.x]; pass 2 reads nparts of them
-  int8_t *out;          // [N][OC] payload (pass 2)
-  int32_t *dot;         // [N][OC] or null (pass 2)
-  int64_t OC, IC, N;
-  int nparts;
-  int relu;
-  int vec;              // OC % 16 == 0: 16-byte int8 stores, 16-byte dot stores
-                        // (W8A8: OC % 4 == 0 and y, dot 16-byte aligned)
-  const float *cscale;  // W8A8: per-channel weight scales [OC]
-  const float *rscale;  // W8A8: per-row activation scales [N]
-  float *y;             // W8A8: [N][OC] F32 output
-  int map;              // tile assignment: kMapStride, kMapXLocal or kMapWLocal
-  int rep;              // XCD-local maps: workgroups per XCD per block of the local operand
+  // Every member has a default, so a default-constructed MatArgs is inert:
+  // null pointers (no bias, no dot output, no F32 output) and zero sizes.
+  const int8_t *w = nullptr;      // [OC][IC] payload
+  const int8_t *x = nullptr;      // [N][IC] payload
+  const uint8_t *ws = nullptr;    // in-band scale of w
+  const uint8_t *xs = nullptr;    // in-band scale of x
+  const float *bias = nullptr;    // [OC] or null
+  float *parts = nullptr;         // pass 1 writes parts[blockIdx.x]; pass 2 reads nparts of them
+  int8_t *out = nullptr;          // [N][OC] payload (pass 2)
+  int32_t *dot = nullptr;         // [N][OC] or null (pass 2)
+  int64_t OC = 0, IC = 0, N = 0;
+  int nparts = 0;
+  int relu = 0;
+  int vec = 0;                    // OC % 16 == 0: 16-byte int8 stores, 16-byte dot stores
+                                  // (W8A8: OC % 4 == 0 and y, dot 16-byte aligned)
+  const float *cscale = nullptr;  // W8A8: per-channel weight scales [OC]
+  const float *rscale = nullptr;  // W8A8: per-row activation scales [N]
+  float *y = nullptr;             // W8A8: [N][OC] F32 output
+  int map = 0;                    // tile assignment: kMapStride, kMapXLocal or kMapWLocal
+  int rep = 1;                    // XCD-local maps: workgroups per XCD per block of the local operand
 };
 
 // Tile assignment of the MFMA contraction.  Workgroup b runs on XCD b % 8

@@ -215,7 +215,12 @@ def i2s_mul_mat_ex(packed: torch.Tensor, rows: int, K: int, x: torch.Tensor, wor
 
 def i2s_mul_mat(packed: torch.Tensor, rows: int, K: int, x: torch.Tensor, workspace=None, y=None, dot_out=None,
                 stream=None):
-    """The I2_S matmul with automatic kernel choice (GEMV for N <= 8, else GEMM)."""
+    """The I2_S matmul with the library's automatic kernel choice
+    (i2s_mul_mat_kernel / i2s_mul_mat_variant report it): for N <= 3 at
+    K <= 9216 one fused quantize + v_dot4 GEMV launch; otherwise a quantize
+    launch, then the v_dot4 GEMV (N = 1, or N = 2 at K <= 2048), the skinny
+    int8-MFMA kernel (N <= 32, or N <= 64 with at most 4096 weight rows),
+    else the int8-MFMA GEMM."""
     N = x.shape[0]
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError(f"x must be [N][{K}], got {tuple(x.shape)}")

@@ -5,8 +5,10 @@ F32 outputs must all be identical to the oracle's (the integer steps are exact
 and the three F32 operations are single IEEE round-to-nearest operations in a
 fixed order, so there is exactly one correct bit pattern).  Every case goes
 through the C ABI (via the ctypes binding) on the same seeded inputs the
-oracle gets.  Full-size workloads are compared on sampled output rows that the
-oracle computes one by one.
+oracle gets.  Every output of every workload is compared, full-size shapes
+included: the oracle runs over slices of the output features on the host
+threads (oracle.mul_mat_sliced), which is the same computation split by
+weight row.
 """
 
 from __future__ import annotations
@@ -52,19 +54,10 @@ def gpu_pack(w: np.ndarray, ws: float) -> torch.Tensor:
     return i2s.i2s_pack(dev(w), ws)
 
 
-def oracle_rows(packed: np.ndarray, rows: int, K: int, x: np.ndarray, sample: np.ndarray):
-    """Oracle y and dot for the sampled output rows only (all N)."""
-    q, s, rs = oracle.quantize_act(x)
-    ws = oracle.weight_scale(packed, rows, K)
-    ys, ds = [], []
-    for o in sample:
-        d = oracle.dot(packed[o * K // 4:(o + 1) * K // 4], 1, K, q)
-        ds.append(d[:, 0])
-        ys.append(oracle.epilogue(d, rs, s, ws)[:, 0])
-    return np.stack(ys, 1), np.stack(ds, 1)
-
-
-def check_mul_mat(case: workloads.Case, kernel=0, variant=0, sample=None, packed_gpu=None, packed_np=None):
+def check_mul_mat(case: workloads.Case, kernel=0, variant=0, packed_gpu=None, packed_np=None, expected=None):
+    """The whole op through the C ABI against the oracle on every output:
+    int32 dots and F32 bits; `expected` = (y, dot) of the oracle when a
+    caller checks several kernels against one oracle run."""
     rows, K, N = case.rows, case.K, case.N
     say(f"[parity] {case.name} rows={rows} K={K} N={N} kernel={kernel} variant={variant}")
     if packed_np is None:
@@ -77,11 +70,9 @@ def check_mul_mat(case: workloads.Case, kernel=0, variant=0, sample=None, packed
     y_only = i2s.i2s_mul_mat_ex(packed_gpu, rows, K, x, kernel=kernel, variant=variant)
     y, d, y_only = host(y), host(d), host(y_only)
     assert np.array_equal(bits(y), bits(y_only)), "y differs with and without dot_out"
-    if sample is None:
-        ye, de = oracle.mul_mat(packed_np, rows, K, case.x, with_dot=True)
-    else:
-        ye, de = oracle_rows(packed_np, rows, K, case.x, sample)
-        y, d = y[:, sample], d[:, sample]
+    if expected is None:
+        expected = oracle.mul_mat_sliced(packed_np, rows, K, case.x, with_dot=True)
+    ye, de = expected
     assert np.array_equal(d, de), f"dot mismatch at {np.argwhere(d != de)[:5]}"
     assert np.array_equal(bits(y), bits(ye)), f"y mismatch at {np.argwhere(bits(y) != bits(ye))[:5]}"
     return y
@@ -175,21 +166,22 @@ def test_down_small_batch_full():
     check_mul_mat(workloads.down_small_batch_case())
 
 
-def test_prefill_gate_gemm_sampled():
+def test_prefill_gate_gemm_full():
+    """The 512-row prefill on the gate shape, every one of its 512 x 8960
+    outputs, through the automatic choice (the schedule the benchmark times)
+    and through every GEMM variant."""
     case = workloads.prefill_gate_case()
-    sample = np.unique(np.concatenate([np.arange(0, 48), np.arange(8960 - 40, 8960),
-                                       np.random.default_rng(0).choice(8960, 64, replace=False)]))
-    check_mul_mat(case, sample=sample)
+    pnp = oracle.pack(case.w, case.ws)
+    pg = gpu_pack(case.w, case.ws)
+    exp = oracle.mul_mat_sliced(pnp, case.rows, case.K, case.x, with_dot=True)
+    check_mul_mat(case, packed_gpu=pg, packed_np=pnp, expected=exp)
+    for v in range(1, i2s.i2s_kernel_variants(2) + 1):
+        check_mul_mat(case, kernel=2, variant=v, packed_gpu=pg, packed_np=pnp, expected=exp)
 
 
 @pytest.mark.parametrize("case", workloads.layer_sweep_cases(), ids=lambda c: c.name)
 def test_layer_sweep(case):
-    rows = case.rows
-    sample = None
-    if case.N * rows * case.K > 60_000_000:
-        sample = np.unique(np.concatenate([np.arange(0, 20), np.arange(rows - 20, rows),
-                                           np.random.default_rng(1).choice(rows, 40, replace=False)]))
-    check_mul_mat(case, sample=sample)
+    check_mul_mat(case)
 
 
 # --- every launch geometry gives the same bits (the M2 grid) -------------------------
@@ -238,14 +230,13 @@ def test_all_fused_variants_decode_shapes(N):
         case = workloads.random_case(23, rows, K, N)
         pnp = oracle.pack(case.w, case.ws)
         pg = gpu_pack(case.w, case.ws)
-        sample = np.unique(np.concatenate([np.arange(0, 24), np.arange(rows - 24, rows),
-                                           np.random.default_rng(4).choice(rows, 48, replace=False)]))
+        exp = oracle.mul_mat_sliced(pnp, rows, K, case.x, with_dot=True)
         for v in range(1, i2s.i2s_kernel_variants(3) + 1):
             if K > 2048 and v <= 3:
                 with pytest.raises(i2s.I2SError):
                     i2s.i2s_mul_mat_ex(pg, rows, K, dev(case.x), kernel=3, variant=v)
                 continue
-            check_mul_mat(case, kernel=3, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
+            check_mul_mat(case, kernel=3, variant=v, packed_gpu=pg, packed_np=pnp, expected=exp)
 
 
 @pytest.mark.parametrize("N", [1, 3, 8])
@@ -255,10 +246,9 @@ def test_all_gemv_variants_full_decode_shapes(N):
         case = workloads.random_case(21, rows, K, N)
         pnp = oracle.pack(case.w, case.ws)
         pg = gpu_pack(case.w, case.ws)
-        sample = np.unique(np.concatenate([np.arange(0, 24), np.arange(rows - 24, rows),
-                                           np.random.default_rng(2).choice(rows, 48, replace=False)]))
+        exp = oracle.mul_mat_sliced(pnp, rows, K, case.x, with_dot=True)
         for v in range(1, i2s.i2s_kernel_variants(1) + 1):
-            check_mul_mat(case, kernel=1, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
+            check_mul_mat(case, kernel=1, variant=v, packed_gpu=pg, packed_np=pnp, expected=exp)
 
 
 @pytest.mark.parametrize("N", [16, 17, 32, 33, 48, 64])
@@ -270,33 +260,30 @@ def test_all_skinny_variants_decode_shapes(N):
         case = workloads.random_case(29 + N, rows, K, N)
         pnp = oracle.pack(case.w, case.ws)
         pg = gpu_pack(case.w, case.ws)
-        sample = np.unique(np.concatenate([np.arange(0, 24), np.arange(rows - 24, rows),
-                                           np.random.default_rng(4).choice(rows, 48, replace=False)]))
+        exp = oracle.mul_mat_sliced(pnp, rows, K, case.x, with_dot=True)
         for v in range(1, i2s.i2s_kernel_variants(4) + 1):
-            check_mul_mat(case, kernel=4, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
+            check_mul_mat(case, kernel=4, variant=v, packed_gpu=pg, packed_np=pnp, expected=exp)
 
 
 def test_all_gemm_variants_prefill_shape():
     case = workloads.prefill_gate_case(N=200)
     pnp = oracle.pack(case.w, case.ws)
     pg = gpu_pack(case.w, case.ws)
-    sample = np.unique(np.concatenate([np.arange(0, 40), np.arange(8960 - 40, 8960),
-                                       np.random.default_rng(3).choice(8960, 40, replace=False)]))
+    exp = oracle.mul_mat_sliced(pnp, case.rows, case.K, case.x, with_dot=True)
     for v in range(1, i2s.i2s_kernel_variants(2) + 1):
-        check_mul_mat(case, kernel=2, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
+        check_mul_mat(case, kernel=2, variant=v, packed_gpu=pg, packed_np=pnp, expected=exp)
 
 
 def test_gemm_variants_many_groups_per_wave():
     """N = 2048 on the gate shape: 9 subtiles per wave, so every resident
     variant runs several groups and a short last one (groups of 2, 3 and 4);
-    checked on sampled output features."""
+    every output checked."""
     case = workloads.prefill_gate_case(seed=5, N=2048)
     pnp = oracle.pack(case.w, case.ws)
     pg = gpu_pack(case.w, case.ws)
-    sample = np.unique(np.concatenate([np.arange(0, 24), np.arange(8960 - 24, 8960),
-                                       np.random.default_rng(8).choice(8960, 24, replace=False)]))
+    exp = oracle.mul_mat_sliced(pnp, case.rows, case.K, case.x, with_dot=True)
     for v in (0, 11, 12, 13, 14):
-        check_mul_mat(case, kernel=2, variant=v, sample=sample, packed_gpu=pg, packed_np=pnp)
+        check_mul_mat(case, kernel=2, variant=v, packed_gpu=pg, packed_np=pnp, expected=exp)
 
 
 # --- edge cases -----------------------------------------------------------------------
@@ -304,15 +291,17 @@ def test_gemm_variants_many_groups_per_wave():
 @pytest.mark.parametrize("N", [1, 8, 64])
 def test_headroom(N):
     case = workloads.headroom_case(N)
-    y = check_mul_mat(case, sample=np.array([0, 1, 777, 1535]))
-    assert (bits(y) == 0x46855999).all()
+    y = check_mul_mat(case)
+    assert y.shape == (N, 1536)
+    assert (bits(y) == 0x46855999).all()  # every output: the closed form
 
 
 @pytest.mark.parametrize("N,row", [(1, 0), (64, 17)])
 def test_zero_activation_row(N, row):
     case = workloads.zero_row_case(N, row)
-    y = check_mul_mat(case, sample=np.array([0, 5, 4000, 8959]))
-    assert (bits(y[row]) == 0).all()
+    y = check_mul_mat(case)
+    assert y.shape == (N, 8960)
+    assert (bits(y[row]) == 0).all()  # all 8960 features of the zero row are +0
     assert not np.isnan(y).any()
 
 
@@ -328,10 +317,10 @@ def test_zero_weights_zero_scale():
                                       (5, 8960, 100), (1000, 256, 300), (50, 10240, 3), (70, 3072, 6)])
 def test_ragged_shapes(rows, K, N):
     case = workloads.random_case(rows + N, rows, K, N, ws=0.031)
-    sample = None if rows * K * N < 40_000_000 else np.arange(0, rows, 97)
-    check_mul_mat(case, sample=sample)
+    exp = oracle.mul_mat_sliced(oracle.pack(case.w, case.ws), rows, K, case.x, with_dot=True)
+    check_mul_mat(case, expected=exp)
     if N <= 8:
-        check_mul_mat(case, kernel=2, variant=1, sample=sample)
+        check_mul_mat(case, kernel=2, variant=1, expected=exp)
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -431,9 +420,8 @@ def test_graph_replay_matches_eager(rows, K, N):
     ws = i2s.new_workspace(N, K, DEV)
     y = torch.empty((N, rows), device=DEV)
     y_eager = host(i2s.i2s_mul_mat(pg, rows, K, x, workspace=ws)).copy()
-    sample = np.arange(0, rows, max(1, rows // 50))
-    ye, _ = oracle_rows(oracle.pack(case.w, case.ws), rows, K, case.x, sample)
-    assert np.array_equal(bits(y_eager[:, sample]), bits(ye))
+    ye = oracle.mul_mat_sliced(oracle.pack(case.w, case.ws), rows, K, case.x)
+    assert np.array_equal(bits(y_eager), bits(ye))
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):

@@ -1,8 +1,10 @@
 """GPU parity of the per-channel W8A8 path against the CPU oracle, bit for bit:
 both quantizers (the hand-worked rounding row, near ties, zero rows, ragged
 K), the contraction on every tile variant with ragged shapes and full-scale
-accumulators, and the whole op on the Qwen2-1.5B projection shapes (prefill
-checked on sampled rows: rows are independent)."""
+accumulators, the activation-resident kernel's full and short subtile groups,
+and the whole op on the Qwen2-1.5B projection shapes; every output is
+compared (the oracle runs over slices of the activation rows on the host
+threads)."""
 
 from __future__ import annotations
 
@@ -179,9 +181,41 @@ def test_matmul_full_scale():
         assert np.array_equal(host(c), rc) and np.array_equal(bits(host(y)), bits(rd))
 
 
-@pytest.mark.parametrize("name,OC,K,M,rows", [("decode_up", 8960, 1536, 1, None), ("down_small_batch", 1536, 8960, 8, None),
-                                             ("qkv_64", 256, 1536, 64, None), ("prefill_gate", 8960, 1536, 512, 40)])
-def test_whole_op_qwen2_shapes(name, OC, K, M, rows):
+# Shapes for the activation-resident kernel (variant 10): a block of ms
+# 16-channel subtiles is dealt to 8 waves, each working through its subtiles
+# in groups of G (4 from 4096 channels, 3 below), the last group possibly
+# short.  (ms, subtiles per wave) for each shape:
+#   4100 x 2048 rows: ms 33 -> waves of 5 and 4 (a full group of 4, one of 1)
+#   4097 x 2048: the same without 16-byte stores (OC % 4 != 0)
+#   4100 x 4096: ms 65 -> waves of 9 and 8 (two full groups of 4, one of 1)
+#   4100 x 4000: as above with a ragged last activation tile
+#   3000 x 2048: ms 24 -> 3 per wave (one full group of 3)
+#   3001 x 4096: ms 47 -> 6 or 5 per wave (two groups of 3, a short one), no 16-byte stores
+#   8960 x 1024 at K 1536: ms 35 -> 5 or 4 per wave, the prefill's shape at twice the rows
+RES_GROUP_SHAPES = [(4100, 128, 2048), (4097, 128, 2048), (4100, 128, 4096), (4100, 64, 4000), (3000, 128, 2048),
+                    (3001, 192, 4096), (8960, 1536, 1024)]
+
+
+@pytest.mark.parametrize("OC,K,M", RES_GROUP_SHAPES)
+def test_resident_kernel_full_and_short_groups(OC, K, M):
+    rng = np.random.default_rng(OC * 3 + K + M)
+    wq = rng.integers(-127, 128, size=(OC, K), dtype=np.int8)
+    aq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    ws = rng.uniform(1e-4, 0.05, size=OC).astype(np.float32)
+    as_ = rng.uniform(1e-3, 0.2, size=M).astype(np.float32)
+    rd, rc = oracle.w8a8_matmul_sliced(aq, as_, wq, ws, with_c=True)
+    say(f"w8a8_matmul resident groups OC={OC} K={K} M={M}")
+    for v in (10, 0):
+        y, c = w8a8.w8a8_matmul(dev(wq), dev(ws), dev(aq), dev(as_), dot_out=True, variant=v)
+        y2 = w8a8.w8a8_matmul(dev(wq), dev(ws), dev(aq), dev(as_), variant=v)
+        assert np.array_equal(host(c), rc), v
+        assert np.array_equal(bits(host(y)), bits(rd)), v
+        assert np.array_equal(bits(host(y2)), bits(rd)), (v, "without dot_out")
+
+
+@pytest.mark.parametrize("name,OC,K,M", [("decode_up", 8960, 1536, 1), ("down_small_batch", 1536, 8960, 8),
+                                        ("qkv_64", 256, 1536, 64), ("prefill_gate", 8960, 1536, 512)])
+def test_whole_op_qwen2_shapes(name, OC, K, M):
     say(f"w8a8_mul_mat {name} OC={OC} K={K} M={M}")
     rng = np.random.default_rng(0)
     w = (rng.normal(0, 0.02, size=(OC, K))).astype(np.float32)
@@ -191,9 +225,8 @@ def test_whole_op_qwen2_shapes(name, OC, K, M, rows):
     rwq, rws = oracle.w8a8_quantize_weight(w)
     assert np.array_equal(host(wq), rwq) and np.array_equal(bits(host(ws)), bits(rws))
     y = host(w8a8.w8a8_mul_mat(wq, ws, dev(x)))
-    pick = np.arange(M) if rows is None else np.sort(rng.choice(M, size=rows, replace=False))
-    rd = oracle.w8a8_mul_mat(rwq, rws, x[pick])
-    assert np.array_equal(bits(y[pick]), bits(rd))
+    rd = oracle.w8a8_mul_mat_sliced(rwq, rws, x)
+    assert np.array_equal(bits(y), bits(rd))
 
 
 def test_whole_op_zero_rows_and_streams():

@@ -347,3 +347,17 @@ def test_batched_is_the_same_rows_reindexed():
     assert yb.shape == (B, N, rows)
     assert np.array_equal(db.reshape(B * N, rows), d2)
     assert np.array_equal(yb.reshape(B * N, rows).view(np.uint32), y2.view(np.uint32))
+
+
+def test_sliced_oracle_is_the_whole_call():
+    """mul_mat_sliced (output features split over threads) gives mul_mat's
+    bits: every slice is a valid packed tensor and rows are independent."""
+    rng = np.random.default_rng(77)
+    for rows, K, N, threads in ((97, 384, 5, 4), (16, 128, 3, 16), (5, 1152, 2, 7), (300, 256, 1, 0)):
+        w = workloads.ternary(rng, rows, K)
+        x = workloads.normal(rng, N, K)
+        p = oracle.pack(w, 0.0125)
+        y, d = oracle.mul_mat(p, rows, K, x, with_dot=True)
+        ys, ds = oracle.mul_mat_sliced(p, rows, K, x, with_dot=True, threads=threads)
+        assert np.array_equal(ds, d)
+        assert np.array_equal(ys.view(np.uint32), y.view(np.uint32))
