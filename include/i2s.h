@@ -56,6 +56,8 @@ extern "C" {
 #define I2S_ERANGE 5     /* a size beyond what this library addresses */
 #define I2S_EKERNEL 6    /* i2s_mul_mat_ex/_ws: unknown kernel or variant, or
                             one that does not accept this N or K */
+#define I2S_ESCRATCH 7   /* i2s_mul_mat_noalloc: the shape's workspace exceeds
+                            I2S_NOALLOC_SCRATCH_BYTES */
 
 /* Bytes of an I2_S tensor of `rows` x `K` weights: rows*K/4 bytes of 2-bit
  * codes, then a 32-byte slot whose first 4 bytes are the F32 weight scale
@@ -208,6 +210,30 @@ int i2s_mul_mat_group_ex(const i2s_proj *projs, int count, int64_t K,
                          const float *x, int64_t N,
                          void *workspace, size_t workspace_bytes,
                          int kernel, int variant, void *stream);
+
+/* i2s_mul_mat without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The library calls no allocator in it.  The
+ * activation workspace is instead a fixed array in the library's device
+ * memory, I2S_NOALLOC_SCRATCH_BYTES (32 MiB) on every GPU the library runs on,
+ * held until the process ends; the kernels and every result bit are those of
+ * i2s_mul_mat.  Arguments as i2s_mul_mat's.
+ * Shapes with i2s_act_workspace_bytes(N, K) > I2S_NOALLOC_SCRATCH_BYTES return
+ * I2S_ESCRATCH before anything is launched (N * K up to about 16 million
+ * fits: 512 x 1536 and 1024 x 8960 do).  All calls on one GPU share that
+ * GPU's array, so calls that overlap on one GPU (other streams, other host
+ * threads) race on it: order them on one stream, or use i2s_mul_mat with a
+ * workspace each.  The array needs no clearing: every call writes the parts
+ * it reads.  The first call on a device looks up the array's address there
+ * (no allocation).
+ * Errors: as i2s_mul_mat, and I2S_ESCRATCH. */
+#define I2S_NOALLOC_SCRATCH_BYTES (32u << 20)
+int i2s_mul_mat_noalloc(const uint8_t *packed, int64_t rows, int64_t K,
+                        const float *x, int64_t N,
+                        float *y, int32_t *dot_out, void *stream);
+
+/* The size of that array: I2S_NOALLOC_SCRATCH_BYTES. */
+size_t i2s_noalloc_scratch_bytes(void);
 
 /* The contraction kernel i2s_mul_mat launches for this shape (1 = GEMV after
  * a separate quantize launch, 2 = MFMA GEMM after a separate quantize launch,

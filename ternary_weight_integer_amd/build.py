@@ -16,7 +16,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "i2s.hip"), os.path.join(PKG, "csrc", "i8s.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("i2s.hip", "i8s.hip", "noalloc.hip")]
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("i2s.h", "i8s.h", "w8a8.h")]
 LIB = os.path.join(PKG, "libi2s.so")
 ARCH = "gfx950"

@@ -2488,6 +2488,7 @@ extern "C" const char *i2s_strerror(int status) {
     case I2S_EHIP: return "HIP runtime error at launch";
     case I2S_ERANGE: return "size beyond what the library addresses";
     case I2S_EKERNEL: return "unknown kernel or variant, or one that does not accept this N or K";
+    case I2S_ESCRATCH: return "the shape needs more workspace than i2s_mul_mat_noalloc's fixed array holds";
     default: return "unknown status";
   }
 }

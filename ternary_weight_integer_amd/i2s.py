@@ -24,6 +24,7 @@ I2S_EWORKSPACE = 3
 I2S_EHIP = 4
 I2S_ERANGE = 5
 I2S_EKERNEL = 6
+I2S_ESCRATCH = 7
 
 KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM = 0, 1, 2
 
@@ -92,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.i2s_kernel_variants.argtypes = [ci]
         L.i2s_strerror.restype = ctypes.c_char_p
         L.i2s_strerror.argtypes = [ci]
+        L.i2s_mul_mat_noalloc.restype = ci
+        L.i2s_mul_mat_noalloc.argtypes = [p, i64, i64, p, i64, p, p, p]
+        L.i2s_noalloc_scratch_bytes.restype = sz
+        L.i2s_noalloc_scratch_bytes.argtypes = []
         _lib = L
     return _lib
 
@@ -240,6 +245,29 @@ def i2s_mul_mat(packed: torch.Tensor, rows: int, K: int, x: torch.Tensor, worksp
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _dev(y, torch.float32, "y"), dptr,
         _stream(stream)))
     return (y, dot_out) if want_dot else y
+
+
+def i2s_noalloc_scratch_bytes() -> int:
+    return int(lib().i2s_noalloc_scratch_bytes())
+
+
+def i2s_mul_mat_noalloc(packed: torch.Tensor, rows: int, K: int, x: torch.Tensor, y: torch.Tensor,
+                        dot_out=None, stream=None):
+    """i2s_mul_mat with the library's fixed device array as its workspace:
+    the caller passes every buffer (y and, if wanted, dot_out), so nothing is
+    allocated on the way in or inside."""
+    N = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [N][{K}], got {tuple(x.shape)}")
+    if packed.numel() < i2s_packed_bytes(rows, K):
+        raise ValueError("packed tensor smaller than i2s_packed_bytes(rows, K)")
+    if y.numel() < N * rows or (dot_out is not None and dot_out.numel() < N * rows):
+        raise ValueError("y or dot_out too small")
+    dptr = _dev(dot_out, torch.int32, "dot_out") if dot_out is not None else None
+    _check("i2s_mul_mat_noalloc", lib().i2s_mul_mat_noalloc(
+        _dev(packed, torch.uint8, "packed"), rows, K, _dev(x, torch.float32, "x"), N, _dev(y, torch.float32, "y"),
+        dptr, _stream(stream)))
+    return y
 
 
 def i2s_quantize_act_ws(x: torch.Tensor, workspace: torch.Tensor, stream=None) -> torch.Tensor:

@@ -46,11 +46,11 @@ def test_kernel_variant_counts():
 
 def test_strerror_covers_every_status():
     seen = set()
-    for st in range(0, 7):
+    for st in range(0, 8):
         msg = i2s.i2s_strerror(st)
         assert msg and msg != "unknown status"
         seen.add(msg)
-    assert len(seen) == 7
+    assert len(seen) == 8
     assert i2s.i2s_strerror(99) == "unknown status"
 
 
@@ -146,3 +146,14 @@ def test_mul_mat_variant_choice():
     assert i2s.i2s_mul_mat_variant(2048, 1536, 512) == 12   # 4
     with pytest.raises(i2s.I2SError):
         i2s.i2s_mul_mat_variant(4, 100, 1)
+
+
+def test_noalloc_limit_is_checked_on_the_host():
+    """i2s_mul_mat_noalloc refuses a shape whose workspace exceeds its fixed
+    array before touching the GPU (fake pointers, no device needed)."""
+    assert i2s.i2s_noalloc_scratch_bytes() == 32 << 20
+    assert i2s.i2s_act_workspace_bytes(1024, 8960) <= i2s.i2s_noalloc_scratch_bytes()
+    assert i2s.i2s_act_workspace_bytes(2048, 8960) > i2s.i2s_noalloc_scratch_bytes()
+    st = i2s.lib().i2s_mul_mat_noalloc(FAKE, 4, 8960, FAKE, 2048, FAKE, None, None)
+    assert st == i2s.I2S_ESCRATCH
+    assert i2s.lib().i2s_mul_mat_noalloc(FAKE, 4, 100, FAKE, 1, FAKE, None, None) == i2s.I2S_EALIGN
