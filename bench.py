@@ -8,16 +8,23 @@ before timing, as it does offline for a checkpoint.
 
 Default workload: the Qwen2-1.5B FFN up projection at decode time, ternary
 weight [8960][1536] (P(-1,0,+1) = 0.3/0.4/0.3, scale 0.015) against one F32
-activation row ~ N(0,1) with 1% of its entries scaled by 20, seed 0.
+activation row ~ N(0,1) with 1% of its entries scaled by 20, seed 0 (the
+line's value, against HBM); beside it, under "prefill_gemm", the gate
+projection's prefill: the same weight shape against 512 rows ~ N(0,1), whose
+contraction is the int8-MFMA GEMM (its roofline against int8 MFMA).
 
 Measurement:
   * every input is resident in device memory before the timed region; the
     packed weight is replicated into enough distinct copies (>= 512 MiB in
     total, twice the 256 MiB Infinity Cache) and step i uses copy i mod R,
     so each step reads its weights from HBM, as a 28-layer decode does;
-  * the K timed steps are captured once in a HIP graph (launches from Python
-    would otherwise be slower than the kernels) and replayed between two HIP
-    events on the launch stream, bracketed by device synchronizations;
+  * the K timed steps are captured in a HIP graph (launches from Python
+    would otherwise be slower than the kernels), repeated inside it as many
+    times as make a run of about --min-region-ms (starting a graph costs a
+    few microseconds, which a 20-step graph would spread over its steps), and
+    the graph is replayed between two HIP events on the launch stream,
+    bracketed by device synchronizations; ms_per_step is the region over the
+    steps it ran (config.timed_steps);
   * the dominant kernel's average launch duration comes from a second graph of
     back-to-back launches of that kernel alone, timed the same way inside the
     same bracket; roofline.achieved = algorithmic bytes per launch / that time;
@@ -87,8 +94,8 @@ def parse_args(argv=None):
                    help="launch from Python without graphs (for counter collection runs)")
     p.add_argument("--no-prefill", action="store_true",
                    help="default workload only: skip the prefill GEMM reported beside the decode GEMV")
-    p.add_argument("--min-region-ms", type=float, default=2.0,
-                   help="replay the K-step graph back to back until the timed region is about this long")
+    p.add_argument("--min-region-ms", type=float, default=3.0,
+                   help="repeat the K steps inside the timed graph until it runs for about this long")
     p.add_argument("--copy-kernel-mib", type=int, default=0,
                    help="only run a plain copy of this many MiB (counter calibration) and exit")
     return p.parse_args(argv)
@@ -810,17 +817,20 @@ def main(argv=None):
     return 0
 
 
-def min_region_replays(torch, g, steps: int, target_ms: float) -> int:
-    """How many back-to-back replays of the K-step graph g make a timed region
-    of about target_ms, so that the one-off cost of starting a graph is
-    spread over enough work that the step time does not depend on K."""
+def graph_repeats(torch, step, steps: int, target_ms: float) -> int:
+    """How many times the K timed steps are repeated inside the timed graph so
+    that it runs for about target_ms: starting a graph costs a few
+    microseconds of its own, which a short graph would add to every step."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g = graph_of(lambda: [step(i) for i in range(steps)], torch)
+    g.replay()
     torch.cuda.synchronize()
     e0.record()
     g.replay()
     e1.record()
     torch.cuda.synchronize()
     once = max(e0.elapsed_time(e1), 1e-3)
+    del g
     return max(1, int(-(-target_ms // once)))
 
 
@@ -860,7 +870,7 @@ def bench_case(args, torch, i2s, case):
     y_eager = y.clone()
 
     K_steps = args.steps
-    replays = 1
+    repeats = 1
     if args.eager:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -874,7 +884,8 @@ def bench_case(args, torch, i2s, case):
         step_ms = e0.elapsed_time(e1) / K_steps
         kern_us = None
     else:
-        g_step = graph_of(lambda: [step(i) for i in range(K_steps)], torch)
+        repeats = graph_repeats(torch, step, K_steps, args.min_region_ms)
+        g_step = graph_of(lambda: [step(i) for i in range(K_steps * repeats)], torch)
         n_kern = max(R, 256)
         g_kern = graph_of(lambda: [contraction(i) for i in range(n_kern)], torch)
         g_step.replay()
@@ -883,19 +894,17 @@ def bench_case(args, torch, i2s, case):
         # y now holds the last contraction of copy (n_kern-1) % R; every copy is identical.
         if not torch.equal(y.view(torch.int32), y_eager.view(torch.int32)):
             raise RuntimeError("graph replay result differs from the eager result")
-        replays = min_region_replays(torch, g_step, K_steps, args.min_region_ms)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev[0].record()
-        for _ in range(replays):
-            g_step.replay()
+        g_step.replay()
         ev[1].record()
         g_kern.replay()
         ev[2].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        step_ms = ev[0].elapsed_time(ev[1]) / (K_steps * replays)
+        step_ms = ev[0].elapsed_time(ev[1]) / (K_steps * repeats)
         kern_us = ev[1].elapsed_time(ev[2]) * 1e3 / n_kern
         if not torch.equal(y.view(torch.int32), y_eager.view(torch.int32)):
             raise RuntimeError("graph replay result differs from the eager result")
@@ -921,7 +930,7 @@ def bench_case(args, torch, i2s, case):
         "config": {"workload": case.name, "rows": rows, "K": K, "N": N, "weight_scale": case.ws,
                    "weight_copies_rotated": R, "rotated_bytes": R * packed0.numel(),
                    "timing": "eager" if args.eager else "hip_graph",
-                   "graph_replays": replays, "timed_steps": K_steps * replays},
+                   "step_repeats": repeats, "timed_steps": K_steps * repeats},
         "int8_tops": round(ops / (step_ms * 1e-3) / 1e12, 4),
         "wall_s": round(wall, 4),
     }
