@@ -220,6 +220,8 @@ def copy_kernel_only(mib: int):
 
 def kernel_name_of(kind: int, variant: int) -> str:
     if kind == 2:
+        if variant == 15:
+            return "gemm_wk_kernel"
         return "gemm_pipe_kernel" if variant == 10 else ("gemm_res_kernel" if variant >= 5 else "gemm_kernel")
     return {1: "gemv_kernel", 3: "gemv_fused_kernel", 4: "gemv_mfma_kernel"}[kind]
 

@@ -77,6 +77,14 @@ def build(verbose: bool = False) -> str:
         os.remove(obj)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc link failed ({res.returncode}):\n{_errors(res.stderr)}")
+    # A kernel whose host-side stub the compiler dropped links as an
+    # undefined symbol; refuse such a library here rather than at first use.
+    import ctypes
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"built library does not load: {e}") from e
     os.replace(tmp, LIB)
     return LIB
 

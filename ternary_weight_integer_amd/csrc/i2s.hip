@@ -1071,33 +1071,36 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
     }
     load_w(groups > 1 ? 1 : 0, 0, wb);
   } else {
-    load_w(0, 0, wa);
-    // Copy the whole activation tile: wave w copies rows w*kRowsPerWave..,
-    // 16-byte pieces lane, lane+64, ... of each padded row; pieces past K
-    // read as zero.
-    const int per_row = chunks * S * 16;
-    for (int c0 = 0; c0 < per_row; c0 += 128) {
-      v4i v[kRowsPerWave][2];
-#pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) {
-        const int r = wave * kRowsPerWave + i;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int c = c0 + 64 * h + lane;
-          const uint32_t off = c < k_pieces ? static_cast<uint32_t>(r * K + 16 * c) : kOutOfRange;
-          v[i][h] = __builtin_amdgcn_raw_buffer_load_b128(qbuf, off, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) {
-        const int r = wave * kRowsPerWave + i;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int c = c0 + 64 * h + lane;
-          if (c < per_row) *reinterpret_cast<v4i *>(lds_res + r * pitch + 16 * c) = v[i][h];
-        }
+    // The whole activation tile goes from memory straight into LDS (buffer
+    // loads with the LDS-direct bit: no registers, no wait per piece), issued
+    // before the first group's weights so that the tile does not queue behind
+    // them.  The tile is a run of 16-byte slots, pitch/16 per row; load
+    // instruction i fills slots 64i..64i+63, lane l slot 64i+l, i.e. piece c
+    // of row r for slot r*(pitch/16) + c.  Slots past K (the row's padding),
+    // rows past N and slots past the tile read out of range, so they hold
+    // zeros.  The LDS allocation is a whole number of these KiB runs.
+    const int P = static_cast<int>(pitch / 16);
+    const int insts = (BN * P + 63) / 64;
+    int r = (64 * wave + lane) / P, c = (64 * wave + lane) % P;
+    const int dr = (64 * WAVES) / P, dc = (64 * WAVES) % P;
+    for (int i = wave; i < insts; i += WAVES) {
+      const uint32_t off = r < n_here && c < k_pieces ? static_cast<uint32_t>(r * K + 16 * c) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qbuf, (__attribute__((address_space(3))) void *)(lds_res + 1024 * i), 16, off, 0, 0, 0);
+      r += dr;
+      c += dc;
+      if (c >= P) {
+        c -= P;
+        ++r;
       }
     }
+    load_w(0, 0, wa);
+    // This wave's tile loads are complete once at most the G*S weight loads
+    // issued after them are outstanding; the barrier then publishes every
+    // wave's part of the tile.
+    constexpr int kWeightLoads = G * S;
+    static_assert(kWeightLoads < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((kWeightLoads & 15) | ((kWeightLoads >> 4) << 14) | (7 << 4) | (15 << 8));
     __syncthreads();
   }
 
@@ -1129,16 +1132,18 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       }
     }
   };
-  auto with_bias = [&](float v, int gi, int r) {
-    return has_bias ? add_bias(v, __int_as_float(bv[gi][r])) : v;
-  };
 
   v4i acc[G][WN];
   // Stores of a finished group, non-temporal (the outputs are not read
   // again by this kernel); subtiles past the group (gi >= gs) and outputs
-  // past the tensor get an out-of-range offset instead of a branch.
+  // past the tensor get an out-of-range offset instead of a branch.  The
+  // accumulators start at -row_sum (init_acc), so each holds dot - row_sum
+  // and the epilogue is one conversion and one multiply; with DOT the raw
+  // dot is that plus the row sum.  The bias test is one wave-uniform branch
+  // around the whole group.
   constexpr int kStreamStore = 2;
-  auto epilogue_group = [&](int grp, int gs) {
+  auto store_group = [&](int grp, int gs, auto biased) {
+    constexpr bool kBias = decltype(biased)::value;
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       const bool sub_ok = gi < gs;
@@ -1146,32 +1151,43 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 #pragma unroll
       for (int n = 0; n < WN; ++n) {
         const uint32_t base = static_cast<uint32_t>((16 * n + li) * ldy);  // element offset of this lane's row
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = static_cast<float>(acc[gi][n][r]) * tn[n];
+          if constexpr (kBias) v[r] = add_bias(v[r], __int_as_float(bv[gi][r]));
+        }
         if constexpr (VEC4) {
           const uint32_t off = sub_ok && o < rows ? 4 * (base + static_cast<uint32_t>(o)) : kOutOfRange;
-          const v4i yv = {__float_as_int(with_bias(epilogue(acc[gi][n][0], rsn[n], tn[n]), gi, 0)),
-                          __float_as_int(with_bias(epilogue(acc[gi][n][1], rsn[n], tn[n]), gi, 1)),
-                          __float_as_int(with_bias(epilogue(acc[gi][n][2], rsn[n], tn[n]), gi, 2)),
-                          __float_as_int(with_bias(epilogue(acc[gi][n][3], rsn[n], tn[n]), gi, 3))};
+          const v4i yv = {__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])};
           __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, kStreamStore);
-          if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b128(acc[gi][n], dbuf, off, 0, kStreamStore);
+          if constexpr (DOT) {
+            const v4i dv = acc[gi][n] + v4i{rsn[n], rsn[n], rsn[n], rsn[n]};
+            __builtin_amdgcn_raw_buffer_store_b128(dv, dbuf, off, 0, kStreamStore);
+          }
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t off = sub_ok && o + r < rows ? 4 * (base + static_cast<uint32_t>(o + r)) : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(with_bias(epilogue(acc[gi][n][r], rsn[n], tn[n]), gi, r)),
-                                                  ybuf, off, 0, kStreamStore);
-            if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(acc[gi][n][r], dbuf, off, 0, kStreamStore);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[r]), ybuf, off, 0, kStreamStore);
+            if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(acc[gi][n][r] + rsn[n], dbuf, off, 0, kStreamStore);
           }
         }
       }
     }
+  };
+  auto epilogue_group = [&](int grp, int gs) {
+    if (has_bias)
+      store_group(grp, gs, std::true_type{});
+    else
+      store_group(grp, gs, std::false_type{});
   };
 
   auto zero_acc = [&]() {
 #pragma unroll
     for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-      for (int n = 0; n < WN; ++n) acc[gi][n] = v4i{0, 0, 0, 0};
+      for (int n = 0; n < WN; ++n) acc[gi][n] = v4i{-rsn[n], -rsn[n], -rsn[n], -rsn[n]};
   };
 
   // The MFMAs (and, with PERM, the permutes) of the group's gs subtiles only.
@@ -1271,6 +1287,283 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       if (it + 1 >= iters) break;
       item(wb, wa);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight-resident MFMA GEMM for the prefill shapes (K <= 256*CH, at most 8*G
+// weight subtiles per block; positions past K are zeros on both sides).
+// Same operand pairing as gemm_res_kernel; the schedule differs:
+//  * loads go out chunk by chunk (256 positions), a window of three chunks
+//    ahead of the MFMAs: the chunk's slice of the block's activation tile
+//    (64 rows x 256 bytes, straight into LDS with LDS-direct buffer loads,
+//    two of the chunk's sixteen 1 KiB runs per wave), then this wave's
+//    weights for the chunk (G subtiles x 16 bytes per lane, row-contiguous:
+//    lane l reads row l/4, bytes 16*(l%4) of the chunk).  Every group of 4
+//    lanes reads 64 contiguous bytes, and the MFMAs of chunk c wait only for
+//    chunk c (one barrier per chunk publishes the other waves' parts of the
+//    tile).  A compute unit's vector-memory path takes about one 1 KiB load
+//    every 30 cycles, so issuing every load up front held each wave in its
+//    load instructions for microseconds before its first MFMA;
+//  * the weights stay in registers; each chunk is moved into MFMA lane order
+//    (ds_bpermute) during the chunk before it, and its four 64-position steps
+//    are unpacked one step ahead of their MFMAs;
+//  * the B operands of the next step are read from LDS while the current
+//    step's MFMAs run (two register sets), and sched_group_barrier keeps the
+//    VALU and LDS work between the MFMAs;
+//  * the accumulators start at -row_sum, so the epilogue is one conversion
+//    and one multiply (plus the bias add when there is a bias);
+//  * wave w holds subtiles 2w and 2w+1 (then 16+w, 24+w, ...): the two
+//    subtiles' stores fill whole 128-byte lines of y.
+// LDS layout of the activation tile: chunk-major, 16 KiB per chunk; piece p
+// (16 bytes) of row r in chunk c at 16 * (1024c + 16r + (p ^ (r % 16))).  A
+// B read (16 lanes: rows 16n..16n+15 at one piece) then touches 16 different
+// bank groups, and an LDS-direct run (64 consecutive slots: 4 rows x 16
+// pieces) fetches 64 contiguous bytes per 4 consecutive lanes.
+
+// The subtile (block-relative) that slot g of wave w holds.
+template <int G>
+__device__ __forceinline__ int wk_subtile(int w, int g) {
+  if constexpr (G == 1) return w;
+  return g < 2 ? 2 * w + g : 16 + 8 * (g - 2) + w;
+}
+
+constexpr int kWkChunkBytes = 64 * 256;  // one chunk of the 64-row activation tile
+
+// One LDS-direct buffer load: lane l's 16 bytes at buffer offset `off` go to
+// LDS byte lds + 16*l (out-of-range offsets write zeros).
+__device__ __forceinline__ void lds_direct16(__amdgpu_buffer_rsrc_t rsrc, int8_t *lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
+}
+
+template <int G, int CH, bool VEC4, bool DOT>
+__global__ void __launch_bounds__(512)
+gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const int8_t *__restrict__ qp, int64_t N,
+               const float *__restrict__ act_scale, const int32_t *__restrict__ row_sum, float *__restrict__ y,
+               int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t ldy, int tiles_m, int ms) {
+  extern __shared__ __attribute__((aligned(16))) int8_t lds_wk[];
+  constexpr int WN = 4, BN = 64;
+  const int KB = K / 4;           // packed bytes per row
+  const int k_pieces = K / 16;    // 16-byte activation pieces per row
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, kb = lane >> 4;
+  const int tile_m = static_cast<int>(blockIdx.x) % tiles_m, tile_n = static_cast<int>(blockIdx.x) / tiles_m;
+  const int64_t o_tile = static_cast<int64_t>(tile_m) * ms * 16;
+  const int64_t n0 = static_cast<int64_t>(tile_n) * BN;
+  const int n_here = static_cast<int>(N - n0 < BN ? N - n0 : BN);
+  const int64_t present = (rows - o_tile + 15) / 16;
+  const int msub = static_cast<int>(present < ms ? present : ms);
+  int mine = 0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) mine += wk_subtile<G>(wave, g) < msub ? 1 : 0;
+
+  const __amdgpu_buffer_rsrc_t qbuf = buffer_of(qp + n0 * K, static_cast<uint32_t>(n_here * K));
+  const __amdgpu_buffer_rsrc_t wbuf =
+      buffer_of(packed + o_tile * KB, static_cast<uint32_t>((rows - o_tile) * KB));
+  const int perm_addr = 4 * (4 * li + kb);
+  // LDS-direct run j of chunk c fills slots 1024c + 64j + lane: row 4j +
+  // lane/16, piece (lane % 16) ^ (row % 16) of the chunk.
+  const int dma_r0 = lane >> 4;
+  auto dma_off = [&](int c, int j) -> uint32_t {
+    const int r = 4 * j + dma_r0;
+    const int p = 16 * c + ((lane & 15) ^ (r & 15));
+    return r < n_here && p < k_pieces ? static_cast<uint32_t>(r * K + 16 * p) : kOutOfRange;
+  };
+  // LDS byte of the B operand of column block n, chunk c, step d for this
+  // lane: row 16n + li, piece 4kb + d of the chunk.
+  uint32_t bbase[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) bbase[d] = static_cast<uint32_t>(256 * li + 16 * ((4 * kb + d) ^ li));
+
+  const uint32_t out_bytes = static_cast<uint32_t>((static_cast<int64_t>(n_here - 1) * ldy + rows) * 4);
+  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + n0 * ldy, out_bytes);
+  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + n0 * ldy : nullptr, DOT ? out_bytes : 0);
+  const bool has_bias = bias != nullptr;
+
+  auto run = [&](auto gsc) {
+    constexpr int GS = decltype(gsc)::value;
+    constexpr int STEPS = 4 * CH;
+    constexpr int kPerChunk = 2 + GS;  // loads per chunk: two tile runs, GS weight chunks
+    // Epilogue constants and the row sums the accumulators start from: small
+    // loads, issued before the big ones so that waiting for them never waits
+    // for the tile or the weights.
+    float tn[WN], ws = 0.0f;
+    int32_t rsn[WN];
+    v4i bv[GS > 0 ? GS : 1];
+    if constexpr (GS > 0) {
+      ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          buffer_of(packed + rows * static_cast<int64_t>(KB), 4), 0, 0, 0));
+      const __amdgpu_buffer_rsrc_t sbuf = buffer_of(act_scale + n0, static_cast<uint32_t>(4 * n_here));
+      const __amdgpu_buffer_rsrc_t rbuf = buffer_of(row_sum + n0, static_cast<uint32_t>(4 * n_here));
+#pragma unroll
+      for (int n = 0; n < WN; ++n) {
+        tn[n] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, 4 * (16 * n + li), 0, 0));
+        rsn[n] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, 4 * (16 * n + li), 0, 0);
+      }
+      const __amdgpu_buffer_rsrc_t bbuf =
+          buffer_of(has_bias ? bias + o_tile : nullptr, has_bias ? static_cast<uint32_t>(4 * (rows - o_tile)) : 0u);
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+        bv[g] = __builtin_amdgcn_raw_buffer_load_b128(bbuf, 4 * (16 * wk_subtile<G>(wave, g) + 4 * kb), 0, 0);
+    }
+    // Loads of chunk c: its two tile runs, then this wave's GS weight chunks.
+    // Chunks 0..PD-1 are issued at the start, chunk c+PD during the first
+    // step of chunk c: the memory path accepts one 1 KiB load about every 16
+    // cycles per compute unit, so issuing everything up front would hold
+    // every wave in its load instructions for microseconds before its first
+    // MFMA.
+    constexpr int PD = CH < 3 ? CH : 3;
+    v4i wr[CH][GS > 0 ? GS : 1];
+    uint32_t woff[GS > 0 ? GS : 1];
+#pragma unroll
+    for (int g = 0; g < GS; ++g)
+      woff[g] = static_cast<uint32_t>((16 * wk_subtile<G>(wave, g) + (lane >> 2)) * KB + 16 * (lane & 3));
+    auto issue_chunk = [&](int c) {
+#pragma unroll
+      for (int j = 2 * wave; j < 2 * wave + 2; ++j) lds_direct16(qbuf, lds_wk + c * kWkChunkBytes + 1024 * j, dma_off(c, j));
+      const bool piece_ok = 4 * c + (lane & 3) < K / 64;
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+        wr[c][g] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, piece_ok ? woff[g] + 64 * c : kOutOfRange, 0, 0);
+    };
+#pragma unroll
+    for (int c = 0; c < PD; ++c) issue_chunk(c);
+    // Chunk c of the tile is in LDS once this wave has at most the loads
+    // issued after its chunk-c runs outstanding (the chunk's GS weight loads
+    // and those of chunks c+1..last, the last chunk issued so far), and the
+    // barrier has seen every wave get there.
+    auto tile_wait = [&](int c, int last) {
+      const int after = GS + (last - c) * kPerChunk;
+      switch (after) {
+#define I2S_WK_WAIT(n) case n: __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+        I2S_WK_WAIT(0) I2S_WK_WAIT(1) I2S_WK_WAIT(2) I2S_WK_WAIT(3) I2S_WK_WAIT(4) I2S_WK_WAIT(5) I2S_WK_WAIT(6)
+        I2S_WK_WAIT(7) I2S_WK_WAIT(8) I2S_WK_WAIT(9) I2S_WK_WAIT(10) I2S_WK_WAIT(11) I2S_WK_WAIT(12) I2S_WK_WAIT(13)
+        I2S_WK_WAIT(14) I2S_WK_WAIT(15) I2S_WK_WAIT(16) I2S_WK_WAIT(17) I2S_WK_WAIT(18) I2S_WK_WAIT(19) I2S_WK_WAIT(20)
+        I2S_WK_WAIT(21) I2S_WK_WAIT(22) I2S_WK_WAIT(23) I2S_WK_WAIT(24) I2S_WK_WAIT(25) I2S_WK_WAIT(26) I2S_WK_WAIT(27)
+        I2S_WK_WAIT(28) I2S_WK_WAIT(29) I2S_WK_WAIT(30) I2S_WK_WAIT(31) I2S_WK_WAIT(32) I2S_WK_WAIT(33) I2S_WK_WAIT(34)
+        I2S_WK_WAIT(35) I2S_WK_WAIT(36) I2S_WK_WAIT(37) I2S_WK_WAIT(38) I2S_WK_WAIT(39) I2S_WK_WAIT(40) I2S_WK_WAIT(41)
+        I2S_WK_WAIT(42) I2S_WK_WAIT(43) I2S_WK_WAIT(44) I2S_WK_WAIT(45) I2S_WK_WAIT(46) I2S_WK_WAIT(47) I2S_WK_WAIT(48)
+        I2S_WK_WAIT(49) I2S_WK_WAIT(50) I2S_WK_WAIT(51) I2S_WK_WAIT(52) I2S_WK_WAIT(53) I2S_WK_WAIT(54) I2S_WK_WAIT(55)
+        I2S_WK_WAIT(56) I2S_WK_WAIT(57) I2S_WK_WAIT(58) I2S_WK_WAIT(59) I2S_WK_WAIT(60) I2S_WK_WAIT(61) I2S_WK_WAIT(62)
+#undef I2S_WK_WAIT
+        default: __builtin_amdgcn_s_waitcnt(0); break;
+      }
+      __builtin_amdgcn_s_barrier();
+    };
+
+    if constexpr (GS == 0) {
+      // No subtiles: this wave only loads its part of the tile and meets
+      // every barrier of the waves that compute.
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (c >= 1 && c - 1 + PD < CH) issue_chunk(c - 1 + PD);
+        tile_wait(c, c == 0 ? PD - 1 : (c - 1 + PD < CH ? c - 1 + PD : CH - 1));
+      }
+    } else {
+      v4i acc[GS][WN], a[2][GS], b[2][WN];
+      auto bread = [&](int n, int c, int d) -> v4i {
+        return *reinterpret_cast<const v4i *>(lds_wk + bbase[d] + c * kWkChunkBytes + n * 4096);
+      };
+      tile_wait(0, PD - 1);
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wr[0][g][e] = __builtin_amdgcn_ds_bpermute(perm_addr, wr[0][g][e]);
+#pragma unroll
+      for (int n = 0; n < WN; ++n) b[0][n] = bread(n, 0, 0);
+#pragma unroll
+      for (int g = 0; g < GS; ++g) a[0][g] = unpack_codes(static_cast<uint32_t>(wr[0][g][0]));
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+#pragma unroll
+        for (int n = 0; n < WN; ++n) acc[g][n] = v4i{-rsn[n], -rsn[n], -rsn[n], -rsn[n]};
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) {
+        const int cur = t & 1, nxt = cur ^ 1;
+        const int c = t >> 2, d = t & 3;
+        // The loads of chunk c+PD go out in the first step of chunk c.
+        if (d == 0 && c + PD < CH) issue_chunk(c + PD);
+        // Before the first B read of the next chunk, that chunk of the tile
+        // must be complete.
+        if (d == 3 && c + 1 < CH) {
+          tile_wait(c + 1, c + PD < CH ? c + PD : CH - 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // Next chunk's permutes, a quarter per step.
+        if (c + 1 < CH) {
+#pragma unroll
+          for (int g = 0; g < GS; ++g) wr[c + 1][g][d] = __builtin_amdgcn_ds_bpermute(perm_addr, wr[c + 1][g][d]);
+        }
+        if (t + 1 < STEPS) {
+          const int c1 = (t + 1) >> 2, d1 = (t + 1) & 3;
+#pragma unroll
+          for (int n = 0; n < WN; ++n) b[nxt][n] = bread(n, c1, d1);
+#pragma unroll
+          for (int g = 0; g < GS; ++g) a[nxt][g] = unpack_codes(static_cast<uint32_t>(wr[c1][g][d1]));
+        }
+#pragma unroll
+        for (int g = 0; g < GS; ++g)
+#pragma unroll
+          for (int n = 0; n < WN; ++n)
+            acc[g][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[cur][g], b[cur][n], acc[g][n], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < GS * WN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);  // one LDS operation (read or permute)
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Outputs: activation row n0 + 16n + li, output features
+      // o_tile + 16*subtile + 4kb .. +3.
+      float t_n[WN];
+#pragma unroll
+      for (int n = 0; n < WN; ++n) t_n[n] = ws * tn[n];
+      auto store = [&](auto biased) {
+        constexpr bool kBias = decltype(biased)::value;
+#pragma unroll
+        for (int g = 0; g < GS; ++g) {
+          const int64_t o = o_tile + 16 * static_cast<int64_t>(wk_subtile<G>(wave, g)) + 4 * kb;
+#pragma unroll
+          for (int n = 0; n < WN; ++n) {
+            const uint32_t base = static_cast<uint32_t>((16 * n + li) * ldy);
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              v[r] = static_cast<float>(acc[g][n][r]) * t_n[n];
+              if constexpr (kBias) v[r] = add_bias(v[r], __int_as_float(bv[g][r]));
+            }
+            if constexpr (VEC4) {
+              const uint32_t off = o < rows ? 4 * (base + static_cast<uint32_t>(o)) : kOutOfRange;
+              const v4i yv = {__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])};
+              __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, 0);
+              if constexpr (DOT)
+                __builtin_amdgcn_raw_buffer_store_b128(acc[g][n] + v4i{rsn[n], rsn[n], rsn[n], rsn[n]}, dbuf, off, 0, 0);
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const uint32_t off = o + r < rows ? 4 * (base + static_cast<uint32_t>(o + r)) : kOutOfRange;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[r]), ybuf, off, 0, 0);
+                if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(acc[g][n][r] + rsn[n], dbuf, off, 0, 0);
+              }
+            }
+          }
+        }
+      };
+      if (has_bias)
+        store(std::true_type{});
+      else
+        store(std::false_type{});
+    }
+  };
+  switch (mine) {
+    case 0: run(std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (G >= 2) run(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (G >= 3) run(std::integral_constant<int, 3>{}); break;
+    default: break;
   }
 }
 
@@ -1972,7 +2265,8 @@ template <int G, int WN, int S, int WAVES, bool PERM = false>
 int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
                    int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   constexpr int64_t BN = 16 * WN;
-  const int64_t lds = BN * res_pitch(K, S);
+  // Whole KiB: the tile is filled by 1 KiB LDS-direct load runs.
+  const int64_t lds = (BN * res_pitch(K, S) + 1023) / 1024 * 1024;
   if (lds > kResMaxLds) return I2S_EKERNEL;
   const int64_t lim = int64_t{1} << 31;
   // Largest weight offset: rows past the tile by up to 16*WAVES*G (re-reads of
@@ -2067,32 +2361,111 @@ int launch_pipe_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, c
 #undef I2S_SEQ
 }
 
+
+// Weight-resident launch (variant 15):
+// K up to 1536 (the decoder's q/k/v/o/gate/up input width, CH = 6 chunks;
+// shorter K runs its missing positions as zeros), 64-row activation tiles,
+// about one block per compute unit, at most 24 subtiles per block (G = 1, 2,
+// 3 for 8, 16, 24).
+template <int G, int CH, bool VEC4, bool DOT>
+int launch_wk_inst(int64_t blocks, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
+                   float *y, int32_t *dot_out, const float *bias, int64_t ldy, int64_t tiles_m, int64_t ms,
+                   hipStream_t stream) {
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return I2S_EHIP;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_wk_kernel<G, CH, VEC4, DOT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kResMaxLds) != hipSuccess)
+      return I2S_EHIP;
+    attr_done.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL((gemm_wk_kernel<G, CH, VEC4, DOT>), dim3(static_cast<unsigned>(blocks)), dim3(512),
+                     static_cast<size_t>(CH * kWkChunkBytes), stream, packed, rows, static_cast<int>(K), ws.q, N,
+                     ws.scale, ws.row_sum, y, dot_out, bias, ldy, static_cast<int>(tiles_m), static_cast<int>(ms));
+  return hip_status();
+}
+
+template <int G, int CH>
+int launch_wk_g(int64_t blocks, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
+                float *y, int32_t *dot_out, const float *bias, int64_t ldy, int64_t tiles_m, int64_t ms,
+                hipStream_t stream) {
+  const bool vec4 = (rows % 4) == 0 && (ldy % 4) == 0 && aligned16(y) && (!dot_out || aligned16(dot_out));
+  if (vec4) {
+    if (dot_out) return launch_wk_inst<G, CH, true, true>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+    return launch_wk_inst<G, CH, true, false>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+  }
+  if (dot_out) return launch_wk_inst<G, CH, false, true>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+  return launch_wk_inst<G, CH, false, false>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+}
+
+// The block grid of the weight-resident kernel: tiles of 64 activation rows,
+// weight tiles of ms subtiles, about one block per compute unit.
+inline void wk_grid(int64_t rows, int64_t N, int64_t *tiles_m, int64_t *ms, int64_t *blocks) {
+  const int64_t tiles_n = (N + 63) / 64;
+  const int64_t mt = (rows + 15) / 16;
+  int64_t tm = 256 / tiles_n;
+  if (tm < 1) tm = 1;
+  int64_t m = (mt + tm - 1) / tm;
+  if (m < 1) m = 1;
+  *ms = m;
+  *tiles_m = (mt + m - 1) / m;
+  *blocks = *tiles_m * tiles_n;
+}
+
+bool wk_fits(int64_t rows, int64_t K, int64_t N) {
+  if (K > 1536 || N < 1) return false;
+  int64_t tm, ms, blocks;
+  wk_grid(rows, N, &tm, &ms, &blocks);
+  return ms <= 24 && blocks <= kMaxDim && (rows + 16) * (K / 4) < (int64_t{1} << 31) && 64 * K < (int64_t{1} << 31);
+}
+
+int launch_wk(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
+              int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
+  if (!wk_fits(rows, K, N) || 64 * ldy * 4 >= (int64_t{1} << 31)) return I2S_EKERNEL;
+  int64_t tiles_m, ms, blocks;
+  wk_grid(rows, N, &tiles_m, &ms, &blocks);
+  if (ms <= 8) return launch_wk_g<1, 6>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+  if (ms <= 16) return launch_wk_g<2, 6>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+  return launch_wk_g<3, 6>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+}
+
+
 // GEMM variants (1-based): 1-4 streaming (GemmA..D), 5-9 activation-resident
 // (G, WN, S, waves) = (3,4,6,4), (2,4,6,8), (3,4,3,8), (3,2,6,8), (3,1,6,8), 10 pipelined
 // (G, WN, waves, steps) = (2,2,4,6), 11 = 7 with row-contiguous weight loads
-// permuted into MFMA lane order.
-constexpr int kGemmVariants = 14;
+// permuted into MFMA lane order, 12-14 the same in 2-step chunks with groups
+// of 2, 4 and 3, 15 weight-resident (K <= 1536).
+constexpr int kGemmVariants = 15;
 
 int gemm_auto_variant(int64_t rows, int64_t K, int64_t N) {
   int variant;
-  // Measured on MI355X (rows 256 .. 8960, K 1024 .. 8960, N 64 .. 2048):
-  // the 8-wave resident kernel with row-contiguous weight loads is fastest
-  // from 4 subtiles per block; with fewer (few rows or large N) the 4-wave
-  // pipelined kernel is, where K fits it.  Narrower resident tiles for longer
-  // K.
+  // Measured on MI355X (rows 256 .. 8960, K 1024 .. 8960, N 64 .. 2048; K =
+  // 1536 swept again for the weight-resident kernel): with at most 8
+  // subtiles per block the weight-resident kernel (one subtile per wave) is
+  // fastest where K fits it (1536 x 1536 at N = 512: 5.4 against 7.2 us for
+  // the pipelined kernel; 256 x 1536: 4.5 against 6.0; 8960 x 1536 at
+  // N = 128: 7.0 against 7.6); beyond, the 8-wave resident kernel with
+  // row-contiguous weight loads, its group size by the subtiles each wave
+  // holds.  Where K is too long for either, the 4-wave pipelined kernel from
+  // few subtiles, narrower resident tiles for longer K.
   const int64_t tiles_n = (N + 63) / 64;
   const int64_t tiles_m = tiles_n < 256 ? 256 / tiles_n : 1;
   const int64_t ms7 = ((rows + 15) / 16 + tiles_m - 1) / tiles_m;  // subtiles per block of variant 7
   const bool fits7 = 64 * res_pitch(K, 3) <= kResMaxLds && N > 16;
   const bool fits2 = 64 * res_pitch(K, 2) <= kResMaxLds && N > 16;
-  if ((K + 255) / 256 <= 6 && (!fits7 || ms7 < (fits2 ? 4 : 8))) {
+  if (wk_fits(rows, K, N) && ms7 <= 8) {
+    variant = 15;
+  } else if ((K + 255) / 256 <= 6 && (!fits7 || ms7 < (fits2 ? 4 : 8))) {
     variant = 10;
   } else if (fits2) {
     // Row-contiguous weight loads and 2-step chunks; the group size follows
-    // the subtiles each wave holds (spw): whole groups with few, one or two
-    // groups for 3-5, groups of 3 beyond.
+    // the subtiles each wave holds (spw): whole groups of 2 with up to 2,
+    // groups of 3 for 3 (8960 x 1536 at N = 512: 11.9 against 12.2 us with
+    // groups of 4), groups of 4 for 4-5, groups of 3 beyond.
     const int64_t spw = (ms7 + 7) / 8;
-    variant = spw <= 2 ? 12 : (spw <= 5 ? 13 : 14);
+    variant = spw <= 2 ? 12 : (spw == 3 ? 14 : (spw <= 5 ? 13 : 14));
   } else if (fits7) {
     variant = 11;  // variant 7's tiles with row-contiguous weight loads: 4-6% faster, measured
   } else if (16 * res_pitch(K, 6) <= kResMaxLds) {
@@ -2121,6 +2494,7 @@ int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int
     case 12: return launch_res_cfg<2, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     case 13: return launch_res_cfg<4, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     case 14: return launch_res_cfg<3, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 15: return launch_wk(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }
