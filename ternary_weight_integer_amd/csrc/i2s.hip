@@ -1321,14 +1321,19 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 // bank groups, and an LDS-direct run (64 consecutive slots: 4 rows x 16
 // pieces) fetches 64 contiguous bytes per 4 consecutive lanes.
 
-// The subtile (block-relative) that slot g of wave w holds.
-template <int G>
+// The subtile (block-relative) that slot g of wave w (of WAVES) holds: one
+// per wave with G = 1; otherwise adjacent pairs 2w, 2w+1 for the first
+// WAVES/2 waves (8 waves: all of them), then one more per wave.
+template <int G, int WAVES>
 __device__ __forceinline__ int wk_subtile(int w, int g) {
   if constexpr (G == 1) return w;
-  return g < 2 ? 2 * w + g : 16 + 8 * (g - 2) + w;
+  if constexpr (WAVES == 8) return g < 2 ? 2 * w + g : 16 + 8 * (g - 2) + w;
+  // 12 waves, G = 2: waves 0..5 hold 2w, 2w+1; waves 6..11 hold w+6, w+12.
+  return g == 0 ? (w < 6 ? 2 * w : w + 6) : (w < 6 ? 2 * w + 1 : w + 12);
 }
 
 constexpr int kWkChunkBytes = 64 * 256;  // one chunk of the 64-row activation tile
+constexpr int kWkStore = 2;              // output stores non-temporal (not read again by this kernel)
 
 // One LDS-direct buffer load: lane l's 16 bytes at buffer offset `off` go to
 // LDS byte lds + 16*l (out-of-range offsets write zeros).
@@ -1336,8 +1341,8 @@ __device__ __forceinline__ void lds_direct16(__amdgpu_buffer_rsrc_t rsrc, int8_t
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
 }
 
-template <int G, int CH, bool VEC4, bool DOT>
-__global__ void __launch_bounds__(512)
+template <int G, int CH, int WAVES, bool VEC4, bool DOT>
+__global__ void __launch_bounds__(64 * WAVES)
 gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const int8_t *__restrict__ qp, int64_t N,
                const float *__restrict__ act_scale, const int32_t *__restrict__ row_sum, float *__restrict__ y,
                int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t ldy, int tiles_m, int ms) {
@@ -1356,7 +1361,7 @@ gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const in
   const int msub = static_cast<int>(present < ms ? present : ms);
   int mine = 0;
 #pragma unroll
-  for (int g = 0; g < G; ++g) mine += wk_subtile<G>(wave, g) < msub ? 1 : 0;
+  for (int g = 0; g < G; ++g) mine += wk_subtile<G, WAVES>(wave, g) < msub ? 1 : 0;
 
   const __amdgpu_buffer_rsrc_t qbuf = buffer_of(qp + n0 * K, static_cast<uint32_t>(n_here * K));
   const __amdgpu_buffer_rsrc_t wbuf =
@@ -1384,7 +1389,10 @@ gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const in
   auto run = [&](auto gsc) {
     constexpr int GS = decltype(gsc)::value;
     constexpr int STEPS = 4 * CH;
-    constexpr int kPerChunk = 2 + GS;  // loads per chunk: two tile runs, GS weight chunks
+    // Loads per chunk: this wave's tile runs (runs wave, wave + WAVES, ... of
+    // the chunk's 16), then its GS weight chunks.
+    const int nruns = (16 - wave + WAVES - 1) / WAVES;
+    const int kPerChunk = nruns + GS;
     // Epilogue constants and the row sums the accumulators start from: small
     // loads, issued before the big ones so that waiting for them never waits
     // for the tile or the weights.
@@ -1405,7 +1413,7 @@ gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const in
           buffer_of(has_bias ? bias + o_tile : nullptr, has_bias ? static_cast<uint32_t>(4 * (rows - o_tile)) : 0u);
 #pragma unroll
       for (int g = 0; g < GS; ++g)
-        bv[g] = __builtin_amdgcn_raw_buffer_load_b128(bbuf, 4 * (16 * wk_subtile<G>(wave, g) + 4 * kb), 0, 0);
+        bv[g] = __builtin_amdgcn_raw_buffer_load_b128(bbuf, 4 * (16 * wk_subtile<G, WAVES>(wave, g) + 4 * kb), 0, 0);
     }
     // Loads of chunk c: its two tile runs, then this wave's GS weight chunks.
     // Chunks 0..PD-1 are issued at the start, chunk c+PD during the first
@@ -1418,10 +1426,10 @@ gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const in
     uint32_t woff[GS > 0 ? GS : 1];
 #pragma unroll
     for (int g = 0; g < GS; ++g)
-      woff[g] = static_cast<uint32_t>((16 * wk_subtile<G>(wave, g) + (lane >> 2)) * KB + 16 * (lane & 3));
+      woff[g] = static_cast<uint32_t>((16 * wk_subtile<G, WAVES>(wave, g) + (lane >> 2)) * KB + 16 * (lane & 3));
     auto issue_chunk = [&](int c) {
 #pragma unroll
-      for (int j = 2 * wave; j < 2 * wave + 2; ++j) lds_direct16(qbuf, lds_wk + c * kWkChunkBytes + 1024 * j, dma_off(c, j));
+      for (int j = wave; j < 16; j += WAVES) lds_direct16(qbuf, lds_wk + c * kWkChunkBytes + 1024 * j, dma_off(c, j));
       const bool piece_ok = 4 * c + (lane & 3) < K / 64;
 #pragma unroll
       for (int g = 0; g < GS; ++g)
@@ -1525,7 +1533,7 @@ gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const in
         constexpr bool kBias = decltype(biased)::value;
 #pragma unroll
         for (int g = 0; g < GS; ++g) {
-          const int64_t o = o_tile + 16 * static_cast<int64_t>(wk_subtile<G>(wave, g)) + 4 * kb;
+          const int64_t o = o_tile + 16 * static_cast<int64_t>(wk_subtile<G, WAVES>(wave, g)) + 4 * kb;
 #pragma unroll
           for (int n = 0; n < WN; ++n) {
             const uint32_t base = static_cast<uint32_t>((16 * n + li) * ldy);
@@ -1538,15 +1546,15 @@ gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const in
             if constexpr (VEC4) {
               const uint32_t off = o < rows ? 4 * (base + static_cast<uint32_t>(o)) : kOutOfRange;
               const v4i yv = {__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])};
-              __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, kWkStore);
               if constexpr (DOT)
-                __builtin_amdgcn_raw_buffer_store_b128(acc[g][n] + v4i{rsn[n], rsn[n], rsn[n], rsn[n]}, dbuf, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(acc[g][n] + v4i{rsn[n], rsn[n], rsn[n], rsn[n]}, dbuf, off, 0, kWkStore);
             } else {
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const uint32_t off = o + r < rows ? 4 * (base + static_cast<uint32_t>(o + r)) : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[r]), ybuf, off, 0, 0);
-                if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(acc[g][n][r] + rsn[n], dbuf, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[r]), ybuf, off, 0, kWkStore);
+                if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(acc[g][n][r] + rsn[n], dbuf, off, 0, kWkStore);
               }
             }
           }
@@ -2025,13 +2033,13 @@ gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   if constexpr (VEC4) {
     const uint32_t off = n_ok && o < rows ? 4 * base : kOutOfRange;
     const v4i yv = {__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])};
-    __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, kWkStore);
     if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b128(tot, dbuf, off, 0, 0);
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t off = n_ok && o + r < rows ? 4 * (base + r) : kOutOfRange;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[r]), ybuf, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[r]), ybuf, off, 0, kWkStore);
       if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(tot[r], dbuf, off, 0, 0);
     }
   }
@@ -2362,12 +2370,13 @@ int launch_pipe_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, c
 }
 
 
-// Weight-resident launch (variant 15):
+// Weight-resident launch (variant 15; the kernel also builds with 12 waves per
+// block, which measured no faster on the prefill shapes):
 // K up to 1536 (the decoder's q/k/v/o/gate/up input width, CH = 6 chunks;
 // shorter K runs its missing positions as zeros), 64-row activation tiles,
 // about one block per compute unit, at most 24 subtiles per block (G = 1, 2,
 // 3 for 8, 16, 24).
-template <int G, int CH, bool VEC4, bool DOT>
+template <int G, int CH, int WAVES, bool VEC4, bool DOT>
 int launch_wk_inst(int64_t blocks, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
                    float *y, int32_t *dot_out, const float *bias, int64_t ldy, int64_t tiles_m, int64_t ms,
                    hipStream_t stream) {
@@ -2376,28 +2385,28 @@ int launch_wk_inst(int64_t blocks, const uint8_t *packed, int64_t rows, int64_t 
   if (hipGetDevice(&dev) != hipSuccess) return I2S_EHIP;
   const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
   if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_wk_kernel<G, CH, VEC4, DOT>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_wk_kernel<G, CH, WAVES, VEC4, DOT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kResMaxLds) != hipSuccess)
       return I2S_EHIP;
     attr_done.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemm_wk_kernel<G, CH, VEC4, DOT>), dim3(static_cast<unsigned>(blocks)), dim3(512),
+  hipLaunchKernelGGL((gemm_wk_kernel<G, CH, WAVES, VEC4, DOT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * WAVES),
                      static_cast<size_t>(CH * kWkChunkBytes), stream, packed, rows, static_cast<int>(K), ws.q, N,
                      ws.scale, ws.row_sum, y, dot_out, bias, ldy, static_cast<int>(tiles_m), static_cast<int>(ms));
   return hip_status();
 }
 
-template <int G, int CH>
+template <int G, int CH, int WAVES>
 int launch_wk_g(int64_t blocks, const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws,
                 float *y, int32_t *dot_out, const float *bias, int64_t ldy, int64_t tiles_m, int64_t ms,
                 hipStream_t stream) {
   const bool vec4 = (rows % 4) == 0 && (ldy % 4) == 0 && aligned16(y) && (!dot_out || aligned16(dot_out));
   if (vec4) {
-    if (dot_out) return launch_wk_inst<G, CH, true, true>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
-    return launch_wk_inst<G, CH, true, false>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+    if (dot_out) return launch_wk_inst<G, CH, WAVES, true, true>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+    return launch_wk_inst<G, CH, WAVES, true, false>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
   }
-  if (dot_out) return launch_wk_inst<G, CH, false, true>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
-  return launch_wk_inst<G, CH, false, false>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+  if (dot_out) return launch_wk_inst<G, CH, WAVES, false, true>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+  return launch_wk_inst<G, CH, WAVES, false, false>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
 }
 
 // The block grid of the weight-resident kernel: tiles of 64 activation rows,
@@ -2421,16 +2430,20 @@ bool wk_fits(int64_t rows, int64_t K, int64_t N) {
   return ms <= 24 && blocks <= kMaxDim && (rows + 16) * (K / 4) < (int64_t{1} << 31) && 64 * K < (int64_t{1} << 31);
 }
 
+template <int WAVES>
 int launch_wk(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
               int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   if (!wk_fits(rows, K, N) || 64 * ldy * 4 >= (int64_t{1} << 31)) return I2S_EKERNEL;
   int64_t tiles_m, ms, blocks;
   wk_grid(rows, N, &tiles_m, &ms, &blocks);
-  if (ms <= 8) return launch_wk_g<1, 6>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
-  if (ms <= 16) return launch_wk_g<2, 6>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
-  return launch_wk_g<3, 6>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+  if (ms <= WAVES) return launch_wk_g<1, 6, WAVES>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+  if constexpr (WAVES == 8) {
+    if (ms <= 16) return launch_wk_g<2, 6, 8>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+    return launch_wk_g<3, 6, 8>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+  } else {
+    return launch_wk_g<2, 6, WAVES>(blocks, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, stream);
+  }
 }
-
 
 // GEMM variants (1-based): 1-4 streaming (GemmA..D), 5-9 activation-resident
 // (G, WN, S, waves) = (3,4,6,4), (2,4,6,8), (3,4,3,8), (3,2,6,8), (3,1,6,8), 10 pipelined
@@ -2442,20 +2455,21 @@ constexpr int kGemmVariants = 15;
 int gemm_auto_variant(int64_t rows, int64_t K, int64_t N) {
   int variant;
   // Measured on MI355X (rows 256 .. 8960, K 1024 .. 8960, N 64 .. 2048; K =
-  // 1536 swept again for the weight-resident kernel): with at most 8
-  // subtiles per block the weight-resident kernel (one subtile per wave) is
-  // fastest where K fits it (1536 x 1536 at N = 512: 5.4 against 7.2 us for
-  // the pipelined kernel; 256 x 1536: 4.5 against 6.0; 8960 x 1536 at
-  // N = 128: 7.0 against 7.6); beyond, the 8-wave resident kernel with
-  // row-contiguous weight loads, its group size by the subtiles each wave
-  // holds.  Where K is too long for either, the 4-wave pipelined kernel from
+  // 1536 swept again for the weight-resident kernel): with at most 16
+  // subtiles per block (two per wave) the weight-resident kernel is fastest
+  // where K fits it (1536 x 1536 at N = 512: 5.7 against 7.2 us for the
+  // pipelined kernel; 256 x 1536: 4.5 against 6.0; 8960 x 1536 at N = 128:
+  // 7.0 against 7.7, at N = 256: 9.0 against 9.2; 4096 x 1536 at N = 512:
+  // 8.2 against 8.8); beyond, the 8-wave resident kernel with row-contiguous
+  // weight loads, its group size by the subtiles each wave holds (at 18
+  // subtiles per block the two kernels are within run-to-run spread).  Where K is too long for either, the 4-wave pipelined kernel from
   // few subtiles, narrower resident tiles for longer K.
   const int64_t tiles_n = (N + 63) / 64;
   const int64_t tiles_m = tiles_n < 256 ? 256 / tiles_n : 1;
   const int64_t ms7 = ((rows + 15) / 16 + tiles_m - 1) / tiles_m;  // subtiles per block of variant 7
   const bool fits7 = 64 * res_pitch(K, 3) <= kResMaxLds && N > 16;
   const bool fits2 = 64 * res_pitch(K, 2) <= kResMaxLds && N > 16;
-  if (wk_fits(rows, K, N) && ms7 <= 8) {
+  if (wk_fits(rows, K, N) && ms7 <= 16) {
     variant = 15;
   } else if ((K + 255) / 256 <= 6 && (!fits7 || ms7 < (fits2 ? 4 : 8))) {
     variant = 10;
@@ -2494,7 +2508,7 @@ int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int
     case 12: return launch_res_cfg<2, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     case 13: return launch_res_cfg<4, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     case 14: return launch_res_cfg<3, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
-    case 15: return launch_wk(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 15: return launch_wk<8>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }

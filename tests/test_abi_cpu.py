@@ -133,20 +133,21 @@ def test_mul_mat_variant_choice():
         k = i2s.i2s_mul_mat_kernel(rows, K, N)
         v = i2s.i2s_mul_mat_variant(rows, K, N)
         assert 1 <= v <= i2s.i2s_kernel_variants(k), (rows, K, N, k, v)
-    # the weight-resident GEMM up to 8 subtiles per block where K <= 1536;
+    # the weight-resident GEMM up to 16 subtiles per block where K <= 1536;
     # beyond, the resident GEMM with row-contiguous weight loads, its group
     # size by the 16-row subtiles each wave holds
     assert i2s.i2s_mul_mat_variant(8960, 1536, 128) == 15   # 5 subtiles per block
     assert i2s.i2s_mul_mat_variant(1536, 1536, 128) == 15   # 1
     assert i2s.i2s_mul_mat_variant(1536, 1536, 512) == 15   # 3
     assert i2s.i2s_mul_mat_variant(256, 1536, 1024) == 15
-    assert i2s.i2s_mul_mat_variant(8960, 1536, 256) == 12   # 9: 2 per wave, groups of 2
+    assert i2s.i2s_mul_mat_variant(8960, 1536, 256) == 15   # 9
+    assert i2s.i2s_mul_mat_variant(4096, 1536, 512) == 15   # 16
     assert i2s.i2s_mul_mat_variant(8960, 1536, 512) == 14   # 18: 3 per wave, groups of 3
     assert i2s.i2s_mul_mat_variant(8960, 1536, 1024) == 13  # 35: 5 per wave, groups of 4
     assert i2s.i2s_mul_mat_variant(8960, 1536, 2048) == 14  # 70: 9 per wave, groups of 3
     assert i2s.i2s_mul_mat_variant(8960, 2304, 512) == 11   # past the 2-step chunks' LDS limit: 3-step chunks
     assert i2s.i2s_mul_mat_variant(1536, 2048, 512) == 12   # K past the weight-resident kernel
-    assert i2s.i2s_mul_mat_variant(2048, 1792, 512) == 12   # 4 subtiles, K = 1792
+    assert i2s.i2s_mul_mat_variant(2048, 1792, 512) == 12   # 4 subtiles, K = 1792: 1 per wave, groups of 2
     with pytest.raises(i2s.I2SError):
         i2s.i2s_mul_mat_variant(4, 100, 1)
 
