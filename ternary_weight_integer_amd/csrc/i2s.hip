@@ -140,6 +140,70 @@ __device__ inline int lanes_sum(int v) {
 
 __device__ inline int wave_sum(int v) { return lanes_sum<64>(v); }
 
+// Quantizes the 4*XPT activation values a thread holds with the row's scale
+// s (an IEEE quotient amax/127): code = clamp(roundf(x / s), -127, 127) with
+// x / s the IEEE quotient, four codes per dword (value t of float4 i in byte
+// t of packed[i]).  Values past the row are 0 and give code 0.
+//
+// x / s is formed as x * rcp(s) with v_rcp_f32 (1 ulp): |x / s| <= 127.5,
+// so the product is within 127.5 * 1.5 * 2^-23 < 2^-15 of the real quotient
+// and within 2^-15 + 2^-18 < 2^-14 of the IEEE one.  A product farther than
+// 2^-14 from every half-integer therefore lies strictly between the same two
+// half-integers as the IEEE quotient, and round-to-nearest-even of the
+// product (one v_rndne) equals roundf of that quotient.  If any value of the
+// wave comes within 2^-14 of a half-integer (fract(|p|) within 2^-14 of
+// 0.5), the whole wave divides and applies roundf instead: a wave-uniform
+// branch, since per-value branches would serialize the values.  NaN and
+// infinite inputs take the same values on both paths (rcp(inf) = 0).
+template <int XPT>
+__device__ inline void quantize_codes(const float4 (&v)[XPT], float s, uint32_t (&packed)[XPT]) {
+  const float inv = __builtin_amdgcn_rcpf(s);
+  float rq[XPT][4];
+  float dmin = 1.0f;  // nearest distance of a product to a half-integer
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      rq[i][t] = e[t] * inv;
+      dmin = fminf(dmin, fabsf(__builtin_amdgcn_fractf(fabsf(rq[i][t])) - 0.5f));
+    }
+  }
+  if (__any(dmin <= 0x1p-14f)) {
+    // The divisor passes through an empty asm statement, so that the
+    // divisions cannot be hoisted out of this branch (speculated, they would
+    // run in every wave).
+    float sd = s;
+    __asm__ volatile("" : "+v"(sd));
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) rq[i][t] = roundf(e[t] / sd);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) rq[i][t] = __builtin_rintf(rq[i][t]);
+  }
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    uint32_t p4 = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float r = fminf(fmaxf(rq[i][t], -127.0f), 127.0f);
+      p4 |= (static_cast<uint32_t>(static_cast<int>(r)) & 0xffu) << (8 * t);
+    }
+    packed[i] = p4;
+  }
+}
+
+// Sum of the four signed bytes of a dword added to acc (one v_dot4).
+__device__ inline int add_bytes(uint32_t p4, int acc) {
+  return __builtin_amdgcn_sdot4(static_cast<int>(p4), 0x01010101, acc, false);
+}
+
 // ---------------------------------------------------------------------------
 // Activation quantization + row sum: one workgroup per activation row (the
 // row-wide absmax cannot be split).  Pass 1 reduces max|x| over the row;
@@ -215,8 +279,9 @@ quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int64_t n_inner, 
 // Block per row, single pass, for K <= 4*256*XPT: each of the 256 threads
 // loads up to XPT float4 of the row into registers, the row's absmax and int8
 // sum are block reductions, and each float4 becomes 4 bytes of q (4
-// consecutive positions stay consecutive in the interleaved order).  Same
-// arithmetic as quantize_rowsum_kernel, with a few divisions per thread.
+// consecutive positions stay consecutive in the interleaved order).  The
+// codes equal quantize_rowsum_kernel's bit for bit (quantize_codes: one
+// reciprocal per thread, divisions only in a wave near a rounding tie).
 template <bool kInterleaved, int XPT, int THREADS>
 __global__ void __launch_bounds__(THREADS)
 quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int64_t n_inner, int64_t ldx, int64_t bsx,
@@ -246,50 +311,20 @@ quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int64_t n_inn
   for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, red_f[w]);
   amax = fmaxf(amax, 1e-5f);
   const float s = amax / 127.0f;
-  // x / s as x * (1/s), with the whole wave dividing when any of its
-  // values comes within 2^-14 of a half-integer (the argument of the fused
-  // GEMV's quantizer: the result is roundf(x / s) bit for bit).
-  const float inv = 1.0f / s;
-  float rq[XPT][4];
-  float dmin = 1.0f;  // nearest distance of a product to a half-integer
-#pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      rq[i][t] = e[t] * inv;
-      const float m = fabsf(rq[i][t]);
-      dmin = fminf(dmin, fabsf(m - truncf(m) - 0.5f));
-    }
-  }
-  if (__any(dmin <= 0x1p-14f)) {
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) rq[i][t] = e[t] / s;
-    }
-  }
+  uint32_t codes[XPT];
+  quantize_codes<XPT>(v, s, codes);
   int sum = 0;
   int8_t *qr = q + n * K;
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const int idx = tid + THREADS * i;
     if (idx < k4) {
-      uint32_t packed = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float r = roundf(rq[i][t]);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        const int qi = static_cast<int>(r);
-        sum += qi;
-        packed |= (static_cast<uint32_t>(qi) & 0xffu) << (8 * t);
-      }
+      sum = add_bytes(codes[i], sum);
       const int p = 4 * idx;
       const int jj = p & 127;
       const int off = kInterleaved ? (p & ~127) + 16 * ((jj & 31) >> 2) + 4 * (jj >> 5) : p;
-      *reinterpret_cast<uint32_t *>(qr + off) = packed;
-      if (kInterleaved && qt) *reinterpret_cast<uint32_t *>(qt + tiled_offset(n, off, (K + 255) / 256)) = packed;
+      *reinterpret_cast<uint32_t *>(qr + off) = codes[i];
+      if (kInterleaved && qt) *reinterpret_cast<uint32_t *>(qt + tiled_offset(n, off, (K + 255) / 256)) = codes[i];
     }
   }
   sum = wave_sum(sum);
@@ -544,7 +579,9 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
 
   // 2. Weight loads for every row and chunk of this lane, unconditional:
   // rows past the end read as 0x00 bytes (all codes 0, which add nothing to
-  // sum(code*q)) and are never stored.
+  // sum(code*q)) and are never stored.  (A load past the row still takes an
+  // issue slot, and a branch around it costs more: the configurations size
+  // CPL to the row.)
   const __amdgpu_buffer_rsrc_t wbuf = buffer_of(packed, static_cast<uint32_t>(rows * row_bytes));
   v4i wv[RPL][CPL];
 #pragma unroll
@@ -580,50 +617,18 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
     float a = fmaxf(fmaxf(red_f[n][0], red_f[n][1]), fmaxf(red_f[n][2], red_f[n][3]));
     a = fmaxf(a, 1e-5f);
     sc[n] = a / 127.0f;
-    // x / s as x * (1/s): |x / s| < 128, so the product is within 2^-15 of
-    // the correctly rounded quotient and rounds the same way unless that
-    // quotient lies within 2^-15 of a half-integer.  If any value of the wave
-    // comes within 2^-14 of one, the whole wave divides (a wave-uniform
-    // branch; per-value branches would serialize the values).
-    const float inv = 1.0f / sc[n];
-    float rq[XPT][4];
-    float dmin = 1.0f;  // nearest distance of a product to a half-integer
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const float e[4] = {xv[n][i].x, xv[n][i].y, xv[n][i].z, xv[n][i].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        rq[i][t] = e[t] * inv;
-        const float m = fabsf(rq[i][t]);
-        dmin = fminf(dmin, fabsf(m - truncf(m) - 0.5f));
-      }
-    }
-    if (__any(dmin <= 0x1p-14f)) {
-#pragma unroll
-      for (int i = 0; i < XPT; ++i) {
-        const float e[4] = {xv[n][i].x, xv[n][i].y, xv[n][i].z, xv[n][i].w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) rq[i][t] = e[t] / sc[n];
-      }
-    }
+    uint32_t codes[XPT];
+    quantize_codes<XPT>(xv[n], sc[n], codes);
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int idx = tid + kGemvThreads * i;
       if (idx < k4) {
-        uint32_t packed4 = 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float r = roundf(rq[i][t]);
-          r = fminf(fmaxf(r, -127.0f), 127.0f);
-          const int qi = static_cast<int>(r);
-          sum += qi;
-          packed4 |= (static_cast<uint32_t>(qi) & 0xffu) << (8 * t);
-        }
+        sum = add_bytes(codes[i], sum);
         const int p = 4 * idx;
         const int jj = p & 127;
         const int off = (p & ~127) + 16 * ((jj & 31) >> 2) + 4 * (jj >> 5);
-        *reinterpret_cast<uint32_t *>(qs + n * K + off) = packed4;
+        *reinterpret_cast<uint32_t *>(qs + n * K + off) = codes[i];
       }
     }
     sum = wave_sum(sum);
@@ -2113,13 +2118,19 @@ int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float
 }
 
 // Fused quantize + GEMV configurations (1-based): (L, RPL, CPL, XPT) =
-// (8, 2, 3, 2), (8, 1, 4, 2), (16, 1, 2, 2) for K <= 1536/2048/2048, and
-// (64, 1, 3, 9), (32, 1, 5, 9) for K <= 9216 (the down projection).
+// (8, 2, 3, 2), (8, 1, 4, 2), (16, 1, 2, 2) for K <= 1536/2048/2048,
+// (64, 1, 3, 9), (32, 1, 5, 9) for K <= 9216 (the down projection), and
+// (8, 1, 3, 2) for K <= 1536 (variant 2 without its fourth chunk batch,
+// which at K = 1536 would be a load past every row).
 // Automatic: measured fastest on MI355X for the decoder shapes.
-constexpr int kFusedVariants = 5;
+constexpr int kFusedVariants = 6;
 constexpr int64_t kFusedMaxK = 9216;
 
-int fused_auto_variant(int64_t rows, int64_t K) { return K <= 2048 ? (rows <= 2048 ? 3 : 2) : 5; }
+int fused_auto_variant(int64_t rows, int64_t K) {
+  if (K > 2048) return 5;
+  if (rows <= 2048) return 3;
+  return K <= 1536 ? 6 : 2;
+}
 
 template <int NC>
 int launch_fused_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t ldx, float *y,
@@ -2131,6 +2142,7 @@ int launch_fused_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K,
     case 3: return launch_fused_cfg<NC, 16, 1, 2, 2>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     case 4: return launch_fused_cfg<NC, 64, 1, 3, 9>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     case 5: return launch_fused_cfg<NC, 32, 1, 5, 9>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
+    case 6: return launch_fused_cfg<NC, 8, 1, 3, 2>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }
@@ -2173,6 +2185,7 @@ int launch_fused_group_nc(int variant, const FusedGroup &g, int64_t total_rows, 
     case 3: return launch_fused_group_cfg<NC, 16, 1, 2, 2>(g, K, x, stream);
     case 4: return launch_fused_group_cfg<NC, 64, 1, 3, 9>(g, K, x, stream);
     case 5: return launch_fused_group_cfg<NC, 32, 1, 5, 9>(g, K, x, stream);
+    case 6: return launch_fused_group_cfg<NC, 8, 1, 3, 2>(g, K, x, stream);
     default: return I2S_EKERNEL;
   }
 }

@@ -112,3 +112,23 @@ def near_tie_rows(amaxes=(100.0, 3.3, 0.77, 12345.678)) -> list[np.ndarray]:
         pad = (-row.size) % 128
         rows.append(np.concatenate([row, np.zeros(pad, np.float32)]))
     return rows
+
+
+def tie_margin_rows(amaxes=(100.0, 3.3, 0.77, 12345.678)) -> list[np.ndarray]:
+    """F32 rows whose values put x/s at 1.25, 2 and 4 times 2^-14 either side
+    of each .5 boundary (and none nearer): a quantizer that rounds a product
+    x * (1/s) instead of the quotient, and switches to the quotient only for
+    values within 2^-14 of a boundary, takes its fast path on every value of
+    these rows, at the edge of its error margin."""
+    rows = []
+    for amax in (np.float32(a) for a in amaxes):
+        s = f32_round(frac(amax) / 127)
+        vals = [amax]
+        for m in range(-126, 127):
+            for k in (Fraction(5, 4), Fraction(2), Fraction(4)):
+                for sign in (-1, 1):
+                    vals.append(np.float32(float((frac(m) + Fraction(1, 2) + sign * k / 2**14) * frac(s))))
+        row = np.array([v for v in vals if abs(v) <= amax], dtype=np.float32)
+        pad = (-row.size) % 128
+        rows.append(np.concatenate([row, np.zeros(pad, np.float32)]))
+    return rows

@@ -21,7 +21,7 @@ import pytest
 import torch
 
 import oracle
-from exact import near_tie_rows
+from exact import near_tie_rows, tie_margin_rows
 from ternary_weight_integer_amd import i2s, workloads
 
 pytestmark = pytest.mark.gpu
@@ -106,6 +106,9 @@ def _quant_inputs():
     ties = near_tie_rows()
     L = max(r.size for r in ties)
     out.append(("near_ties", np.stack([np.pad(r, (0, L - r.size)) for r in ties])))
+    margins = tie_margin_rows()
+    L = max(r.size for r in margins)
+    out.append(("tie_margins", np.stack([np.pad(r, (0, L - r.size)) for r in margins])))
     z = np.zeros((3, 256), np.float32)
     z[1] = np.float32(1e-7)
     z[2, 5] = np.float32(-3e-6)
@@ -126,11 +129,14 @@ def test_quantize_matches_oracle(name, x):
     assert np.array_equal(host(rs), rse)
 
 
-def test_near_ties_through_every_kernel():
-    """Activation rows on and around the .5 boundaries of x/s, quantized
-    inside each contraction path (the fused kernels quantize for themselves):
-    any q off by one shows in dot (random codes over 96 weight rows) and y."""
-    ties = near_tie_rows()
+@pytest.mark.parametrize("rows_of", [near_tie_rows, tie_margin_rows], ids=["on_ties", "at_margin"])
+def test_near_ties_through_every_kernel(rows_of):
+    """Activation rows on and around the .5 boundaries of x/s (on_ties), and
+    just outside the 2^-14 band in which the kernels' quantizer switches from
+    a reciprocal product to the quotient (at_margin), quantized inside each
+    contraction path (the fused kernels quantize for themselves): any q off
+    by one shows in dot (random codes over 96 weight rows) and y."""
+    ties = rows_of()
     K = max(r.size for r in ties)
     x = np.stack([np.pad(r, (0, K - r.size)) for r in ties])
     N = x.shape[0]
@@ -147,7 +153,7 @@ def test_near_ties_through_every_kernel():
             except i2s.I2SError as e:
                 assert e.status == i2s.I2S_EKERNEL
                 continue
-            say(f"[near ties] K={K} N={N} kernel={kern} variant={var}")
+            say(f"[{rows_of.__name__}] K={K} N={N} kernel={kern} variant={var}")
             assert np.array_equal(host(d), de), (kern, var)
             assert np.array_equal(bits(host(y)), bits(ye)), (kern, var)
 
@@ -222,6 +228,10 @@ def test_grid_all_kernels_and_variants(K):
                 assert np.array_equal(bits(y2), bits(ye)), (K, rows, N, kern, var, "no dot_out")
 
 
+# Longest K of each fused configuration (64 * lanes per row * chunk batches).
+FUSED_MAX_K = {1: 1536, 2: 2048, 3: 2048, 4: 12288, 5: 10240, 6: 1536}
+
+
 @pytest.mark.parametrize("N", [1, 2, 4])
 def test_all_fused_variants_decode_shapes(N):
     """Fused quantize + GEMV variants on the decoder shapes (K = 1536 and the
@@ -232,7 +242,7 @@ def test_all_fused_variants_decode_shapes(N):
         pg = gpu_pack(case.w, case.ws)
         exp = oracle.mul_mat_sliced(pnp, rows, K, case.x, with_dot=True)
         for v in range(1, i2s.i2s_kernel_variants(3) + 1):
-            if K > 2048 and v <= 3:
+            if K > FUSED_MAX_K[v]:
                 with pytest.raises(i2s.I2SError):
                     i2s.i2s_mul_mat_ex(pg, rows, K, dev(case.x), kernel=3, variant=v)
                 continue
