@@ -813,10 +813,35 @@ def main(argv=None):
         # half, reported under its own key (the line's value stays the decode).
         pre = bench_case(args, torch, i2s, make_case("prefill_gate"))
         out["prefill_gemm"] = {k: pre[k] for k in ("value", "unit", "ms_per_step", "int8_tops", "config",
-                                                   "roofline", "cpu_baseline") if k in pre}
+                                                   "roofline", "quantize", "cpu_baseline") if k in pre}
         out["prefill_gemm"]["value_is"] = "packed weight bytes per second of the whole step (quantize + GEMM)"
     print(json.dumps(out), flush=True)
     return 0
+
+
+def quantize_line(torch, i2s, x, ws, N: int, K: int, in_step_us: float):
+    """The activation quantize launch of a GEMM step on its own: a graph of
+    back-to-back i2s_quantize_act_ws calls on the step's rows (which then
+    stay cache-resident), against the HBM roofline of its algorithmic bytes
+    (F32 rows read, int8 rows, scales and row sums written); in_step_us is
+    the step time less the contraction's, i.e. what the launch costs after
+    a contraction."""
+    n = 256
+    g = graph_of(lambda: [i2s.i2s_quantize_act_ws(x, ws) for _ in range(n)], torch)
+    g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    del g
+    qbytes = N * K * 4 + N * K + 8 * N
+    achieved = qbytes / (us * 1e-6) / 1e9
+    return {"kernel": "quantize_rowsum_reg_kernel", "kernel_us": round(us, 4), "in_step_us": round(in_step_us, 4),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "alg_bytes_per_launch": qbytes}}
 
 
 def graph_repeats(torch, step, steps: int, target_ms: float) -> int:
@@ -952,6 +977,8 @@ def bench_case(args, torch, i2s, case):
                                "alg_bytes_per_launch": alg_bytes}
     if kern_us is not None and kernel_kind != 2:
         out["roofline"]["copy_ceiling"] = copy_ceiling(torch, alg_bytes)
+    if kern_us is not None and kernel_kind == 2:
+        out["quantize"] = quantize_line(torch, i2s, x, ws, N, K, step_ms * 1e3 - kern_us)
     props = torch.cuda.get_device_properties(0)
     out["gpu"] = {"name": props.name, "cus": props.multi_processor_count,
                   "arch": getattr(props, "gcnArchName", "")}
