@@ -38,6 +38,11 @@ def flags() -> list[str]:
         "-Wall",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-ffp-contract=off",
+        # Kernel arguments preloaded into SGPRs at wave launch (where the
+        # firmware supports it; otherwise the compiler's compatibility
+        # prologue loads them), so that the first vector loads need not wait
+        # for a scalar load round trip.
+        "-mllvm", "-amdgpu-kernarg-preload-count=16",
         "-I", os.path.join(ROOT, "include"),
     ]
 

@@ -699,12 +699,16 @@ gemv_fused_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 }
 
 // Several projections of the same activation rows in one launch (the decoder
-// layer's q/k/v, or gate/up): workgroups are numbered through the
-// projections in order, and each one quantizes the shared rows itself, as
-// above, before its share of one projection.
+// layer's q/k/v, or gate/up): a two-dimensional grid, blockIdx.y the
+// projection and blockIdx.x the workgroup within it (workgroups past a
+// shorter projection's rows exit at once), and each workgroup quantizes the
+// shared rows itself, as above, before its share of one projection.  With
+// the projection in a register from the start, its pointers are one batch
+// of kernel-argument loads; numbering workgroups through the projections
+// instead needs a search over their boundaries first, a chain of dependent
+// scalar loads ahead of the weight loads.
 struct FusedGroup {
   int count = 0;
-  int64_t block_end[I2S_GROUP_MAX] = {};  // workgroups of projections 0..p
   const uint8_t *packed[I2S_GROUP_MAX] = {};
   int64_t rows[I2S_GROUP_MAX] = {};
   const float *bias[I2S_GROUP_MAX] = {};
@@ -716,11 +720,21 @@ template <int NC, int L, int RPL, int CPL, int XPT>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_fused_group_kernel(const FusedGroup g, int64_t K, const float *__restrict__ x) {
   extern __shared__ __attribute__((aligned(16))) int8_t qs[];
-  int p = 0;
-  while (p + 1 < g.count && static_cast<int64_t>(blockIdx.x) >= g.block_end[p]) ++p;
-  const int64_t block = static_cast<int64_t>(blockIdx.x) - (p > 0 ? g.block_end[p - 1] : 0);
-  fused_body<NC, L, RPL, CPL, XPT>(g.packed[p], g.rows[p], K, x, K, g.y[p], g.dot[p], g.bias[p], g.rows[p], block,
-                                   qs);
+  constexpr int64_t kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
+  const int p = static_cast<int>(blockIdx.y);
+  const int64_t block = blockIdx.x;
+  const uint8_t *packed = g.packed[p];
+  const int64_t rows = g.rows[p];
+  const float *bias = g.bias[p];
+  float *y = g.y[p];
+  int32_t *dot = g.dot[p];
+  // Every kernel argument the workgroup needs, in one batch of scalar loads
+  // ahead of the exit test (the empty asm takes them as operands; loaded
+  // after the test they would be one more round trip before the first
+  // vector load).
+  __asm__ volatile("" ::"s"(packed), "s"(rows), "s"(bias), "s"(y), "s"(dot), "s"(x), "s"(K));
+  if (block * kRowsPerBlock >= rows) return;  // the whole workgroup, before any barrier
+  fused_body<NC, L, RPL, CPL, XPT>(packed, rows, K, x, K, y, dot, bias, rows, block, qs);
 }
 
 // ---------------------------------------------------------------------------
@@ -2159,19 +2173,20 @@ int launch_fused(int variant, const uint8_t *packed, int64_t rows, int64_t K, in
 }
 
 template <int NC, int L, int RPL, int CPL, int XPT>
-int launch_fused_group_cfg(FusedGroup g, int64_t K, const float *x, hipStream_t stream) {
+int launch_fused_group_cfg(const FusedGroup &g, int64_t K, const float *x, hipStream_t stream) {
   if (K > 64 * L * CPL || K > 4 * kGemvThreads * XPT) return I2S_EKERNEL;
   constexpr int kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
-  int64_t total = 0;
+  int64_t widest = 0;  // workgroups of the projection with the most rows
   for (int p = 0; p < g.count; ++p) {
     if (g.rows[p] * (K / 4) >= (int64_t{1} << 31)) return I2S_EKERNEL;  // 32-bit buffer offsets
-    total += (g.rows[p] + kRowsPerBlock - 1) / kRowsPerBlock;
-    g.block_end[p] = total;
+    const int64_t b = (g.rows[p] + kRowsPerBlock - 1) / kRowsPerBlock;
+    widest = b > widest ? b : widest;
   }
-  if (total == 0) return I2S_OK;
-  if (total > kMaxDim) return I2S_ERANGE;
-  hipLaunchKernelGGL((gemv_fused_group_kernel<NC, L, RPL, CPL, XPT>), dim3(static_cast<unsigned>(total)),
-                     dim3(kGemvThreads), static_cast<size_t>(NC * K), stream, g, K, x);
+  if (widest == 0) return I2S_OK;
+  if (widest > kMaxDim) return I2S_ERANGE;
+  hipLaunchKernelGGL((gemv_fused_group_kernel<NC, L, RPL, CPL, XPT>),
+                     dim3(static_cast<unsigned>(widest), static_cast<unsigned>(g.count)), dim3(kGemvThreads),
+                     static_cast<size_t>(NC * K), stream, g, K, x);
   return hip_status();
 }
 
