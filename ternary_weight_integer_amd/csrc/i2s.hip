@@ -285,8 +285,11 @@ quantize_rowsum_kernel(const float *__restrict__ x, int64_t K, int64_t n_inner, 
 template <bool kInterleaved, int XPT, int THREADS>
 __global__ void __launch_bounds__(THREADS)
 quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int64_t n_inner, int64_t ldx, int64_t bsx,
-                           int8_t *__restrict__ q, float *__restrict__ act_scale, int32_t *__restrict__ row_sum,
-                           int8_t *__restrict__ qt) {
+                           int8_t *__restrict__ q, int8_t *__restrict__ qt, float *__restrict__ act_scale,
+                           int32_t *__restrict__ row_sum) {
+  // Argument order: everything up to qt is preloaded into scalar registers
+  // at launch; the scale and row-sum pointers (written at the very end) are
+  // fetched while the row loads are in flight (below).
   constexpr int kWaves = THREADS / 64;
   __shared__ float red_f[kWaves];
   __shared__ int red_i[kWaves];
@@ -301,8 +304,14 @@ quantize_rowsum_reg_kernel(const float *__restrict__ x, int64_t K, int64_t n_inn
   for (int i = 0; i < XPT; ++i) {
     const int idx = tid + THREADS * i;
     v[i] = idx < k4 ? xr[idx] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
   }
+  // The two pointers as operands of an empty asm: their scalar load (and its
+  // wait) happens here, in the shadow of the row loads, instead of being
+  // sunk to the final stores.
+  __asm__ volatile("" ::"s"(act_scale), "s"(row_sum));
+#pragma unroll
+  for (int i = 0; i < XPT; ++i)
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
   amax = wave_max(amax);
   if (lane == 0) red_f[wave] = amax;
   __syncthreads();
@@ -976,10 +985,15 @@ __device__ __forceinline__ void res_mfma_chunk(v4i (&acc)[G][WN], const v4i (&wv
 
 template <int G, int WN, int S, int WAVES, bool VEC4, bool DOT, bool SINGLE, bool PERM>
 __global__ void __launch_bounds__(64 * WAVES)
-gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
-                const int8_t *__restrict__ qp, int64_t N, const float *__restrict__ act_scale,
-                const int32_t *__restrict__ row_sum, float *__restrict__ y,
-                int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t ldy, int64_t tiles_m, int ms) {
+gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
+                const int8_t *__restrict__ qp, int64_t N, const int32_t *__restrict__ row_sum,
+                const float *__restrict__ act_scale, float *__restrict__ y,
+                int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t ldy) {
+  // Argument order: the arguments up to row_sum are preloaded into scalar
+  // registers at launch, and they are all that the loads issued before the
+  // first weights need (the tile, the weights, the row sums); the scales,
+  // the outputs and the bias come from a scalar load that completes while
+  // the tile streams in.
   extern __shared__ __attribute__((aligned(16))) int8_t lds_res[];
   constexpr int BN = 16 * WN;
   static_assert(BN % WAVES == 0, "whole activation rows per wave");
@@ -1031,24 +1045,30 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
     }
   };
 
-  // Epilogue constants of this lane's activation rows (clamped inside the
-  // tensor; lanes past N never store), loaded before any prefetch so that
-  // waiting for them never waits for the prefetches.
-  const float ws = *reinterpret_cast<const float *>(packed + rows * static_cast<int64_t>(row_bytes));
-  float sn[WN];
+  // Row sums of this lane's activation rows (clamped inside the tensor;
+  // lanes past N never store), loaded before any prefetch so that waiting
+  // for them (the accumulators start at -row_sum) never waits for the
+  // prefetches; buffer loads keep their place (a plain read-only load may be
+  // sunk to its first use, behind them).  The scales and the weight scale,
+  // needed only by the epilogue, go out after the first weights
+  // (load_scales).
   int32_t rsn[WN];
   {
-    // Buffer loads keep their place ahead of the prefetches (a plain
-    // read-only load may be sunk to its first use, behind them).
-    const __amdgpu_buffer_rsrc_t sbuf = buffer_of(act_scale + n0, static_cast<uint32_t>(4 * n_here));
     const __amdgpu_buffer_rsrc_t rbuf = buffer_of(row_sum + n0, static_cast<uint32_t>(4 * n_here));
 #pragma unroll
-    for (int n = 0; n < WN; ++n) {
-      const uint32_t off = static_cast<uint32_t>(4 * (16 * n + li));  // past N: reads 0, never stored
-      sn[n] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, off, 0, 0));
-      rsn[n] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, off, 0, 0);
-    }
+    for (int n = 0; n < WN; ++n)
+      rsn[n] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, static_cast<uint32_t>(4 * (16 * n + li)), 0, 0);
   }
+  float sn[WN], ws;
+  constexpr int kScaleLoads = WN + 1;
+  auto load_scales = [&]() {
+    const __amdgpu_buffer_rsrc_t sbuf = buffer_of(act_scale + n0, static_cast<uint32_t>(4 * n_here));
+#pragma unroll
+    for (int n = 0; n < WN; ++n)
+      sn[n] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, static_cast<uint32_t>(4 * (16 * n + li)), 0, 0));
+    ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_of(packed + rows * static_cast<int64_t>(row_bytes), 4),
+                                                             0, 0, 0));
+  };
 
   v4i wa[G][S], wb[G][S];
   const int k_pieces = static_cast<int>(K / 16);
@@ -1089,6 +1109,7 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       }
     }
     load_w(groups > 1 ? 1 : 0, 0, wb);
+    load_scales();
   } else {
     // The whole activation tile goes from memory straight into LDS (buffer
     // loads with the LDS-direct bit: no registers, no wait per piece), issued
@@ -1114,10 +1135,11 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
       }
     }
     load_w(0, 0, wa);
+    load_scales();
     // This wave's tile loads are complete once at most the G*S weight loads
-    // issued after them are outstanding; the barrier then publishes every
-    // wave's part of the tile.
-    constexpr int kWeightLoads = G * S;
+    // and the scale loads issued after them are outstanding; the barrier
+    // then publishes every wave's part of the tile.
+    constexpr int kWeightLoads = G * S + kScaleLoads;
     static_assert(kWeightLoads < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((kWeightLoads & 15) | ((kWeightLoads >> 4) << 14) | (7 << 4) | (15 << 8));
     __syncthreads();
@@ -1128,10 +1150,6 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + n0 * ldy, out_bytes);
   const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + n0 * ldy : nullptr, DOT ? out_bytes : 0);
   const int8_t *lb0 = lds_res + li * pitch + 64 * kb;
-
-  float tn[WN];
-#pragma unroll
-  for (int n = 0; n < WN; ++n) tn[n] = ws * sn[n];
 
   // Bias of the outputs of a group (this lane's 4 consecutive output features
   // of each subtile), loaded unconditionally ahead of its MFMAs; without a
@@ -1163,6 +1181,9 @@ gemm_res_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
   constexpr int kStreamStore = 2;
   auto store_group = [&](int grp, int gs, auto biased) {
     constexpr bool kBias = decltype(biased)::value;
+    float tn[WN];  // the epilogue's t = ws * s, formed here so that only the epilogue waits for the scales
+#pragma unroll
+    for (int n = 0; n < WN; ++n) tn[n] = ws * sn[n];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       const bool sub_ok = gi < gs;
@@ -1362,9 +1383,14 @@ __device__ __forceinline__ void lds_direct16(__amdgpu_buffer_rsrc_t rsrc, int8_t
 
 template <int G, int CH, int WAVES, bool VEC4, bool DOT>
 __global__ void __launch_bounds__(64 * WAVES)
-gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const int8_t *__restrict__ qp, int64_t N,
-               const float *__restrict__ act_scale, const int32_t *__restrict__ row_sum, float *__restrict__ y,
-               int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t ldy, int tiles_m, int ms) {
+gemm_wk_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t rows, int K,
+               const int8_t *__restrict__ qp, int64_t N, const int32_t *__restrict__ row_sum,
+               const float *__restrict__ act_scale, const float *__restrict__ bias, float *__restrict__ y,
+               int32_t *__restrict__ dot_out, int64_t ldy) {
+  // Argument order: the arguments up to row_sum are preloaded into scalar
+  // registers at launch, and they are all that the loads issued before the
+  // first chunks need; the rest come from a scalar load that completes while
+  // the first chunks stream in.
   extern __shared__ __attribute__((aligned(16))) int8_t lds_wk[];
   constexpr int WN = 4, BN = 64;
   const int KB = K / 4;           // packed bytes per row
@@ -1400,11 +1426,6 @@ gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const in
 #pragma unroll
   for (int d = 0; d < 4; ++d) bbase[d] = static_cast<uint32_t>(256 * li + 16 * ((4 * kb + d) ^ li));
 
-  const uint32_t out_bytes = static_cast<uint32_t>((static_cast<int64_t>(n_here - 1) * ldy + rows) * 4);
-  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + n0 * ldy, out_bytes);
-  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + n0 * ldy : nullptr, DOT ? out_bytes : 0);
-  const bool has_bias = bias != nullptr;
-
   auto run = [&](auto gsc) {
     constexpr int GS = decltype(gsc)::value;
     constexpr int STEPS = 4 * CH;
@@ -1412,28 +1433,36 @@ gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const in
     // the chunk's 16), then its GS weight chunks.
     const int nruns = (16 - wave + WAVES - 1) / WAVES;
     const int kPerChunk = nruns + GS;
-    // Epilogue constants and the row sums the accumulators start from: small
-    // loads, issued before the big ones so that waiting for them never waits
-    // for the tile or the weights.
+    // The row sums the accumulators start from: small loads, issued before
+    // the big ones so that waiting for them never waits for the tile or the
+    // weights.  The epilogue constants (scales, weight scale, biases) go out
+    // after the first chunks (load_small), whose loads need only the
+    // preloaded arguments.
     float tn[WN], ws = 0.0f;
     int32_t rsn[WN];
     v4i bv[GS > 0 ? GS : 1];
     if constexpr (GS > 0) {
-      ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          buffer_of(packed + rows * static_cast<int64_t>(KB), 4), 0, 0, 0));
-      const __amdgpu_buffer_rsrc_t sbuf = buffer_of(act_scale + n0, static_cast<uint32_t>(4 * n_here));
       const __amdgpu_buffer_rsrc_t rbuf = buffer_of(row_sum + n0, static_cast<uint32_t>(4 * n_here));
 #pragma unroll
-      for (int n = 0; n < WN; ++n) {
-        tn[n] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, 4 * (16 * n + li), 0, 0));
-        rsn[n] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, 4 * (16 * n + li), 0, 0);
-      }
-      const __amdgpu_buffer_rsrc_t bbuf =
-          buffer_of(has_bias ? bias + o_tile : nullptr, has_bias ? static_cast<uint32_t>(4 * (rows - o_tile)) : 0u);
-#pragma unroll
-      for (int g = 0; g < GS; ++g)
-        bv[g] = __builtin_amdgcn_raw_buffer_load_b128(bbuf, 4 * (16 * wk_subtile<G, WAVES>(wave, g) + 4 * kb), 0, 0);
+      for (int n = 0; n < WN; ++n) rsn[n] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, 4 * (16 * n + li), 0, 0);
     }
+    constexpr int kSmall = GS > 0 ? WN + 1 + GS : 0;  // loads of load_small
+    auto load_small = [&]() {
+      if constexpr (GS > 0) {
+        ws = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            buffer_of(packed + rows * static_cast<int64_t>(KB), 4), 0, 0, 0));
+        const __amdgpu_buffer_rsrc_t sbuf = buffer_of(act_scale + n0, static_cast<uint32_t>(4 * n_here));
+#pragma unroll
+        for (int n = 0; n < WN; ++n)
+          tn[n] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, 4 * (16 * n + li), 0, 0));
+        const bool with_bias = bias != nullptr;
+        const __amdgpu_buffer_rsrc_t bbuf =
+            buffer_of(with_bias ? bias + o_tile : nullptr, with_bias ? static_cast<uint32_t>(4 * (rows - o_tile)) : 0u);
+#pragma unroll
+        for (int g = 0; g < GS; ++g)
+          bv[g] = __builtin_amdgcn_raw_buffer_load_b128(bbuf, 4 * (16 * wk_subtile<G, WAVES>(wave, g) + 4 * kb), 0, 0);
+      }
+    };
     // Loads of chunk c: its two tile runs, then this wave's GS weight chunks.
     // Chunks 0..PD-1 are issued at the start, chunk c+PD during the first
     // step of chunk c: the memory path accepts one 1 KiB load about every 16
@@ -1456,12 +1485,20 @@ gemm_wk_kernel(const uint8_t *__restrict__ packed, int64_t rows, int K, const in
     };
 #pragma unroll
     for (int c = 0; c < PD; ++c) issue_chunk(c);
+    load_small();
+    // Output descriptors and the bias test from the arguments that are not
+    // preloaded, after the first loads.
+    const uint32_t out_bytes = static_cast<uint32_t>((static_cast<int64_t>(n_here - 1) * ldy + rows) * 4);
+    const __amdgpu_buffer_rsrc_t ybuf = buffer_of(y + n0 * ldy, out_bytes);
+    const __amdgpu_buffer_rsrc_t dbuf = buffer_of(DOT ? dot_out + n0 * ldy : nullptr, DOT ? out_bytes : 0);
+    const bool has_bias = bias != nullptr;
     // Chunk c of the tile is in LDS once this wave has at most the loads
-    // issued after its chunk-c runs outstanding (the chunk's GS weight loads
-    // and those of chunks c+1..last, the last chunk issued so far), and the
-    // barrier has seen every wave get there.
+    // issued after its chunk-c runs outstanding (the chunk's GS weight loads,
+    // those of chunks c+1..last, the last chunk issued so far, and, for the
+    // first PD chunks, the kSmall loads issued after them), and the barrier
+    // has seen every wave get there.
     auto tile_wait = [&](int c, int last) {
-      const int after = GS + (last - c) * kPerChunk;
+      const int after = GS + (last - c) * kPerChunk + (c < PD ? kSmall : 0);
       switch (after) {
 #define I2S_WK_WAIT(n) case n: __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
         I2S_WK_WAIT(0) I2S_WK_WAIT(1) I2S_WK_WAIT(2) I2S_WK_WAIT(3) I2S_WK_WAIT(4) I2S_WK_WAIT(5) I2S_WK_WAIT(6)
@@ -2292,8 +2329,8 @@ int launch_res_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t 
     attr_done.fetch_or(bit, std::memory_order_acq_rel);
   }
   hipLaunchKernelGGL((gemm_res_kernel<G, WN, S, WAVES, VEC4, DOT, SINGLE, PERM>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(64 * WAVES), static_cast<size_t>(lds), stream, packed, rows, K, ws.q, N, ws.scale,
-                     ws.row_sum, y, dot_out, bias, ldy, tiles_m, static_cast<int>(ms));
+                     dim3(64 * WAVES), static_cast<size_t>(lds), stream, static_cast<int>(tiles_m), static_cast<int>(ms),
+                     packed, rows, K, ws.q, N, ws.row_sum, ws.scale, y, dot_out, bias, ldy);
   return hip_status();
 }
 
@@ -2419,8 +2456,8 @@ int launch_wk_inst(int64_t blocks, const uint8_t *packed, int64_t rows, int64_t 
     attr_done.fetch_or(bit, std::memory_order_acq_rel);
   }
   hipLaunchKernelGGL((gemm_wk_kernel<G, CH, WAVES, VEC4, DOT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * WAVES),
-                     static_cast<size_t>(CH * kWkChunkBytes), stream, packed, rows, static_cast<int>(K), ws.q, N,
-                     ws.scale, ws.row_sum, y, dot_out, bias, ldy, static_cast<int>(tiles_m), static_cast<int>(ms));
+                     static_cast<size_t>(CH * kWkChunkBytes), stream, static_cast<int>(tiles_m), static_cast<int>(ms),
+                     packed, rows, static_cast<int>(K), ws.q, N, ws.row_sum, ws.scale, bias, y, dot_out, ldy);
   return hip_status();
 }
 
@@ -2629,10 +2666,10 @@ int quantize_launch(const float *x, int64_t N, int64_t K, int64_t n_inner, int64
   do {                                                                                                     \
     if (interleaved)                                                                                       \
       hipLaunchKernelGGL((quantize_rowsum_reg_kernel<true, XPT, T>), dim3(static_cast<unsigned>(N)),       \
-                         dim3(T), 0, stream, x, K, n_inner, ldx, bsx, q, s, rs, qt);                              \
+                         dim3(T), 0, stream, x, K, n_inner, ldx, bsx, q, qt, s, rs);                              \
     else                                                                                                   \
       hipLaunchKernelGGL((quantize_rowsum_reg_kernel<false, XPT, T>), dim3(static_cast<unsigned>(N)),      \
-                         dim3(T), 0, stream, x, K, n_inner, ldx, bsx, q, s, rs, nullptr);                         \
+                         dim3(T), 0, stream, x, K, n_inner, ldx, bsx, q, nullptr, s, rs);                         \
     return hip_status();                                                                                   \
   } while (0)
   if (K <= 4 * 256 * 2) I2S_QREG(2, 256);
