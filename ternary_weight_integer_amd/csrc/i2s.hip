@@ -1955,11 +1955,15 @@ gemm_pipe_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 
 template <int W, int NB, int SPW, bool VEC4, bool DOT>
 __global__ void __launch_bounds__(64 * W)
-gemv_mfma_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
-                 const int8_t *__restrict__ qt, int64_t qt_row0, int64_t qt_bytes, int64_t N,
-                 const float *__restrict__ act_scale,
-                 const int32_t *__restrict__ row_sum, float *__restrict__ y, int32_t *__restrict__ dot_out,
-                 const float *__restrict__ bias, int64_t ldy) {
+gemv_mfma_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ qt,
+                 const float *__restrict__ act_scale, const int32_t *__restrict__ row_sum,
+                 const float *__restrict__ bias, int rows32, int K32, uint32_t qt_bytes, int row0_n,
+                 float *__restrict__ y, int32_t *__restrict__ dot_out, int64_t ldy) {
+  // Argument layout: everything the loads before the contraction need fits
+  // in the 14 argument dwords preloaded into scalar registers at launch --
+  // rows and K as 32-bit values, and the tiled copy's first row (< 16) and
+  // N (<= 64) in one word, row0_n = (qt_row0 << 16) | N.
+  const int64_t rows = rows32, K = K32, N = row0_n & 0xffff, qt_row0 = row0_n >> 16;
   static_assert(NB >= 1 && NB <= W, "one epilogue wave per activation block");
   __shared__ __attribute__((aligned(16))) v4i part[W][NB][64];
   const int tid = threadIdx.x;
@@ -2610,11 +2614,13 @@ int launch_skinny_inst(const uint8_t *packed, int64_t rows, int64_t K, int64_t N
   // at N = 32); fewer: 8 waves split each subtile's K-steps further.
   if (tiles > 256) {
     hipLaunchKernelGGL((gemv_mfma_kernel<4, NB, SPW, VEC4, DOT>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
-                       stream, packed, rows, K, qt, row0, qbytes, N, ws.scale, ws.row_sum, y, dot_out, bias, ldy);
+                       stream, packed, qt, ws.scale, ws.row_sum, bias, static_cast<int>(rows), static_cast<int>(K),
+                       static_cast<uint32_t>(qbytes), static_cast<int>((row0 << 16) | N), y, dot_out, ldy);
     return hip_status();
   }
   hipLaunchKernelGGL((gemv_mfma_kernel<8, NB, SPW, VEC4, DOT>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, stream,
-                     packed, rows, K, qt, row0, qbytes, N, ws.scale, ws.row_sum, y, dot_out, bias, ldy);
+                     packed, qt, ws.scale, ws.row_sum, bias, static_cast<int>(rows), static_cast<int>(K),
+                     static_cast<uint32_t>(qbytes), static_cast<int>((row0 << 16) | N), y, dot_out, ldy);
   return hip_status();
 }
 
