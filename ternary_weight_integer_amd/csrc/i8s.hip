@@ -245,6 +245,46 @@ struct MatArgs {
   int rep = 1;                    // XCD-local maps: workgroups per XCD per block of the local operand
 };
 
+// The contraction kernels take MatArgs as scalar arguments: the launch
+// preloads the first 14 argument dwords into SGPRs (a struct argument is
+// never preloaded), so the operand pointers, the sizes (as 32-bit values),
+// the tile map and the per-channel vector (the bias, or W8A8's weight
+// scales) and W8A8's row scales come first -- everything the first loads
+// need, with the grid size (gridDim.x is itself an argument load) -- and
+// the kernel rebuilds its MatArgs from them.  cvec serves as
+// both bias and cscale: the F32 (W8A8) kernels read only cscale, the others
+// only bias.
+#define I8S_KARGS                                                                                                \
+  const int8_t *__restrict__ kw, const int8_t *__restrict__ kx, int kOC, int kIC, int kN, int kmap, int krep, int kG, \
+      const float *__restrict__ kcvec, const float *__restrict__ krscale, int kvec, const uint8_t *__restrict__ kws, \
+      const uint8_t *__restrict__ kxs, float *__restrict__ kparts, int8_t *__restrict__ kout,                   \
+      int32_t *__restrict__ kdot, float *__restrict__ ky, int knparts, int krelu
+#define I8S_KARGS_OF(a, f32, g)                                                                                  \
+  (a).w, (a).x, static_cast<int>((a).OC), static_cast<int>((a).IC), static_cast<int>((a).N), (a).map, (a).rep,  \
+      static_cast<int>(g), (f32) ? (a).cscale : (a).bias, (a).rscale, (a).vec, (a).ws, (a).xs, (a).parts,      \
+      (a).out, (a).dot, (a).y, (a).nparts, (a).relu
+#define I8S_MAT_ARGS()                                                                                           \
+  MatArgs a;                                                                                                     \
+  a.w = kw;                                                                                                      \
+  a.x = kx;                                                                                                      \
+  a.OC = kOC;                                                                                                    \
+  a.IC = kIC;                                                                                                    \
+  a.N = kN;                                                                                                      \
+  a.map = kmap;                                                                                                  \
+  a.rep = krep;                                                                                                  \
+  a.vec = kvec;                                                                                                  \
+  a.bias = kcvec;                                                                                                \
+  a.cscale = kcvec;                                                                                              \
+  a.rscale = krscale;                                                                                            \
+  a.ws = kws;                                                                                                    \
+  a.xs = kxs;                                                                                                    \
+  a.parts = kparts;                                                                                              \
+  a.out = kout;                                                                                                  \
+  a.dot = kdot;                                                                                                  \
+  a.y = ky;                                                                                                      \
+  a.nparts = knparts;                                                                                            \
+  a.relu = krelu
+
 // Tile assignment of the MFMA contraction.  Workgroup b runs on XCD b % 8
 // (workgroups are dealt round-robin over the 8 XCDs, each with its own L2).
 //   kMapStride: tiles b, b + G, b + 2G, ... (channel block fastest).
@@ -272,7 +312,8 @@ __device__ inline float value_of(int32_t acc, float t, float b, bool has_bias, i
 // Plain per-output contraction for any IC (byte loads); one thread per
 // output, grid-stride.  Used when IC % 16 != 0.
 template <bool QUANT>
-__global__ void __launch_bounds__(kThreads) i8s_mm_plain_kernel(const MatArgs a) {
+__global__ void __launch_bounds__(kThreads) i8s_mm_plain_kernel(I8S_KARGS) {
+  I8S_MAT_ARGS();
   __shared__ float red[4];
   const float t = load_scale(a.ws) * load_scale(a.xs);
   float s = 1.0f;
@@ -283,7 +324,7 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_plain_kernel(const MatArgs a)
   float m = 0.0f;
   const int64_t total = a.N * a.OC;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * kThreads) {
+       i += static_cast<int64_t>(kG) * kThreads) {
     const int64_t n = i / a.OC, o = i - n * a.OC;
     const int8_t *wr = a.w + o * a.IC;
     const int8_t *xr = a.x + n * a.IC;
@@ -344,7 +385,8 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_plain_kernel(const MatArgs a)
 // into +0, which neither |f| nor q can see), and lo is 0 for the relu form and
 // -inf otherwise, so the value has no data-dependent branch.
 template <int TM, int TN, int KS, int MODE>
-__global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) {
+__global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(I8S_KARGS) {
+  I8S_MAT_ARGS();
   constexpr bool QUANT = MODE == kModeQuant;
   constexpr int WAVES_M = TM / 64;
   constexpr int WAVES_N = 4 / WAVES_M;
@@ -377,7 +419,7 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(const MatArgs a) 
   // them (and through the K chunks of each) without divisions.
   const int tiles_o = (OC + TM - 1) / TM, tiles_n = (N + TN - 1) / TN;
   const int tiles = tiles_o * tiles_n;
-  const int G = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+  const int G = kG, b = static_cast<int>(blockIdx.x);
   const int kchunks = IC > 0 ? (IC + 64 * KS - 1) / (64 * KS) : 1;
   struct Cursor {
     int ob, nb, kc;
@@ -880,7 +922,8 @@ __device__ inline float wave_group_max(float v, float *red) {
 }
 
 template <int W, int FN, int SPW, int MODE>
-__global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(const MatArgs a) {
+__global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(I8S_KARGS) {
+  I8S_MAT_ARGS();
   __shared__ __attribute__((aligned(16))) v4i part[W][FN][64];
   __shared__ float red[W];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -912,7 +955,7 @@ __global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(const MatArgs a) 
   const int items = blocks_o * blocks_n;
   const int steps = (IC + 63) / 64;
   float m = 0.0f;
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+  for (int item = blockIdx.x; item < items; item += kG) {
     const int o0 = (item % blocks_o) * 16, n0 = (item / blocks_o) * (16 * FN);
     const bool o_ok = o0 + li < OC;
     // Epilogue constants of this lane (channels o0 + 4*kq + r; rows
@@ -1243,11 +1286,14 @@ int launch_mfma(MatArgs a, bool f32, hipStream_t stream) {
   }
   a.nparts = g;
   if (f32) {  // W8A8: one pass, F32 out
-    hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, kModeF32>), dim3(g), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, kModeF32>), dim3(g), dim3(kThreads), 0, stream,
+                       I8S_KARGS_OF(a, true, g));
     return hip_status();
   }
-  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, kModeMax>), dim3(g), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, kModeQuant>), dim3(g), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, kModeMax>), dim3(g), dim3(kThreads), 0, stream,
+                     I8S_KARGS_OF(a, false, g));
+  hipLaunchKernelGGL((i8s_mm_mfma_kernel<TM, TN, KS, kModeQuant>), dim3(g), dim3(kThreads), 0, stream,
+                     I8S_KARGS_OF(a, false, g));
   return hip_status();
 }
 
@@ -1257,11 +1303,14 @@ int launch_skinny_fn_w(MatArgs a, bool f32, int64_t items, hipStream_t stream) {
   const int g = parts_for(items);
   a.nparts = g;
   if (f32) {
-    hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeF32>), dim3(g), dim3(64 * W), 0, stream, a);
+    hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeF32>), dim3(g), dim3(64 * W), 0, stream,
+                       I8S_KARGS_OF(a, true, g));
     return hip_status();
   }
-  hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeMax>), dim3(g), dim3(64 * W), 0, stream, a);
-  hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeQuant>), dim3(g), dim3(64 * W), 0, stream, a);
+  hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeMax>), dim3(g), dim3(64 * W), 0, stream,
+                     I8S_KARGS_OF(a, false, g));
+  hipLaunchKernelGGL((i8s_mm_skinny_kernel<W, FN, SPW, kModeQuant>), dim3(g), dim3(64 * W), 0, stream,
+                     I8S_KARGS_OF(a, false, g));
   return hip_status();
 }
 
@@ -1286,8 +1335,8 @@ int launch_skinny(MatArgs a, bool f32, hipStream_t stream) {
 int launch_plain(MatArgs a, hipStream_t stream) {
   const int g = parts_for((a.N * a.OC + kThreads - 1) / kThreads);
   a.nparts = g;
-  hipLaunchKernelGGL(i8s_mm_plain_kernel<false>, dim3(g), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL(i8s_mm_plain_kernel<true>, dim3(g), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(i8s_mm_plain_kernel<false>, dim3(g), dim3(kThreads), 0, stream, I8S_KARGS_OF(a, false, g));
+  hipLaunchKernelGGL(i8s_mm_plain_kernel<true>, dim3(g), dim3(kThreads), 0, stream, I8S_KARGS_OF(a, false, g));
   return hip_status();
 }
 
@@ -1319,6 +1368,7 @@ int check_mm(const uint8_t *w, int64_t OC, int64_t IC, const uint8_t *x, int64_t
   if ((bias && !aligned(bias, 4)) || (dot_out && !aligned(dot_out, 4))) return I2S_EINVAL;
   if (IC > I8S_MAX_IC) return I2S_ERANGE;
   if (OC * IC >= kMaxBytes || N * IC >= kMaxBytes || N * OC >= kMaxBytes / 4) return I2S_ERANGE;
+  if (OC > kMaxBytes || N > kMaxBytes) return I2S_ERANGE;  // sizes go to the kernels as 32-bit values
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < kMaxParts * sizeof(float)) return I2S_EWORKSPACE;
   return I2S_OK;
 }
@@ -1465,6 +1515,7 @@ extern "C" int w8a8_matmul(const int8_t *wq, const float *wscale, int64_t OC, in
   if (dot_out && !aligned(dot_out, 16)) return I2S_EINVAL;
   if (K == 0 || K % 16 != 0) return I2S_EALIGN;
   if (OC * K >= kMaxBytes || M * K >= kMaxBytes || M * OC >= kMaxBytes / 4) return I2S_ERANGE;
+  if (OC > kMaxBytes || M > kMaxBytes) return I2S_ERANGE;  // sizes go to the kernels as 32-bit values
   if (variant < 0 || variant == 1 || variant > kW8a8Variants) return I2S_EKERNEL;
   if (variant == 10 && !w8a8_res_fits(K)) return I2S_EKERNEL;
   if (variant == 0) variant = w8a8_auto_variant(OC, K, M);
@@ -1510,6 +1561,7 @@ extern "C" int w8a8_mul_mat_ex(const int8_t *wq, const float *wscale, int64_t OC
     return I2S_EINVAL;
   if (K == 0 || K % 16 != 0) return I2S_EALIGN;
   if (OC * K >= kMaxBytes || M * K >= kMaxBytes || M * OC >= kMaxBytes / 4) return I2S_ERANGE;
+  if (OC > kMaxBytes || M > kMaxBytes) return I2S_ERANGE;  // sizes go to the kernels as 32-bit values
   if (variant < 0 || variant == 1 || variant > kW8a8Variants) return I2S_EKERNEL;
   if (variant == 10 && !w8a8_res_fits(K)) return I2S_EKERNEL;
   int st = w8a8_quantize_act(x, M, K, aq, as, stream);
