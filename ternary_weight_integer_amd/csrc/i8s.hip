@@ -253,16 +253,19 @@ struct MatArgs {
 // need, with the grid size (gridDim.x is itself an argument load) -- and
 // the kernel rebuilds its MatArgs from them.  cvec serves as
 // both bias and cscale: the F32 (W8A8) kernels read only cscale, the others
-// only bias.
+// only bias.  The tenth argument is the row scales in F32 mode and the
+// partial maxima (the same array as parts) otherwise, so that the
+// quantizing pass finds them in a preloaded dword; it aliases parts, hence
+// no restrict on it.
 #define I8S_KARGS                                                                                                \
   const int8_t *__restrict__ kw, const int8_t *__restrict__ kx, int kOC, int kIC, int kN, int kmap, int krep, int kG, \
-      const float *__restrict__ kcvec, const float *__restrict__ krscale, int kvec, const uint8_t *__restrict__ kws, \
+      const float *__restrict__ kcvec, const float *krscale, int kvec, const uint8_t *__restrict__ kws,           \
       const uint8_t *__restrict__ kxs, float *__restrict__ kparts, int8_t *__restrict__ kout,                   \
       int32_t *__restrict__ kdot, float *__restrict__ ky, int knparts, int krelu
 #define I8S_KARGS_OF(a, f32, g)                                                                                  \
   (a).w, (a).x, static_cast<int>((a).OC), static_cast<int>((a).IC), static_cast<int>((a).N), (a).map, (a).rep,  \
-      static_cast<int>(g), (f32) ? (a).cscale : (a).bias, (a).rscale, (a).vec, (a).ws, (a).xs, (a).parts,      \
-      (a).out, (a).dot, (a).y, (a).nparts, (a).relu
+      static_cast<int>(g), (f32) ? (a).cscale : (a).bias, (f32) ? (a).rscale : (a).parts, (a).vec, (a).ws,     \
+      (a).xs, (a).parts, (a).out, (a).dot, (a).y, (a).nparts, (a).relu
 #define I8S_MAT_ARGS()                                                                                           \
   MatArgs a;                                                                                                     \
   a.w = kw;                                                                                                      \
@@ -931,25 +934,28 @@ __global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(I8S_KARGS) {
   const int OC = static_cast<int>(a.OC), IC = static_cast<int>(a.IC), N = static_cast<int>(a.N);
   const __amdgpu_buffer_rsrc_t wbuf = buffer_of(a.w, static_cast<uint32_t>(a.OC * a.IC));
   const __amdgpu_buffer_rsrc_t xbuf = buffer_of(a.x, static_cast<uint32_t>(a.N * a.IC));
-  const __amdgpu_buffer_rsrc_t obuf = buffer_of(a.out, static_cast<uint32_t>(a.N * a.OC));
-  const __amdgpu_buffer_rsrc_t dbuf = buffer_of(a.dot, a.dot ? static_cast<uint32_t>(a.N * a.OC * 4) : 0u);
-  const __amdgpu_buffer_rsrc_t ybuf = buffer_of(a.y, MODE == kModeF32 ? static_cast<uint32_t>(a.N * a.OC * 4) : 0u);
   const float *cvec = MODE == kModeF32 ? a.cscale : a.bias;
   const __amdgpu_buffer_rsrc_t bbuf = buffer_of(cvec, cvec ? static_cast<uint32_t>(a.OC * 4) : 0u);
   const __amdgpu_buffer_rsrc_t rbuf = buffer_of(a.rscale, MODE == kModeF32 ? static_cast<uint32_t>(a.N * 4) : 0u);
 
-  const float ws = MODE == kModeF32 ? 1.0f : load_scale(a.ws), xs = MODE == kModeF32 ? 1.0f : load_scale(a.xs);
-  const float t = ws * xs;
-  const float lo = a.relu ? 0.0f : -INFINITY;
+  // Quant mode: the Max pass ran on this same grid and left one maximum per
+  // workgroup, kG of them, at the tenth argument (which carries the per-row
+  // scales in F32 mode).  This thread's first one is loaded behind the first
+  // item's first operand batch and the tensor scale is reduced after that
+  // item's K-loop, so that the two memory latencies overlap.
+  const __amdgpu_buffer_rsrc_t pbuf = buffer_of(a.rscale, MODE == kModeQuant ? static_cast<uint32_t>(4 * kG) : 0u);
   float s = 1.0f;
-  if constexpr (MODE == kModeQuant) {
-    float pm = 0.0f;
-    for (int i = tid; i < a.nparts; i += 64 * W) pm = fmaxf(pm, a.parts[i]);
-    pm = wave_group_max<W>(pm, red);
-    if (pm < kAmaxFloor) pm = kAmaxFloor;
-    s = pm / 127.0f;
-    if (blockIdx.x == 0) write_slot(reinterpret_cast<uint8_t *>(a.out) + a.N * a.OC, s);
-  }
+  bool have_s = MODE != kModeQuant;
+  auto tensor_scale = [&](float pm) {
+    for (int i = tid + 64 * W; i < kG; i += 64 * W) pm = fmaxf(pm, a.rscale[i]);
+    float r = wave_group_max<W>(pm, red);
+    if (r < kAmaxFloor) r = kAmaxFloor;
+    s = r / 127.0f;
+    int8_t *outp = a.out;  // pinned here so that its address is not computed ahead of the loads
+    __asm__ volatile("" : "+s"(outp));
+    if (blockIdx.x == 0) write_slot(reinterpret_cast<uint8_t *>(outp) + a.N * a.OC, s);
+    have_s = true;
+  };
 
   const int blocks_o = (OC + 15) / 16, blocks_n = (N + 16 * FN - 1) / (16 * FN);
   const int items = blocks_o * blocks_n;
@@ -1008,6 +1014,10 @@ __global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(I8S_KARGS) {
     const int batches = (mine + SPW - 1) / SPW;
     v4i aa[SPW], ab[SPW], ba[SPW][FN], bb[SPW][FN];
     if (batches > 0) load(0, aa, ba);
+    float p0 = 0.0f;  // out of range, and so 0, once the scale is known
+    if constexpr (MODE == kModeQuant)
+      p0 = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          pbuf, have_s ? kOutOfRange : static_cast<uint32_t>(4 * tid), 0, 0));
     for (int g = 0; g < batches; g += 2) {
       if (g + 1 < batches) load(g + 1, ab, bb);
       compute(aa, ba);
@@ -1015,10 +1025,28 @@ __global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(I8S_KARGS) {
       if (g + 2 < batches) load(g + 2, aa, ba);
       compute(ab, bb);
     }
+    if constexpr (MODE == kModeQuant) {
+      if (!have_s) tensor_scale(p0);
+    }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) part[wave][fn][lane] = acc[fn];
     __syncthreads();
     if (wave == 0) {
+      // Output descriptors are built here, from pointers the compiler may not
+      // hoist, so that the first operand loads wait on no argument outside
+      // the preloaded ones.
+      int8_t *outp = a.out;
+      int32_t *dotp = a.dot;
+      float *yp = a.y;
+      const uint8_t *wsp = a.ws, *xsp = a.xs;
+      int relu = a.relu;
+      __asm__ volatile("" : "+s"(outp), "+s"(dotp), "+s"(yp), "+s"(wsp), "+s"(xsp), "+s"(relu));
+      const float t = MODE == kModeF32 ? 1.0f : load_scale(wsp) * load_scale(xsp);
+      const float lo = relu ? 0.0f : -INFINITY;
+      const __amdgpu_buffer_rsrc_t obuf = buffer_of(outp, static_cast<uint32_t>(a.N * a.OC));
+      const __amdgpu_buffer_rsrc_t dbuf = buffer_of(dotp, dotp ? static_cast<uint32_t>(a.N * a.OC * 4) : 0u);
+      const __amdgpu_buffer_rsrc_t ybuf =
+          buffer_of(yp, MODE == kModeF32 ? static_cast<uint32_t>(a.N * a.OC * 4) : 0u);
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         v4i tot = part[0][fn][lane];
@@ -1046,12 +1074,17 @@ __global__ void __launch_bounds__(64 * W) i8s_mm_skinny_kernel(I8S_KARGS) {
               __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(quant(v, s)), obuf, off, 0, 0);
             }
           }
-          if (a.dot && MODE != kModeMax)
+          if (dotp && MODE != kModeMax)
             __builtin_amdgcn_raw_buffer_store_b32(acc[fn][r], dbuf, ok ? 4 * off : kOutOfRange, 0, 0);
         }
       }
     }
     __syncthreads();  // part[] is reused by the next item
+  }
+  if constexpr (MODE == kModeQuant) {
+    // A workgroup with no item still reports the scale.
+    if (!have_s)
+      tensor_scale(__int_as_float(__builtin_amdgcn_raw_buffer_load_b32(pbuf, static_cast<uint32_t>(4 * tid), 0, 0)));
   }
   if constexpr (MODE == kModeMax) {
     m = wave_group_max<W>(m, red);
