@@ -1024,7 +1024,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
   // its MFMA operand directly (16 rows x 64 bytes per instruction).
   const uint32_t lane_off = PERM ? (lane >> 2) * row_bytes + 16 * (lane & 3) : li * row_bytes + 16 * kb;
   const int perm_addr = 4 * (4 * li + kb);
-  auto permute_step = [&](const v4i (&src)[G][S], v4i (&dst)[G][S], int st, auto gsc) {
+  auto permute_step = [&](const v4i (&src)[G][S], v4i (&dst)[G][S], int st, auto gsc) __attribute__((always_inline)) {
 #pragma unroll
     for (int gi = 0; gi < decltype(gsc)::value; ++gi)
 #pragma unroll
@@ -1033,7 +1033,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
   // Subtiles of a short group past this wave's last one read nothing (an
   // out-of-range offset: no memory traffic, and the same number of loads in
   // flight, so every wait below stays as it is).
-  auto load_w = [&](int grp, int ch, v4i (&wv)[G][S]) {
+  auto load_w = [&](int grp, int ch, v4i (&wv)[G][S]) __attribute__((always_inline)) {
     const int gs = grp + 1 < groups ? G : mine - grp * G;
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
@@ -1061,7 +1061,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
   }
   float sn[WN], ws;
   constexpr int kScaleLoads = WN + 1;
-  auto load_scales = [&]() {
+  auto load_scales = [&]() __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t sbuf = buffer_of(act_scale + n0, static_cast<uint32_t>(4 * n_here));
 #pragma unroll
     for (int n = 0; n < WN; ++n)
@@ -1078,13 +1078,13 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
   // 16 pieces of 16 bytes, kPieceLanes per lane.
   constexpr int kStepPieces = kRowsPerWave * 16;
   constexpr int kPieceLanes = (kStepPieces + 63) / 64;
-  auto step_goff = [&](int st, int p) -> uint32_t {
+  auto step_goff = [&](int st, int p) __attribute__((always_inline)) -> uint32_t {
     const int pc = 64 * p + lane;
     const int r = wave * kRowsPerWave + pc / 16;
     const int c = 16 * st + pc % 16;  // 16-byte piece index within the padded row
     return pc < kStepPieces && c < k_pieces ? static_cast<uint32_t>(r * K + 16 * c) : kOutOfRange;
   };
-  auto step_loff = [&](int st, int p) -> uint32_t {
+  auto step_loff = [&](int st, int p) __attribute__((always_inline)) -> uint32_t {
     const int pc = 64 * p + lane;
     const int r = wave * kRowsPerWave + pc / 16;
     return static_cast<uint32_t>(r) * pitch + 16 * (16 * st + pc % 16);
@@ -1157,7 +1157,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
   const bool has_bias = bias != nullptr;
   const __amdgpu_buffer_rsrc_t bbuf = buffer_of(bias, has_bias ? static_cast<uint32_t>(4 * rows) : 0);
   v4i bv[G];
-  auto load_bias = [&](int grp) {
+  auto load_bias = [&](int grp) __attribute__((always_inline)) {
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       const uint32_t o = static_cast<uint32_t>(o_tile + 16 * static_cast<int64_t>(wave + WAVES * (grp * G + gi)) + 4 * kb);
@@ -1179,7 +1179,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
   // dot is that plus the row sum.  The bias test is one wave-uniform branch
   // around the whole group.
   constexpr int kStreamStore = 2;
-  auto store_group = [&](int grp, int gs, auto biased) {
+  auto store_group = [&](int grp, int gs, auto biased) __attribute__((always_inline)) {
     constexpr bool kBias = decltype(biased)::value;
     float tn[WN];  // the epilogue's t = ws * s, formed here so that only the epilogue waits for the scales
 #pragma unroll
@@ -1216,14 +1216,14 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
       }
     }
   };
-  auto epilogue_group = [&](int grp, int gs) {
+  auto epilogue_group = [&](int grp, int gs) __attribute__((always_inline)) {
     if (has_bias)
       store_group(grp, gs, std::true_type{});
     else
       store_group(grp, gs, std::false_type{});
   };
 
-  auto zero_acc = [&]() {
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int gi = 0; gi < G; ++gi)
 #pragma unroll
@@ -1231,8 +1231,8 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
   };
 
   // The MFMAs (and, with PERM, the permutes) of the group's gs subtiles only.
-  auto mfma_group = [&](const v4i (&cur_in)[G][S], int gs, const int8_t *lb) {
-    auto run = [&](auto gsc) {
+  auto mfma_group = [&](const v4i (&cur_in)[G][S], int gs, const int8_t *lb) __attribute__((always_inline)) {
+    auto run = [&](auto gsc) __attribute__((always_inline)) {
       constexpr int GS = decltype(gsc)::value;
       v4i pm[G][S];
       if constexpr (PERM) {
@@ -1261,7 +1261,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
   // a single chunk (K <= 256*S) an item is a whole group and the body has no
   // branch around any memory operation.
   int grp = 0, ch = 0;
-  auto item = [&](const v4i (&cur)[G][S], v4i (&nxt)[G][S]) {
+  auto item = [&](const v4i (&cur)[G][S], v4i (&nxt)[G][S]) __attribute__((always_inline)) {
     const int gs = grp + 1 < groups ? G : mine - grp * G;
     if constexpr (SINGLE) {
       load_bias(grp);
@@ -1295,7 +1295,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
       for (int p = 0; p < kPieceLanes; ++p)
         if (64 * p + lane < kStepPieces) *reinterpret_cast<v4i *>(lds_res + step_loff(st, p)) = bst[st][p];
       __syncthreads();
-      auto run0 = [&](auto gsc) {
+      auto run0 = [&](auto gsc) __attribute__((always_inline)) {
         constexpr int GS = decltype(gsc)::value;
         v4i pw[G][S];
         if constexpr (PERM) permute_step(wa, pw, st, gsc);
