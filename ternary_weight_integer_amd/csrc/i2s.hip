@@ -150,36 +150,48 @@ __device__ inline int wave_sum(int v) { return lanes_sum<64>(v); }
 // and within 2^-15 + 2^-18 < 2^-14 of the IEEE one.  A product farther than
 // 2^-14 from every half-integer therefore lies strictly between the same two
 // half-integers as the IEEE quotient, and round-to-nearest-even of the
-// product (one v_rndne) equals roundf of that quotient.  If any value of the
-// wave comes within 2^-14 of a half-integer (fract(|p|) within 2^-14 of
-// 0.5), the whole wave divides and applies roundf instead: a wave-uniform
-// branch, since per-value branches would serialize the values.  NaN and
-// infinite inputs take the same values on both paths (rcp(inf) = 0).
+// product (one v_rndne) equals roundf of that quotient.  A value nearer
+// than that to a tie takes the exact division and roundf instead.  The
+// branches are wave-uniform: one over the thread's values (no value of the
+// wave near a tie: the common case, every value rounded from its product),
+// and inside it one per float4 (only a float4 position where some lane is
+// near a tie divides, so a long row that meets a tie somewhere divides a
+// few values instead of all of them).  NaN and infinite inputs take the
+// same values on both paths (rcp(inf) = 0).
 template <int XPT>
 __device__ inline void quantize_codes(const float4 (&v)[XPT], float s, uint32_t (&packed)[XPT]) {
   const float inv = __builtin_amdgcn_rcpf(s);
   float rq[XPT][4];
-  float dmin = 1.0f;  // nearest distance of a product to a half-integer
+  float dm[XPT];  // per float4: nearest distance of a product to a half-integer
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    dm[i] = 1.0f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       rq[i][t] = e[t] * inv;
-      dmin = fminf(dmin, fabsf(__builtin_amdgcn_fractf(fabsf(rq[i][t])) - 0.5f));
+      dm[i] = fminf(dm[i], fabsf(__builtin_amdgcn_fractf(fabsf(rq[i][t])) - 0.5f));
     }
   }
+  float dmin = dm[0];
+#pragma unroll
+  for (int i = 1; i < XPT; ++i) dmin = fminf(dmin, dm[i]);
   if (__any(dmin <= 0x1p-14f)) {
-    // The divisor passes through an empty asm statement, so that the
-    // divisions cannot be hoisted out of this branch (speculated, they would
-    // run in every wave).
-    float sd = s;
-    __asm__ volatile("" : "+v"(sd));
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      if (__any(dm[i] <= 0x1p-14f)) {
+        // The divisor passes through an empty asm statement, so that the
+        // divisions cannot be hoisted out of this branch (speculated, they
+        // would run for every value of every wave).
+        float sd = s;
+        __asm__ volatile("" : "+v"(sd));
+        const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) rq[i][t] = roundf(e[t] / sd);
+        for (int t = 0; t < 4; ++t) rq[i][t] = roundf(e[t] / sd);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rq[i][t] = __builtin_rintf(rq[i][t]);
+      }
     }
   } else {
 #pragma unroll
