@@ -545,20 +545,21 @@ gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
 // s = amax/127, q = clamp(roundf(x/s), +-127), block-wide int8 row sum, the
 // same single IEEE operations as quantize_rowsum_kernel -- into LDS in the
 // group-interleaved order, and runs the v_dot4 contraction of gemv_kernel on
-// it.  Requires K <= 64*L*CPL (one weight batch) and K <= 4*kGemvThreads*XPT
-// (XPT float4 activation loads per thread per row).
+// it.  Requires K <= 64*L*CPL (one weight batch) and K <= 4*T*XPT (T
+// threads per workgroup, XPT float4 activation loads per thread per row).
 
-template <int NC, int L, int RPL, int CPL, int XPT>
+template <int NC, int L, int RPL, int CPL, int XPT, int T>
 __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
                                            const float *__restrict__ x, int64_t ldx, float *__restrict__ y,
                                            int32_t *__restrict__ dot_out, const float *__restrict__ bias,
                                            int64_t ldy, int64_t block,
                                            int8_t *qs /* NC x K group-interleaved int8, LDS */) {
-  __shared__ float red_f[NC][kGemvThreads / 64];
-  __shared__ int red_i[NC][kGemvThreads / 64];
+  constexpr int kWaves = T / 64;
+  __shared__ float red_f[NC][kWaves];
+  __shared__ int red_i[NC][kWaves];
   constexpr int kSlots = 64 / L;
   constexpr int kRowsPerWave = kSlots * RPL;
-  constexpr int kRowsPerBlock = kRowsPerWave * (kGemvThreads / 64);
+  constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int lam = lane % L, slot = lane / L;
@@ -576,7 +577,7 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
     const __amdgpu_buffer_rsrc_t xbuf = buffer_of(x + static_cast<int64_t>(n) * ldx, static_cast<uint32_t>(16 * k4));
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int idx = tid + kGemvThreads * i;
+      const int idx = tid + T * i;
       const v4i v = __builtin_amdgcn_raw_buffer_load_b128(xbuf, idx < k4 ? static_cast<uint32_t>(16 * idx) : kOutOfRange, 0, 0);
       xv[n][i] = make_float4(__int_as_float(v[0]), __int_as_float(v[1]), __int_as_float(v[2]), __int_as_float(v[3]));
     }
@@ -635,7 +636,9 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
   float sc[NC];
 #pragma unroll
   for (int n = 0; n < NC; ++n) {
-    float a = fmaxf(fmaxf(red_f[n][0], red_f[n][1]), fmaxf(red_f[n][2], red_f[n][3]));
+    float a = red_f[n][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) a = fmaxf(a, red_f[n][w]);
     a = fmaxf(a, 1e-5f);
     sc[n] = a / 127.0f;
     uint32_t codes[XPT];
@@ -643,7 +646,7 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int idx = tid + kGemvThreads * i;
+      const int idx = tid + T * i;
       if (idx < k4) {
         sum = add_bytes(codes[i], sum);
         const int p = 4 * idx;
@@ -699,7 +702,9 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
     for (int n = 0; n < NC; ++n) {
       const int total = lanes_sum<L>((acc[m][n][0] + acc[m][n][1]) + (acc[m][n][2] + acc[m][n][3]));
       if (r < rows && lam == n % L) {
-        const int32_t rs = red_i[n][0] + red_i[n][1] + red_i[n][2] + red_i[n][3];
+        int32_t rs = red_i[n][0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) rs += red_i[n][w];
         const float t = ws * sc[n];
         float v = epilogue(total, rs, t);
         if (bias) v = add_bias(v, bv[m]);
@@ -710,13 +715,13 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
   }
 }
 
-template <int NC, int L, int RPL, int CPL, int XPT>
-__global__ void __launch_bounds__(kGemvThreads)
+template <int NC, int L, int RPL, int CPL, int XPT, int T>
+__global__ void __launch_bounds__(T)
 gemv_fused_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
                   const float *__restrict__ x, int64_t ldx, float *__restrict__ y, int32_t *__restrict__ dot_out,
                   const float *__restrict__ bias, int64_t ldy) {
   extern __shared__ __attribute__((aligned(16))) int8_t qs[];
-  fused_body<NC, L, RPL, CPL, XPT>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, blockIdx.x, qs);
+  fused_body<NC, L, RPL, CPL, XPT, T>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, blockIdx.x, qs);
 }
 
 // Several projections of the same activation rows in one launch (the decoder
@@ -737,11 +742,11 @@ struct FusedGroup {
   int32_t *dot[I2S_GROUP_MAX] = {};
 };
 
-template <int NC, int L, int RPL, int CPL, int XPT>
-__global__ void __launch_bounds__(kGemvThreads)
+template <int NC, int L, int RPL, int CPL, int XPT, int T>
+__global__ void __launch_bounds__(T)
 gemv_fused_group_kernel(const FusedGroup g, int64_t K, const float *__restrict__ x) {
   extern __shared__ __attribute__((aligned(16))) int8_t qs[];
-  constexpr int64_t kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
+  constexpr int64_t kRowsPerBlock = (64 / L) * RPL * (T / 64);
   const int p = static_cast<int>(blockIdx.y);
   const int64_t block = blockIdx.x;
   const uint8_t *packed = g.packed[p];
@@ -755,7 +760,7 @@ gemv_fused_group_kernel(const FusedGroup g, int64_t K, const float *__restrict__
   // vector load).
   __asm__ volatile("" ::"s"(packed), "s"(rows), "s"(bias), "s"(y), "s"(dot), "s"(x), "s"(K));
   if (block * kRowsPerBlock >= rows) return;  // the whole workgroup, before any barrier
-  fused_body<NC, L, RPL, CPL, XPT>(packed, rows, K, x, K, y, dot, bias, rows, block, qs);
+  fused_body<NC, L, RPL, CPL, XPT, T>(packed, rows, K, x, K, y, dot, bias, rows, block, qs);
 }
 
 // ---------------------------------------------------------------------------
@@ -2170,32 +2175,40 @@ int launch_gemv(int variant, const uint8_t *packed, int64_t rows, int64_t K, int
   }
 }
 
-template <int NC, int L, int RPL, int CPL, int XPT>
+template <int NC, int L, int RPL, int CPL, int XPT, int T = kGemvThreads>
 int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float *x, int64_t ldx, float *y,
                      int32_t *dot_out, const float *bias, int64_t ldy,
                      hipStream_t stream) {
-  if (K > 64 * L * CPL || K > 4 * kGemvThreads * XPT) return I2S_EKERNEL;
+  if (K > 64 * L * CPL || K > 4 * T * XPT) return I2S_EKERNEL;
   if (rows * (K / 4) >= (int64_t{1} << 31)) return I2S_EKERNEL;  // 32-bit buffer offsets
-  constexpr int kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
+  constexpr int kRowsPerBlock = (64 / L) * RPL * (T / 64);
   const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks > kMaxDim) return I2S_ERANGE;
-  hipLaunchKernelGGL((gemv_fused_kernel<NC, L, RPL, CPL, XPT>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kGemvThreads), static_cast<size_t>(NC * K), stream, packed, rows, K, x, ldx, y, dot_out, bias, ldy);
+  hipLaunchKernelGGL((gemv_fused_kernel<NC, L, RPL, CPL, XPT, T>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(T), static_cast<size_t>(NC * K), stream, packed, rows, K, x, ldx, y, dot_out, bias, ldy);
   return hip_status();
 }
 
 // Fused quantize + GEMV configurations (1-based): (L, RPL, CPL, XPT) =
 // (8, 2, 3, 2), (8, 1, 4, 2), (16, 1, 2, 2) for K <= 1536/2048/2048,
-// (64, 1, 3, 9), (32, 1, 5, 9) for K <= 9216 (the down projection), and
+// (64, 1, 3, 9), (32, 1, 5, 9) for K <= 9216 (the down projection),
 // (8, 1, 3, 2) for K <= 1536 (variant 2 without its fourth chunk batch,
-// which at K = 1536 would be a load past every row).
-// Automatic: measured fastest on MI355X for the decoder shapes.
-constexpr int kFusedVariants = 6;
+// which at K = 1536 would be a load past every row), all with 256 threads;
+// and (8, 1, 3, 1) with 384 threads (48 rows per workgroup) for K <= 1536.
+// Automatic: measured fastest on MI355X for the decoder shapes (8960 rows
+// at K = 1536: 3.00 us with variant 7 against 3.21 with variant 6, whose
+// 280 workgroups exceed the compute units; 6144 rows: 2.54 with variant 6
+// against 2.98; 17920 rows: 3.77 against 4.08).
+constexpr int kFusedVariants = 7;
 constexpr int64_t kFusedMaxK = 9216;
 
 int fused_auto_variant(int64_t rows, int64_t K) {
   if (K > 2048) return 5;
   if (rows <= 2048) return 3;
+  // More than 256 workgroups of 32 rows put a second workgroup on some
+  // compute units, whose activation loads then queue behind the first one's
+  // weights; up to 256 workgroups of 48 rows (6 waves) avoid that.
+  if (K <= 1536 && rows > 8192 && rows <= 12288) return 7;
   return K <= 1536 ? 6 : 2;
 }
 
@@ -2210,6 +2223,7 @@ int launch_fused_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K,
     case 4: return launch_fused_cfg<NC, 64, 1, 3, 9>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     case 5: return launch_fused_cfg<NC, 32, 1, 5, 9>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     case 6: return launch_fused_cfg<NC, 8, 1, 3, 2>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
+    case 7: return launch_fused_cfg<NC, 8, 1, 3, 1, 384>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }
@@ -2225,10 +2239,10 @@ int launch_fused(int variant, const uint8_t *packed, int64_t rows, int64_t K, in
   }
 }
 
-template <int NC, int L, int RPL, int CPL, int XPT>
+template <int NC, int L, int RPL, int CPL, int XPT, int T = kGemvThreads>
 int launch_fused_group_cfg(const FusedGroup &g, int64_t K, const float *x, hipStream_t stream) {
-  if (K > 64 * L * CPL || K > 4 * kGemvThreads * XPT) return I2S_EKERNEL;
-  constexpr int kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
+  if (K > 64 * L * CPL || K > 4 * T * XPT) return I2S_EKERNEL;
+  constexpr int kRowsPerBlock = (64 / L) * RPL * (T / 64);
   int64_t widest = 0;  // workgroups of the projection with the most rows
   for (int p = 0; p < g.count; ++p) {
     if (g.rows[p] * (K / 4) >= (int64_t{1} << 31)) return I2S_EKERNEL;  // 32-bit buffer offsets
@@ -2237,8 +2251,8 @@ int launch_fused_group_cfg(const FusedGroup &g, int64_t K, const float *x, hipSt
   }
   if (widest == 0) return I2S_OK;
   if (widest > kMaxDim) return I2S_ERANGE;
-  hipLaunchKernelGGL((gemv_fused_group_kernel<NC, L, RPL, CPL, XPT>),
-                     dim3(static_cast<unsigned>(widest), static_cast<unsigned>(g.count)), dim3(kGemvThreads),
+  hipLaunchKernelGGL((gemv_fused_group_kernel<NC, L, RPL, CPL, XPT, T>),
+                     dim3(static_cast<unsigned>(widest), static_cast<unsigned>(g.count)), dim3(T),
                      static_cast<size_t>(NC * K), stream, g, K, x);
   return hip_status();
 }
@@ -2254,6 +2268,7 @@ int launch_fused_group_nc(int variant, const FusedGroup &g, int64_t total_rows, 
     case 4: return launch_fused_group_cfg<NC, 64, 1, 3, 9>(g, K, x, stream);
     case 5: return launch_fused_group_cfg<NC, 32, 1, 5, 9>(g, K, x, stream);
     case 6: return launch_fused_group_cfg<NC, 8, 1, 3, 2>(g, K, x, stream);
+    case 7: return launch_fused_group_cfg<NC, 8, 1, 3, 1, 384>(g, K, x, stream);
     default: return I2S_EKERNEL;
   }
 }

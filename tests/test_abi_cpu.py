@@ -123,7 +123,9 @@ def test_mul_mat_kernel_choice():
     assert i2s.i2s_mul_mat_kernel(256, 1536, 65) == i2s.KERNEL_GEMM
     assert i2s.i2s_mul_mat_kernel(8960, 1536, 512) == i2s.KERNEL_GEMM
     # fused configurations: chunk batches sized to the row where they can be
-    assert i2s.i2s_mul_mat_variant(8960, 1536, 1) == 6
+    assert i2s.i2s_mul_mat_variant(8960, 1536, 1) == 7
+    assert i2s.i2s_mul_mat_variant(17920, 1536, 1) == 6
+    assert i2s.i2s_mul_mat_variant(6144, 1536, 1) == 6
     assert i2s.i2s_mul_mat_variant(8960, 2048, 1) == 2
     assert i2s.i2s_mul_mat_variant(1536, 1536, 1) == 3
     assert i2s.i2s_mul_mat_variant(1536, 8960, 1) == 5

@@ -229,7 +229,7 @@ def test_grid_all_kernels_and_variants(K):
 
 
 # Longest K of each fused configuration (64 * lanes per row * chunk batches).
-FUSED_MAX_K = {1: 1536, 2: 2048, 3: 2048, 4: 12288, 5: 10240, 6: 1536}
+FUSED_MAX_K = {1: 1536, 2: 2048, 3: 2048, 4: 12288, 5: 10240, 6: 1536, 7: 1536}
 
 
 @pytest.mark.parametrize("N", [1, 2, 4])
