@@ -107,6 +107,7 @@ constexpr int kDppXor1 = 0xB1;         // quad_perm(1,0,3,2)
 constexpr int kDppXor2 = 0x4E;         // quad_perm(2,3,0,1)
 constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8
 constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within each 16
+constexpr int kDppRowRor8 = 0x128;     // lane i <- lane i ^ 8 within each 16 (rotation by 8)
 
 __device__ inline float wave_max(float v) {
   v = fmaxf(v, __int_as_float(dpp_move<kDppXor1>(__float_as_int(v))));
@@ -1000,7 +1001,7 @@ __device__ __forceinline__ void res_mfma_chunk(v4i (&acc)[G][WN], const v4i (&wv
   for (int st = 0; st < S; ++st) res_mfma_step<GS, G, WN, S>(acc, wv, st, lb, pitch);
 }
 
-template <int G, int WN, int S, int WAVES, bool VEC4, bool DOT, bool SINGLE, bool PERM>
+template <int G, int WN, int S, int WAVES, bool VEC4, bool DOT, bool SINGLE, bool PERM, bool PAIR>
 __global__ void __launch_bounds__(64 * WAVES)
 gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
                 const int8_t *__restrict__ qp, int64_t N, const int32_t *__restrict__ row_sum,
@@ -1028,7 +1029,23 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
   const uint32_t pitch = static_cast<uint32_t>(res_pitch(K, S));
   const int64_t present = (rows - o_tile + 15) / 16;
   const int msub = static_cast<int>(present < ms ? present : ms);
-  const int mine = msub > wave ? (msub - wave + WAVES - 1) / WAVES : 0;  // subtiles wave, wave+WAVES, ...
+  // The tile's subtiles dealt to waves: round-robin (wave, wave + WAVES,
+  // ...), or with PAIR the first two of each wave adjacent (2*wave and
+  // 2*wave + 1, so that their outputs share 128-byte lines) and the rest
+  // round-robin from 2*WAVES.  A wave's subtiles are increasing, so those
+  // below msub are a prefix of its list.
+  auto local_sub = [&](int idx) __attribute__((always_inline)) -> int {
+    if constexpr (PAIR)
+      return idx < 2 ? 2 * wave + idx : 2 * WAVES + wave + WAVES * (idx - 2);
+    else
+      return wave + WAVES * idx;
+  };
+  int mine;
+  if constexpr (PAIR)
+    mine = (2 * wave < msub) + (2 * wave + 1 < msub) +
+           (msub > 2 * WAVES + wave ? (msub - 2 * WAVES - wave + WAVES - 1) / WAVES : 0);
+  else
+    mine = msub > wave ? (msub - wave + WAVES - 1) / WAVES : 0;
   const int groups = (mine + G - 1) / G;
   const int iters = groups * chunks;
 
@@ -1054,7 +1071,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
     const int gs = grp + 1 < groups ? G : mine - grp * G;
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
-      const uint32_t sub_off = static_cast<uint32_t>(16 * (wave + WAVES * (grp * G + gi))) * row_bytes + 64 * S * ch;
+      const uint32_t sub_off = static_cast<uint32_t>(16 * local_sub(grp * G + gi)) * row_bytes + 64 * S * ch;
 #pragma unroll
       for (int st = 0; st < S; ++st)
         wv[gi][st] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, gi < gs ? lane_off + sub_off + 64 * st : kOutOfRange,
@@ -1120,7 +1137,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
       for (int p = 0; p < kPieceLanes; ++p) bst[st][p] = __builtin_amdgcn_raw_buffer_load_b128(qbuf, step_goff(st, p), 0, 0);
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
-        const uint32_t sub_off = static_cast<uint32_t>(16 * (wave + WAVES * gi)) * row_bytes;
+        const uint32_t sub_off = static_cast<uint32_t>(16 * local_sub(gi)) * row_bytes;
         wa[gi][st] = __builtin_amdgcn_raw_buffer_load_b128(
             wbuf, gi < (groups > 1 ? G : mine) ? lane_off + sub_off + 64 * st : kOutOfRange, 0, 0);
       }
@@ -1177,7 +1194,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
   auto load_bias = [&](int grp) __attribute__((always_inline)) {
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
-      const uint32_t o = static_cast<uint32_t>(o_tile + 16 * static_cast<int64_t>(wave + WAVES * (grp * G + gi)) + 4 * kb);
+      const uint32_t o = static_cast<uint32_t>(o_tile + 16 * static_cast<int64_t>(local_sub(grp * G + gi)) + 4 * kb);
       if constexpr (VEC4) {
         bv[gi] = __builtin_amdgcn_raw_buffer_load_b128(bbuf, 4 * o, 0, 0);
       } else {
@@ -1201,22 +1218,67 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
     float tn[WN];  // the epilogue's t = ws * s, formed here so that only the epilogue waits for the scales
 #pragma unroll
     for (int n = 0; n < WN; ++n) tn[n] = ws * sn[n];
+    // The values of subtile gi for activation block n, scaled and biased.
+    auto values = [&](int gi, int n) __attribute__((always_inline)) {
+      v4i yv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = static_cast<float>(acc[gi][n][r]) * tn[n];
+        if constexpr (kBias) v = add_bias(v, __int_as_float(bv[gi][r]));
+        yv[r] = __float_as_int(v);
+      }
+      return yv;
+    };
+    // PAIR: the first group's first two subtiles are adjacent (32 output
+    // features).  Lane (li, kb) holds 4 features of each for activation row
+    // li; the second subtile's values move to lane li ^ 8 (a DPP rotation by
+    // 8 within each row of 16 lanes), and each store then writes 8 rows x
+    // 128 contiguous bytes: rows 0-7 of the block from lanes li < 8 (first
+    // subtile, their own values) and li >= 8 (second subtile, the moved
+    // values), then rows 8-15 the other way round.  Whole lines, where
+    // each 16 x 16 tile alone covers half lines.
+    int g_first = 0;
+    if constexpr (PAIR && VEC4 && G >= 2) {
+      if (grp == 0 && gs >= 2) {
+        g_first = 2;
+        const bool lo = li < 8;
+        const int64_t o0 = o_tile + 16 * static_cast<int64_t>(local_sub(0)) + 4 * kb;
+        const int64_t oa = o0 + (lo ? 0 : 16), ob = o0 + (lo ? 16 : 0);
+#pragma unroll
+        for (int n = 0; n < WN; ++n) {
+          const uint32_t ra = static_cast<uint32_t>((16 * n + (li & 7)) * ldy);
+          const uint32_t rb = static_cast<uint32_t>((16 * n + 8 + (li & 7)) * ldy);
+          const uint32_t offa = oa < rows ? 4 * (ra + static_cast<uint32_t>(oa)) : kOutOfRange;
+          const uint32_t offb = ob < rows ? 4 * (rb + static_cast<uint32_t>(ob)) : kOutOfRange;
+          const v4i y0 = values(0, n), y1 = values(1, n);
+          v4i x1;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x1[r] = dpp_move<kDppRowRor8>(y1[r]);
+          __builtin_amdgcn_raw_buffer_store_b128(lo ? y0 : x1, ybuf, offa, 0, kStreamStore);
+          __builtin_amdgcn_raw_buffer_store_b128(lo ? x1 : y0, ybuf, offb, 0, kStreamStore);
+          if constexpr (DOT) {
+            const v4i rs4 = v4i{rsn[n], rsn[n], rsn[n], rsn[n]};
+            const v4i d0 = acc[0][n] + rs4, d1 = acc[1][n] + rs4;
+            v4i xd;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xd[r] = dpp_move<kDppRowRor8>(d1[r]);
+            __builtin_amdgcn_raw_buffer_store_b128(lo ? d0 : xd, dbuf, offa, 0, kStreamStore);
+            __builtin_amdgcn_raw_buffer_store_b128(lo ? xd : d0, dbuf, offb, 0, kStreamStore);
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
+      if (gi < g_first) continue;
       const bool sub_ok = gi < gs;
-      const int64_t o = o_tile + 16 * static_cast<int64_t>(wave + WAVES * (grp * G + gi)) + 4 * kb;
+      const int64_t o = o_tile + 16 * static_cast<int64_t>(local_sub(grp * G + gi)) + 4 * kb;
 #pragma unroll
       for (int n = 0; n < WN; ++n) {
         const uint32_t base = static_cast<uint32_t>((16 * n + li) * ldy);  // element offset of this lane's row
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = static_cast<float>(acc[gi][n][r]) * tn[n];
-          if constexpr (kBias) v[r] = add_bias(v[r], __int_as_float(bv[gi][r]));
-        }
+        const v4i yv = values(gi, n);
         if constexpr (VEC4) {
           const uint32_t off = sub_ok && o < rows ? 4 * (base + static_cast<uint32_t>(o)) : kOutOfRange;
-          const v4i yv = {__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])};
           __builtin_amdgcn_raw_buffer_store_b128(yv, ybuf, off, 0, kStreamStore);
           if constexpr (DOT) {
             const v4i dv = acc[gi][n] + v4i{rsn[n], rsn[n], rsn[n], rsn[n]};
@@ -1226,7 +1288,7 @@ gemm_res_kernel(int tiles_m, int ms, const uint8_t *__restrict__ packed, int64_t
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t off = sub_ok && o + r < rows ? 4 * (base + static_cast<uint32_t>(o + r)) : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[r]), ybuf, off, 0, kStreamStore);
+            __builtin_amdgcn_raw_buffer_store_b32(yv[r], ybuf, off, 0, kStreamStore);
             if constexpr (DOT) __builtin_amdgcn_raw_buffer_store_b32(acc[gi][n][r] + rsn[n], dbuf, off, 0, kStreamStore);
           }
         }
@@ -2342,7 +2404,7 @@ int pick_stream_variant(int64_t rows, int64_t N) {
 // is about one block per compute unit.  Buffer offsets are 32-bit, so the
 // packed payload, the activation tile and the block's outputs must stay below
 // 2^31 bytes (else I2S_EKERNEL, and the automatic choice streams instead).
-template <int G, int WN, int S, int WAVES, bool VEC4, bool DOT, bool SINGLE, bool PERM>
+template <int G, int WN, int S, int WAVES, bool VEC4, bool DOT, bool SINGLE, bool PERM, bool PAIR>
 int launch_res_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
                     const ActWorkspace &ws, float *y, int32_t *dot_out, const float *bias, int64_t ldy,
                     int64_t tiles_m, int64_t ms,
@@ -2354,18 +2416,18 @@ int launch_res_inst(int64_t blocks, int64_t lds, const uint8_t *packed, int64_t 
   if (hipGetDevice(&dev) != hipSuccess) return I2S_EHIP;
   const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
   if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_res_kernel<G, WN, S, WAVES, VEC4, DOT, SINGLE, PERM>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_res_kernel<G, WN, S, WAVES, VEC4, DOT, SINGLE, PERM, PAIR>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kResMaxLds) != hipSuccess)
       return I2S_EHIP;
     attr_done.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((gemm_res_kernel<G, WN, S, WAVES, VEC4, DOT, SINGLE, PERM>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((gemm_res_kernel<G, WN, S, WAVES, VEC4, DOT, SINGLE, PERM, PAIR>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * WAVES), static_cast<size_t>(lds), stream, static_cast<int>(tiles_m), static_cast<int>(ms),
                      packed, rows, K, ws.q, N, ws.row_sum, ws.scale, y, dot_out, bias, ldy);
   return hip_status();
 }
 
-template <int G, int WN, int S, int WAVES, bool PERM = false>
+template <int G, int WN, int S, int WAVES, bool PERM = false, bool PAIR = false>
 int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const ActWorkspace &ws, float *y,
                    int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   constexpr int64_t BN = 16 * WN;
@@ -2390,7 +2452,7 @@ int launch_res_cfg(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, co
   const bool vec4 = (rows % 4) == 0 && (ldy % 4) == 0 && aligned16(y) && (!dot_out || aligned16(dot_out));
   const bool single = (K + 255) / 256 <= S;
 #define I2S_RES(V, D, SG)                                                                                         \
-  return launch_res_inst<G, WN, S, WAVES, V, D, SG, PERM>(blocks, lds, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, \
+  return launch_res_inst<G, WN, S, WAVES, V, D, SG, PERM, PAIR>(blocks, lds, packed, rows, K, N, ws, y, dot_out, bias, ldy, tiles_m, ms, \
                                                     stream)
   if (single) {
     if (vec4) {
@@ -2546,7 +2608,7 @@ int launch_wk(const uint8_t *packed, int64_t rows, int64_t K, int64_t N, const A
 // (G, WN, waves, steps) = (2,2,4,6), 11 = 7 with row-contiguous weight loads
 // permuted into MFMA lane order, 12-14 the same in 2-step chunks with groups
 // of 2, 4 and 3, 15 weight-resident (K <= 1536).
-constexpr int kGemmVariants = 15;
+constexpr int kGemmVariants = 18;
 
 int gemm_auto_variant(int64_t rows, int64_t K, int64_t N) {
   int variant;
@@ -2573,9 +2635,13 @@ int gemm_auto_variant(int64_t rows, int64_t K, int64_t N) {
     // Row-contiguous weight loads and 2-step chunks; the group size follows
     // the subtiles each wave holds (spw): whole groups of 2 with up to 2,
     // groups of 3 for 3 (8960 x 1536 at N = 512: 11.9 against 12.2 us with
-    // groups of 4), groups of 4 for 4-5, groups of 3 beyond.
+    // groups of 4), groups of 4 for 4-5, groups of 3 beyond.  Groups of 3
+    // store each wave's first two subtiles as whole 128-byte lines (variant
+    // 16: 8960 x 1536 at N = 512, 11.0 against 11.6 us; at N = 2048, 37.8
+    // against 39.4); with groups of 4 the pairing measured slower (N = 1024:
+    // 21.2 against 20.8).
     const int64_t spw = (ms7 + 7) / 8;
-    variant = spw <= 2 ? 12 : (spw == 3 ? 14 : (spw <= 5 ? 13 : 14));
+    variant = spw <= 2 ? 12 : (spw == 3 ? 16 : (spw <= 5 ? 13 : 16));
   } else if (fits7) {
     variant = 11;  // variant 7's tiles with row-contiguous weight loads: 4-6% faster, measured
   } else if (16 * res_pitch(K, 6) <= kResMaxLds) {
@@ -2605,6 +2671,9 @@ int launch_gemm(int variant, const uint8_t *packed, int64_t rows, int64_t K, int
     case 13: return launch_res_cfg<4, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     case 14: return launch_res_cfg<3, 4, 2, 8, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     case 15: return launch_wk<8>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 16: return launch_res_cfg<3, 4, 2, 8, true, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 17: return launch_res_cfg<2, 4, 2, 8, true, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
+    case 18: return launch_res_cfg<4, 4, 2, 8, true, true>(packed, rows, K, N, ws, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }

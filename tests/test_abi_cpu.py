@@ -149,9 +149,9 @@ def test_mul_mat_variant_choice():
     assert i2s.i2s_mul_mat_variant(256, 1536, 1024) == 15
     assert i2s.i2s_mul_mat_variant(8960, 1536, 256) == 15   # 9
     assert i2s.i2s_mul_mat_variant(4096, 1536, 512) == 15   # 16
-    assert i2s.i2s_mul_mat_variant(8960, 1536, 512) == 14   # 18: 3 per wave, groups of 3
+    assert i2s.i2s_mul_mat_variant(8960, 1536, 512) == 16   # 18: 3 per wave, groups of 3, first two paired
     assert i2s.i2s_mul_mat_variant(8960, 1536, 1024) == 13  # 35: 5 per wave, groups of 4
-    assert i2s.i2s_mul_mat_variant(8960, 1536, 2048) == 14  # 70: 9 per wave, groups of 3
+    assert i2s.i2s_mul_mat_variant(8960, 1536, 2048) == 16  # 70: 9 per wave, groups of 3, first two paired
     assert i2s.i2s_mul_mat_variant(8960, 2304, 512) == 11   # past the 2-step chunks' LDS limit: 3-step chunks
     assert i2s.i2s_mul_mat_variant(1536, 2048, 512) == 12   # K past the weight-resident kernel
     assert i2s.i2s_mul_mat_variant(2048, 1792, 512) == 12   # 4 subtiles, K = 1792: 1 per wave, groups of 2
