@@ -150,8 +150,8 @@ __device__ inline int wave_sum(int v) { return lanes_sum<64>(v); }
 // so the product is within 127.5 * 1.5 * 2^-23 < 2^-15 of the real quotient
 // and within 2^-15 + 2^-18 < 2^-14 of the IEEE one.  A product farther than
 // 2^-14 from every half-integer therefore lies strictly between the same two
-// half-integers as the IEEE quotient, and round-to-nearest-even of the
-// product (one v_rndne) equals roundf of that quotient.  A value nearer
+// half-integers as the IEEE quotient, and rounding the product to nearest
+// even gives roundf of that quotient.  A value nearer
 // than that to a tie takes the exact division and roundf instead.  The
 // branches are wave-uniform: one over the thread's values (no value of the
 // wave near a tie: the common case, every value rounded from its product),
@@ -177,6 +177,8 @@ __device__ inline void quantize_codes(const float4 (&v)[XPT], float s, uint32_t 
   float dmin = dm[0];
 #pragma unroll
   for (int i = 1; i < XPT; ++i) dmin = fminf(dmin, dm[i]);
+  // Near a tie a position's values are replaced by roundf of the quotient
+  // (already integers); everywhere else they stay products, rounded below.
   if (__any(dmin <= 0x1p-14f)) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
@@ -189,26 +191,25 @@ __device__ inline void quantize_codes(const float4 (&v)[XPT], float s, uint32_t 
         const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) rq[i][t] = roundf(e[t] / sd);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) rq[i][t] = __builtin_rintf(rq[i][t]);
       }
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < XPT; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) rq[i][t] = __builtin_rintf(rq[i][t]);
   }
+  // Clamp to [-127, 127], then round to nearest even and convert in one add:
+  // for |r| <= 127, r + 1.5 * 2^23 lies in [2^23, 2^24), where the spacing
+  // of floats is 1, so the sum is r rounded to nearest even (exact for the
+  // integers of the near-tie path), and its low byte is that integer's
+  // two's-complement byte (1.5 * 2^23 = 0x4B400000 has a zero low byte).
+  // Clamping first gives the same codes as rounding first: any value beyond
+  // +-127 (at most 127.5 here) rounds to +-127 or +-128 and is clamped to
+  // +-127.  fmaxf/fminf map NaN to -127, as the conversion path did.
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
-    uint32_t p4 = 0;
+    uint32_t b[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float r = fminf(fmaxf(rq[i][t], -127.0f), 127.0f);
-      p4 |= (static_cast<uint32_t>(static_cast<int>(r)) & 0xffu) << (8 * t);
-    }
-    packed[i] = p4;
+    for (int t = 0; t < 4; ++t) b[t] = __float_as_uint(fminf(fmaxf(rq[i][t], -127.0f), 127.0f) + 0x1.8p23f);
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // bytes: b0.0, b1.0, 0, 0
+    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);  // bytes: b2.0, b3.0, 0, 0
+    packed[i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);             // lo.0, lo.1, hi.0, hi.1
   }
 }
 
