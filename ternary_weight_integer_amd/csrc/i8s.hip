@@ -118,20 +118,35 @@ __device__ inline int quant(float v, float s) {
 // half-integers: both round to the integer nearest r, whatever the tie rule,
 // and rint(r) (ties to even, one instruction) gives q, already within +-127.
 // A group with any value nearer a tie takes the exact division for all 16.
+// The result is returned as floats whose low byte is q: x + 1.5 * 2^23, for
+// |x| <= 127.0001, lands where floats are one apart, so the sum is x rounded
+// to nearest even (ties to even, as rint; exact for the division path's
+// integers) and its low byte is that integer's two's-complement byte
+// (1.5 * 2^23 = 0x4B400000 has a zero low byte).
 constexpr float kTieMargin = 6.103515625e-05f;  // 2^-14
+constexpr float kRoundMagic = 0x1.8p23f;
 
-__device__ inline void quant16(const float (&v)[16], float s, float inv, int (&q)[16]) {
+__device__ inline void quant16(const float (&v)[16], float s, float inv, uint32_t (&qb)[16]) {
   bool near = false;
+  float r[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const float r = v[j] * inv;
-    near |= fabsf(__builtin_amdgcn_fractf(fabsf(r)) - 0.5f) <= kTieMargin;
-    q[j] = static_cast<int>(rintf(r));
+    r[j] = v[j] * inv;
+    near |= fabsf(__builtin_amdgcn_fractf(fabsf(r[j])) - 0.5f) <= kTieMargin;
   }
   if (near) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = quant(v[j], s);
+    for (int j = 0; j < 16; ++j) r[j] = static_cast<float>(quant(v[j], s));
   }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) qb[j] = __float_as_uint(r[j] + kRoundMagic);
+}
+
+// The low bytes of four dwords packed little-endian into one dword.
+__device__ inline uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // b0.0, b1.0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);  // b2.0, b3.0, 0, 0
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 // Four int8 values (each in [-127, 127]) packed little-endian into one dword.
@@ -664,7 +679,7 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(I8S_KARGS) {
         const int n = n0 + wn * WTN + 16 * fn + li;
         const bool n_ok = n < N;
         float v[16];
-        int q[16];
+        uint32_t q[16];  // q in the low byte of each
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -674,7 +689,8 @@ __global__ void __launch_bounds__(kThreads) i8s_mm_mfma_kernel(I8S_KARGS) {
         if (a.vec) {
           v4i pk;
 #pragma unroll
-          for (int b = 0; b < 4; ++b) pk[b] = pack4(q[4 * b], q[4 * b + 1], q[4 * b + 2], q[4 * b + 3]);
+          for (int b = 0; b < 4; ++b)
+            pk[b] = static_cast<int>(pack_low_bytes(q[4 * b], q[4 * b + 1], q[4 * b + 2], q[4 * b + 3]));
           const uint32_t off = n_ok && og < OC ? row + og : kOutOfRange;
           __builtin_amdgcn_raw_buffer_store_b128(pk, obuf, off, 0, 0);
           if (a.dot) {
