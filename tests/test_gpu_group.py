@@ -114,6 +114,17 @@ def test_group_every_kernel_and_variant(K):
             check_group(ws, b, x, K, kernel=kern, variant=var)
 
 
+@pytest.mark.parametrize("variant", [0, 16, 17, 18])
+def test_group_paired_subtiles_with_bias(variant):
+    """Resident GEMM variants that deal each wave two adjacent subtiles and
+    store them as whole lines, with biases: at N = 512 each block of the
+    2048-row projection holds 4 subtiles (waves 0 and 1 a pair each); the
+    1030-row projection (rows % 4 != 0) takes the per-subtile stores with the
+    same subtile deal and a ragged last subtile.  Every output checked."""
+    ws, b, x = make_group(91, [2048, 1030], 256, 512, [True, True])
+    check_group(ws, b, x, 256, kernel=2, variant=variant)
+
+
 def test_bias_with_negative_zero_and_zero_rows():
     K, N = 256, 2
     rng = np.random.default_rng(53)

@@ -286,13 +286,15 @@ def test_all_gemm_variants_prefill_shape():
 
 def test_gemm_variants_many_groups_per_wave():
     """N = 2048 on the gate shape: 9 subtiles per wave, so every resident
-    variant runs several groups and a short last one (groups of 2, 3 and 4);
-    every output checked."""
+    variant runs several groups and a short last one (groups of 2, 3 and 4;
+    16-18 with each wave's first two subtiles paired for whole-line stores,
+    and cached stores because the waves hold several groups); every output
+    checked."""
     case = workloads.prefill_gate_case(seed=5, N=2048)
     pnp = oracle.pack(case.w, case.ws)
     pg = gpu_pack(case.w, case.ws)
     exp = oracle.mul_mat_sliced(pnp, case.rows, case.K, case.x, with_dot=True)
-    for v in (0, 11, 12, 13, 14):
+    for v in (0, 11, 12, 13, 14, 16, 17, 18):
         check_mul_mat(case, kernel=2, variant=v, packed_gpu=pg, packed_np=pnp, expected=exp)
 
 
