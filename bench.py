@@ -470,7 +470,8 @@ def bench_encoder(args, torch):
 
 def bench_w8a8(args, torch):
     """Per-channel W8A8: quantize the activation rows and contract (two
-    launches); weight copies rotate through >= 512 MiB as for I2_S."""
+    launches, or for M <= 4 one launch that does both); weight copies rotate
+    through >= 512 MiB as for I2_S."""
     from ternary_weight_integer_amd import w8a8, workloads
     dev = torch.device("cuda:0")
     case = workloads.w8a8_case(args.workload.split("_", 1)[1])
@@ -485,6 +486,7 @@ def bench_w8a8(args, torch):
     asc = torch.empty(M, dtype=torch.float32, device=dev)
     w8a8.w8a8_quantize_act(x, aq, asc)
     variant = w8a8.w8a8_mul_mat_variant(OC, K, M)
+    fused = variant == 11  # the step is one launch: quantizer and contraction together
 
     def step(i):
         wq, wsc = copies[i % R]
@@ -492,7 +494,10 @@ def bench_w8a8(args, torch):
 
     def contraction(i):
         wq, wsc = copies[i % R]
-        w8a8.w8a8_matmul(wq, wsc, aq, asc, y=y)
+        if fused:
+            w8a8.w8a8_mul_mat(wq, wsc, x, workspace=ws, y=y)
+        else:
+            w8a8.w8a8_matmul(wq, wsc, aq, asc, y=y)
 
     for i in range(args.warmup):
         step(i)
@@ -530,7 +535,8 @@ def bench_w8a8(args, torch):
     kern_us = ev[1].elapsed_time(ev[2]) * 1e3 / n_kern
     ops = 2 * OC * K * M
     wbytes = OC * K + 4 * OC
-    alg_bytes = wbytes + M * K + 4 * M + 4 * M * OC
+    # the dominant launch's operands: F32 rows for the fused launch, else the codes and scales
+    alg_bytes = wbytes + (4 * M * K if fused else M * K + 4 * M) + 4 * M * OC
     out = {
         "metric": METRIC,
         "value": round(wbytes / (step_ms * 1e-3) / 1e9, 3),
@@ -550,8 +556,11 @@ def bench_w8a8(args, torch):
         "int8_tops": round(ops / (step_ms * 1e-3) / 1e12, 4),
         "wall_s": round(wall, 4),
     }
-    kname = {9: "i8s_mm_skinny_kernel", 10: "w8a8_res_kernel"}.get(variant, "i8s_mm_mfma_kernel") + \
-        " (F32 dequantizing epilogue)"
+    if fused:
+        kname = "w8a8_gemv_fused_kernel (activation quantizer, int8 GEMV and F32 dequantizing epilogue in one launch)"
+    else:
+        kname = {9: "i8s_mm_skinny_kernel", 10: "w8a8_res_kernel"}.get(variant, "i8s_mm_mfma_kernel") + \
+            " (F32 dequantizing epilogue)"
     if M >= 64:
         achieved = ops / (kern_us * 1e-6) / 1e12
         out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_MFMA_PEAK_TOPS,

@@ -54,17 +54,23 @@ int w8a8_quantize_act(const float *x, int64_t M, int64_t K,
  * below 2^29 - 2^14.  variant 0 = automatic, else an MFMA tile configuration
  * 2..i8s_variants() of the I8_S contraction, or 10: the activation-resident
  * kernel (64 activation rows in LDS, the int8 weights streamed; needs
- * K % 64 == 0 and K <= 2544).  Errors: I2S_EINVAL, I2S_EALIGN (K),
- * I2S_ERANGE, I2S_EKERNEL (variant, or variant 10 with K it does not take),
- * I2S_EHIP. */
+ * K % 64 == 0 and K <= 2544).  Variant 11 quantizes F32 rows itself and is
+ * refused here.  Errors: I2S_EINVAL, I2S_EALIGN (K), I2S_ERANGE, I2S_EKERNEL
+ * (variant, or variant 10 with K it does not take), I2S_EHIP. */
 int w8a8_matmul(const int8_t *wq, const float *wscale, int64_t OC, int64_t K,
                 const int8_t *aq, const float *ascale, int64_t M,
                 float *y, int32_t *dot_out, int variant, void *stream);
 
 /* The whole op on F32 activations x[M][K] (16-byte aligned): quantize the
  * rows into `workspace` (>= w8a8_act_workspace_bytes(M, K), 256-byte
- * aligned, overwritten), then w8a8_matmul.  Errors as above plus
- * I2S_EWORKSPACE. */
+ * aligned, overwritten: the codes q[M][K], then at the next multiple of 256
+ * bytes the scales, as w8a8_quantize_act writes them), then w8a8_matmul.
+ * For 1 <= M <= 4 and K <= 9216 the automatic choice is variant 11, which
+ * does both in one launch (every workgroup quantizes the rows itself, with
+ * the same operations, then runs an int8 GEMV over its weight rows); the
+ * results, and what the workspace holds afterwards, are those of the two
+ * launches bit for bit.  Errors as above plus I2S_EWORKSPACE, and
+ * I2S_EKERNEL for variant 11 outside 1 <= M <= 4, K <= 9216. */
 int w8a8_mul_mat(const int8_t *wq, const float *wscale, int64_t OC, int64_t K,
                  const float *x, int64_t M, void *workspace, size_t workspace_bytes,
                  float *y, void *stream);
@@ -74,11 +80,13 @@ int w8a8_mul_mat_ex(const int8_t *wq, const float *wscale, int64_t OC, int64_t K
                     const float *x, int64_t M, void *workspace, size_t workspace_bytes,
                     float *y, int32_t *dot_out, int variant, void *stream);
 
-/* The tile variant the automatic choice takes for this shape. */
+/* The variant the automatic choice of w8a8_mul_mat takes for this shape:
+ * 11 (the fused decode launch) for 1 <= M <= 4 and K <= 9216 (K % 16 == 0),
+ * else the contraction's choice. */
 int w8a8_mul_mat_variant(int64_t OC, int64_t K, int64_t M);
 
-/* The largest valid variant number of w8a8_matmul (variant 1 and variants
- * beyond it are refused). */
+/* The largest valid variant number (variant 1 and variants beyond it are
+ * refused; w8a8_matmul also refuses 11). */
 int w8a8_variants(void);
 
 #ifdef __cplusplus

@@ -1240,10 +1240,158 @@ bool launch_act_reg_fit(const float *x, int64_t M, int64_t K, int8_t *q, float *
 }
 
 // ---------------------------------------------------------------------------
+// W8A8 decode in one launch: the activation quantizer and an int8 GEMV for
+// M <= 4 activation rows (W8A8 variant 11, F32-input entry points only).
+//
+// Every workgroup quantizes the M rows itself, with the operations of
+// w8a8_quant_rows_kernel<false> ("Experiment - int8 W8A8 path (the practical
+// default)", Implementation): mx = max(1e-9, max|x|), inv = 127/mx, code =
+// w8a8_round_act(x, inv), scale mx/127 -- so the codes and scales are those
+// of the two-launch path bit for bit -- into LDS.  It then contracts its
+// R = T/L weight rows: L lanes per row, lane j holding the row's 16-byte
+// chunks j, j + L, ..., four v_dot4 (int8 x int8 -> int32) per chunk and
+// activation row, a sum over the row's L lanes (integer, exact in any
+// order), and the epilogue y = (ascale * wscale) * (float)C, the order of
+// the page's dequantization.  The activations are loaded before the weights
+// (loads retire in order: waiting for x does not wait for the weight
+// stream), and every load is unconditional: chunks past K read zeros (their
+// products are 0 whatever the LDS bytes they meet), rows past OC read zeros
+// and are never stored.  Workgroup 0 also writes the codes and scales where
+// the two-launch path's quantizer would.
+
+// Sum over each group of L consecutive lanes (L a power of two up to 64),
+// in every lane of the group.
+template <int L>
+__device__ inline int lanes_sum(int v) {
+  static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "power-of-two lane group");
+  if constexpr (L >= 2) v += dpp_move<0xB1>(v);   // quad_perm(1,0,3,2)
+  if constexpr (L >= 4) v += dpp_move<0x4E>(v);   // quad_perm(2,3,0,1)
+  if constexpr (L >= 8) v += dpp_move<0x141>(v);  // row_half_mirror
+  if constexpr (L >= 16) v += dpp_move<0x140>(v); // row_mirror
+  if constexpr (L == 32) {
+    const int lo = __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16);
+    const int hi = __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+    v = (threadIdx.x & 32) ? hi : lo;
+  }
+  if constexpr (L == 64)
+    v = (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+        (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+  return v;
+}
+
+template <int NC, int L, int CPL, int XPT, int T>
+__global__ void __launch_bounds__(T) w8a8_gemv_fused_kernel(const int8_t *__restrict__ wq, const float *__restrict__ x,
+                                                            int OC, int K, const float *__restrict__ wscale,
+                                                            float *__restrict__ y, int32_t *__restrict__ dot,
+                                                            int8_t *__restrict__ aq, float *__restrict__ ascale) {
+  constexpr int W = T / 64;
+  constexpr int R = T / L;  // weight rows per workgroup
+  constexpr int kRowBytes = (4 * T * XPT > 16 * L * CPL) ? 4 * T * XPT : 16 * L * CPL;
+  __shared__ __attribute__((aligned(16))) int8_t lq[NC][kRowBytes];
+  __shared__ float red[NC][W];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rl = tid / L, j = tid % L;
+  const int row0 = static_cast<int>(blockIdx.x) * R;
+  const int K4 = K >> 2;
+
+  // The activation rows (float4 i of row c at thread i % T, slot i / T).
+  const __amdgpu_buffer_rsrc_t xbuf = buffer_of(x, static_cast<uint32_t>(NC * K * 4));
+  float4 xv[NC][XPT];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int idx = tid + T * i;
+      const v4i t = __builtin_amdgcn_raw_buffer_load_b128(
+          xbuf, idx < K4 ? static_cast<uint32_t>(16 * (c * K4 + idx)) : kOutOfRange, 0, 0);
+      xv[c][i] = make_float4(__int_as_float(t[0]), __int_as_float(t[1]), __int_as_float(t[2]), __int_as_float(t[3]));
+    }
+  // This lane's weight chunks and its row's weight scale.
+  const __amdgpu_buffer_rsrc_t wbuf =
+      buffer_of(wq + static_cast<int64_t>(row0) * K, static_cast<uint32_t>((OC - row0) * K));
+  v4i wv[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int ch = j + L * i;
+    wv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+        wbuf, 16 * ch < K ? static_cast<uint32_t>(rl * K + 16 * ch) : kOutOfRange, 0, 0);
+  }
+  const __amdgpu_buffer_rsrc_t sbuf = buffer_of(wscale + row0, static_cast<uint32_t>(4 * (OC - row0)));
+  const float wsn = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(sbuf, static_cast<uint32_t>(4 * rl), 0, 0));
+  __builtin_amdgcn_sched_barrier(0);  // every load is issued before the first use of x
+
+  // Row maxima over the workgroup.
+  float mx[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float m = 1e-9f;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(xv[c][i].x), fabsf(xv[c][i].y)), fmaxf(fabsf(xv[c][i].z), fabsf(xv[c][i].w))));
+    m = wave_max(m);
+    if (lane == 0) red[c][wave] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float m = red[c][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) m = fmaxf(m, red[c][w]);
+    mx[c] = m;
+  }
+  // Codes into LDS (and, from workgroup 0, where the quantizer writes them).
+  const bool first = blockIdx.x == 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const float inv = 127.0f / mx[c];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int idx = tid + T * i;
+      if (idx < K4) {
+        const uint32_t b0 = static_cast<uint32_t>(w8a8_round_act(xv[c][i].x, inv)) & 0xFFu;
+        const uint32_t b1 = static_cast<uint32_t>(w8a8_round_act(xv[c][i].y, inv)) & 0xFFu;
+        const uint32_t b2 = static_cast<uint32_t>(w8a8_round_act(xv[c][i].z, inv)) & 0xFFu;
+        const uint32_t b3 = static_cast<uint32_t>(w8a8_round_act(xv[c][i].w, inv)) & 0xFFu;
+        const uint32_t q4 = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        *reinterpret_cast<uint32_t *>(&lq[c][4 * idx]) = q4;
+        if (first) reinterpret_cast<uint32_t *>(aq + static_cast<int64_t>(c) * K)[idx] = q4;
+      }
+    }
+    if (first && tid == 0) ascale[c] = mx[c] / 127.0f;
+  }
+  __syncthreads();
+
+  // Contraction: four v_dot4 per chunk and activation row.
+  int acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = 0;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int ch = j + L * i;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const v4i b = *reinterpret_cast<const v4i *>(&lq[c][16 * ch]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[c] = __builtin_amdgcn_sdot4(wv[i][e], b[e], acc[c], false);
+    }
+  }
+  const int row = row0 + rl;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int C = lanes_sum<L>(acc[c]);
+    if (j == c && row < OC) {
+      const float as = mx[c] / 127.0f;
+      y[static_cast<int64_t>(c) * OC + row] = (as * wsn) * static_cast<float>(C);
+      if (dot) dot[static_cast<int64_t>(c) * OC + row] = C;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 constexpr int kVariants = 9;
-constexpr int kW8a8Variants = 10;  // the I8_S variants, and 10: activation-resident (W8A8 only)
+constexpr int kW8a8Variants = 11;  // the I8_S variants, 10: activation-resident, 11: fused decode (W8A8 only)
 constexpr int64_t kW8a8ResMaxLds = 160 * 1024;
 
 // Variant 10 needs K a multiple of 64 and the 64-row activation tile (pitch
@@ -1512,6 +1660,47 @@ namespace {
 // kernel while it wins, the activation-resident kernel from 128 rows where K
 // fits it (gate 8960 x 1536, M = 512: 22 against 31 us with weights from
 // HBM), the tile kernels otherwise.
+// W8A8 variant 11: lanes per weight row by K (16 for K <= 2048, 32 to 4096,
+// 64 to 9216), activation rows NC = M <= 4.  Measured on MI355X (weights
+// from HBM): gate 8960 x 1536 at M = 1 takes 4.14 us with 16 lanes and 256
+// threads (4.25-4.50 with 8 or 32 lanes, or 512 threads); the down
+// projection 1536 x 8960 4.37 us at M = 1 and 7.9 at M = 4 with 64 lanes and
+// 512 threads, against 5.2 and 10.7 with 256 threads and 4.8 and 9.7 with
+// 32 lanes.
+constexpr int64_t kW8a8FusedMaxM = 4;
+constexpr int kW8a8FusedMaxK = 9216;
+bool w8a8_fused_fits(int64_t K, int64_t M) { return M >= 1 && M <= kW8a8FusedMaxM && K <= kW8a8FusedMaxK; }
+
+template <int KMAX, int NC, int L, int CPL, int XPT, int T>
+int launch_w8a8_fused_cfg(const int8_t *wq, const float *wscale, int64_t OC, int64_t K, const float *x, float *y,
+                          int32_t *dot, int8_t *aq, float *as, hipStream_t stream) {
+  static_assert(4 * T * XPT >= KMAX && 16 * L * CPL >= KMAX, "the threads hold a row of KMAX values, the lanes its chunks");
+  constexpr int R = T / L;
+  const int64_t blocks = (OC + R - 1) / R;
+  hipLaunchKernelGGL((w8a8_gemv_fused_kernel<NC, L, CPL, XPT, T>), dim3(static_cast<uint32_t>(blocks)), dim3(T), 0,
+                     stream, wq, x, static_cast<int>(OC), static_cast<int>(K), wscale, y, dot, aq, as);
+  return hip_status();
+}
+
+template <int NC>
+int launch_w8a8_fused_nc(const int8_t *wq, const float *wscale, int64_t OC, int64_t K, const float *x, float *y,
+                         int32_t *dot, int8_t *aq, float *as, hipStream_t stream) {
+  if (K <= 1536) return launch_w8a8_fused_cfg<1536, NC, 16, 6, 2, 256>(wq, wscale, OC, K, x, y, dot, aq, as, stream);
+  if (K <= 2048) return launch_w8a8_fused_cfg<2048, NC, 16, 8, 2, 256>(wq, wscale, OC, K, x, y, dot, aq, as, stream);
+  if (K <= 4096) return launch_w8a8_fused_cfg<4096, NC, 32, 8, 4, 256>(wq, wscale, OC, K, x, y, dot, aq, as, stream);
+  return launch_w8a8_fused_cfg<kW8a8FusedMaxK, NC, 64, 9, 5, 512>(wq, wscale, OC, K, x, y, dot, aq, as, stream);
+}
+
+int launch_w8a8_fused(const int8_t *wq, const float *wscale, int64_t OC, int64_t K, const float *x, int64_t M,
+                      float *y, int32_t *dot, int8_t *aq, float *as, hipStream_t stream) {
+  switch (M) {
+    case 1: return launch_w8a8_fused_nc<1>(wq, wscale, OC, K, x, y, dot, aq, as, stream);
+    case 2: return launch_w8a8_fused_nc<2>(wq, wscale, OC, K, x, y, dot, aq, as, stream);
+    case 3: return launch_w8a8_fused_nc<3>(wq, wscale, OC, K, x, y, dot, aq, as, stream);
+    default: return launch_w8a8_fused_nc<4>(wq, wscale, OC, K, x, y, dot, aq, as, stream);
+  }
+}
+
 int w8a8_auto_variant(int64_t OC, int64_t K, int64_t M) {
   if (skinny_wins(OC, M)) return 9;
   if (OC <= 64) return 6;
@@ -1552,7 +1741,14 @@ extern "C" int w8a8_quantize_act(const float *x, int64_t M, int64_t K, int8_t *q
   return hip_status();
 }
 
-extern "C" int w8a8_mul_mat_variant(int64_t OC, int64_t K, int64_t M) { return w8a8_auto_variant(OC, K, M); }
+// The automatic choice of the F32-input entry points: the fused decode
+// kernel for M <= 4 (K % 16 == 0 as the contraction needs), else the
+// contraction's own choice after a separate quantizer launch.
+int w8a8_mul_mat_auto(int64_t OC, int64_t K, int64_t M) {
+  return (w8a8_fused_fits(K, M) && K % 16 == 0) ? 11 : w8a8_auto_variant(OC, K, M);
+}
+
+extern "C" int w8a8_mul_mat_variant(int64_t OC, int64_t K, int64_t M) { return w8a8_mul_mat_auto(OC, K, M); }
 
 extern "C" int w8a8_variants(void) { return kW8a8Variants; }
 
@@ -1565,7 +1761,8 @@ extern "C" int w8a8_matmul(const int8_t *wq, const float *wscale, int64_t OC, in
   if (K == 0 || K % 16 != 0) return I2S_EALIGN;
   if (OC * K >= kMaxBytes || M * K >= kMaxBytes || M * OC >= kMaxBytes / 4) return I2S_ERANGE;
   if (OC > kMaxBytes || M > kMaxBytes) return I2S_ERANGE;  // sizes go to the kernels as 32-bit values
-  if (variant < 0 || variant == 1 || variant > kW8a8Variants) return I2S_EKERNEL;
+  // variant 11 quantizes F32 rows itself: only the F32-input entry points take it
+  if (variant < 0 || variant == 1 || variant == 11 || variant > kW8a8Variants) return I2S_EKERNEL;
   if (variant == 10 && !w8a8_res_fits(K)) return I2S_EKERNEL;
   if (variant == 0) variant = w8a8_auto_variant(OC, K, M);
   if (OC == 0 || M == 0) return I2S_OK;
@@ -1613,6 +1810,12 @@ extern "C" int w8a8_mul_mat_ex(const int8_t *wq, const float *wscale, int64_t OC
   if (OC > kMaxBytes || M > kMaxBytes) return I2S_ERANGE;  // sizes go to the kernels as 32-bit values
   if (variant < 0 || variant == 1 || variant > kW8a8Variants) return I2S_EKERNEL;
   if (variant == 10 && !w8a8_res_fits(K)) return I2S_EKERNEL;
+  if (variant == 11 && !w8a8_fused_fits(K, M)) return I2S_EKERNEL;
+  if (variant == 0) variant = w8a8_mul_mat_auto(OC, K, M);
+  if (variant == 11) {
+    if (OC == 0) return w8a8_quantize_act(x, M, K, aq, as, stream);  // nothing to contract; the codes as ever
+    return launch_w8a8_fused(wq, wscale, OC, K, x, M, y, dot_out, aq, as, static_cast<hipStream_t>(stream));
+  }
   int st = w8a8_quantize_act(x, M, K, aq, as, stream);
   if (st != I2S_OK) return st;
   return w8a8_matmul(wq, wscale, OC, K, aq, as, M, y, dot_out, variant, stream);

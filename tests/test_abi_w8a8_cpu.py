@@ -28,10 +28,13 @@ def test_workspace_and_variant():
     assert w8a8.w8a8_act_workspace_bytes(-1, 16) == 0
     for shape in [(8960, 1536, 512), (1536, 8960, 1), (256, 1536, 64), (32, 64, 1000)]:
         assert 2 <= w8a8.w8a8_mul_mat_variant(*shape) <= w8a8.w8a8_variants()
-    assert w8a8.w8a8_variants() == i8s.i8s_variants() + 1  # variant 10: W8A8 only
+    assert w8a8.w8a8_variants() == i8s.i8s_variants() + 2  # variants 10 and 11: W8A8 only
     assert w8a8.w8a8_mul_mat_variant(8960, 1536, 512) == 10   # activation-resident
     assert w8a8.w8a8_mul_mat_variant(1536, 8960, 512) == 7    # K beyond its LDS tile
-    assert w8a8.w8a8_mul_mat_variant(8960, 1536, 1) == 9      # skinny
+    assert w8a8.w8a8_mul_mat_variant(8960, 1536, 1) == 11     # fused decode kernel
+    assert w8a8.w8a8_mul_mat_variant(1536, 8960, 4) == 11
+    assert w8a8.w8a8_mul_mat_variant(8960, 1536, 5) == 9      # skinny, after the quantizer's launch
+    assert w8a8.w8a8_mul_mat_variant(64, 9232, 1) == 9        # K beyond the fused kernel's registers
 
 
 def _mm(wq=FAKE, ws=FAKE, OC=64, K=64, aq=FAKE, as_=FAKE, M=8, y=FAKE, dot=None, variant=0):
@@ -67,3 +70,16 @@ def test_mul_mat_and_quantizers_reject_on_host():
     assert L.w8a8_quantize_weight(None, 4, 16, FAKE, FAKE, None) == i2s.I2S_EINVAL
     assert L.w8a8_quantize_act(FAKE, -1, 16, FAKE, FAKE, None) == i2s.I2S_EINVAL
     assert L.w8a8_quantize_act(FAKE, 1 << 20, 4096, FAKE, FAKE, None) == i2s.I2S_ERANGE
+
+
+def test_fused_variant_refused_on_host():
+    """Variant 11 (the fused decode kernel) takes 1 <= M <= 4 and K <= 9216,
+    and only on the F32-input entry point; the refusals come before any
+    launch."""
+    L = w8a8.lib()
+    ex = lambda M, K, v: L.w8a8_mul_mat_ex(FAKE, FAKE, 64, K, FAKE, M, FAKE, 1 << 24, FAKE, None, v, None)
+    assert ex(5, 64, 11) == i2s.I2S_EKERNEL
+    assert ex(0, 64, 11) == i2s.I2S_EKERNEL
+    assert ex(1, 9232, 11) == i2s.I2S_EKERNEL
+    assert ex(1, 40, 11) == i2s.I2S_EALIGN
+    assert _mm(variant=11) == i2s.I2S_EKERNEL

@@ -118,8 +118,10 @@ SHAPES = [(70, 128, 37), (64, 64, 64), (200, 96, 129), (16, 16, 1), (1, 48, 5), 
 
 
 def variant_takes(v: int, K: int) -> bool:
-    """Variant 10 (activation-resident) takes K % 64 == 0 up to 2544."""
-    return v != 10 or (K % 64 == 0 and K <= 2544)
+    """Variant 10 (activation-resident) takes K % 64 == 0 up to 2544;
+    variant 11 (the fused decode kernel) quantizes F32 rows itself, so the
+    contraction on quantized rows never takes it."""
+    return v != 11 and (v != 10 or (K % 64 == 0 and K <= 2544))
 
 
 @pytest.mark.parametrize("OC,K,M", SHAPES + [(2048, 1536, 256), (1536, 2496, 130), (513, 1600, 64), (4100, 640, 130),
@@ -269,3 +271,75 @@ def test_graph_replay_matches_eager(OC, K, M):
         torch.cuda.synchronize()
         g.replay()
         assert np.array_equal(bits(host(y)), bits(eager)), f"replay {r}"
+
+
+# The fused decode kernel (W8A8 variant 11: the rows quantized inside the
+# contraction's launch, M <= 4): every K class of its launch configuration
+# (up to 1536, 2048, 4096 and 9216), OC ragged against its 16-, 8- and 4-row
+# workgroups, K not a multiple of 64, and every M from 1 to 4.
+FUSED_SHAPES = [(8960, 1536, 1), (37, 16, 1), (513, 48, 2), (1000, 2048, 3), (257, 4096, 4), (100, 2064, 1),
+                (65, 9216, 2), (1536, 8960, 4), (17, 1552, 3)]
+
+
+def check_fused(wq, ws, x, tag):
+    """The fused path (automatic and forced) against the oracle: y and C bit
+    for bit, and the codes and scales where the quantizer would leave them."""
+    OC, K = wq.shape
+    M = x.shape[0]
+    rq, rs = oracle.w8a8_quantize_act(x)
+    rd, rc = oracle.w8a8_matmul(rq, rs, wq, ws, with_c=True)
+    assert w8a8.w8a8_mul_mat_variant(OC, K, M) == 11
+    for v in (0, 11):
+        say(f"w8a8_mul_mat_ex fused {tag} OC={OC} K={K} M={M} variant={v}")
+        wsp = w8a8.new_workspace(M, K, DEV)
+        y, c = w8a8.w8a8_mul_mat_ex(dev(wq), dev(ws), dev(x), workspace=wsp, dot_out=True, variant=v)
+        assert np.array_equal(host(c), rc), v
+        assert np.array_equal(bits(host(y)), bits(rd)), v
+        wh = host(wsp)
+        assert np.array_equal(wh[: M * K].view(np.int8).reshape(M, K), rq), v
+        so = -(-M * K // 256) * 256
+        assert np.array_equal(wh[so: so + 4 * M].view(np.uint32), bits(rs)), v
+    y2 = w8a8.w8a8_mul_mat(dev(wq), dev(ws), dev(x))
+    assert np.array_equal(bits(host(y2)), bits(rd)), "without dot_out"
+
+
+@pytest.mark.parametrize("OC,K,M", FUSED_SHAPES)
+def test_fused_decode(OC, K, M):
+    rng = np.random.default_rng(OC + 7 * K + M)
+    wq = rng.integers(-127, 128, size=(OC, K), dtype=np.int8)
+    ws = rng.uniform(1e-4, 0.05, size=OC).astype(np.float32)
+    x = rng.normal(0, 1, size=(M, K)).astype(np.float32)
+    x[:, rng.integers(0, K, size=max(1, K // 100))] *= 20
+    check_fused(wq, ws, x, "random")
+
+
+def test_fused_decode_near_ties_and_full_scale():
+    rows = near_tie_rows((3.3, 0.77, 100.0))
+    K = -(-max(r.size for r in rows) // 16) * 16
+    x = np.zeros((3, K), np.float32)
+    for i, r in enumerate(rows):
+        x[i, : r.size] = r
+    rng = np.random.default_rng(11)
+    wq = rng.integers(-127, 128, size=(300, K), dtype=np.int8)
+    check_fused(wq, rng.uniform(1e-4, 0.05, size=300).astype(np.float32), x, "near ties")
+    # the largest accumulators: every product 127 * 127 (or its negative)
+    K = 8192
+    wq = np.full((64, K), 127, np.int8)
+    wq[1::2] = -127
+    x = np.full((2, K), 3.0, np.float32)
+    x[1] = -3.0
+    check_fused(wq, np.full(64, 0.001, np.float32), x, "full scale")
+
+
+def test_fused_decode_refusals():
+    wq = torch.zeros((64, 64), dtype=torch.int8, device=DEV)
+    ws = torch.ones(64, dtype=torch.float32, device=DEV)
+    for M, K in [(5, 64), (1, 9232)]:
+        w = torch.zeros((64, K), dtype=torch.int8, device=DEV)
+        with pytest.raises(i2s.I2SError) as ei:
+            w8a8.w8a8_mul_mat_ex(w, ws, torch.zeros((M, K), dtype=torch.float32, device=DEV), variant=11)
+        assert ei.value.status == i2s.I2S_EKERNEL
+    aq = torch.zeros((1, 64), dtype=torch.int8, device=DEV)
+    with pytest.raises(i2s.I2SError) as ei:
+        w8a8.w8a8_matmul(wq, ws, aq, torch.ones(1, dtype=torch.float32, device=DEV), variant=11)
+    assert ei.value.status == i2s.I2S_EKERNEL
