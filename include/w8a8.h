@@ -15,7 +15,8 @@
  * Weights are stored wq[OC][K] (K contiguous, like the I2_S and I8_S
  * weights); the page transposes them for its NPU, which changes no value.
  * The contraction is the int8-MFMA tile kernel of the I8_S path with an F32
- * epilogue.
+ * epilogue (an activation-resident kernel from 128 rows); at one to four
+ * rows the whole op is one launch that quantizes and runs an int8 GEMV.
  *
  * Conventions as in i2s.h: device pointers, a hipStream_t or NULL, host-side
  * validation, no synchronization or allocation, I2S_* status codes.

@@ -111,7 +111,8 @@ def w8a8_matmul(wq: torch.Tensor, wscale: torch.Tensor, aq: torch.Tensor, ascale
 
 def w8a8_mul_mat_ex(wq: torch.Tensor, wscale: torch.Tensor, x: torch.Tensor, workspace=None, y=None, dot_out=None,
                     variant: int = 0, stream=None):
-    """The whole op on F32 x[M][K]: quantize the rows, contract, dequantize."""
+    """The whole op on F32 x[M][K]: quantize the rows, contract, dequantize
+    (one launch for 1 <= M <= 4: variant 11)."""
     OC, K = wq.shape
     M = x.shape[0]
     if x.dim() != 2 or x.shape[1] != K:
