@@ -343,3 +343,21 @@ def test_fused_decode_refusals():
     with pytest.raises(i2s.I2SError) as ei:
         w8a8.w8a8_matmul(wq, ws, aq, torch.ones(1, dtype=torch.float32, device=DEV), variant=11)
     assert ei.value.status == i2s.I2S_EKERNEL
+
+
+def test_fused_decode_zero_row_on_a_stream():
+    """A zero activation row through the fused launch: its maximum is the
+    1e-9 floor, every code 0, every output +0; on a side stream."""
+    rng = np.random.default_rng(5)
+    w = rng.normal(0, 1, size=(200, 320)).astype(np.float32)
+    x = rng.normal(0, 1, size=(3, 320)).astype(np.float32)
+    x[1] = 0
+    wq, ws = oracle.w8a8_quantize_weight(w)
+    assert w8a8.w8a8_mul_mat_variant(200, 320, 3) == 11
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = w8a8.w8a8_mul_mat(dev(wq), dev(ws), dev(x), stream=s)
+    s.synchronize()
+    yh = host(y)
+    assert not bits(yh[1]).any()
+    assert np.array_equal(bits(yh), bits(oracle.w8a8_mul_mat(wq, ws, x)))
