@@ -98,6 +98,18 @@ def test_down_projection_with_bias_long_k():
     check_group(ws, b, x, 8960)
 
 
+@pytest.mark.parametrize("K", [128, 1536])
+def test_group_of_one_every_fused_variant(K):
+    """A group of one projection runs the single-weight fused kernel: with
+    and without a bias, ragged rows, N = 1..4, every fused variant."""
+    for N in (1, 2, 4):
+        for rows, with_bias in ((70, True), (1, False), (200, True)):
+            ws, b, x = make_group(K + N + rows, [rows], K, N, [with_bias])
+            for var in range(0, i2s.i2s_kernel_variants(3) + 1):
+                check_group(ws, b, x, K, kernel=3, variant=var)
+            check_group(ws, b, x, K)
+
+
 @pytest.mark.parametrize("K", [128, 1152])
 def test_group_every_kernel_and_variant(K):
     shapes = [70, 5, 64, 1]          # rows not a multiple of 4, a single row
