@@ -765,6 +765,38 @@ gemv_fused_group_kernel(const FusedGroup g, int64_t K, const float *__restrict__
   fused_body<NC, L, RPL, CPL, XPT, T>(packed, rows, K, x, K, y, dot, bias, rows, block, qs);
 }
 
+// One of two values, by value (a conditional between two named objects would
+// select between their addresses, here kernel-argument slots in memory).
+template <class T>
+__device__ __forceinline__ T pick(bool c, T a, T b) {
+  return c ? a : b;
+}
+
+// The same for a pair of projections without biases or dot outputs (the
+// decoder layer's gate and up), with every argument plain: the weight
+// pointers, row counts, K, x and the two outputs are the first 14 argument
+// dwords, all preloaded into scalar registers at wave launch, so the
+// activation and weight loads go out at once and no scalar load is waited
+// for anywhere (the table of the general kernel is a struct argument, which
+// is never preloaded, and x and K come after it: gate+up at N = 1 took 4.30
+// us with it, 4.09 with bias and dot pointers read as further arguments,
+// and less without them).  A projection without rows has its workgroups
+// exit at once.
+template <int NC, int L, int RPL, int CPL, int XPT, int T>
+__global__ void __launch_bounds__(T)
+gemv_fused_pair_kernel(const uint8_t *__restrict__ p0, const uint8_t *__restrict__ p1, int r0, int r1, int K,
+                       const float *__restrict__ x, float *y0, float *y1) {
+  extern __shared__ __attribute__((aligned(16))) int8_t qs[];
+  constexpr int64_t kRowsPerBlock = (64 / L) * RPL * (T / 64);
+  const bool second = blockIdx.y != 0;
+  const int64_t block = blockIdx.x;
+  const uint8_t *packed = pick(second, p1, p0);
+  const int64_t rows = pick(second, r1, r0);
+  if (block * kRowsPerBlock >= rows) return;  // the whole workgroup, before any barrier
+  fused_body<NC, L, RPL, CPL, XPT, T>(packed, rows, static_cast<int64_t>(K), x, K, pick(second, y1, y0), nullptr, nullptr,
+                                      rows, block, qs);
+}
+
 // ---------------------------------------------------------------------------
 // GEMM for larger N: int8 MFMA (v_mfma_i32_16x16x64_i8).
 //
@@ -2323,6 +2355,12 @@ int launch_fused_group_cfg(const FusedGroup &g, int64_t K, const float *x, hipSt
   }
   if (widest == 0) return I2S_OK;
   if (widest > kMaxDim) return I2S_ERANGE;
+  if (g.count == 2 && !g.bias[0] && !g.bias[1] && !g.dot[0] && !g.dot[1]) {
+    hipLaunchKernelGGL((gemv_fused_pair_kernel<NC, L, RPL, CPL, XPT, T>), dim3(static_cast<unsigned>(widest), 2u), dim3(T),
+                       static_cast<size_t>(NC * K), stream, g.packed[0], g.packed[1], static_cast<int>(g.rows[0]),
+                       static_cast<int>(g.rows[1]), static_cast<int>(K), x, g.y[0], g.y[1]);
+    return hip_status();
+  }
   hipLaunchKernelGGL((gemv_fused_group_kernel<NC, L, RPL, CPL, XPT, T>),
                      dim3(static_cast<unsigned>(widest), static_cast<unsigned>(g.count)), dim3(T),
                      static_cast<size_t>(NC * K), stream, g, K, x);
