@@ -366,7 +366,7 @@ def bench_layer(args, torch, i2s):
         "wall_s": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
-                     "kernel": "gemv_fused_group_kernel (gate+up)", "kernel_us": round(kern_us, 4),
+                     "kernel": "gemv_fused_pair_kernel (gate+up)", "kernel_us": round(kern_us, 4),
                      "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu:
