@@ -717,11 +717,14 @@ __device__ __forceinline__ void fused_body(const uint8_t *__restrict__ packed, i
   }
 }
 
+// The pointers first and the four sizes as 32-bit values: the 14 argument
+// dwords are all preloaded into scalar registers at wave launch, so no
+// scalar load is waited for before the weight loads (with 64-bit sizes the
+// bias pointer came after the preloaded dwords).
 template <int NC, int L, int RPL, int CPL, int XPT, int T>
 __global__ void __launch_bounds__(T)
-gemv_fused_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
-                  const float *__restrict__ x, int64_t ldx, float *__restrict__ y, int32_t *__restrict__ dot_out,
-                  const float *__restrict__ bias, int64_t ldy) {
+gemv_fused_kernel(const uint8_t *__restrict__ packed, const float *__restrict__ x, float *__restrict__ y,
+                  const float *__restrict__ bias, int32_t *__restrict__ dot_out, int rows, int K, int ldx, int ldy) {
   extern __shared__ __attribute__((aligned(16))) int8_t qs[];
   fused_body<NC, L, RPL, CPL, XPT, T>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, blockIdx.x, qs);
 }
@@ -2288,8 +2291,10 @@ int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float
   constexpr int kRowsPerBlock = (64 / L) * RPL * (T / 64);
   const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (blocks > kMaxDim) return I2S_ERANGE;
+  if (ldx > kMaxDim || ldy > kMaxDim) return I2S_ERANGE;  // the kernel takes 32-bit sizes
   hipLaunchKernelGGL((gemv_fused_kernel<NC, L, RPL, CPL, XPT, T>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(T), static_cast<size_t>(NC * K), stream, packed, rows, K, x, ldx, y, dot_out, bias, ldy);
+                     dim3(T), static_cast<size_t>(NC * K), stream, packed, x, y, bias, dot_out, static_cast<int>(rows),
+                     static_cast<int>(K), static_cast<int>(ldx), static_cast<int>(ldy));
   return hip_status();
 }
 
