@@ -437,10 +437,16 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_of(const void *base, uint32_t by
 
 template <int NC, int L, int RPL, int CPL>
 __global__ void __launch_bounds__(kGemvThreads)
-gemv_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t K,
-            const int8_t *__restrict__ qp, const float *__restrict__ act_scale,
-            const int32_t *__restrict__ row_sum, float *__restrict__ y,
-            int32_t *__restrict__ dot_out, const float *__restrict__ bias, int64_t ldy) {
+gemv_kernel(const uint8_t *__restrict__ packed, const int8_t *__restrict__ qp, const float *__restrict__ act_scale,
+            const int32_t *__restrict__ row_sum, const float *__restrict__ bias, int rows32, int K32, int ldy32,
+            float *__restrict__ y, int32_t *__restrict__ dot_out) {
+  // Argument order: the five pointers and three sizes that the first loads
+  // need fill the 13 leading dwords, which are preloaded into scalar
+  // registers at wave launch; only the output pointers, needed at the stores,
+  // are loaded from the argument segment.  (With 64-bit sizes the bias
+  // pointer came after the preloaded dwords, and every wave waited for its
+  // scalar load before the first weight load.)
+  const int64_t rows = rows32, K = K32, ldy = ldy32;
   constexpr int kSlots = 64 / L;
   constexpr int kRowsPerWave = kSlots * RPL;
   constexpr int kRowsPerBlock = kRowsPerWave * (kGemvThreads / 64);
@@ -2239,9 +2245,10 @@ int launch_gemv_cfg(const uint8_t *packed, int64_t rows, int64_t K, const ActWor
                     float *y, int32_t *dot_out, const float *bias, int64_t ldy, hipStream_t stream) {
   constexpr int kRowsPerBlock = (64 / L) * RPL * (kGemvThreads / 64);
   const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  if (blocks > kMaxDim) return I2S_ERANGE;
+  if (blocks > kMaxDim || rows > kMaxDim || K > kMaxDim || ldy > kMaxDim) return I2S_ERANGE;
   hipLaunchKernelGGL((gemv_kernel<NC, L, RPL, CPL>), dim3(static_cast<unsigned>(blocks)), dim3(kGemvThreads), 0,
-                     stream, packed, rows, K, ws.q, ws.scale, ws.row_sum, y, dot_out, bias, ldy);
+                     stream, packed, ws.q, ws.scale, ws.row_sum, bias, static_cast<int>(rows), static_cast<int>(K),
+                     static_cast<int>(ldy), y, dot_out);
   return hip_status();
 }
 
