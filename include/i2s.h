@@ -167,7 +167,8 @@ int i2s_mul_mat_ws(const uint8_t *packed, int64_t rows, int64_t K, int64_t N,
  * themselves are 16-byte aligned.  workspace >= i2s_act_workspace_bytes(N*B, K).
  * Dense strides run as one i2s_mul_mat of N*B rows; otherwise one quantize
  * launch (or, for N <= 3, one fused launch per batch) and one contraction per
- * batch.  Errors: as i2s_mul_mat, I2S_EINVAL for a bad stride. */
+ * batch.  Errors: as i2s_mul_mat, I2S_EINVAL for a bad stride, I2S_ERANGE for
+ * ldx, ldy or N*B beyond 2^31 - 1. */
 int i2s_mul_mat_batched(const uint8_t *packed, int64_t rows, int64_t K,
                         const float *x, int64_t N, int64_t B, int64_t ldx, int64_t bsx,
                         void *workspace, size_t workspace_bytes,

@@ -87,6 +87,33 @@ def test_mul_mat_ex_host_validation(args, expect):
     assert i2s.lib().i2s_mul_mat_ex(*args, None) == expect
 
 
+def _batched(rows=4, K=128, N=2, B=2, ldx=128, bsx=256, ldy=4, bsy=8, ws_bytes=1 << 20, x=FAKE, y=FAKE):
+    return i2s.lib().i2s_mul_mat_batched(FAKE, rows, K, x, N, B, ldx, bsx, FAKE, ws_bytes, y, ldy, bsy, None, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=-1), i2s.I2S_EINVAL),
+    (dict(B=-1), i2s.I2S_EINVAL),
+    (dict(N=1 << 16, B=1 << 16), i2s.I2S_ERANGE),     # N * B beyond 2^31 - 1
+    (dict(x=None), i2s.I2S_EINVAL),
+    (dict(x=FAKE + 4), i2s.I2S_EINVAL),
+    (dict(ldx=64), i2s.I2S_EINVAL),                  # ldx < K
+    (dict(ldx=130, bsx=260), i2s.I2S_EINVAL),        # activation rows not 16-byte aligned
+    (dict(bsx=258), i2s.I2S_EINVAL),
+    (dict(ldy=3), i2s.I2S_EINVAL),                   # ldy < rows
+    (dict(bsy=7), i2s.I2S_EINVAL),                   # batch outputs would overlap
+    (dict(B=1, bsy=0, ldx=1 << 31, bsx=0), i2s.I2S_ERANGE),   # strides the kernels cannot address
+    (dict(B=1, bsy=0, ldy=1 << 31), i2s.I2S_ERANGE),
+    (dict(ws_bytes=64), i2s.I2S_EWORKSPACE),
+    (dict(K=96, ldx=96, bsx=192), i2s.I2S_EALIGN),
+    (dict(N=0), i2s.I2S_OK),                         # nothing to do, nothing launched
+    (dict(B=0), i2s.I2S_OK),
+])
+def test_batched_host_validation(kw, expect):
+    """The batched entry point's refusals come before any launch."""
+    assert _batched(**kw) == expect
+
+
 def test_mul_mat_host_validation():
     L = i2s.lib()
     assert L.i2s_mul_mat(FAKE, 4, 96, FAKE, 1, FAKE, 1 << 20, FAKE, None, None) == i2s.I2S_EALIGN
