@@ -278,7 +278,10 @@ def test_graph_replay_matches_eager(OC, K, M):
 # (up to 1536, 2048, 4096 and 9216), OC ragged against its 16-, 8- and 4-row
 # workgroups, K not a multiple of 64, and every M from 1 to 4.
 FUSED_SHAPES = [(8960, 1536, 1), (37, 16, 1), (513, 48, 2), (1000, 2048, 3), (257, 4096, 4), (100, 2064, 1),
-                (65, 9216, 2), (1536, 8960, 4), (17, 1552, 3)]
+                (65, 9216, 2), (1536, 8960, 4), (17, 1552, 3),
+                # 48-row workgroups (8192 < OC <= 12288, K <= 1536): a ragged last
+                # workgroup, a short row, exactly 256 workgroups, and just past the range
+                (8193, 1536, 4), (9000, 64, 3), (12288, 1520, 2), (12289, 1536, 1)]
 
 
 def check_fused(wq, ws, x, tag):
