@@ -2315,7 +2315,7 @@ int launch_fused_cfg(const uint8_t *packed, int64_t rows, int64_t K, const float
 // at K = 1536: 3.00 us with variant 7 against 3.21 with variant 6, whose
 // 280 workgroups exceed the compute units; 6144 rows: 2.54 with variant 6
 // against 2.98; 17920 rows: 3.77 against 4.08).
-constexpr int kFusedVariants = 7;
+constexpr int kFusedVariants = 8;
 constexpr int64_t kFusedMaxK = 9216;
 
 int fused_auto_variant(int64_t rows, int64_t K) {
@@ -2323,8 +2323,10 @@ int fused_auto_variant(int64_t rows, int64_t K) {
   if (rows <= 2048) return 3;
   // More than 256 workgroups of 32 rows put a second workgroup on some
   // compute units, whose activation loads then queue behind the first one's
-  // weights; up to 256 workgroups of 48 rows (6 waves) avoid that.
-  if (K <= 1536 && rows > 8192 && rows <= 12288) return 7;
+  // weights; up to 256 workgroups of 48 rows (6 waves) avoid that
+  // (8960 x 1536: 2.84 us against 3.10; 8960 x 2048: 3.16 against 3.38).
+  // With fewer rows the 32-row workgroups fill more of the chip.
+  if (rows > 8192 && rows <= 12288) return K <= 1536 ? 7 : 8;
   return K <= 1536 ? 6 : 2;
 }
 
@@ -2340,6 +2342,7 @@ int launch_fused_nc(int variant, const uint8_t *packed, int64_t rows, int64_t K,
     case 5: return launch_fused_cfg<NC, 32, 1, 5, 9>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     case 6: return launch_fused_cfg<NC, 8, 1, 3, 2>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     case 7: return launch_fused_cfg<NC, 8, 1, 3, 1, 384>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
+    case 8: return launch_fused_cfg<NC, 8, 1, 4, 2, 384>(packed, rows, K, x, ldx, y, dot_out, bias, ldy, stream);
     default: return I2S_EKERNEL;
   }
 }
@@ -2391,6 +2394,7 @@ int launch_fused_group_nc(int variant, const FusedGroup &g, int64_t total_rows, 
     case 5: return launch_fused_group_cfg<NC, 32, 1, 5, 9>(g, K, x, stream);
     case 6: return launch_fused_group_cfg<NC, 8, 1, 3, 2>(g, K, x, stream);
     case 7: return launch_fused_group_cfg<NC, 8, 1, 3, 1, 384>(g, K, x, stream);
+    case 8: return launch_fused_group_cfg<NC, 8, 1, 4, 2, 384>(g, K, x, stream);
     default: return I2S_EKERNEL;
   }
 }

@@ -136,6 +136,10 @@ def test_mul_mat_kernel_choice():
     assert i2s.i2s_mul_mat_kernel(8960, 1536, 1) == i2s.KERNEL_FUSED   # decode: one launch
     assert i2s.i2s_mul_mat_kernel(1536, 8960, 1) == i2s.KERNEL_FUSED   # long K too
     assert i2s.i2s_mul_mat_kernel(1536, 8960, 3) == i2s.KERNEL_FUSED
+    assert i2s.i2s_kernel_variants(3) == 8
+    for rows, K, v in ((8960, 1536, 7), (8960, 2048, 8), (12288, 1664, 8), (8192, 2048, 2), (12289, 2048, 2),
+                       (4096, 1536, 6), (2048, 2048, 3), (1536, 8960, 5)):
+        assert i2s.i2s_mul_mat_variant(rows, K, 1) == v, (rows, K)
     assert i2s.i2s_mul_mat_kernel(1536, 9344, 1) == i2s.KERNEL_GEMV    # beyond the fused K limit
     assert i2s.i2s_mul_mat_kernel(1536, 9344, 2) == i2s.KERNEL_SKINNY
     assert i2s.i2s_mul_mat_kernel(1536, 8960, 4) == i2s.KERNEL_SKINNY
@@ -153,7 +157,7 @@ def test_mul_mat_kernel_choice():
     assert i2s.i2s_mul_mat_variant(8960, 1536, 1) == 7
     assert i2s.i2s_mul_mat_variant(17920, 1536, 1) == 6
     assert i2s.i2s_mul_mat_variant(6144, 1536, 1) == 6
-    assert i2s.i2s_mul_mat_variant(8960, 2048, 1) == 2
+    assert i2s.i2s_mul_mat_variant(8960, 2048, 1) == 8   # 48-row workgroups
     assert i2s.i2s_mul_mat_variant(1536, 1536, 1) == 3
     assert i2s.i2s_mul_mat_variant(1536, 8960, 1) == 5
     with pytest.raises(i2s.I2SError):

@@ -229,7 +229,7 @@ def test_grid_all_kernels_and_variants(K):
 
 
 # Longest K of each fused configuration (64 * lanes per row * chunk batches).
-FUSED_MAX_K = {1: 1536, 2: 2048, 3: 2048, 4: 12288, 5: 10240, 6: 1536, 7: 1536}
+FUSED_MAX_K = {1: 1536, 2: 2048, 3: 2048, 4: 12288, 5: 10240, 6: 1536, 7: 1536, 8: 2048}
 
 
 @pytest.mark.parametrize("N", [1, 2, 4])
@@ -247,6 +247,17 @@ def test_all_fused_variants_decode_shapes(N):
                     i2s.i2s_mul_mat_ex(pg, rows, K, dev(case.x), kernel=3, variant=v)
                 continue
             check_mul_mat(case, kernel=3, variant=v, packed_gpu=pg, packed_np=pnp, expected=exp)
+
+
+@pytest.mark.parametrize("rows,K,N", [(8960, 2048, 1), (8200, 1664, 3), (12288, 2048, 2), (12289, 1920, 1),
+                                        (8193, 2048, 3)])
+def test_fused_48_row_range(rows, K, N):
+    """The automatic fused choice for 8192 < rows <= 12288 at 1536 < K <= 2048
+    (48-row workgroups; a ragged last one at 8200 and 8193 rows, exactly 256 at
+    12288) and just past it, every output against the oracle."""
+    assert i2s.i2s_mul_mat_variant(rows, K, N) == (8 if rows <= 12288 else 2)
+    case = workloads.random_case(29 + N, rows, K, N)
+    check_mul_mat(case)
 
 
 @pytest.mark.parametrize("N", [1, 3, 8])
